@@ -1,0 +1,10 @@
+"""fp64 CPU oracle for fused linear cross-entropy (test infrastructure only).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s ``cpu_baseline``
+leg may import this package.  It shares no code with the HIP library.
+"""
+from .flce_ref import (IGNORE_INDEX, Result, dW_rows, dX_rows, flce, forward_rows,
+                   loss_blocked)
+
+__all__ = ["IGNORE_INDEX", "Result", "flce", "forward_rows", "loss_blocked",
+           "dX_rows", "dW_rows"]
