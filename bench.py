@@ -1,0 +1,216 @@
+#!/usr/bin/env python3
+"""Benchmark: chunked fused linear cross-entropy, forward + backward, one MI355X.
+
+One step is one ``flce_fwd_bwd`` call over the whole workload (every chunk:
+forward tile GEMM + log-sum-exp epilogue, combine, in-place dlogits, dX GEMM,
+dW GEMM, final loss, and the call's stream synchronisation), with inputs
+already resident in HBM.  The default workload is the Llama-3-8B LM head
+(N = 8192 tokens = 8 x 1024, H = 4096, V = 128256, bf16 inputs, fp32
+accumulation and fp32 dW, 5% of labels ignored, chunks of 1024 tokens).
+
+FLOPs are counted as 6 N H V per step (three GEMMs of 2 N H V each).
+
+Printed: one JSON line on stdout.  ``roofline`` describes the kernel class
+with the largest total time, from HIP events recorded around each launch on
+the launch stream during the timed steps; ``cpu_baseline`` times the fp64
+oracle on a bounded sample of the same workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+METRIC = "FLCE fwd+bwd tokens/s and TFLOP/s (% bf16 MFMA peak), Llama-3-8B head"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_work(name, chunks, H, V, ldz):
+    """Algorithmic work of one kernel class summed over a step's launches.
+
+    Returns (bound, amount, unit): flops for the GEMMs, bytes for the rest."""
+    if name in ("fwd_tile", "dx_gemm"):
+        return "mfma", sum(2.0 * c * H * V for c in chunks), "flop"
+    if name == "dw_gemm":
+        # fp32 dW read-modify-write (store only on the first chunk) + G + X reads
+        b = sum((4.0 if i == 0 else 8.0) * V * H + 2.0 * c * V + 2.0 * c * H
+                for i, c in enumerate(chunks))
+        return "hbm", b, "byte"
+    if name == "dlogits":
+        return "hbm", sum(4.0 * c * ldz for c in chunks), "byte"
+    if name == "dx_reduce":
+        return "hbm", None, "byte"
+    return "hbm", None, "byte"
+
+
+def cpu_baseline(inp, n_tok):
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"), default=1)
+    except Exception:       # pragma: no cover - informational only
+        threads = os.cpu_count() or 1
+    X = inp.X_f64()[:n_tok]
+    W = inp.W_f64()
+    y = inp.labels[:n_tok]
+    t0 = time.perf_counter()
+    oracle.flce(X, W, y)
+    dt = time.perf_counter() - t0
+    return {"value": n_tok / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "seconds": round(dt, 3),
+            "sample": f"first {n_tok} tokens of the {inp.wl.name} workload (H={inp.wl.H}, "
+                      f"V={inp.wl.V}), fp64 loss + dX + dW on the host"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=1, help="workload id (datagen.WORKLOADS)")
+    ap.add_argument("--chunk", type=int, default=None, help="chunk tokens (default: the workload's)")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=192)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the multi-GPU "
+              "sharding of this path is a design only)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import datagen
+    import linear_cross_entropy_04_amd as fl
+
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    inp = datagen.make(args.workload)
+    wl = inp.wl
+    log(f"workload {wl.name}: N={wl.N} H={wl.H} V={wl.V} drawn in {time.time() - t0:.1f}s")
+    N, H, V = wl.N, wl.H, wl.V
+    chunk = wl.chunk_tokens if args.chunk is None else args.chunk
+    dt = fl.FLCE_BF16 if wl.dtype == "bf16" else fl.FLCE_F32
+    st, C, peak_scratch = fl.flce_plan(N, H, V, dt, chunk_tokens=chunk)
+    if st != fl.FLCE_OK:
+        raise fl.FLCEError(st, "flce_plan")
+
+    if wl.dtype == "bf16":
+        X = torch.from_numpy(inp.X.view(np.int16)).to(dev).view(torch.bfloat16)
+        W = torch.from_numpy(inp.W.view(np.int16)).to(dev).view(torch.bfloat16)
+    else:
+        X = torch.from_numpy(inp.X).to(dev)
+        W = torch.from_numpy(inp.W).to(dev)
+    y = torch.from_numpy(inp.labels).to(dev)
+    dX = torch.empty_like(X)
+    dW = torch.empty((V, H), dtype=torch.float32, device=dev)
+    ws = fl.workspace(N, H, V, dt, chunk, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        return fl.flce_fwd_bwd(X, W, y, -100, chunk, dX, dW, ws, stream=stream)
+
+    for _ in range(args.warmup):
+        loss = step()
+    torch.cuda.synchronize()
+
+    # timed steps, with per-kernel events on the launch stream
+    fl.flce_profile_enable(True)
+    fl.flce_profile_read()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        loss = step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    prof = fl.flce_profile_read()
+    fl.flce_profile_enable(False)
+
+    # the same steps without events, to show what the event records cost
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed_noev = time.perf_counter() - t1
+
+    ms = 1e3 * elapsed / args.steps
+    flops = 6.0 * N * H * V
+    tflops = flops / (ms * 1e-3) / 1e12
+    chunks = [min(C, N - c0) for c0 in range(0, N, C)]
+    ldz = (V + 7) // 8 * 8 if dt == fl.FLCE_BF16 else (V + 3) // 4 * 4
+
+    kernels = {}
+    for name, (tot, n) in prof.items():
+        if n == 0:
+            continue
+        steps_n = n / args.steps
+        avg = tot / n
+        bound, amount, unit = kernel_work(name, chunks, H, V, ldz)
+        k = {"avg_ms": round(avg, 5), "launches_per_step": steps_n,
+             "ms_per_step": round(tot / args.steps, 4)}
+        if amount is not None:
+            per_launch = amount / steps_n
+            if unit == "flop":
+                k["tflops"] = round(per_launch / (avg * 1e-3) / 1e12, 2)
+            else:
+                k["gbps"] = round(per_launch / (avg * 1e-3) / 1e9, 1)
+        kernels[name] = k
+    dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
+    bound, amount, unit = kernel_work(dom, chunks, H, V, ldz)
+    if amount is not None and unit == "flop":
+        ach = kernels[dom]["tflops"]
+        roof = {"kernel": dom, "bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None}
+    else:
+        ach = kernels[dom].get("gbps")
+        roof = {"kernel": dom, "bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4) if ach else None,
+                "traffic": None}
+
+    out = {
+        "metric": METRIC,
+        "value": round(N / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded; X ~ N(0,1), W ~ N(0,0.02^2), uniform labels, 5% ignored)",
+        "config": {"workload": wl.name, "N": N, "H": H, "V": V, "chunk_tokens": C,
+                   "ignored_tokens": int((inp.labels == -100).sum()),
+                   "peak_scratch_bytes": peak_scratch},
+        "tflops": round(tflops, 2),
+        "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        "ms_per_step_without_events": round(1e3 * elapsed_noev / args.steps, 4),
+        "loss": loss,
+        "kernels": kernels,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        log(f"cpu baseline: oracle on {args.cpu_sample_tokens} tokens ...")
+        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_sample_tokens)
+    else:
+        out["cpu_baseline"] = None
+    log(f"{ms:.3f} ms/step  {tflops:.1f} TFLOP/s  ({out['pct_bf16_peak']:.1f}% of bf16 peak)  "
+        f"loss={loss:.6f}")
+    for name, k in kernels.items():
+        log(f"  {name:12s} {k}")
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,157 @@
+/*
+ * flce.h - C ABI of libflce: chunked fused linear cross-entropy on gfx950.
+ *
+ * The operation (Liger Kernel pages: the ms-swift blog page, mechanism
+ * paragraph, describes fused linear cross entropy as the last linear layer
+ * merged with the cross-entropy loss; the project overview page, "Método de
+ * API de Baixo Nível", calls it as loss_fn(weight, input, target) with
+ * weight = nn.Linear(H, V).weight):
+ *
+ *     Z       = X W^T                                  [N, V], never stored whole
+ *     loss    = (1 / N_valid) * sum_{i: y_i != ii} (logsumexp(Z_i) - Z_{i, y_i})
+ *     G       = (softmax(Z) - onehot(y)) / N_valid     (0 on ignored rows)
+ *     dX      = G W        dW = G^T X
+ *
+ * The work runs over consecutive chunks of tokens (overview page, "Computação
+ * em Chunk"), so scratch memory is bounded by the chunk size, not by N x V.
+ * Within a chunk the logits are rewritten in place into G (overview page,
+ * "Operações In-Place").  The result is exact up to floating-point rounding
+ * (overview page, "Implementação Técnica").
+ *
+ * Conventions for every entry point:
+ *   - All arrays are row-major and contiguous: X [N, H], W [V, H], dX [N, H],
+ *     dW [V, H], labels [N].
+ *   - "device" pointers are HIP device memory of the current device; "host"
+ *     pointers are ordinary host memory.  The caller owns every buffer; the
+ *     library allocates no device memory.  The workspace is a caller-provided
+ *     device buffer of at least flce_workspace_bytes(...) bytes, 256-byte
+ *     aligned; its contents on entry do not matter.
+ *   - stream is a hipStream_t (NULL = the default stream).  All device work is
+ *     enqueued on it.  flce_fwd_bwd and flce_fwd synchronise the stream once,
+ *     at the end, to return the loss and the label check.
+ *   - Argument errors are detected on the host before any device work and
+ *     return FLCE_EINVAL / FLCE_EUNSUPPORTED / FLCE_EWORKSPACE; outputs are
+ *     then untouched.  Errors are never thrown across the ABI.
+ *   - Calls that share a workspace must not overlap in time.
+ */
+#ifndef FLCE_H
+#define FLCE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FLCE_OK = 0,
+  FLCE_EINVAL = 1,       /* bad argument: null pointer, negative size, unknown dtype, misalignment */
+  FLCE_ELABEL = 2,       /* a label is neither ignore_index nor in [0, V); outputs unspecified */
+  FLCE_EWORKSPACE = 3,   /* workspace_bytes < flce_workspace_bytes(...) */
+  FLCE_EHIP = 4,         /* a HIP call failed; see flce_last_error() */
+  FLCE_EUNSUPPORTED = 5  /* valid but unsupported shape (bf16 needs H % 8 == 0 and 16-byte aligned X, W, dX) */
+} flce_status;
+
+typedef enum {
+  FLCE_F32 = 0,          /* X, W, dX in fp32; scratch in fp32 */
+  FLCE_BF16 = 1          /* X, W, dX in bf16; fp32 accumulation; logits/dlogits scratch in bf16 */
+} flce_dtype;
+
+/* Default scratch budget used when chunk_tokens <= 0 (auto): 1.5 GiB. */
+#define FLCE_DEFAULT_SCRATCH_BUDGET ((size_t)3 << 29)
+
+/*
+ * Bytes of workspace a call with these sizes needs (scratch for one chunk:
+ * logits/dlogits [C, V], per-vocab-tile log-sum-exp partials, per-token
+ * statistics, and the split-K partial sums of dX).  chunk_tokens <= 0 means
+ * "auto" (as chosen by flce_plan with the default budget); chunk_tokens > N is
+ * clamped to N.  Returns 0 for invalid sizes or dtype.  Host only; no device
+ * call.
+ */
+size_t flce_workspace_bytes(int64_t N, int64_t H, int64_t V, int dtype, int64_t chunk_tokens);
+
+/*
+ * Choose the chunk size.  On entry *chunk_tokens is the requested chunk
+ * (<= 0: choose the largest power-of-two multiple of 256 tokens, at most N,
+ * whose workspace fits scratch_budget_bytes; 0 budget = the default).  On
+ * return *chunk_tokens holds the chunk that will be used and
+ * *peak_scratch_bytes (may be NULL) the workspace it needs, which is the
+ * peak device scratch of a call.  Host only; no device call.
+ */
+int flce_plan(int64_t N, int64_t H, int64_t V, int dtype, size_t scratch_budget_bytes,
+              int64_t *chunk_tokens, size_t *peak_scratch_bytes);
+
+/*
+ * Forward and backward in one call.
+ *   X          device [N, H] (dtype)        read only
+ *   W          device [V, H] (dtype)        read only
+ *   labels     device [N] int64             read only; ignore_index marks ignored tokens
+ *   loss       host   float                 mean loss over valid tokens (0 if none)
+ *   dX         device [N, H] (dtype)        overwritten with dLoss/dX (rows of ignored tokens are 0)
+ *   dW         device [V, H] fp32           overwritten with dLoss/dW (not accumulated into)
+ *   row_loss   device [N] fp32 or NULL      per-token loss lse_i - z_{i,y_i} (0 if ignored)
+ *   row_lse    device [N] fp32 or NULL      per-token log-sum-exp of the logits row
+ *   workspace  device scratch, workspace_bytes long
+ * N == 0 is allowed: loss = 0 and dW = 0.
+ */
+int flce_fwd_bwd(const void *X, const void *W, const int64_t *labels,
+                 int64_t N, int64_t H, int64_t V, int dtype,
+                 int64_t ignore_index, int64_t chunk_tokens,
+                 float *loss, void *dX, float *dW,
+                 float *row_loss, float *row_lse,
+                 void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Forward only: the loss (and optional per-token outputs) without gradients.
+ * Arguments as for flce_fwd_bwd.  Needs no more workspace than flce_fwd_bwd.
+ */
+int flce_fwd(const void *X, const void *W, const int64_t *labels,
+             int64_t N, int64_t H, int64_t V, int dtype,
+             int64_t ignore_index, int64_t chunk_tokens,
+             float *loss, float *row_loss, float *row_lse,
+             void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * buf[i] *= *scale for i < n, in place, on the stream (no sync).  buf is a
+ * device array of dtype (FLCE_F32 or FLCE_BF16); scale is a device fp32
+ * scalar.  Used to apply an upstream gradient d(out)/d(loss) != 1 to dX, dW.
+ */
+int flce_scale_inplace(void *buf, int64_t n, int dtype, const float *scale, void *stream);
+
+/*
+ * Per-kernel timing.  While enabled (process-wide), every kernel that
+ * flce_fwd_bwd / flce_fwd launch is bracketed by a pair of HIP events on the
+ * call's stream.  flce_profile_read waits for the recorded events, writes the
+ * summed milliseconds and the launch count of each kernel class k < n
+ * (FLCE_K_*) into ms[k] and launches[k] (either may be NULL), and clears the
+ * records.  Both return FLCE_OK or FLCE_EHIP.
+ */
+enum {
+  FLCE_K_LABELS = 0,      /* label check and N_valid */
+  FLCE_K_FWD_TILE = 1,    /* forward GEMM tile + log-sum-exp epilogue */
+  FLCE_K_LSE_COMBINE = 2, /* combine of the per-tile partials */
+  FLCE_K_DLOGITS = 3,     /* in-place rewrite of logits into dlogits */
+  FLCE_K_DX_GEMM = 4,     /* dX split-K GEMM */
+  FLCE_K_DX_REDUCE = 5,   /* dX split-K reduction */
+  FLCE_K_DW_GEMM = 6,     /* dW GEMM */
+  FLCE_K_FINAL = 7,       /* final mean loss, fills */
+  FLCE_K_COUNT = 8
+};
+int flce_profile_enable(int enable);
+int flce_profile_read(double *ms, int64_t *launches, int n);
+
+/* Static name of a kernel class (FLCE_K_*), "" if out of range. */
+const char *flce_kernel_name(int k);
+
+/* Static text for a status code. */
+const char *flce_status_string(int status);
+
+/* Text of the last FLCE_EHIP error raised on the calling thread ("" if none). */
+const char *flce_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLCE_H */

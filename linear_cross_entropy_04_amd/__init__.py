@@ -1,0 +1,274 @@
+"""Chunked fused linear cross-entropy for AMD MI355X (gfx950).
+
+Python binding of ``libflce.so`` (declared in ``include/flce.h``): argument
+marshalling only.  Every step of the computation runs in the library's HIP
+kernels; there is no Python or CPU fallback, and a missing library raises.
+
+The operation is the one the Liger Kernel pages call as
+``loss_fn(weight, input, target)`` (project overview page, "Método de API de
+Baixo Nível"): the LM-head projection fused with mean cross-entropy over
+tokens whose target is not ``ignore_index``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "FLCE_F32", "FLCE_BF16", "FLCEError", "flce_workspace_bytes", "flce_plan", "flce_fwd_bwd",
+    "flce_fwd", "flce_scale_inplace", "flce_status_string", "flce_last_error", "lib_path",
+    "flce_profile_enable", "flce_profile_read",
+    "workspace", "loss", "FusedLinearCrossEntropyLoss",
+]
+
+FLCE_F32 = 0
+FLCE_BF16 = 1
+FLCE_OK, FLCE_EINVAL, FLCE_ELABEL, FLCE_EWORKSPACE, FLCE_EHIP, FLCE_EUNSUPPORTED = range(6)
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libflce.so")
+_lib = None
+
+_p, _i64, _i32, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+
+
+class FLCEError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        msg = f"{where}: {flce_status_string(status)} (status {status})"
+        if status == FLCE_EHIP:
+            msg += f": {flce_last_error()}"
+        super().__init__(msg)
+        self.status = status
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is not built; run `python -m "
+                          "linear_cross_entropy_04_amd.build_lib` (or __graft_entry__.build())")
+    l = ctypes.CDLL(_LIB_PATH)
+    l.flce_workspace_bytes.argtypes = [_i64, _i64, _i64, _i32, _i64]
+    l.flce_workspace_bytes.restype = _sz
+    l.flce_plan.argtypes = [_i64, _i64, _i64, _i32, _sz, ctypes.POINTER(_i64),
+                            ctypes.POINTER(_sz)]
+    l.flce_plan.restype = _i32
+    l.flce_fwd_bwd.argtypes = [_p, _p, _p, _i64, _i64, _i64, _i32, _i64, _i64,
+                               ctypes.POINTER(ctypes.c_float), _p, _p, _p, _p, _p, _sz, _p]
+    l.flce_fwd_bwd.restype = _i32
+    l.flce_fwd.argtypes = [_p, _p, _p, _i64, _i64, _i64, _i32, _i64, _i64,
+                           ctypes.POINTER(ctypes.c_float), _p, _p, _p, _sz, _p]
+    l.flce_fwd.restype = _i32
+    l.flce_scale_inplace.argtypes = [_p, _i64, _i32, _p, _p]
+    l.flce_scale_inplace.restype = _i32
+    l.flce_status_string.argtypes = [_i32]
+    l.flce_status_string.restype = ctypes.c_char_p
+    l.flce_last_error.argtypes = []
+    l.flce_last_error.restype = ctypes.c_char_p
+    l.flce_profile_enable.argtypes = [_i32]
+    l.flce_profile_enable.restype = _i32
+    l.flce_profile_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i64), _i32]
+    l.flce_profile_read.restype = _i32
+    l.flce_kernel_name.argtypes = [_i32]
+    l.flce_kernel_name.restype = ctypes.c_char_p
+    _lib = l
+    return l
+
+
+def flce_status_string(status: int) -> str:
+    return _load().flce_status_string(int(status)).decode()
+
+
+def flce_last_error() -> str:
+    return _load().flce_last_error().decode()
+
+
+KERNEL_CLASSES = 8
+
+
+def flce_profile_enable(enable: bool = True) -> None:
+    """Turn per-kernel event timing on or off (process-wide)."""
+    _load().flce_profile_enable(1 if enable else 0)
+
+
+def flce_profile_read() -> dict:
+    """{kernel class name: (summed ms, launches)} since the last read; clears."""
+    ms = (ctypes.c_double * KERNEL_CLASSES)()
+    n = (_i64 * KERNEL_CLASSES)()
+    st = _load().flce_profile_read(ms, n, KERNEL_CLASSES)
+    if st != FLCE_OK:
+        raise FLCEError(st, "flce_profile_read")
+    return {_load().flce_kernel_name(k).decode(): (float(ms[k]), int(n[k]))
+            for k in range(KERNEL_CLASSES)}
+
+
+def flce_workspace_bytes(N: int, H: int, V: int, dtype: int, chunk_tokens: int = 0) -> int:
+    return int(_load().flce_workspace_bytes(N, H, V, dtype, chunk_tokens))
+
+
+def flce_plan(N: int, H: int, V: int, dtype: int, scratch_budget_bytes: int = 0,
+              chunk_tokens: int = 0) -> tuple[int, int, int]:
+    """Returns (status, chunk_tokens, peak_scratch_bytes)."""
+    c = _i64(chunk_tokens)
+    peak = _sz(0)
+    st = _load().flce_plan(N, H, V, dtype, scratch_budget_bytes, ctypes.byref(c), ctypes.byref(peak))
+    return int(st), int(c.value), int(peak.value)
+
+
+# ------------------------------------------------------------------ marshalling
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return FLCE_BF16
+    if t.dtype == torch.float32:
+        return FLCE_F32
+    raise ValueError(f"unsupported dtype {t.dtype}; expected bfloat16 or float32")
+
+
+def _dev(t, name, dtype=None, shape=None):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise ValueError(f"{name} must be a HIP device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream, device):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def workspace(N: int, H: int, V: int, dtype: int, chunk_tokens: int = 0, device=None) -> torch.Tensor:
+    """A device workspace of the size flce_workspace_bytes reports."""
+    nbytes = flce_workspace_bytes(N, H, V, dtype, chunk_tokens)
+    if nbytes == 0:
+        raise FLCEError(FLCE_EINVAL, "flce_workspace_bytes")
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def flce_fwd_bwd(X: torch.Tensor, W: torch.Tensor, labels: torch.Tensor, ignore_index: int,
+                 chunk_tokens: int, dX: torch.Tensor, dW: torch.Tensor, workspace: torch.Tensor,
+                 stream=None, row_loss: torch.Tensor | None = None,
+                 row_lse: torch.Tensor | None = None) -> float:
+    """Call libflce's flce_fwd_bwd on device tensors; returns the loss."""
+    N, H = X.shape
+    V = W.shape[0]
+    dt = _dtype_code(X)
+    _dev(X, "X")
+    _dev(W, "W", X.dtype, (V, H))
+    _dev(labels, "labels", torch.int64, (N,))
+    _dev(dX, "dX", X.dtype, (N, H))
+    _dev(dW, "dW", torch.float32, (V, H))
+    _dev(workspace, "workspace")
+    _dev(row_loss, "row_loss", torch.float32, (N,))
+    _dev(row_lse, "row_lse", torch.float32, (N,))
+    loss = ctypes.c_float(0.0)
+    st = _load().flce_fwd_bwd(_ptr(X), _ptr(W), _ptr(labels), N, H, V, dt, ignore_index,
+                              chunk_tokens, ctypes.byref(loss), _ptr(dX), _ptr(dW),
+                              _ptr(row_loss), _ptr(row_lse), _ptr(workspace),
+                              workspace.numel(), _stream(stream, X.device))
+    if st != FLCE_OK:
+        raise FLCEError(st, "flce_fwd_bwd")
+    return float(loss.value)
+
+
+def flce_fwd(X: torch.Tensor, W: torch.Tensor, labels: torch.Tensor, ignore_index: int,
+             chunk_tokens: int, workspace: torch.Tensor, stream=None,
+             row_loss: torch.Tensor | None = None, row_lse: torch.Tensor | None = None) -> float:
+    """Call libflce's flce_fwd on device tensors; returns the loss."""
+    N, H = X.shape
+    V = W.shape[0]
+    dt = _dtype_code(X)
+    _dev(X, "X")
+    _dev(W, "W", X.dtype, (V, H))
+    _dev(labels, "labels", torch.int64, (N,))
+    _dev(workspace, "workspace")
+    _dev(row_loss, "row_loss", torch.float32, (N,))
+    _dev(row_lse, "row_lse", torch.float32, (N,))
+    loss = ctypes.c_float(0.0)
+    st = _load().flce_fwd(_ptr(X), _ptr(W), _ptr(labels), N, H, V, dt, ignore_index,
+                          chunk_tokens, ctypes.byref(loss), _ptr(row_loss), _ptr(row_lse),
+                          _ptr(workspace), workspace.numel(), _stream(stream, X.device))
+    if st != FLCE_OK:
+        raise FLCEError(st, "flce_fwd")
+    return float(loss.value)
+
+
+def flce_scale_inplace(buf: torch.Tensor, scale: torch.Tensor, stream=None) -> None:
+    """buf *= scale (a one-element fp32 device tensor), in place, on the stream."""
+    _dev(buf, "buf")
+    _dev(scale, "scale", torch.float32)
+    if scale.numel() != 1:
+        raise ValueError("scale must hold one element")
+    st = _load().flce_scale_inplace(_ptr(buf), buf.numel(), _dtype_code(buf), _ptr(scale),
+                                    _stream(stream, buf.device))
+    if st != FLCE_OK:
+        raise FLCEError(st, "flce_scale_inplace")
+
+
+# ------------------------------------------------------------------ autograd
+
+class _FLCEFunction(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, weight, input, target, ignore_index, chunk_tokens):
+        N, H = input.shape
+        V = weight.shape[0]
+        dt = _dtype_code(input)
+        ws = workspace(N, H, V, dt, chunk_tokens, device=input.device)
+        need = ctx.needs_input_grad[0] or ctx.needs_input_grad[1]
+        if need:
+            dX = torch.empty_like(input)
+            dW = torch.empty((V, H), dtype=torch.float32, device=input.device)
+            val = flce_fwd_bwd(input, weight, target, ignore_index, chunk_tokens, dX, dW, ws)
+            ctx.save_for_backward(dX, dW)
+        else:
+            val = flce_fwd(input, weight, target, ignore_index, chunk_tokens, ws)
+        ctx.wdtype = weight.dtype
+        return torch.tensor(val, dtype=torch.float32, device=input.device)
+
+    @staticmethod
+    def backward(ctx, grad_out):
+        dX, dW = ctx.saved_tensors
+        g = grad_out.detach().to(torch.float32).reshape(1).contiguous()
+        flce_scale_inplace(dX, g)
+        flce_scale_inplace(dW, g)
+        gw = dW if ctx.wdtype == torch.float32 else dW.to(ctx.wdtype)
+        return gw, dX, None, None, None
+
+
+def loss(weight: torch.Tensor, input: torch.Tensor, target: torch.Tensor,
+         ignore_index: int = -100, chunk_tokens: int = 0) -> torch.Tensor:
+    """Mean cross-entropy of input @ weight.T against target, fused and chunked.
+
+    weight [V, H], input [N, H] (both bf16 or both fp32, contiguous, on the
+    GPU), target [N] int64.  Gradients flow to weight and input."""
+    return _FLCEFunction.apply(weight, input, target, ignore_index, chunk_tokens)
+
+
+class FusedLinearCrossEntropyLoss(torch.nn.Module):
+    """Module form of :func:`loss`: ``loss_fn(weight, input, target)``."""
+
+    def __init__(self, ignore_index: int = -100, chunk_tokens: int = 0):
+        super().__init__()
+        self.ignore_index = ignore_index
+        self.chunk_tokens = chunk_tokens
+
+    def forward(self, weight, input, target):
+        return loss(weight, input, target, self.ignore_index, self.chunk_tokens)

@@ -1,0 +1,381 @@
+// libflce: C ABI, argument validation, chunk planner and the per-chunk launch
+// sequence of the chunked fused linear cross-entropy (see include/flce.h).
+//
+// Per chunk of c <= C consecutive tokens (the overview page of Liger Kernel,
+// "Computação em Chunk", splits memory-heavy work into chunks to cut peak
+// memory), all on the caller's stream:
+//   1. forward tile GEMM  Z_c^T = W X_c^T, per (token, vocab tile) max and
+//      sum-exp partials, target logit, Z_c stored to scratch (bf16 or fp32);
+//   2. combine partials -> lse, per-token loss;
+//   3. rewrite Z_c in place into G_c = (softmax - onehot) / N_valid (the
+//      page's "Operações In-Place");
+//   4. dX_c = G_c W;
+//   5. dW  (+)= G_c^T X_c (the first chunk stores).
+// Before the chunks a label pass counts N_valid and checks label ranges; after
+// them one kernel forms the mean loss, which returns to the host with the
+// label flag in the call's single stream synchronisation.
+#include <algorithm>
+#include <atomic>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/flce.h"
+#include "flce_internal.h"
+
+#define FLCE_API extern "C" __attribute__((visibility("default")))
+
+namespace flce {
+namespace {
+
+thread_local std::string g_last_error;
+
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline int64_t round_up(int64_t a, int64_t b) { return cdiv(a, b) * b; }
+
+// Shape limits that keep every in-kernel offset within 32-bit ranges.
+constexpr int64_t kMaxV = 8000000;
+constexpr int64_t kMaxH = 1 << 20;
+constexpr int64_t kMaxN = (int64_t)1 << 40;
+
+int check_sizes(int64_t N, int64_t H, int64_t V, int dtype) {
+  if (dtype != FLCE_F32 && dtype != FLCE_BF16) return FLCE_EINVAL;
+  if (N < 0 || H <= 0 || V <= 0) return FLCE_EINVAL;
+  if (V > kMaxV || H > kMaxH || N > kMaxN) return FLCE_EUNSUPPORTED;
+  if (dtype == FLCE_BF16 && (H % 8) != 0) return FLCE_EUNSUPPORTED;
+  return FLCE_OK;
+}
+
+// Largest power-of-two multiple of 256 tokens (capped at N) whose workspace
+// fits the budget; -1 if even the smallest does not fit.
+int64_t auto_chunk(int64_t N, int64_t H, int64_t V, int dtype, size_t budget) {
+  if (N <= 0) return 0;
+  int64_t best = -1;
+  for (int64_t C = 256;; C *= 2) {
+    const int64_t Cc = std::min(C, N);
+    Plan p;
+    make_plan(N, H, V, dtype, Cc, &p);
+    if (p.total > budget) break;
+    best = Cc;
+    if (C >= N) break;
+  }
+  return best;
+}
+
+int64_t resolve_chunk(int64_t N, int64_t H, int64_t V, int dtype, int64_t req, size_t budget,
+                      bool *fits) {
+  *fits = true;
+  if (N <= 0) return 0;
+  if (req > 0) return std::min(req, N);
+  const int64_t c = auto_chunk(N, H, V, dtype, budget ? budget : FLCE_DEFAULT_SCRATCH_BUDGET);
+  if (c > 0) return c;
+  *fits = false;
+  return std::min<int64_t>(256, N);
+}
+
+int hip_fail(hipError_t e, const char *what) {
+  g_last_error = std::string(what) + ": " + hipGetErrorString(e);
+  return FLCE_EHIP;
+}
+
+#define CK(x)                                           \
+  do {                                                  \
+    hipError_t e_ = (x);                                \
+    if (e_ != hipSuccess) return hip_fail(e_, #x);      \
+  } while (0)
+
+bool misaligned(const void *p, uintptr_t a) { return ((uintptr_t)p % a) != 0; }
+
+// ---------------------------------------------------------------- kernel timing
+struct Profiler {
+  std::atomic<bool> on{false};
+  std::mutex mu;
+  struct Rec {
+    int cls;
+    hipEvent_t a, b;
+  };
+  std::vector<Rec> recs;
+  std::vector<hipEvent_t> pool;
+
+  hipError_t take(hipEvent_t *e) {
+    if (!pool.empty()) {
+      *e = pool.back();
+      pool.pop_back();
+      return hipSuccess;
+    }
+    return hipEventCreate(e);
+  }
+};
+
+Profiler &prof() {
+  static Profiler p;
+  return p;
+}
+
+// Run one launcher; while timing is on, bracket it with events on stream s.
+template <class F>
+hipError_t timed(int cls, hipStream_t s, F &&launch) {
+  Profiler &P = prof();
+  if (!P.on.load(std::memory_order_relaxed)) return launch();
+  hipEvent_t a, b;
+  {
+    std::lock_guard<std::mutex> g(P.mu);
+    hipError_t e = P.take(&a);
+    if (e != hipSuccess) return e;
+    e = P.take(&b);
+    if (e != hipSuccess) return e;
+  }
+  hipError_t e = hipEventRecord(a, s);
+  if (e != hipSuccess) return e;
+  e = launch();
+  if (e != hipSuccess) return e;
+  e = hipEventRecord(b, s);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> g(P.mu);
+  P.recs.push_back({cls, a, b});
+  return hipSuccess;
+}
+
+#define LAUNCH(cls, call) CK(timed(cls, s, [&]() { return (call); }))
+
+int run(bool bwd, const void *X, const void *W, const int64_t *labels, int64_t N, int64_t H,
+        int64_t V, int dtype, int64_t ii, int64_t chunk_tokens, float *loss, void *dX, float *dW,
+        float *row_loss, float *row_lse, void *workspace, size_t workspace_bytes, void *stream) {
+  int st = check_sizes(N, H, V, dtype);
+  if (st != FLCE_OK) return st;
+  if (!loss || !W || !workspace) return FLCE_EINVAL;
+  if (N > 0 && (!X || !labels)) return FLCE_EINVAL;
+  if (bwd && (!dW || (N > 0 && !dX))) return FLCE_EINVAL;
+  if (misaligned(workspace, 256)) return FLCE_EINVAL;
+  if (dtype == FLCE_BF16 && (misaligned(X, 16) || misaligned(W, 16) || (bwd && misaligned(dX, 16))))
+    return FLCE_EUNSUPPORTED;
+  if (dtype == FLCE_F32 && (misaligned(X, 4) || misaligned(W, 4) || (bwd && misaligned(dX, 4))))
+    return FLCE_EINVAL;
+  if (misaligned(labels, 8) || (bwd && misaligned(dW, 4))) return FLCE_EINVAL;
+
+  bool fits;
+  const int64_t C = resolve_chunk(N, H, V, dtype, chunk_tokens, 0, &fits);
+  Plan p;
+  make_plan(N, H, V, dtype, C, &p);
+  if (workspace_bytes < p.total) return FLCE_EWORKSPACE;
+
+  hipStream_t s = (hipStream_t)stream;
+  char *ws = (char *)workspace;
+  Scalars *sc = (Scalars *)(ws + p.off_scal);
+  float *pm = (float *)(ws + p.off_pm);
+  float *ps = (float *)(ws + p.off_ps);
+  float *zy = (float *)(ws + p.off_zy);
+  float *lse = (float *)(ws + p.off_lse);
+  float *rowloss = row_loss ? row_loss : (float *)(ws + p.off_rowloss);
+  const int Hi = (int)H, Vi = (int)V;
+
+  LAUNCH(FLCE_K_LABELS, launch_label_check(labels, N, V, ii, sc, s));
+  if (bwd && N == 0) LAUNCH(FLCE_K_FINAL, launch_fill_f32(dW, V * H, 0.f, s));
+
+  for (int64_t c0 = 0; c0 < N; c0 += C) {
+    const int c = (int)std::min(C, N - c0);
+    const int64_t *lab = labels + c0;
+    float *rl = rowloss + c0;
+    float *rs = row_lse ? row_lse + c0 : nullptr;
+    if (dtype == FLCE_BF16) {
+      const uint16_t *Wb = (const uint16_t *)W;
+      const uint16_t *Xc = (const uint16_t *)X + c0 * H;
+      uint16_t *z = (uint16_t *)(ws + p.off_z);
+      LAUNCH(FLCE_K_FWD_TILE, launch_fwd_tile_bf16(Wb, Xc, lab, ii, c, Hi, Vi, z, p.ldz, pm, ps, zy, p.nvt, bwd, s));
+      LAUNCH(FLCE_K_LSE_COMBINE, launch_lse_combine(pm, ps, zy, lab, ii, c, p.nvt, lse, rl, rs, s));
+      if (bwd) {
+        LAUNCH(FLCE_K_DLOGITS, launch_dlogits_bf16(z, p.ldz, c, Vi, lse, lab, ii, sc, s));
+        float *dxp = (float *)(ws + p.off_dxp);
+        LAUNCH(FLCE_K_DX_GEMM, launch_dx_bf16(z, p.ldz, Wb, c, Hi, Vi, p.splitk, p.ksplit, dxp, s));
+        LAUNCH(FLCE_K_DX_REDUCE,
+               launch_dx_reduce_bf16(dxp, p.splitk, c, Hi, (uint16_t *)dX + c0 * H, s));
+        LAUNCH(FLCE_K_DW_GEMM, launch_dw_bf16(z, p.ldz, Xc, c, Hi, Vi, dW, c0 > 0, s));
+      }
+    } else {
+      const float *Wf = (const float *)W;
+      const float *Xc = (const float *)X + c0 * H;
+      float *z = (float *)(ws + p.off_z);
+      LAUNCH(FLCE_K_FWD_TILE, launch_fwd_tile_f32(Wf, Xc, lab, ii, c, Hi, Vi, z, p.ldz, pm, ps, zy, p.nvt, bwd, s));
+      LAUNCH(FLCE_K_LSE_COMBINE, launch_lse_combine(pm, ps, zy, lab, ii, c, p.nvt, lse, rl, rs, s));
+      if (bwd) {
+        LAUNCH(FLCE_K_DLOGITS, launch_dlogits_f32(z, p.ldz, c, Vi, lse, lab, ii, sc, s));
+        LAUNCH(FLCE_K_DX_GEMM, launch_dx_f32(z, p.ldz, Wf, c, Hi, Vi, (float *)dX + c0 * H, s));
+        LAUNCH(FLCE_K_DW_GEMM, launch_dw_f32(z, p.ldz, Xc, c, Hi, Vi, dW, c0 > 0, s));
+      }
+    }
+  }
+  LAUNCH(FLCE_K_FINAL, launch_final_loss(rowloss, N, sc, s));
+  float host[2];
+  CK(hipMemcpyAsync(host, sc, sizeof(host), hipMemcpyDeviceToHost, s));
+  CK(hipStreamSynchronize(s));
+  int flag;
+  std::memcpy(&flag, &host[1], sizeof(flag));
+  if (flag) return FLCE_ELABEL;
+  *loss = host[0];
+  return FLCE_OK;
+}
+
+}  // namespace
+
+int choose_splitk(int64_t C, int64_t H, int64_t V) {
+  // Spread the dX GEMM's few output tiles over the 256 CUs: pick the split
+  // count that fills whole waves of 256 workgroups, at least two of them,
+  // with every split at least 1024 vocabulary rows deep.
+  const int64_t tiles = cdiv(C, 256) * cdiv(H, 256);
+  double best = -1.0;
+  int bestS = 1;
+  for (int S = 1; S <= kMaxSplitK; ++S) {
+    if (S > 1 && V / S < 1024) break;
+    const int64_t units = tiles * S;
+    const int64_t waves = cdiv(units, 256);
+    const double eff = (double)units / (double)(waves * 256);
+    const double fill = std::min(1.0, (double)units / 512.0);
+    const double score = eff * fill - 0.001 * S;
+    if (score > best + 1e-12) {
+      best = score;
+      bestS = S;
+    }
+  }
+  return bestS;
+}
+
+void make_plan(int64_t N, int64_t H, int64_t V, int dtype, int64_t C, Plan *p) {
+  const bool bf = dtype == FLCE_BF16;
+  const int64_t esz = bf ? 2 : 4;
+  p->dtype = dtype;
+  p->N = N;
+  p->H = H;
+  p->V = V;
+  p->C = C;
+  p->ldz = bf ? round_up(V, 8) : round_up(V, 4);
+  p->nvt = cdiv(V, bf ? kTileVBf16 : kTileVF32);
+  if (bf && C > 0) {
+    int S = choose_splitk(C, H, V);
+    p->ksplit = round_up(cdiv(V, S), 64);
+    p->splitk = (int)cdiv(V, p->ksplit);
+  } else {
+    p->splitk = 0;
+    p->ksplit = 0;
+  }
+  size_t o = 0;
+  p->off_scal = o;
+  o += 256;
+  p->off_z = o;
+  o += align256((size_t)C * p->ldz * esz);
+  p->off_pm = o;
+  o += align256((size_t)C * p->nvt * 4);
+  p->off_ps = o;
+  o += align256((size_t)C * p->nvt * 4);
+  p->off_zy = o;
+  o += align256((size_t)C * 4);
+  p->off_lse = o;
+  o += align256((size_t)C * 4);
+  p->off_rowloss = o;
+  o += align256((size_t)N * 4);
+  p->off_dxp = o;
+  o += align256((size_t)p->splitk * C * H * 4);
+  p->total = o;
+}
+
+}  // namespace flce
+
+using namespace flce;
+
+FLCE_API size_t flce_workspace_bytes(int64_t N, int64_t H, int64_t V, int dtype,
+                                     int64_t chunk_tokens) {
+  if (check_sizes(N, H, V, dtype) != FLCE_OK) return 0;
+  bool fits;
+  const int64_t C = resolve_chunk(N, H, V, dtype, chunk_tokens, 0, &fits);
+  Plan p;
+  make_plan(N, H, V, dtype, C, &p);
+  return p.total;
+}
+
+FLCE_API int flce_plan(int64_t N, int64_t H, int64_t V, int dtype, size_t scratch_budget_bytes,
+                       int64_t *chunk_tokens, size_t *peak_scratch_bytes) {
+  const int st = check_sizes(N, H, V, dtype);
+  if (st != FLCE_OK) return st;
+  if (!chunk_tokens) return FLCE_EINVAL;
+  bool fits;
+  const int64_t C = resolve_chunk(N, H, V, dtype, *chunk_tokens, scratch_budget_bytes, &fits);
+  Plan p;
+  make_plan(N, H, V, dtype, C, &p);
+  *chunk_tokens = C;
+  if (peak_scratch_bytes) *peak_scratch_bytes = p.total;
+  return fits ? FLCE_OK : FLCE_EWORKSPACE;
+}
+
+FLCE_API int flce_fwd_bwd(const void *X, const void *W, const int64_t *labels, int64_t N,
+                          int64_t H, int64_t V, int dtype, int64_t ignore_index,
+                          int64_t chunk_tokens, float *loss, void *dX, float *dW, float *row_loss,
+                          float *row_lse, void *workspace, size_t workspace_bytes, void *stream) {
+  return run(true, X, W, labels, N, H, V, dtype, ignore_index, chunk_tokens, loss, dX, dW,
+             row_loss, row_lse, workspace, workspace_bytes, stream);
+}
+
+FLCE_API int flce_fwd(const void *X, const void *W, const int64_t *labels, int64_t N, int64_t H,
+                      int64_t V, int dtype, int64_t ignore_index, int64_t chunk_tokens,
+                      float *loss, float *row_loss, float *row_lse, void *workspace,
+                      size_t workspace_bytes, void *stream) {
+  return run(false, X, W, labels, N, H, V, dtype, ignore_index, chunk_tokens, loss, nullptr,
+             nullptr, row_loss, row_lse, workspace, workspace_bytes, stream);
+}
+
+FLCE_API int flce_scale_inplace(void *buf, int64_t n, int dtype, const float *scale,
+                                void *stream) {
+  if (dtype != FLCE_F32 && dtype != FLCE_BF16) return FLCE_EINVAL;
+  if (n < 0 || !scale || (n > 0 && !buf)) return FLCE_EINVAL;
+  CK(launch_scale(buf, n, dtype, scale, (hipStream_t)stream));
+  return FLCE_OK;
+}
+
+FLCE_API int flce_profile_enable(int enable) {
+  prof().on.store(enable != 0);
+  return FLCE_OK;
+}
+
+FLCE_API int flce_profile_read(double *ms, int64_t *launches, int n) {
+  Profiler &P = prof();
+  std::lock_guard<std::mutex> g(P.mu);
+  for (int k = 0; k < n; ++k) {
+    if (ms) ms[k] = 0.0;
+    if (launches) launches[k] = 0;
+  }
+  int st = FLCE_OK;
+  for (auto &r : P.recs) {
+    float t = 0.f;
+    hipError_t e = hipEventSynchronize(r.b);
+    if (e == hipSuccess) e = hipEventElapsedTime(&t, r.a, r.b);
+    if (e != hipSuccess && st == FLCE_OK) st = hip_fail(e, "flce_profile_read");
+    if (r.cls >= 0 && r.cls < n) {
+      if (ms) ms[r.cls] += t;
+      if (launches) launches[r.cls] += 1;
+    }
+    P.pool.push_back(r.a);
+    P.pool.push_back(r.b);
+  }
+  P.recs.clear();
+  return st;
+}
+
+FLCE_API const char *flce_kernel_name(int k) {
+  static const char *names[FLCE_K_COUNT] = {"label_check", "fwd_tile", "lse_combine", "dlogits",
+                                            "dx_gemm", "dx_reduce", "dw_gemm", "final"};
+  return (k >= 0 && k < FLCE_K_COUNT) ? names[k] : "";
+}
+
+FLCE_API const char *flce_status_string(int status) {
+  switch (status) {
+    case FLCE_OK: return "ok";
+    case FLCE_EINVAL: return "invalid argument";
+    case FLCE_ELABEL: return "label outside [0, V) that is not ignore_index";
+    case FLCE_EWORKSPACE: return "workspace too small";
+    case FLCE_EHIP: return "HIP runtime error";
+    case FLCE_EUNSUPPORTED: return "unsupported shape or alignment";
+    default: return "unknown status";
+  }
+}
+
+FLCE_API const char *flce_last_error(void) { return g_last_error.c_str(); }

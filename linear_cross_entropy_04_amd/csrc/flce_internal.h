@@ -1,0 +1,83 @@
+// Internal declarations of libflce: the chunk plan and the kernel launchers.
+// Not part of the ABI (see include/flce.h for that).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+namespace flce {
+
+// Vocabulary tile width of the log-sum-exp partials: 256 on the bf16 MFMA
+// path (one workgroup tile), 64 on the fp32 path.
+constexpr int kTileVBf16 = 256;
+constexpr int kTileVF32 = 64;
+constexpr int kMaxSplitK = 32;
+
+// Device-side scalars kept in the workspace.  loss and flag sit first so a
+// single 8-byte copy returns both to the host.
+struct Scalars {
+  float loss;        // final mean loss
+  int flag;          // 1 if a label was neither ignore_index nor in [0, V)
+  int nvalid;        // number of non-ignored labels
+  float inv_nvalid;  // 1 / max(nvalid, 1)
+};
+
+// Sizes and workspace layout of one call.
+struct Plan {
+  int dtype = 0;
+  int64_t N = 0, H = 0, V = 0;
+  int64_t C = 0;        // tokens per chunk (last chunk may be shorter)
+  int64_t ldz = 0;      // leading dimension (elements) of the chunk logits scratch
+  int64_t nvt = 0;      // vocabulary tiles = log-sum-exp partials per token
+  int splitk = 0;       // K-splits of the dX GEMM (0: the fp32 path writes dX directly)
+  int64_t ksplit = 0;   // vocabulary rows per split (multiple of 64)
+  size_t off_z = 0, off_pm = 0, off_ps = 0, off_zy = 0, off_lse = 0, off_rowloss = 0,
+         off_dxp = 0, off_scal = 0, total = 0;
+};
+
+// Fill *p for the given sizes and chunk (C >= 1, C <= N or N == 0).
+void make_plan(int64_t N, int64_t H, int64_t V, int dtype, int64_t C, Plan *p);
+// Number of dX K-splits chosen for a chunk of C tokens.
+int choose_splitk(int64_t C, int64_t H, int64_t V);
+
+// ---------------------------------------------------------------- common kernels
+hipError_t launch_label_check(const int64_t *labels, int64_t N, int64_t V, int64_t ii,
+                              Scalars *sc, hipStream_t s);
+hipError_t launch_lse_combine(const float *pm, const float *ps, const float *zy,
+                              const int64_t *labels_c, int64_t ii, int c, int64_t nvt,
+                              float *lse_c, float *rowloss_c, float *rowlse_c, hipStream_t s);
+hipError_t launch_final_loss(const float *rowloss, int64_t N, Scalars *sc, hipStream_t s);
+hipError_t launch_fill_f32(float *p, int64_t n, float v, hipStream_t s);
+hipError_t launch_scale(void *buf, int64_t n, int dtype, const float *scale, hipStream_t s);
+
+// ---------------------------------------------------------------- bf16 path (MFMA)
+hipError_t launch_fwd_tile_bf16(const uint16_t *W, const uint16_t *Xc, const int64_t *labels_c,
+                                int64_t ii, int c, int H, int V, uint16_t *zbuf, int64_t ldz,
+                                float *pm, float *ps, float *zy, int64_t nvt, bool store_z,
+                                hipStream_t s);
+hipError_t launch_dlogits_bf16(uint16_t *zbuf, int64_t ldz, int c, int V, const float *lse_c,
+                               const int64_t *labels_c, int64_t ii, const Scalars *sc,
+                               hipStream_t s);
+hipError_t launch_dx_bf16(const uint16_t *G, int64_t ldz, const uint16_t *W, int c, int H, int V,
+                          int splitk, int64_t ksplit, float *dxp, hipStream_t s);
+hipError_t launch_dx_reduce_bf16(const float *dxp, int splitk, int c, int H, uint16_t *dXc,
+                                 hipStream_t s);
+hipError_t launch_dw_bf16(const uint16_t *G, int64_t ldz, const uint16_t *Xc, int c, int H, int V,
+                          float *dW, bool accumulate, hipStream_t s);
+
+// ---------------------------------------------------------------- fp32 path (SIMT)
+hipError_t launch_fwd_tile_f32(const float *W, const float *Xc, const int64_t *labels_c,
+                               int64_t ii, int c, int H, int V, float *zbuf, int64_t ldz,
+                               float *pm, float *ps, float *zy, int64_t nvt, bool store_z,
+                               hipStream_t s);
+hipError_t launch_dlogits_f32(float *zbuf, int64_t ldz, int c, int V, const float *lse_c,
+                              const int64_t *labels_c, int64_t ii, const Scalars *sc,
+                              hipStream_t s);
+hipError_t launch_dx_f32(const float *G, int64_t ldz, const float *W, int c, int H, int V,
+                         float *dXc, hipStream_t s);
+hipError_t launch_dw_f32(const float *G, int64_t ldz, const float *Xc, int c, int H, int V,
+                         float *dW, bool accumulate, hipStream_t s);
+
+}  // namespace flce

@@ -1,0 +1,161 @@
+// Small kernels shared by both precisions: the label pre-pass, the
+// log-sum-exp combine over vocabulary tiles, the final mean, fills, scaling.
+// All reductions use a fixed order, so results are bitwise reproducible.
+#include "flce_internal.h"
+
+namespace flce {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// N_valid = #{i : y_i != ii}; flag if a valid label lies outside [0, V).
+// One workgroup of 1024 threads.
+__global__ __launch_bounds__(1024) void label_check_kernel(const int64_t *__restrict__ labels,
+                                                           int64_t N, int64_t V, int64_t ii,
+                                                           Scalars *__restrict__ sc) {
+  __shared__ int s_cnt[16], s_bad[16];
+  int cnt = 0, bad = 0;
+  for (int64_t i = threadIdx.x; i < N; i += 1024) {
+    const int64_t y = labels[i];
+    if (y != ii) {
+      ++cnt;
+      bad |= (y < 0 || y >= V) ? 1 : 0;
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    cnt += __shfl_xor(cnt, o);
+    bad |= __shfl_xor(bad, o);
+  }
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    s_cnt[w] = cnt;
+    s_bad[w] = bad;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int c = 0, b = 0;
+    for (int q = 0; q < 16; ++q) {
+      c += s_cnt[q];
+      b |= s_bad[q];
+    }
+    sc->nvalid = c;
+    sc->inv_nvalid = 1.0f / (float)(c > 0 ? c : 1);
+    sc->flag = b;
+    sc->loss = 0.f;
+  }
+}
+
+// One wave per token: lse = M + ln sum_t s_t exp(m_t - M) over the token's
+// vocabulary-tile partials (m_t = tile max, s_t = sum of exp(z - m_t)).
+__global__ __launch_bounds__(256) void lse_combine_kernel(
+    const float *__restrict__ pm, const float *__restrict__ ps, const float *__restrict__ zy,
+    const int64_t *__restrict__ labels_c, int64_t ii, int c, int64_t nvt, float *__restrict__ lse_c,
+    float *__restrict__ rowloss_c, float *__restrict__ rowlse_c) {
+  const int tok = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (tok >= c) return;
+  const float *m = pm + (int64_t)tok * nvt;
+  const float *s = ps + (int64_t)tok * nvt;
+  float M = -INFINITY;
+  for (int64_t t = lane; t < nvt; t += 64) M = fmaxf(M, m[t]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+  float S = 0.f;
+  for (int64_t t = lane; t < nvt; t += 64) S += s[t] * __builtin_amdgcn_exp2f((m[t] - M) * kLog2e);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) S += __shfl_xor(S, o);
+  if (lane == 0) {
+    const float lse = M + __builtin_amdgcn_logf(S) * kLn2;
+    const int64_t y = labels_c[tok];
+    lse_c[tok] = lse;
+    rowloss_c[tok] = (y != ii) ? lse - zy[tok] : 0.f;
+    if (rowlse_c) rowlse_c[tok] = lse;
+  }
+}
+
+// loss = sum_i rowloss_i / max(N_valid, 1), summed in fp64 in a fixed tree.
+__global__ __launch_bounds__(1024) void final_loss_kernel(const float *__restrict__ rowloss,
+                                                          int64_t N, Scalars *__restrict__ sc) {
+  __shared__ double part[1024];
+  double acc = 0.0;
+  for (int64_t i = threadIdx.x; i < N; i += 1024) acc += (double)rowloss[i];
+  part[threadIdx.x] = acc;
+  __syncthreads();
+  for (int o = 512; o > 0; o >>= 1) {
+    if ((int)threadIdx.x < o) part[threadIdx.x] += part[threadIdx.x + o];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const int nv = sc->nvalid;
+    sc->loss = (float)(part[0] / (double)(nv > 0 ? nv : 1));
+  }
+}
+
+__global__ void fill_f32_kernel(float *__restrict__ p, int64_t n, float v) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = v;
+}
+
+__global__ void scale_f32_kernel(float *__restrict__ p, int64_t n, const float *__restrict__ sc) {
+  const float a = *sc;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    p[i] *= a;
+}
+
+__global__ void scale_bf16_kernel(uint16_t *__restrict__ p, int64_t n, const float *__restrict__ sc) {
+  const float a = *sc;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const float x = __builtin_bit_cast(float, (uint32_t)p[i] << 16) * a;
+    p[i] = __builtin_bit_cast(uint16_t, (__bf16)x);
+  }
+}
+
+inline int grid_for(int64_t n, int block, int cap) {
+  int64_t g = (n + block - 1) / block;
+  if (g < 1) g = 1;
+  return (int)(g < cap ? g : cap);
+}
+
+}  // namespace
+
+hipError_t launch_label_check(const int64_t *labels, int64_t N, int64_t V, int64_t ii,
+                              Scalars *sc, hipStream_t s) {
+  hipLaunchKernelGGL(label_check_kernel, dim3(1), dim3(1024), 0, s, labels, N, V, ii, sc);
+  return hipGetLastError();
+}
+
+hipError_t launch_lse_combine(const float *pm, const float *ps, const float *zy,
+                              const int64_t *labels_c, int64_t ii, int c, int64_t nvt,
+                              float *lse_c, float *rowloss_c, float *rowlse_c, hipStream_t s) {
+  hipLaunchKernelGGL(lse_combine_kernel, dim3((c + 3) / 4), dim3(256), 0, s, pm, ps, zy, labels_c,
+                     ii, c, nvt, lse_c, rowloss_c, rowlse_c);
+  return hipGetLastError();
+}
+
+hipError_t launch_final_loss(const float *rowloss, int64_t N, Scalars *sc, hipStream_t s) {
+  hipLaunchKernelGGL(final_loss_kernel, dim3(1), dim3(1024), 0, s, rowloss, N, sc);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_f32(float *p, int64_t n, float v, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(fill_f32_kernel, dim3(grid_for(n, 256, 256 * 64)), dim3(256), 0, s, p, n, v);
+  return hipGetLastError();
+}
+
+hipError_t launch_scale(void *buf, int64_t n, int dtype, const float *scale, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int g = grid_for(n, 256, 256 * 64);
+  if (dtype == 0)
+    hipLaunchKernelGGL(scale_f32_kernel, dim3(g), dim3(256), 0, s, (float *)buf, n, scale);
+  else
+    hipLaunchKernelGGL(scale_bf16_kernel, dim3(g), dim3(256), 0, s, (uint16_t *)buf, n, scale);
+  return hipGetLastError();
+}
+
+}  // namespace flce

@@ -1,0 +1,149 @@
+"""libflce's C ABI on the host: exported symbols, argument validation, planner.
+
+None of these make a device call: validation happens before any HIP call,
+so fake (never dereferenced) pointers are enough.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import linear_cross_entropy_04_amd as fl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "flce.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fl.lib_path()):
+        from linear_cross_entropy_04_amd import build_lib
+        build_lib.build()
+    return fl._load()
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(flce_\w+)\s*\(", text)))
+
+
+def test_header_declares_abi():
+    names = _declared()
+    for n in ("flce_fwd_bwd", "flce_fwd", "flce_plan", "flce_workspace_bytes",
+              "flce_status_string", "flce_scale_inplace", "flce_last_error"):
+        assert n in names
+
+
+def test_exports_match_header(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", fl.lib_path()], stdout=subprocess.PIPE,
+                         text=True, check=True).stdout
+    exported = sorted(set(re.findall(r"\bT (flce_\w+)", out)))
+    assert exported == _declared()
+    for n in _declared():
+        assert hasattr(lib, n)
+
+
+FAKE = ctypes.c_void_p(0x100000)        # 256-aligned, never dereferenced
+FAKE_ODD = ctypes.c_void_p(0x100008)
+
+
+def _fwd_bwd(lib, X=FAKE, W=FAKE, labels=FAKE, N=16, H=64, V=100, dt=fl.FLCE_BF16, chunk=0,
+             loss=True, dX=FAKE, dW=FAKE, ws=FAKE, ws_bytes=1 << 40):
+    lv = ctypes.c_float(0)
+    return lib.flce_fwd_bwd(X, W, labels, N, H, V, dt, -100, chunk,
+                            ctypes.byref(lv) if loss else None, dX, dW, None, None, ws,
+                            ws_bytes, None)
+
+
+def test_validation_codes(lib):
+    assert _fwd_bwd(lib, dt=7) == fl.FLCE_EINVAL
+    assert _fwd_bwd(lib, N=-1) == fl.FLCE_EINVAL
+    assert _fwd_bwd(lib, H=0) == fl.FLCE_EINVAL
+    assert _fwd_bwd(lib, V=0) == fl.FLCE_EINVAL
+    assert _fwd_bwd(lib, loss=False) == fl.FLCE_EINVAL
+    assert _fwd_bwd(lib, X=None) == fl.FLCE_EINVAL
+    assert _fwd_bwd(lib, W=None) == fl.FLCE_EINVAL
+    assert _fwd_bwd(lib, labels=None) == fl.FLCE_EINVAL
+    assert _fwd_bwd(lib, dX=None) == fl.FLCE_EINVAL
+    assert _fwd_bwd(lib, dW=None) == fl.FLCE_EINVAL
+    assert _fwd_bwd(lib, ws=None) == fl.FLCE_EINVAL
+    assert _fwd_bwd(lib, ws=FAKE_ODD) == fl.FLCE_EINVAL
+    assert _fwd_bwd(lib, H=12) == fl.FLCE_EUNSUPPORTED            # bf16 needs H % 8 == 0
+    assert _fwd_bwd(lib, X=FAKE_ODD) == fl.FLCE_EUNSUPPORTED      # bf16 needs 16-byte rows
+    assert _fwd_bwd(lib, V=9_000_000) == fl.FLCE_EUNSUPPORTED
+    need = fl.flce_workspace_bytes(16, 64, 100, fl.FLCE_BF16, 0)
+    assert _fwd_bwd(lib, ws_bytes=need - 1) == fl.FLCE_EWORKSPACE
+    # fp32 accepts any H
+    need32 = fl.flce_workspace_bytes(16, 12, 100, fl.FLCE_F32, 0)
+    assert need32 > 0
+    assert _fwd_bwd(lib, H=12, dt=fl.FLCE_F32, ws_bytes=need32 - 1) == fl.FLCE_EWORKSPACE
+
+
+def test_fwd_validation(lib):
+    lv = ctypes.c_float(0)
+    st = lib.flce_fwd(FAKE, FAKE, FAKE, 16, 64, 100, fl.FLCE_BF16, -100, 0, ctypes.byref(lv),
+                      None, None, FAKE, 10, None)
+    assert st == fl.FLCE_EWORKSPACE
+    st = lib.flce_fwd(FAKE, FAKE, FAKE, 16, 64, 100, 3, -100, 0, ctypes.byref(lv), None, None,
+                      FAKE, 1 << 40, None)
+    assert st == fl.FLCE_EINVAL
+
+
+def test_scale_validation(lib):
+    assert lib.flce_scale_inplace(FAKE, 10, 5, FAKE, None) == fl.FLCE_EINVAL
+    assert lib.flce_scale_inplace(FAKE, -1, 0, FAKE, None) == fl.FLCE_EINVAL
+    assert lib.flce_scale_inplace(FAKE, 10, 0, None, None) == fl.FLCE_EINVAL
+
+
+def test_status_strings(lib):
+    for s in range(6):
+        assert fl.flce_status_string(s) and fl.flce_status_string(s) != "unknown status"
+    assert fl.flce_status_string(99) == "unknown status"
+    assert fl.flce_last_error() == ""
+
+
+def test_workspace_bounded_by_chunk_not_N():
+    # Llama-3-8B head, long context: scratch grows with the chunk, not with N.
+    H, V = 4096, 128256
+    a = fl.flce_workspace_bytes(16384, H, V, fl.FLCE_BF16, 1024)
+    b = fl.flce_workspace_bytes(16384 * 4, H, V, fl.FLCE_BF16, 1024)
+    assert b - a == pytest.approx(16384 * 3 * 4, abs=512)     # only the per-token loss array grows
+    sizes = [fl.flce_workspace_bytes(16384, H, V, fl.FLCE_BF16, c) for c in (512, 1024, 4096)]
+    assert sizes[0] < sizes[1] < sizes[2]
+    for c, s in zip((512, 1024, 4096), sizes):
+        assert s >= c * V * 2                                  # the bf16 logits chunk
+        assert s < c * V * 2 * 2.2                             # plus partials and split-K sums
+    full_logits = 16384 * V * 2
+    assert sizes[1] < full_logits / 8
+
+
+def test_plan_auto_and_explicit():
+    st, c, peak = fl.flce_plan(8192, 2304, 256000, fl.FLCE_BF16)      # large-vocabulary head
+    assert st == fl.FLCE_OK and c == 2048
+    assert peak == fl.flce_workspace_bytes(8192, 2304, 256000, fl.FLCE_BF16, 0)
+    assert peak <= 3 << 29
+    st, c, peak = fl.flce_plan(8192, 4096, 128256, fl.FLCE_BF16, chunk_tokens=1024)
+    assert st == fl.FLCE_OK and c == 1024
+    assert peak == fl.flce_workspace_bytes(8192, 4096, 128256, fl.FLCE_BF16, 1024)
+    st, c, _ = fl.flce_plan(100, 64, 1000, fl.FLCE_BF16, chunk_tokens=5000)
+    assert st == fl.FLCE_OK and c == 100                                  # clamped to N
+    st, c, _ = fl.flce_plan(100, 64, 1000, fl.FLCE_BF16)
+    assert st == fl.FLCE_OK and c == 100
+    st, c, _ = fl.flce_plan(8192, 4096, 128256, fl.FLCE_BF16, scratch_budget_bytes=1 << 20)
+    assert st == fl.FLCE_EWORKSPACE and c == 256                          # smallest chunk reported
+    st, c, _ = fl.flce_plan(8192, 4096, 128256, fl.FLCE_BF16, scratch_budget_bytes=600 << 20)
+    assert st == fl.FLCE_OK and c == 1024
+    st, c, peak = fl.flce_plan(0, 64, 100, fl.FLCE_BF16)
+    assert st == fl.FLCE_OK and c == 0 and peak > 0
+
+
+def test_binding_has_no_cpu_fallback():
+    import torch
+    X = torch.zeros(4, 8, dtype=torch.bfloat16)
+    W = torch.zeros(16, 8, dtype=torch.bfloat16)
+    y = torch.zeros(4, dtype=torch.int64)
+    with pytest.raises(ValueError):
+        fl.flce_fwd(X, W, y, -100, 0, torch.zeros(1024, dtype=torch.uint8))
