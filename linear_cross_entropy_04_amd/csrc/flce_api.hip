@@ -250,7 +250,7 @@ void make_plan(int64_t N, int64_t H, int64_t V, int dtype, int64_t C, Plan *p) {
   p->V = V;
   p->C = C;
   p->ldz = bf ? round_up(V, 8) : round_up(V, 4);
-  p->nvt = cdiv(V, bf ? kTileVBf16 : kTileVF32);
+  p->nvt = bf ? 2 * cdiv(V, kTileVBf16) : cdiv(V, kTileVF32);
   if (bf && C > 0) {
     int S = choose_splitk(C, H, V);
     p->ksplit = round_up(cdiv(V, S), 64);

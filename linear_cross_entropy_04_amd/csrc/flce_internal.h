@@ -9,8 +9,8 @@
 
 namespace flce {
 
-// Vocabulary tile width of the log-sum-exp partials: 256 on the bf16 MFMA
-// path (one workgroup tile), 64 on the fp32 path.
+// Vocabulary width of one log-sum-exp partial: 128 on the bf16 MFMA path (one
+// wave's half of a 256-row workgroup tile; 2 per tile), 64 on the fp32 path.
 constexpr int kTileVBf16 = 256;
 constexpr int kTileVF32 = 64;
 constexpr int kMaxSplitK = 32;
