@@ -80,6 +80,9 @@ def main():
     ap.add_argument("--chunk", type=int, default=None, help="chunk tokens (default: the workload's)")
     ap.add_argument("--cpu-sample-tokens", type=int, default=192)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-reference-mib", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (a known-size "
+                         "reference for hardware byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -115,6 +118,15 @@ def main():
     dW = torch.empty((V, H), dtype=torch.float32, device=dev)
     ws = fl.workspace(N, H, V, dt, chunk, device=dev)
     stream = torch.cuda.current_stream(dev)
+
+    if args.copy_reference_mib:
+        src = torch.empty(args.copy_reference_mib << 18, dtype=torch.float32, device=dev)
+        src.fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     def step():
         return fl.flce_fwd_bwd(X, W, y, -100, chunk, dX, dW, ws, stream=stream)

@@ -58,8 +58,8 @@ typedef enum {
   FLCE_BF16 = 1          /* X, W, dX in bf16; fp32 accumulation; logits/dlogits scratch in bf16 */
 } flce_dtype;
 
-/* Default scratch budget used when chunk_tokens <= 0 (auto): 1.5 GiB. */
-#define FLCE_DEFAULT_SCRATCH_BUDGET ((size_t)3 << 29)
+/* Default scratch budget used when chunk_tokens <= 0 (auto): 3 GiB. */
+#define FLCE_DEFAULT_SCRATCH_BUDGET ((size_t)3 << 30)
 
 /*
  * Bytes of workspace a call with these sizes needs (scratch for one chunk:
@@ -136,7 +136,8 @@ enum {
   FLCE_K_DX_REDUCE = 5,   /* dX split-K reduction */
   FLCE_K_DW_GEMM = 6,     /* dW GEMM */
   FLCE_K_FINAL = 7,       /* final mean loss, fills */
-  FLCE_K_COUNT = 8
+  FLCE_K_PACK = 8,        /* per-chunk packing of X into the GEMM operand layouts */
+  FLCE_K_COUNT = 9
 };
 int flce_profile_enable(int enable);
 int flce_profile_read(double *ms, int64_t *launches, int n);

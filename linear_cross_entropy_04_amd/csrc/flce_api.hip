@@ -182,16 +182,23 @@ int run(bool bwd, const void *X, const void *W, const int64_t *labels, int64_t N
     if (dtype == FLCE_BF16) {
       const uint16_t *Wb = (const uint16_t *)W;
       const uint16_t *Xc = (const uint16_t *)X + c0 * H;
-      uint16_t *z = (uint16_t *)(ws + p.off_z);
-      LAUNCH(FLCE_K_FWD_TILE, launch_fwd_tile_bf16(Wb, Xc, lab, ii, c, Hi, Vi, z, p.ldz, pm, ps, zy, p.nvt, bwd, s));
+      uint16_t *Zp = (uint16_t *)(ws + p.off_z);
+      uint16_t *GTp = (uint16_t *)(ws + p.off_gt);
+      uint16_t *Xp = (uint16_t *)(ws + p.off_xp);
+      uint16_t *XTp = (uint16_t *)(ws + p.off_xtp);
+      LAUNCH(FLCE_K_PACK, launch_pack_x_bf16(Xc, c, Hi, Xp, p.nks_h, XTp, p.nks_c, s));
+      LAUNCH(FLCE_K_FWD_TILE, launch_fwd_tile_bf16(Wb, Xp, p.nks_h, lab, ii, c, Hi, Vi, Zp,
+                                                   p.nks_z, pm, ps, zy, p.nvt, bwd, s));
       LAUNCH(FLCE_K_LSE_COMBINE, launch_lse_combine(pm, ps, zy, lab, ii, c, p.nvt, lse, rl, rs, s));
       if (bwd) {
-        LAUNCH(FLCE_K_DLOGITS, launch_dlogits_bf16(z, p.ldz, c, Vi, lse, lab, ii, sc, s));
+        LAUNCH(FLCE_K_DLOGITS, launch_dlogits_bf16(Zp, p.nks_z, GTp, p.nks_c, c, Vi, lse, lab,
+                                                   ii, sc, s));
         float *dxp = (float *)(ws + p.off_dxp);
-        LAUNCH(FLCE_K_DX_GEMM, launch_dx_bf16(z, p.ldz, Wb, c, Hi, Vi, p.splitk, p.ksplit, dxp, s));
+        LAUNCH(FLCE_K_DX_GEMM, launch_dx_bf16(Zp, p.nks_z, Wb, c, Hi, Vi, p.splitk, p.ksplit,
+                                              dxp, s));
         LAUNCH(FLCE_K_DX_REDUCE,
                launch_dx_reduce_bf16(dxp, p.splitk, c, Hi, (uint16_t *)dX + c0 * H, s));
-        LAUNCH(FLCE_K_DW_GEMM, launch_dw_bf16(z, p.ldz, Xc, c, Hi, Vi, dW, c0 > 0, s));
+        LAUNCH(FLCE_K_DW_GEMM, launch_dw_bf16(GTp, XTp, p.nks_c, c, Hi, Vi, dW, c0 > 0, s));
       }
     } else {
       const float *Wf = (const float *)W;
@@ -262,8 +269,25 @@ void make_plan(int64_t N, int64_t H, int64_t V, int dtype, int64_t C, Plan *p) {
   size_t o = 0;
   p->off_scal = o;
   o += 256;
-  p->off_z = o;
-  o += align256((size_t)C * p->ldz * esz);
+  if (bf) {
+    // packed layouts: rows padded to 256, k to 32 (see flce_internal.h)
+    p->nks_z = cdiv(V, 32);
+    p->nks_c = cdiv(C, 32);
+    p->nks_h = cdiv(H, 32);
+    const size_t cpad = (size_t)round_up(C, 256), vpad = (size_t)round_up(V, 256),
+                 hpad = (size_t)round_up(H, 256);
+    p->off_z = o;
+    o += align256(cpad * p->nks_z * 64);
+    p->off_gt = o;
+    o += align256(vpad * p->nks_c * 64);
+    p->off_xp = o;
+    o += align256(cpad * p->nks_h * 64);
+    p->off_xtp = o;
+    o += align256(hpad * p->nks_c * 64);
+  } else {
+    p->off_z = o;
+    o += align256((size_t)C * p->ldz * esz);
+  }
   p->off_pm = o;
   o += align256((size_t)C * p->nvt * 4);
   p->off_ps = o;
@@ -362,7 +386,8 @@ FLCE_API int flce_profile_read(double *ms, int64_t *launches, int n) {
 
 FLCE_API const char *flce_kernel_name(int k) {
   static const char *names[FLCE_K_COUNT] = {"label_check", "fwd_tile", "lse_combine", "dlogits",
-                                            "dx_gemm", "dx_reduce", "dw_gemm", "final"};
+                                            "dx_gemm", "dx_reduce", "dw_gemm", "final",
+                                            "pack_x"};
   return (k >= 0 && k < FLCE_K_COUNT) ? names[k] : "";
 }
 
