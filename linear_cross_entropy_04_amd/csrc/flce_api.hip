@@ -48,8 +48,10 @@ int check_sizes(int64_t N, int64_t H, int64_t V, int dtype) {
   return FLCE_OK;
 }
 
-// Largest power-of-two multiple of 256 tokens (capped at N) whose workspace
-// fits the budget; -1 if even the smallest does not fit.
+// Largest power-of-two multiple of 256 tokens (capped at N) whose chunk
+// scratch fits the budget; -1 if even the smallest does not fit.  The budget
+// bounds what grows with the chunk; the packed copy of W (bf16 path) comes on
+// top of it.
 int64_t auto_chunk(int64_t N, int64_t H, int64_t V, int dtype, size_t budget) {
   if (N <= 0) return 0;
   int64_t best = -1;
@@ -57,7 +59,7 @@ int64_t auto_chunk(int64_t N, int64_t H, int64_t V, int dtype, size_t budget) {
     const int64_t Cc = std::min(C, N);
     Plan p;
     make_plan(N, H, V, dtype, Cc, &p);
-    if (p.total > budget) break;
+    if (p.total - p.off_z > budget) break;     // the chunk-dependent part (not the packed W)
     best = Cc;
     if (C >= N) break;
   }
@@ -174,6 +176,9 @@ int run(bool bwd, const void *X, const void *W, const int64_t *labels, int64_t N
   LAUNCH(FLCE_K_LABELS, launch_label_check(labels, N, V, ii, sc, s));
   if (bwd && N == 0) LAUNCH(FLCE_K_FINAL, launch_fill_f32(dW, V * H, 0.f, s));
 
+  if (dtype == FLCE_BF16 && N > 0)
+    LAUNCH(FLCE_K_PACK, launch_pack_bf16((const uint16_t *)W, Vi, Hi, (uint16_t *)(ws + p.off_wp),
+                                         p.nks_h, nullptr, 0, s));
   for (int64_t c0 = 0; c0 < N; c0 += C) {
     const int c = (int)std::min(C, N - c0);
     const int64_t *lab = labels + c0;
@@ -186,8 +191,9 @@ int run(bool bwd, const void *X, const void *W, const int64_t *labels, int64_t N
       uint16_t *GTp = (uint16_t *)(ws + p.off_gt);
       uint16_t *Xp = (uint16_t *)(ws + p.off_xp);
       uint16_t *XTp = (uint16_t *)(ws + p.off_xtp);
-      LAUNCH(FLCE_K_PACK, launch_pack_x_bf16(Xc, c, Hi, Xp, p.nks_h, XTp, p.nks_c, s));
-      LAUNCH(FLCE_K_FWD_TILE, launch_fwd_tile_bf16(Wb, Xp, p.nks_h, lab, ii, c, Hi, Vi, Zp,
+      LAUNCH(FLCE_K_PACK, launch_pack_bf16(Xc, c, Hi, Xp, p.nks_h, XTp, p.nks_c, s));
+      LAUNCH(FLCE_K_FWD_TILE, launch_fwd_tile_bf16((const uint16_t *)(ws + p.off_wp), Xp, p.nks_h,
+                                                   lab, ii, c, Hi, Vi, Zp,
                                                    p.nks_z, pm, ps, zy, p.nvt, bwd, s));
       LAUNCH(FLCE_K_LSE_COMBINE, launch_lse_combine(pm, ps, zy, lab, ii, c, p.nvt, lse, rl, rs, s));
       if (bwd) {
@@ -276,6 +282,8 @@ void make_plan(int64_t N, int64_t H, int64_t V, int dtype, int64_t C, Plan *p) {
     p->nks_h = cdiv(H, 32);
     const size_t cpad = (size_t)round_up(C, 256), vpad = (size_t)round_up(V, 256),
                  hpad = (size_t)round_up(H, 256);
+    p->off_wp = o;                       // W packed once per call (rows = vocabulary)
+    o += align256(vpad * p->nks_h * 64);
     p->off_z = o;
     o += align256(cpad * p->nks_z * 64);
     p->off_gt = o;

@@ -34,7 +34,7 @@ struct Plan {
   int64_t nvt = 0;      // vocabulary tiles = log-sum-exp partials per token
   int splitk = 0;       // K-splits of the dX GEMM (0: the fp32 path writes dX directly)
   int64_t ksplit = 0;   // vocabulary rows per split (multiple of 64)
-  size_t off_z = 0, off_gt = 0, off_xp = 0, off_xtp = 0, off_pm = 0, off_ps = 0, off_zy = 0,
+  size_t off_wp = 0, off_z = 0, off_gt = 0, off_xp = 0, off_xtp = 0, off_pm = 0, off_ps = 0, off_zy = 0,
          off_lse = 0, off_rowloss = 0, off_dxp = 0, off_scal = 0, total = 0;
 };
 
@@ -57,9 +57,11 @@ hipError_t launch_scale(void *buf, int64_t n, int dtype, const float *scale, hip
 // Packed operands (Xp, XTp, Zp, GTp) are 16 KB blocks of 256 rows x 32 k; a
 // matrix with nks k-slices stores row tile rt, slice ks at element
 // (rt * nks + ks) * 8192.
-hipError_t launch_pack_x_bf16(const uint16_t *Xc, int c, int H, uint16_t *Xp, int64_t nks_h,
-                              uint16_t *XTp, int64_t nks_c, hipStream_t s);
-hipError_t launch_fwd_tile_bf16(const uint16_t *W, const uint16_t *Xp, int64_t nks_h,
+// Pack a row-major [R][K] matrix into P (rows R, k = K) and, if PT is not
+// null, its transpose into PT (rows K, k = R).
+hipError_t launch_pack_bf16(const uint16_t *src, int R, int K, uint16_t *P, int64_t nks_p,
+                            uint16_t *PT, int64_t nks_pt, hipStream_t s);
+hipError_t launch_fwd_tile_bf16(const uint16_t *Wp, const uint16_t *Xp, int64_t nks_h,
                                 const int64_t *labels_c, int64_t ii, int c, int H, int V,
                                 uint16_t *Zp, int64_t nks_z, float *pm, float *ps, float *zy,
                                 int64_t nvt, bool store_z, hipStream_t s);

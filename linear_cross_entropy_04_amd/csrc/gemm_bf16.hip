@@ -291,41 +291,44 @@ __device__ __forceinline__ void transpose8x8(const u32x4 (&in)[8], u32x4 (&out)[
     }
 }
 
-using FwdTile = Tile<256, 256, 4, KMAJOR, PACKED>;
+using FwdTile = Tile<256, 256, 4, PACKED, PACKED>;
 using DxTile = Tile<256, 256, 4, PACKED, MNMAJOR>;
 using DwTile = Tile<256, 128, 3, PACKED, PACKED>;
 
-// ---------------------------------------------------------------- pack X
-// One thread per 8 x 8 block (tokens t0..t0+7, hidden h0..h0+7) of the padded
-// chunk: Xp gets the 8 token rows (k = hidden), XTp the 8 hidden rows (k =
-// tokens), zero outside [0, c) x [0, H).
-__global__ __launch_bounds__(256) void pack_x_kernel(const uint16_t *__restrict__ Xc, int c, int H,
-                                                    int hb8, int64_t nblk,
-                                                    uint16_t *__restrict__ Xp, int64_t nks_h,
-                                                    uint16_t *__restrict__ XTp, int64_t nks_c) {
+// ---------------------------------------------------------------- packing
+// One thread per 8 x 8 block (rows t0..t0+7, columns h0..h0+7) of a row-major
+// bf16 matrix [R][K] padded to 256 x 256: P gets the 8 rows (k = columns) in
+// the packed layout, and, when PT is given, PT gets the 8 columns as rows (k =
+// rows of the source).  Values outside [0, R) x [0, K) are zero.  The 32
+// threads sharing t0 read 8 rows x 512 contiguous bytes.
+__global__ __launch_bounds__(256) void pack_kernel(const uint16_t *__restrict__ src, int R, int K,
+                                                  int kb8, int64_t nblk,
+                                                  uint16_t *__restrict__ P, int64_t nks_p,
+                                                  uint16_t *__restrict__ PT, int64_t nks_pt) {
   const int64_t gid = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
   if (gid >= nblk) return;
-  const int h0 = (int)(gid % hb8) * 8;
-  const int t0 = (int)(gid / hb8) * 8;
+  const int h0 = (int)(gid % kb8) * 8;
+  const int64_t t0 = (gid / kb8) * 8;
   u32x4 rows[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i)
-    rows[i] = (t0 + i < c && h0 < H) ? *(const u32x4 *)(Xc + (int64_t)(t0 + i) * H + h0)
+    rows[i] = (t0 + i < R && h0 < K) ? *(const u32x4 *)(src + (t0 + i) * K + h0)
                                      : u32x4{0u, 0u, 0u, 0u};
-  if (h0 < nks_h * 32) {
+  if (h0 < nks_p * 32) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) *(u32x4 *)(Xp + pk_off(t0 + i, h0, nks_h)) = rows[i];
+    for (int i = 0; i < 8; ++i) *(u32x4 *)(P + pk_off(t0 + i, h0, nks_p)) = rows[i];
   }
-  if (t0 < nks_c * 32) {
+  if (PT != nullptr && t0 < nks_pt * 32) {
     u32x4 cols[8];
     transpose8x8(rows, cols);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) *(u32x4 *)(XTp + pk_off(h0 + j, t0, nks_c)) = cols[j];
+    for (int j = 0; j < 8; ++j) *(u32x4 *)(PT + pk_off(h0 + j, t0, nks_pt)) = cols[j];
   }
 }
 
 // ---------------------------------------------------------------- forward tile
-// Z^T tile: rows = 256 vocabulary ids from m0, columns = 256 tokens from n0.
+// Z^T tile: rows = 256 vocabulary ids from m0, columns = 256 tokens from n0;
+// both operands packed (Wp rows = vocabulary, Xp rows = tokens, k = hidden).
 // VTAIL instantiates the tile that reaches past V (its rows >= V are masked).
 //
 // Epilogue, wave by wave: each wave reduces its own 128 vocabulary rows, so a
@@ -342,7 +345,7 @@ __device__ __forceinline__ int zst_off(int r, int v) {     // bytes, tile-local
 
 template <bool VTAIL>
 __global__ __launch_bounds__(NTHREADS, 1) void fwd_tile_kernel(
-    const uint16_t *__restrict__ W, const uint16_t *__restrict__ Xp, int64_t nks_h,
+    const uint16_t *__restrict__ Wp, const uint16_t *__restrict__ Xp, int64_t nks_h,
     const int64_t *__restrict__ labels_c, int64_t ii, int c, int H, int V,
     uint16_t *__restrict__ Zp, int64_t nks_z, float *__restrict__ pm, float *__restrict__ ps,
     float *__restrict__ zy, int64_t nvt, int vt0, int nct, int store_z) {
@@ -352,14 +355,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_tile_kernel(
   const int vt = vt0 + tile / nct, ct = tile % nct;
   const int m0 = vt * T::BM, n0 = ct * T::BN;
 
-  const Op a{W + (int64_t)m0 * H, H, V - m0, H};
+  const Op a{Wp + (int64_t)vt * nks_h * 8192, 8192, 256, H};
   const Op b{Xp + (int64_t)ct * nks_h * 8192, 8192, 256, H};
   f32x16 acc[4][4];
   zero_acc<T>(acc);
-  if (!VTAIL && H % BK == 0)
-    mainloop<T, false>(a, b, H, smem, acc);
-  else
-    mainloop<T, true>(a, b, H, smem, acc);
+  mainloop<T, false>(a, b, H, smem, acc);      // packed operands carry their zero padding
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int wm = w >> 1, wn = w & 1;
@@ -630,31 +630,31 @@ inline int grid_for(int64_t n, int block, int cap) {
 
 }  // namespace
 
-hipError_t launch_pack_x_bf16(const uint16_t *Xc, int c, int H, uint16_t *Xp, int64_t nks_h,
-                              uint16_t *XTp, int64_t nks_c, hipStream_t s) {
-  const int hb8 = (H + 255) / 256 * 32;              // 8-wide hidden blocks over H rounded to 256
-  const int64_t tb8 = (int64_t)(c + 255) / 256 * 32;  // 8-tall token blocks over c rounded to 256
-  const int64_t nblk = tb8 * hb8;
-  hipLaunchKernelGGL(pack_x_kernel, dim3((unsigned)((nblk + 255) / 256)), dim3(256), 0, s, Xc, c, H,
-                     hb8, nblk, Xp, nks_h, XTp, nks_c);
+hipError_t launch_pack_bf16(const uint16_t *src, int R, int K, uint16_t *P, int64_t nks_p,
+                            uint16_t *PT, int64_t nks_pt, hipStream_t s) {
+  const int kb8 = (K + 255) / 256 * 32;              // 8-wide column blocks over K rounded to 256
+  const int64_t rb8 = (int64_t)(R + 255) / 256 * 32;  // 8-tall row blocks over R rounded to 256
+  const int64_t nblk = rb8 * kb8;
+  hipLaunchKernelGGL(pack_kernel, dim3((unsigned)((nblk + 255) / 256)), dim3(256), 0, s, src, R, K,
+                     kb8, nblk, P, nks_p, PT, nks_pt);
   return hipGetLastError();
 }
 
-hipError_t launch_fwd_tile_bf16(const uint16_t *W, const uint16_t *Xp, int64_t nks_h,
+hipError_t launch_fwd_tile_bf16(const uint16_t *Wp, const uint16_t *Xp, int64_t nks_h,
                                 const int64_t *labels_c, int64_t ii, int c, int H, int V,
                                 uint16_t *Zp, int64_t nks_z, float *pm, float *ps, float *zy,
                                 int64_t nvt, bool store_z, hipStream_t s) {
   const int nct = (c + FwdTile::BN - 1) / FwdTile::BN;
   const int nfull = V / FwdTile::BM;                 // vocabulary tiles inside V
   if (nfull > 0) {
-    hipLaunchKernelGGL(fwd_tile_kernel<false>, dim3(nfull * nct), dim3(NTHREADS), 0, s, W, Xp,
+    hipLaunchKernelGGL(fwd_tile_kernel<false>, dim3(nfull * nct), dim3(NTHREADS), 0, s, Wp, Xp,
                        nks_h, labels_c, ii, c, H, V, Zp, nks_z, pm, ps, zy, nvt, 0, nct,
                        store_z ? 1 : 0);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (V % FwdTile::BM != 0) {
-    hipLaunchKernelGGL(fwd_tile_kernel<true>, dim3(nct), dim3(NTHREADS), 0, s, W, Xp, nks_h,
+    hipLaunchKernelGGL(fwd_tile_kernel<true>, dim3(nct), dim3(NTHREADS), 0, s, Wp, Xp, nks_h,
                        labels_c, ii, c, H, V, Zp, nks_z, pm, ps, zy, nvt, nfull, nct,
                        store_z ? 1 : 0);
   }
