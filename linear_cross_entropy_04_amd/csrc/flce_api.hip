@@ -178,33 +178,29 @@ int run(bool bwd, const void *X, const void *W, const int64_t *labels, int64_t N
 
   if (dtype == FLCE_BF16 && N > 0)
     LAUNCH(FLCE_K_PACK, launch_pack_bf16((const uint16_t *)W, Vi, Hi, (uint16_t *)(ws + p.off_wp),
-                                         p.nks_h, nullptr, 0, s));
+                                         p.nks_h, s));
   for (int64_t c0 = 0; c0 < N; c0 += C) {
     const int c = (int)std::min(C, N - c0);
     const int64_t *lab = labels + c0;
     float *rl = rowloss + c0;
     float *rs = row_lse ? row_lse + c0 : nullptr;
     if (dtype == FLCE_BF16) {
-      const uint16_t *Wb = (const uint16_t *)W;
+      const uint16_t *Wp = (const uint16_t *)(ws + p.off_wp);
       const uint16_t *Xc = (const uint16_t *)X + c0 * H;
       uint16_t *Zp = (uint16_t *)(ws + p.off_z);
-      uint16_t *GTp = (uint16_t *)(ws + p.off_gt);
       uint16_t *Xp = (uint16_t *)(ws + p.off_xp);
-      uint16_t *XTp = (uint16_t *)(ws + p.off_xtp);
-      LAUNCH(FLCE_K_PACK, launch_pack_bf16(Xc, c, Hi, Xp, p.nks_h, XTp, p.nks_c, s));
-      LAUNCH(FLCE_K_FWD_TILE, launch_fwd_tile_bf16((const uint16_t *)(ws + p.off_wp), Xp, p.nks_h,
-                                                   lab, ii, c, Hi, Vi, Zp,
+      LAUNCH(FLCE_K_PACK, launch_pack_bf16(Xc, c, Hi, Xp, p.nks_h, s));
+      LAUNCH(FLCE_K_FWD_TILE, launch_fwd_tile_bf16(Wp, Xp, p.nks_h, lab, ii, c, Hi, Vi, Zp,
                                                    p.nks_z, pm, ps, zy, p.nvt, bwd, s));
       LAUNCH(FLCE_K_LSE_COMBINE, launch_lse_combine(pm, ps, zy, lab, ii, c, p.nvt, lse, rl, rs, s));
       if (bwd) {
-        LAUNCH(FLCE_K_DLOGITS, launch_dlogits_bf16(Zp, p.nks_z, GTp, p.nks_c, c, Vi, lse, lab,
-                                                   ii, sc, s));
+        LAUNCH(FLCE_K_DLOGITS, launch_dlogits_bf16(Zp, p.nks_z, c, Vi, lse, lab, ii, sc, s));
         float *dxp = (float *)(ws + p.off_dxp);
-        LAUNCH(FLCE_K_DX_GEMM, launch_dx_bf16(Zp, p.nks_z, Wb, c, Hi, Vi, p.splitk, p.ksplit,
-                                              dxp, s));
+        LAUNCH(FLCE_K_DX_GEMM, launch_dx_bf16(Zp, p.nks_z, Wp, p.nks_h, c, Hi, Vi, p.splitk,
+                                              p.ksplit, dxp, s));
         LAUNCH(FLCE_K_DX_REDUCE,
                launch_dx_reduce_bf16(dxp, p.splitk, c, Hi, (uint16_t *)dX + c0 * H, s));
-        LAUNCH(FLCE_K_DW_GEMM, launch_dw_bf16(GTp, XTp, p.nks_c, c, Hi, Vi, dW, c0 > 0, s));
+        LAUNCH(FLCE_K_DW_GEMM, launch_dw_bf16(Zp, p.nks_z, Xp, p.nks_h, c, Hi, Vi, dW, c0 > 0, s));
       }
     } else {
       const float *Wf = (const float *)W;
@@ -276,22 +272,16 @@ void make_plan(int64_t N, int64_t H, int64_t V, int dtype, int64_t C, Plan *p) {
   p->off_scal = o;
   o += 256;
   if (bf) {
-    // packed layouts: rows padded to 256, k to 32 (see flce_internal.h)
-    p->nks_z = cdiv(V, 32);
-    p->nks_c = cdiv(C, 32);
-    p->nks_h = cdiv(H, 32);
-    const size_t cpad = (size_t)round_up(C, 256), vpad = (size_t)round_up(V, 256),
-                 hpad = (size_t)round_up(H, 256);
+    // packed layouts: rows and columns padded to 256 (see flce_internal.h)
+    p->nks_z = cdiv(V, 256) * 8;
+    p->nks_h = cdiv(H, 256) * 8;
+    const size_t cpad = (size_t)round_up(C, 256), vpad = (size_t)round_up(V, 256);
     p->off_wp = o;                       // W packed once per call (rows = vocabulary)
     o += align256(vpad * p->nks_h * 64);
-    p->off_z = o;
+    p->off_z = o;                        // logits, then G, of the chunk (rows = tokens)
     o += align256(cpad * p->nks_z * 64);
-    p->off_gt = o;
-    o += align256(vpad * p->nks_c * 64);
-    p->off_xp = o;
+    p->off_xp = o;                       // the chunk's X (rows = tokens)
     o += align256(cpad * p->nks_h * 64);
-    p->off_xtp = o;
-    o += align256(hpad * p->nks_c * 64);
   } else {
     p->off_z = o;
     o += align256((size_t)C * p->ldz * esz);

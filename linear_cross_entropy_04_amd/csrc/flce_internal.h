@@ -30,12 +30,12 @@ struct Plan {
   int64_t N = 0, H = 0, V = 0;
   int64_t C = 0;        // tokens per chunk (last chunk may be shorter)
   int64_t ldz = 0;      // fp32 path: leading dimension (elements) of the chunk logits scratch
-  int64_t nks_z = 0, nks_c = 0, nks_h = 0;   // bf16 path: 32-k slices of V, C and H
+  int64_t nks_z = 0, nks_h = 0;   // bf16 path: 32-column slices of V and H, padded to 256
   int64_t nvt = 0;      // vocabulary tiles = log-sum-exp partials per token
   int splitk = 0;       // K-splits of the dX GEMM (0: the fp32 path writes dX directly)
   int64_t ksplit = 0;   // vocabulary rows per split (multiple of 64)
-  size_t off_wp = 0, off_z = 0, off_gt = 0, off_xp = 0, off_xtp = 0, off_pm = 0, off_ps = 0, off_zy = 0,
-         off_lse = 0, off_rowloss = 0, off_dxp = 0, off_scal = 0, total = 0;
+  size_t off_wp = 0, off_z = 0, off_xp = 0, off_pm = 0, off_ps = 0, off_zy = 0, off_lse = 0,
+         off_rowloss = 0, off_dxp = 0, off_scal = 0, total = 0;
 };
 
 // Fill *p for the given sizes and chunk (C >= 1, C <= N or N == 0).
@@ -54,26 +54,27 @@ hipError_t launch_fill_f32(float *p, int64_t n, float v, hipStream_t s);
 hipError_t launch_scale(void *buf, int64_t n, int dtype, const float *scale, hipStream_t s);
 
 // ---------------------------------------------------------------- bf16 path (MFMA)
-// Packed operands (Xp, XTp, Zp, GTp) are 16 KB blocks of 256 rows x 32 k; a
-// matrix with nks k-slices stores row tile rt, slice ks at element
-// (rt * nks + ks) * 8192.
-// Pack a row-major [R][K] matrix into P (rows R, k = K) and, if PT is not
-// null, its transpose into PT (rows K, k = R).
+// Packed matrices (Wp, Xp, Zp) are 16 KB blocks of 256 rows x 32 columns; a
+// matrix with nks column slices (nks a multiple of 8) stores row tile rt,
+// slice ks at element (rt * nks + ks) * 8192.  Each GEMM reads them either
+// along their rows or transposed, so no transposed copy is ever made.
+// Pack a row-major [R][K] matrix into P (rows R padded to 256, nks_p slices).
 hipError_t launch_pack_bf16(const uint16_t *src, int R, int K, uint16_t *P, int64_t nks_p,
-                            uint16_t *PT, int64_t nks_pt, hipStream_t s);
+                            hipStream_t s);
 hipError_t launch_fwd_tile_bf16(const uint16_t *Wp, const uint16_t *Xp, int64_t nks_h,
                                 const int64_t *labels_c, int64_t ii, int c, int H, int V,
                                 uint16_t *Zp, int64_t nks_z, float *pm, float *ps, float *zy,
                                 int64_t nvt, bool store_z, hipStream_t s);
-hipError_t launch_dlogits_bf16(uint16_t *Zp, int64_t nks_z, uint16_t *GTp, int64_t nks_c, int c,
-                               int V, const float *lse_c, const int64_t *labels_c, int64_t ii,
-                               const Scalars *sc, hipStream_t s);
-hipError_t launch_dx_bf16(const uint16_t *Gp, int64_t nks_z, const uint16_t *W, int c, int H,
-                          int V, int splitk, int64_t ksplit, float *dxp, hipStream_t s);
+hipError_t launch_dlogits_bf16(uint16_t *Zp, int64_t nks_z, int c, int V, const float *lse_c,
+                               const int64_t *labels_c, int64_t ii, const Scalars *sc,
+                               hipStream_t s);
+hipError_t launch_dx_bf16(const uint16_t *Gp, int64_t nks_z, const uint16_t *Wp, int64_t nks_h,
+                          int c, int H, int V, int splitk, int64_t ksplit, float *dxp,
+                          hipStream_t s);
 hipError_t launch_dx_reduce_bf16(const float *dxp, int splitk, int c, int H, uint16_t *dXc,
                                  hipStream_t s);
-hipError_t launch_dw_bf16(const uint16_t *GTp, const uint16_t *XTp, int64_t nks_c, int c, int H,
-                          int V, float *dW, bool accumulate, hipStream_t s);
+hipError_t launch_dw_bf16(const uint16_t *Gp, int64_t nks_z, const uint16_t *Xp, int64_t nks_h,
+                          int c, int H, int V, float *dW, bool accumulate, hipStream_t s);
 
 // ---------------------------------------------------------------- fp32 path (SIMT)
 hipError_t launch_fwd_tile_f32(const float *W, const float *Xc, const int64_t *labels_c,

@@ -1,16 +1,15 @@
 // bf16 MFMA GEMMs of the chunked fused linear cross-entropy (gfx950), and
 // the data movement that feeds them.
 //
-// Per chunk of c tokens (the chain rule through the LM-head projection
+// Per call, W is packed once into Wp (rows = vocabulary, k = hidden).  Per
+// chunk of c tokens (the chain rule through the LM-head projection
 // Z = X W^T that the Liger Kernel pages fuse with the cross-entropy loss):
-//   pack      X_c -> Xp (rows = tokens, k = hidden) and XTp (rows = hidden,
-//             k = tokens), both in the packed layout below;
+//   pack      X_c -> Xp (rows = tokens, k = hidden);
 //   forward   Z_c^T = W X_c^T      M = V (vocab), N = c (tokens), K = H
 //             + epilogue: per (token, 128-vocab half tile) max and sum of exp,
-//               the target logit, and the bf16 logits into Zp (packed, rows =
-//               tokens, k = vocab);
-//   dlogits   Zp rewritten in place into G = (softmax - onehot) / N_valid, and
-//             G^T written to GTp (packed, rows = vocab, k = tokens);
+//               the target logit, and the bf16 logits into Zp (rows = tokens,
+//               k = vocabulary);
+//   dlogits   Zp rewritten in place into G = (softmax - onehot) / N_valid;
 //   dX        dX_c  = G_c W        M = c, N = H, K = V (split-K, fp32 partials)
 //   dW        dW   (+)= G_c^T X_c  M = V, N = H, K = c (fp32)
 //
@@ -21,22 +20,27 @@
 // 16 l) in k-slices of 32, STAGES slices in flight, each admitted by an
 // explicit vmcnt wait and one s_barrier.
 //
-// Operand kinds:
-//   PACKED  (Xp, XTp, Zp/G, GTp): the matrix is stored as 16 KB blocks of 256
-//           rows x 32 k; a block is 16 fragments of 1 KB, fragment (r/32, k/16)
-//           holding in lane order what lane l of an MFMA operand read needs
-//           (row r0 + l%32, k = 8 (l/32) + 0..7).  A slice copy is contiguous
-//           on both sides and every fragment read is 1 KB contiguous, which
-//           measured at full copy and LDS rates.  Padding rows and k are zero.
-//   KMAJOR  (W in the forward GEMM): rows of K-contiguous data; 64-byte row
-//           pieces XOR-swizzled by row bits 2..3 in LDS.
-//   MNMAJOR (W in the dX GEMM): k rows of M/N-contiguous data; fragments read
-//           with ds_read_b64_tr_b16, which transposes 16-bit data across each
-//           group of 16 lanes (lane j names a 4-element row R_j; lane i gets
-//           element i%4 of R_{i/4}, R_{4+i/4}, R_{8+i/4}, R_{12+i/4}).
-// Plain-layout tiles that reach past an operand's extent copy 16 zero bytes
-// for the lanes outside it, so every thread issues the same number of copies
-// per slice and the vmcnt arithmetic holds.
+// The packed layout (Wp, Xp, Zp): a matrix of R rows and K columns is stored
+// as 16 KB blocks of 256 rows x 32 columns; block (rt, ks) at element
+// (rt * nks + ks) * 8192, nks = 8 ceil(K / 256) (columns padded to 256 so a
+// 256-wide tile of columns always exists).  A block is 16 fragments of 1 KB;
+// fragment (r/32, k/16) holds 32 rows x 16 columns as 64 slots of 16 bytes (8
+// consecutive columns of one row): row r%32 of column half h = (k/8)%2 sits
+// at slot 32 h + (r%32 ^ 4 h ^ 8 f), f = (k/16)%2.  Padding rows and columns
+// are zero.  Each GEMM reads a packed matrix in one of two directions:
+//   PACKED   rows of the matrix are rows of the GEMM operand (k runs along
+//            the matrix's columns): a slice is 1 KB pieces of one 16 KB block
+//            and an MFMA fragment is one 16-byte read per lane;
+//   PACKED_T columns of the matrix are rows of the GEMM operand (k runs along
+//            the matrix's rows): a slice is 2 KB pieces (two fragments) of
+//            consecutive blocks, and a fragment comes from two
+//            ds_read_b64_tr_b16, which transpose 16-bit data across each group
+//            of 16 lanes (lane j names a 4-element row R_j; lane i gets element
+//            i%4 of R_{i/4}, R_{4+i/4}, R_{8+i/4}, R_{12+i/4}).
+// The two XOR terms of the slot index make both read kinds free of LDS bank
+// conflicts: an aligned group of 16 lanes of a 16-byte read covers 256
+// distinct bytes, and each half-wave of a transposing read covers 32 distinct
+// 8-byte bank pairs.
 #include "flce_internal.h"
 
 namespace flce {
@@ -53,27 +57,22 @@ constexpr int BK = 32;             // k per pipeline slice
 constexpr int NTHREADS = 256;
 constexpr float kLog2e = 1.4426950408889634f;
 
-enum Kind { KMAJOR = 0, MNMAJOR = 1, PACKED = 2 };
-
-// The source of the copies of out-of-range lanes.
-__device__ const uint4 g_zero16 = {0u, 0u, 0u, 0u};
+enum Kind { PACKED = 0, PACKED_T = 1 };
 
 // ---------------------------------------------------------------- packed layout
-// Element offset of (r, k) in a packed matrix with nks slices of 32 k per row tile.
+// 16-byte slot of row r32 = r % 32, column half h = (k / 8) % 2 and fragment
+// half f = (k / 16) % 2 inside a 1 KB fragment.
+__device__ __forceinline__ int pk_slot(int r32, int h, int f) {
+  return (h << 5) + (r32 ^ (h << 2) ^ (f << 3));
+}
+
+// Element offset of (r, k) in a packed matrix with nks 32-column slices.
 __device__ __forceinline__ int64_t pk_off(int64_t r, int64_t k, int64_t nks) {
   const int64_t blk = (r >> 8) * nks + (k >> 5);
   const int rr = (int)(r & 255), kk = (int)(k & 31);
-  const int in = ((((rr >> 5) * 2 + (kk >> 4)) * 64 + ((kk >> 3) & 1) * 32 + (rr & 31)) << 3) + (kk & 7);
-  return (blk << 13) + in;
+  const int frag = ((rr >> 5) << 1) + (kk >> 4);
+  return (blk << 13) + (frag << 9) + (pk_slot(rr & 31, (kk >> 3) & 1, kk >> 4) << 3) + (kk & 7);
 }
-
-// K-major slice: 64-byte rows; chunk q (8 k values) of row r sits at slot q ^ fk(r).
-// Rows r..r+3 already span one 256-byte bank line; rows 4 apart share it, so
-// the swizzle takes row bits 2 and 3 (measured conflict-free; swizzles using
-// row bit 0 or 1 leave a two-way conflict).
-__device__ __forceinline__ int fk(int r) { return (r >> 2) & 3; }
-// MN-major slice: one row per k; 16-byte slot s of row k sits at s ^ fmn(k).
-__device__ __forceinline__ int fmn(int k) { return (k & 3) << 1; }
 
 // Map the hardware's round-robin placement of workgroups over the 8 XCDs to
 // a logical tile order in which consecutive logical tiles share an XCD (and
@@ -95,65 +94,62 @@ struct Tile {
   static constexpr int LDS = STAGES * STAGE_BYTES;
 };
 
-// One operand of a tile.  KMAJOR: element (r, k) at p[r * ld + k]; MNMAJOR:
-// at p[k * ld + r]; PACKED: p is the tile's first block, slice s at p + s * ld
-// (ld = 8192 elements).  r counts from the tile's first row, k from the start
-// of the reduction range; rows / klen bound the plain layouts.
+// One GEMM operand tile in a packed matrix P.
+//   PACKED:   p = the block of the tile's first row and of the range's first
+//             k; slice s at p + s * 8192.
+//   PACKED_T: p = the block of row tile 0 and of the column slice of the
+//             tile's first operand row; ld = nks_P * 8192 (one row tile of P);
+//             kb = the range's first k, a row of P (a multiple of 32).
 struct Op {
   const uint16_t *p;
   int64_t ld;
-  int rows;
-  int klen;
+  int64_t kb;
 };
 
-// Copy k-slice [k0, k0 + 32) of an operand tile of ROWS rows into LDS.
-template <int KIND, int ROWS, bool CHECK>
+// Copy k-slice [k0, k0 + 32) (relative to the range) of an operand tile of
+// ROWS rows into LDS: ROWS / 16 pieces of 1 KB, piece b at tile + 1 KB b.
+// PACKED_T pieces 2q, 2q+1 are the two fragments of operand rows 32q..32q+31.
+template <int KIND, int ROWS>
 __device__ __forceinline__ void issue_tile(const Op &op, int k0, char *tile) {
   constexpr int N = ROWS * BK * 2 / 4096;
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const uint16_t *base;
+  if constexpr (KIND == PACKED) {
+    base = op.p + (int64_t)(k0 >> 5) * 8192;
+  } else {
+    const int64_t kr = op.kb + k0;                 // row of P
+    base = op.p + (kr >> 8) * op.ld + (((kr & 255) >> 5) << 10);
+  }
 #pragma unroll
   for (int i = 0; i < N; ++i) {
-    const int blk = i * 4 + w;                   // 1 KB block written by this wave
+    const int blk = i * 4 + w;                   // 1 KB piece written by this wave
     const uint16_t *src;
-    bool ok = true;
-    if constexpr (KIND == PACKED) {
-      src = op.p + (int64_t)(k0 >> 5) * op.ld + blk * 512 + l * 8;
-    } else if constexpr (KIND == KMAJOR) {
-      const int r = blk * 16 + (l >> 2);
-      const int q = (l & 3) ^ fk(r);
-      src = op.p + (int64_t)r * op.ld + (k0 + q * 8);
-      if (CHECK) ok = (r < op.rows) && (k0 + q * 8 < op.klen);
-    } else {
-      constexpr int KPB = 1024 / (ROWS * 2);     // k rows per block
-      constexpr int LPR = 64 / KPB;              // lanes per k row
-      const int kr = blk * KPB + l / LPR;
-      const int sl = (l % LPR) ^ fmn(kr);
-      src = op.p + (int64_t)(k0 + kr) * op.ld + sl * 8;
-      if (CHECK) ok = (k0 + kr < op.klen) && (sl * 8 < op.rows);
-    }
-    if (KIND != PACKED && CHECK && !ok) src = (const uint16_t *)&g_zero16;
+    if constexpr (KIND == PACKED)
+      src = base + blk * 512 + l * 8;
+    else
+      src = base + (blk >> 1) * 8192 + (blk & 1) * 512 + l * 8;
     __builtin_amdgcn_global_load_lds(src, tile + blk * 1024, 16, 0, 0);
   }
 }
 
-// MFMA fragment of rows r0..r0+31, k = 16 kk .. 16 kk + 15 of an LDS slice:
-// lane l holds row r0 + l%32, k = 16 kk + 8 (l/32) + 0..7.
-template <int KIND, int ROWS>
+// MFMA fragment of operand rows r0..r0+31 (r0 % 32 == 0), k = 16 kk .. 16 kk
+// + 15 of an LDS slice: lane l holds row r0 + l%32, k = 16 kk + 8 (l/32) + 0..7.
+template <int KIND>
 __device__ __forceinline__ bf16x8 frag(const char *tile, int r0, int kk) {
   const int l = threadIdx.x & 63;
   if constexpr (KIND == PACKED) {
-    return *(const bf16x8 *)(tile + ((((r0 >> 5) << 1) + kk) << 10) + (l << 4));
-  } else if constexpr (KIND == KMAJOR) {
-    const int r = r0 + (l & 31);
-    const int q = kk * 2 + (l >> 5);
-    return *(const bf16x8 *)(tile + r * (BK * 2) + ((q ^ fk(r)) << 4));
+    const char *f = tile + ((((r0 >> 5) << 1) + kk) << 10);
+    return *(const bf16x8 *)(f + (pk_slot(l & 31, l >> 5, kk) << 4));
   } else {
+    // operand row r is column r of the slice's P rows, operand k its row;
+    // lane j of a 16-lane group names the 4 operand rows r..r+3 at one k
     const int g = l >> 4, j = l & 15;
-    const int m = r0 + ((g & 1) << 4) + ((j & 3) << 2);
+    const int r = r0 + ((g & 1) << 4) + ((j & 3) << 2);
     const int k = kk * 16 + ((g >> 1) << 3) + (j >> 2);
-    const char *base = tile + (((m >> 3) ^ fmn(k)) << 4) + ((m & 7) << 1);
-    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(base + k * (ROWS * 2)));
-    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(base + (k + 4) * (ROWS * 2)));
+    const int h = (r >> 3) & 1, f = (r >> 4) & 1;
+    const char *p = tile + ((((r >> 5) << 1) + f) << 10) + ((r & 7) << 1);
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p + (pk_slot(k, h, f) << 4)));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p + (pk_slot(k + 4, h, f) << 4)));
     const i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     return __builtin_bit_cast(bf16x8, v);
   }
@@ -189,10 +185,9 @@ __device__ __forceinline__ void load_frags(const char *st, int kk, bf16x8 (&fa)[
   const int w = threadIdx.x >> 6;
   const int wm = w >> 1, wn = w & 1;
 #pragma unroll
-  for (int i = 0; i < T::MI; ++i) fa[i] = frag<T::KA, T::BM>(st, wm * T::WM + 32 * i, kk);
+  for (int i = 0; i < T::MI; ++i) fa[i] = frag<T::KA>(st, wm * T::WM + 32 * i, kk);
 #pragma unroll
-  for (int j = 0; j < T::NI; ++j)
-    fb[j] = frag<T::KB, T::BN>(st + T::A_BYTES, wn * T::WN + 32 * j, kk);
+  for (int j = 0; j < T::NI; ++j) fb[j] = frag<T::KB>(st + T::A_BYTES, wn * T::WN + 32 * j, kk);
 }
 
 template <class T>
@@ -205,11 +200,11 @@ __device__ __forceinline__ void mfma_block(const bf16x8 (&fa)[T::MI], const bf16
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
 }
 
-template <class T, bool CHECK>
+template <class T>
 __device__ __forceinline__ void issue_stage(const Op &a, const Op &b, int step, char *smem) {
   char *st = smem + (step % T::STAGES) * T::STAGE_BYTES;
-  issue_tile<T::KA, T::BM, CHECK>(a, step * BK, st);
-  issue_tile<T::KB, T::BN, CHECK>(b, step * BK, st + T::A_BYTES);
+  issue_tile<T::KA, T::BM>(a, step * BK, st);
+  issue_tile<T::KB, T::BN>(b, step * BK, st + T::A_BYTES);
 }
 
 // acc[i][j] is the 32 x 32 block (i, j) of the wave's quarter.  Lane l of
@@ -221,25 +216,16 @@ __device__ __forceinline__ void issue_stage(const Op &a, const Op &b, int step, 
 // the fragments of slice t+1's first half-step are read from LDS while the
 // MFMAs of slice t's second half-step run, and the barrier itself waits with
 // MFMAs in flight.  Slice t+STAGES-1 is copied into the buffer of slice t-1,
-// whose reads every wave finished before that barrier.
-// acc[i][j] is the 32 x 32 block (i, j) of the wave's quarter.  Lane l of
-// block (i, j), register e, holds row 32 i + 8 (e/4) + 4 (l/32) + e%4 and
-// column 32 j + l%32 of the quarter.  acc enters initialised by the caller.
-//
-// Each 32-deep slice is two MFMA half-steps (k 0..15, 16..31).  The wait and
-// barrier that admit slice t+1 sit between the two half-steps of slice t, so
-// the fragments of slice t+1's first half-step are read from LDS while the
-// MFMAs of slice t's second half-step run, and the barrier itself waits with
-// MFMAs in flight.  Slice t+STAGES-1 is copied into the buffer of slice t-1,
-// whose reads every wave finished before that barrier.
-template <class T, bool CHECK>
+// whose reads every wave finished before that barrier.  Packed operands carry
+// zero padding up to whole slices, so no copy needs a bounds check.
+template <class T>
 __device__ __forceinline__ void mainloop(const Op &a, const Op &b, int klen, char *smem,
                                          f32x16 (&acc)[T::MI][T::NI]) {
   const int nk = (klen + BK - 1) / BK;
   if (nk > 0) {
 #pragma unroll
     for (int s = 0; s < T::STAGES - 1; ++s)
-      if (s < nk) issue_stage<T, CHECK>(a, b, s, smem);
+      if (s < nk) issue_stage<T>(a, b, s, smem);
     wait_groups<T::NPER>(min(T::STAGES - 2, nk - 1));
     bar();
     bf16x8 fa0[T::MI], fb0[T::NI], fa1[T::MI], fb1[T::NI];
@@ -252,7 +238,7 @@ __device__ __forceinline__ void mainloop(const Op &a, const Op &b, int klen, cha
         // slice t+1 must have landed; slices up to t+STAGES-2 may stay in flight
         wait_groups<T::NPER>(min(t + T::STAGES - 2, nk - 1) - (t + 1));
         bar();
-        if (t + T::STAGES - 1 < nk) issue_stage<T, CHECK>(a, b, t + T::STAGES - 1, smem);
+        if (t + T::STAGES - 1 < nk) issue_stage<T>(a, b, t + T::STAGES - 1, smem);
         load_frags<T>(smem + ((t + 1) % T::STAGES) * T::STAGE_BYTES, 0, fa0, fb0);
       }
       mfma_block<T>(fa1, fb1, acc);
@@ -279,50 +265,41 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 __device__ __forceinline__ float bf16_lo(uint32_t u) { return __builtin_bit_cast(float, u << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t u) { return __builtin_bit_cast(float, u & 0xFFFF0000u); }
 
-// Transpose an 8 x 8 block of 16-bit values held as 8 rows of 16 bytes:
-// out[j] holds element j of rows 0..7, two per dword, low half first.
-__device__ __forceinline__ void transpose8x8(const u32x4 (&in)[8], u32x4 (&out)[8]) {
-#pragma unroll
-  for (int j = 0; j < 8; ++j)
-#pragma unroll
-    for (int pp = 0; pp < 4; ++pp) {
-      const uint32_t lo = in[2 * pp][j >> 1], hi = in[2 * pp + 1][j >> 1];
-      out[j][pp] = (j & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
-    }
-}
-
-using FwdTile = Tile<256, 256, 4, PACKED, PACKED>;
-using DxTile = Tile<256, 256, 4, PACKED, MNMAJOR>;
-using DwTile = Tile<256, 128, 3, PACKED, PACKED>;
+using FwdTile = Tile<256, 256, 4, PACKED, PACKED>;     // A = Wp, B = Xp
+using DxTile = Tile<256, 256, 4, PACKED, PACKED_T>;    // A = G (Zp), B = Wp read transposed
+using DwTile = Tile<256, 128, 3, PACKED_T, PACKED_T>;  // A = G (Zp), B = Xp, both transposed
+constexpr int kDwOcc = 2;                              // dW workgroups per CU
 
 // ---------------------------------------------------------------- packing
-// One thread per 8 x 8 block (rows t0..t0+7, columns h0..h0+7) of a row-major
-// bf16 matrix [R][K] padded to 256 x 256: P gets the 8 rows (k = columns) in
-// the packed layout, and, when PT is given, PT gets the 8 columns as rows (k =
-// rows of the source).  Values outside [0, R) x [0, K) are zero.  The 32
-// threads sharing t0 read 8 rows x 512 contiguous bytes.
+// One workgroup per 256 rows x 64 columns (two packed blocks, 32 KB) of a
+// row-major bf16 matrix [R][K]: it reads the rows' 128-byte pieces (8 full
+// rows per wave instruction), places them in LDS in packed order, and writes
+// the two blocks as one contiguous 32 KB copy.  Zero outside [0, R) x [0, K).
 __global__ __launch_bounds__(256) void pack_kernel(const uint16_t *__restrict__ src, int R, int K,
-                                                  int kb8, int64_t nblk,
-                                                  uint16_t *__restrict__ P, int64_t nks_p,
-                                                  uint16_t *__restrict__ PT, int64_t nks_pt) {
-  const int64_t gid = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-  if (gid >= nblk) return;
-  const int h0 = (int)(gid % kb8) * 8;
-  const int64_t t0 = (gid / kb8) * 8;
-  u32x4 rows[8];
+                                                  uint16_t *__restrict__ P, int64_t nks_p) {
+  __shared__ __attribute__((aligned(1024))) char lds[32768];
+  const int npair = (int)(nks_p >> 1);
+  const int64_t rt = blockIdx.x / npair;
+  const int kp = blockIdx.x - (int)(rt * npair);
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
-    rows[i] = (t0 + i < R && h0 < K) ? *(const u32x4 *)(src + (t0 + i) * K + h0)
-                                     : u32x4{0u, 0u, 0u, 0u};
-  if (h0 < nks_p * 32) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) *(u32x4 *)(P + pk_off(t0 + i, h0, nks_p)) = rows[i];
+  for (int i = 0; i < 8; ++i) {
+    const int piece = i * 256 + threadIdx.x;          // 16-byte piece: row piece/8, columns 8 (piece%8)
+    const int row = piece >> 3, cp = piece & 7;
+    const int64_t gr = rt * 256 + row;
+    const int col = kp * 64 + cp * 8;
+    const u32x4 v = (gr < R && col < K) ? *(const u32x4 *)(src + gr * K + col)
+                                        : u32x4{0u, 0u, 0u, 0u};
+    const int kk = (cp * 8) & 31;
+    const int off = ((cp >> 2) << 14) + (((((row >> 5) << 1) + (kk >> 4))) << 10) +
+                    (pk_slot(row & 31, (kk >> 3) & 1, kk >> 4) << 4);
+    *(u32x4 *)(lds + off) = v;
   }
-  if (PT != nullptr && t0 < nks_pt * 32) {
-    u32x4 cols[8];
-    transpose8x8(rows, cols);
+  __syncthreads();
+  uint16_t *dst = P + ((rt * nks_p + 2 * kp) << 13);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) *(u32x4 *)(PT + pk_off(h0 + j, t0, nks_pt)) = cols[j];
+  for (int i = 0; i < 8; ++i) {
+    const int q = i * 256 + threadIdx.x;
+    *(u32x4 *)(dst + q * 8) = *(const u32x4 *)(lds + q * 16);
   }
 }
 
@@ -338,9 +315,8 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint16_t *__restrict__ 
 // order (it is 8 consecutive blocks of Zp) and leaves as one 128 KB copy.
 __device__ __forceinline__ int zst_off(int r, int v) {     // bytes, tile-local
   const int kk = v & 31;
-  return ((v >> 5) << 14) +
-         (((((r >> 5) * 2 + (kk >> 4)) * 64 + ((kk >> 3) & 1) * 32 + (r & 31)) << 4)) +
-         ((kk & 7) << 1);
+  return ((v >> 5) << 14) + ((((r >> 5) << 1) + (kk >> 4)) << 10) +
+         (pk_slot(r & 31, (kk >> 3) & 1, kk >> 4) << 4) + ((kk & 7) << 1);
 }
 
 template <bool VTAIL>
@@ -355,11 +331,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_tile_kernel(
   const int vt = vt0 + tile / nct, ct = tile % nct;
   const int m0 = vt * T::BM, n0 = ct * T::BN;
 
-  const Op a{Wp + (int64_t)vt * nks_h * 8192, 8192, 256, H};
-  const Op b{Xp + (int64_t)ct * nks_h * 8192, 8192, 256, H};
+  const Op a{Wp + (int64_t)vt * nks_h * 8192, 0, 0};
+  const Op b{Xp + (int64_t)ct * nks_h * 8192, 0, 0};
   f32x16 acc[4][4];
   zero_acc<T>(acc);
-  mainloop<T, false>(a, b, H, smem, acc);      // packed operands carry their zero padding
+  mainloop<T>(a, b, H, smem, acc);
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int wm = w >> 1, wn = w & 1;
@@ -405,93 +381,82 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_tile_kernel(
   }
 
   if (store_z) {
-    // rows past V hold -inf here; the dlogits pass zeroes them
+    // rows past V hold products with Wp's zero padding; dlogits zeroes them
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = wn * 128 + j * 32 + (lane & 31);
+    for (int g = 0; g < 4; ++g) {
+      // vocabulary v = wm 128 + 32 i + 8 g + 4 (lane / 32) + 0..3, token r =
+      // wn 128 + 32 j + lane % 32: the lane's part of the LDS offset for this g
+      const int lo = zst_off(lane & 31, 8 * g + 4 * (lane >> 5));
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int v = wm * 128 + 32 * i + 8 * g + 4 * (lane >> 5);
+        for (int i = 0; i < 4; ++i) {
           uint2 pk;
           pk.x = pack_bf16x2(acc[i][j][4 * g], acc[i][j][4 * g + 1]);
           pk.y = pack_bf16x2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
-          *(uint2 *)(smem + zst_off(r, v)) = pk;
+          // + token row group (wn 4 + j) x 2 KB, + vocabulary slice (wm 4 + i) x 16 KB
+          *(uint2 *)(smem + lo + ((wn * 4 + j) << 11) + ((wm * 4 + i) << 14)) = pk;
         }
     }
     __syncthreads();
-    // blocks (ct, 8 vt + s) of Zp, s < 8, that exist (the tail tile may have fewer)
-    const int nslices = (int)min((int64_t)8, nks_z - 8 * (int64_t)vt);
+    // blocks (ct, 8 vt + s), s < 8, of Zp (whose slices cover V padded to 256)
     uint16_t *dst = Zp + ((int64_t)ct * nks_z + 8 * (int64_t)vt) * 8192;
-    const int n16 = nslices * 1024;                     // 16-byte units to copy
-    for (int q = threadIdx.x; q < n16; q += NTHREADS)
+    for (int q = threadIdx.x; q < 8 * 1024; q += NTHREADS)
       *(u32x4 *)(dst + q * 8) = *(const u32x4 *)(smem + q * 16);
   }
 }
 
 // ---------------------------------------------------------------- dlogits
-// One thread per 128-byte unit of Zp, in Zp's memory order: the unit holds
-// tokens r0..r0+7 x vocabulary v0..v0+7 (8 lanes of one fragment half).
+// One thread per 16-byte slot of Zp (one token, 8 consecutive vocabulary
+// columns), in memory order, so a wave reads and writes 1 KB contiguous and
+// its 64 lanes cover 32 consecutive tokens.  In place:
 // G = (exp(Z - lse) - onehot(y)) / N_valid on valid tokens, 0 on ignored
-// tokens and outside [0, c) x [0, V); rewritten in place in Zp and written
-// transposed to GTp.  Units of vocabulary tiles past Zp's slices (they only
-// exist in GTp's 256-row padding) are zero.
+// tokens and outside [0, c) x [0, V).
 __global__ __launch_bounds__(256) void dlogits_kernel(
-    uint16_t *__restrict__ Zp, int64_t nks_z, uint16_t *__restrict__ GTp, int64_t nks_c,
-    int c, int V, int64_t nks_zt, int64_t nunit, const float *__restrict__ lse_c,
-    const int64_t *__restrict__ labels_c, int64_t ii, const Scalars *__restrict__ sc) {
+    uint16_t *__restrict__ Zp, int64_t nks_z, int c, int V, int64_t nslot,
+    const float *__restrict__ lse_c, const int64_t *__restrict__ labels_c, int64_t ii,
+    const Scalars *__restrict__ sc) {
   const int64_t u = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-  if (u >= nunit) return;
-  // u = ((rt * nks_zt + ks) * 16 + f) * 8 + hk * 4 + rg
-  const int rg = (int)(u & 3), hk = (int)((u >> 2) & 1), f = (int)((u >> 3) & 15);
-  const int64_t blk = u >> 7;
-  const int64_t rt = blk / nks_zt, ks = blk - rt * nks_zt;
-  const int r0 = (int)(rt * 256) + (f >> 1) * 32 + rg * 8;
-  const int v0 = (int)(ks * 32) + (f & 1) * 16 + hk * 8;
+  if (u >= nslot) return;
+  // u = ((rt * nks_z + ks) * 16 + f) * 64 + slot, slot = 32 h + (r % 32 ^ 4 h ^ 8 (f % 2))
+  const int sl = (int)(u & 63), f = (int)((u >> 6) & 15);
+  const int64_t blk = u >> 10;
+  const int64_t rt = blk / nks_z, ks = blk - rt * nks_z;
+  const int h = sl >> 5;
+  const int r = (int)(rt * 256) + (f >> 1) * 32 + ((sl & 31) ^ (h << 2) ^ ((f & 1) << 3));
+  const int v0 = (int)(ks * 32) + (f & 1) * 16 + h * 8;
+  int64_t y = ii;
+  float l2 = 0.f;
+  if (r < c) {
+    y = labels_c[r];
+    l2 = lse_c[r] * kLog2e;
+  }
+  const bool valid = r < c && y != ii;
   const float inv = sc->inv_nvalid;
-  const bool inz = ks < nks_z;                       // the unit lies inside Zp
-  uint16_t *zu = Zp + ((rt * nks_z + ks) << 13) + (((f * 64 + hk * 32 + rg * 8)) << 3);
-  u32x4 g[8];
+  uint16_t *zu = Zp + (u << 3);
+  const u32x4 z = *(const u32x4 *)zu;
+  u32x4 g;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int r = r0 + i;
-    int64_t y = ii;
-    float l2 = 0.f;
-    if (r < c) {
-      y = labels_c[r];
-      l2 = lse_c[r] * kLog2e;
+  for (int d = 0; d < 4; ++d) {
+    float fv[2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int v = v0 + 2 * d + hh;
+      const float zz = hh ? bf16_hi(z[d]) : bf16_lo(z[d]);
+      const float e = __builtin_amdgcn_exp2f(zz * kLog2e - l2) - ((int64_t)v == y ? 1.f : 0.f);
+      fv[hh] = (valid && v < V) ? e * inv : 0.f;
     }
-    const bool valid = r < c && y != ii;
-    u32x4 z = inz ? *(const u32x4 *)(zu + i * 8) : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      float fv[2];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int v = v0 + 2 * d + h;
-        const float zz = h ? bf16_hi(z[d]) : bf16_lo(z[d]);
-        const float e = __builtin_amdgcn_exp2f(zz * kLog2e - l2) - ((int64_t)v == y ? 1.f : 0.f);
-        fv[h] = (valid && v < V) ? e * inv : 0.f;
-      }
-      g[i][d] = pack_bf16x2(fv[0], fv[1]);
-    }
-    if (inz) *(u32x4 *)(zu + i * 8) = g[i];
+    g[d] = pack_bf16x2(fv[0], fv[1]);
   }
-  if (r0 < nks_c * 32) {
-    u32x4 gt[8];
-    transpose8x8(g, gt);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) *(u32x4 *)(GTp + pk_off(v0 + j, r0, nks_c)) = gt[j];
-  }
+  *(u32x4 *)zu = g;
 }
 
 // ---------------------------------------------------------------- dX (split-K)
 // Unit (s, mt, nt): dxp[s][tok][h] = sum over vocabulary in split s of
-// G[tok][v] W[v][h].  G comes packed (rows = tokens), W as stored (MN-major).
+// G[tok][v] W[v][h].  G from Zp (rows = tokens), W from Wp read transposed.
 __global__ __launch_bounds__(NTHREADS, 1) void dx_kernel(
-    const uint16_t *__restrict__ Gp, int64_t nks_z, const uint16_t *__restrict__ W, int c, int H,
-    int V, int64_t ksplit, int nmt, int nnt, float *__restrict__ dxp) {
+    const uint16_t *__restrict__ Gp, int64_t nks_z, const uint16_t *__restrict__ Wp,
+    int64_t nks_h, int c, int H, int V, int64_t ksplit, int nmt, int nnt, float *__restrict__ dxp) {
   using T = DxTile;
   __shared__ __attribute__((aligned(1024))) char smem[T::LDS];
   const int unit = xcd_remap(blockIdx.x, gridDim.x);
@@ -503,14 +468,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void dx_kernel(
   const int64_t ke = kb + ksplit < V ? kb + ksplit : V;
   const int klen = (int)(ke - kb);
 
-  const Op a{Gp + ((int64_t)mt * nks_z + (kb >> 5)) * 8192, 8192, 256, klen};
-  const Op b{W + kb * H + n0, H, H - n0, klen};
+  const Op a{Gp + ((int64_t)mt * nks_z + (kb >> 5)) * 8192, 0, 0};
+  const Op b{Wp + (int64_t)(n0 >> 5) * 8192, nks_h * 8192, kb};
   f32x16 acc[4][4];
   zero_acc<T>(acc);
-  if (n0 + T::BN <= H && klen % BK == 0)
-    mainloop<T, false>(a, b, klen, smem, acc);
-  else
-    mainloop<T, true>(a, b, klen, smem, acc);
+  mainloop<T>(a, b, klen, smem, acc);
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int wm = w >> 1, wn = w & 1;
@@ -549,24 +511,25 @@ __global__ void dx_reduce_kernel(const float *__restrict__ dxp, int splitk, int 
 
 // ---------------------------------------------------------------- dW
 // dW[v][h] (+)= sum over the chunk's tokens of G[tok][v] X[tok][h], in
-// 256 x 128 tiles, two workgroups per CU so that one's dW traffic overlaps the
-// other's MFMA work.  Both operands come packed (GTp rows = vocabulary, XTp
-// rows = hidden, k = tokens).
+// BM x BN = 256 x 128 tiles, two workgroups per CU so that one's dW traffic
+// overlaps the other's MFMA work; G from Zp and X from Xp, both read
+// transposed.
 //
-// The epilogue goes through LDS in two halves of 128 rows (64 KB of fp32 each)
+// The epilogue goes through LDS in two halves of 128 rows (BN fp32 per row)
 // so that dW is read and written in row-contiguous 16-byte pieces: the waves
-// holding a half write their accumulators, then every thread moves 16 such
-// pieces, with all 16 loads of the current dW in flight before the adds.
-// LDS rows are 512 bytes; 128-byte column blocks are XOR-swizzled by row
-// bit 2 so the two row groups a write instruction covers use both bank halves.
+// holding a half write their accumulators, then every thread moves its
+// pieces, with all of its loads of the current dW in flight before the adds.
+// 128-byte column blocks of an LDS row are XOR-swizzled by row bit 2 so the
+// two rows a write instruction covers use both halves of the banks.
+template <int BN>
 __device__ __forceinline__ int dwst_off(int r, int col) {   // bytes
-  return r * 512 + ((((col >> 5) ^ ((r >> 2) & 1))) << 7) + ((col & 31) << 2);
+  return r * (BN * 4) + (((col >> 5) ^ ((r >> 2) & 1)) << 7) + ((col & 31) << 2);
 }
 
-__global__ __launch_bounds__(NTHREADS, 2) void dw_kernel(
-    const uint16_t *__restrict__ GTp, const uint16_t *__restrict__ XTp, int64_t nks_c, int c,
-    int H, int V, int nht, float *__restrict__ dW, int accumulate) {
-  using T = DwTile;
+template <class T, int OCC>
+__global__ __launch_bounds__(NTHREADS, OCC) void dw_kernel(
+    const uint16_t *__restrict__ Gp, int64_t nks_z, const uint16_t *__restrict__ Xp,
+    int64_t nks_h, int c, int H, int V, int nht, float *__restrict__ dW, int accumulate) {
   __shared__ __attribute__((aligned(1024))) char smem[T::LDS];
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
   const int vt = tile / nht, ht = tile - vt * nht;
@@ -576,11 +539,14 @@ __global__ __launch_bounds__(NTHREADS, 2) void dw_kernel(
 
   f32x16 acc[T::MI][T::NI];
   zero_acc<T>(acc);
-  const Op a{GTp + (int64_t)vt * nks_c * 8192, 8192, 256, c};
-  const Op b{XTp + (int64_t)(ht >> 1) * nks_c * 8192 + (ht & 1) * 4096, 8192, 128, c};
-  mainloop<T, false>(a, b, c, smem, acc);
+  const Op a{Gp + (int64_t)(m0 >> 5) * 8192, nks_z * 8192, 0};
+  const Op b{Xp + (int64_t)(n0 >> 5) * 8192, nks_h * 8192, 0};
+  mainloop<T>(a, b, c, smem, acc);
 
-  static_assert(T::LDS >= 128 * 512, "epilogue half tile must fit in LDS");
+  constexpr int TPR = T::BN / 4;            // threads per row: one 16-byte piece each
+  constexpr int RPP = NTHREADS / TPR;       // rows per pass of the workgroup
+  constexpr int NQ = 128 / RPP;             // pieces per thread per half
+  static_assert(T::BM == 256 && T::LDS >= 128 * T::BN * 4, "epilogue half tile must fit in LDS");
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
     if (wm == half) {
@@ -592,27 +558,28 @@ __global__ __launch_bounds__(NTHREADS, 2) void dw_kernel(
           for (int e = 0; e < 16; ++e) {
             const int r = 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
             const int col = wn * T::WN + 32 * j + (lane & 31);
-            *(float *)(smem + dwst_off(r, col)) = acc[i][j][e];
+            *(float *)(smem + dwst_off<T::BN>(r, col)) = acc[i][j][e];
           }
     }
     __syncthreads();
-    // 128 rows x 32 pieces of 16 bytes; thread t takes piece t % 32 of rows t/32 + 8 q
-    const int pc = threadIdx.x & 31, col = pc * 4;
+    // thread t takes piece t % TPR of rows t / TPR + RPP q
+    const int col = (threadIdx.x % TPR) * 4;
     const int h = n0 + col;
-    float4 old[16];
+    const int rb = threadIdx.x / TPR;
+    float4 old[NQ];
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int v = m0 + half * 128 + (threadIdx.x >> 5) + 8 * q;
+    for (int q = 0; q < NQ; ++q) {
+      const int v = m0 + half * 128 + rb + RPP * q;
       const bool ok = v < V && h < H;            // H % 8 == 0: a started piece fits
       old[q] = (accumulate && ok) ? *(const float4 *)(dW + (int64_t)v * H + h)
                                   : make_float4(0.f, 0.f, 0.f, 0.f);
     }
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int r = (threadIdx.x >> 5) + 8 * q;
+    for (int q = 0; q < NQ; ++q) {
+      const int r = rb + RPP * q;
       const int v = m0 + half * 128 + r;
       if (v < V && h < H) {
-        const float4 add = *(const float4 *)(smem + dwst_off(r, col));
+        const float4 add = *(const float4 *)(smem + dwst_off<T::BN>(r, col));
         float4 o = old[q];
         o.x += add.x; o.y += add.y; o.z += add.z; o.w += add.w;
         *(float4 *)(dW + (int64_t)v * H + h) = o;
@@ -631,12 +598,10 @@ inline int grid_for(int64_t n, int block, int cap) {
 }  // namespace
 
 hipError_t launch_pack_bf16(const uint16_t *src, int R, int K, uint16_t *P, int64_t nks_p,
-                            uint16_t *PT, int64_t nks_pt, hipStream_t s) {
-  const int kb8 = (K + 255) / 256 * 32;              // 8-wide column blocks over K rounded to 256
-  const int64_t rb8 = (int64_t)(R + 255) / 256 * 32;  // 8-tall row blocks over R rounded to 256
-  const int64_t nblk = rb8 * kb8;
-  hipLaunchKernelGGL(pack_kernel, dim3((unsigned)((nblk + 255) / 256)), dim3(256), 0, s, src, R, K,
-                     kb8, nblk, P, nks_p, PT, nks_pt);
+                            hipStream_t s) {
+  // nks_p is a multiple of 8, so column pairs of slices tile it exactly
+  const int64_t nwg = (int64_t)(R + 255) / 256 * (nks_p / 2);
+  hipLaunchKernelGGL(pack_kernel, dim3((unsigned)nwg), dim3(256), 0, s, src, R, K, P, nks_p);
   return hipGetLastError();
 }
 
@@ -661,22 +626,22 @@ hipError_t launch_fwd_tile_bf16(const uint16_t *Wp, const uint16_t *Xp, int64_t 
   return hipGetLastError();
 }
 
-hipError_t launch_dlogits_bf16(uint16_t *Zp, int64_t nks_z, uint16_t *GTp, int64_t nks_c, int c,
-                               int V, const float *lse_c, const int64_t *labels_c, int64_t ii,
-                               const Scalars *sc, hipStream_t s) {
-  // units over tokens [0, c rounded to 256) x vocabulary [0, V rounded to 256)
-  const int64_t nks_zt = (V + 255) / 256 * 8;        // Zp slices padded to whole 256 tiles
-  const int64_t nunit = (int64_t)((c + 255) / 256) * nks_zt * 128;
-  hipLaunchKernelGGL(dlogits_kernel, dim3((unsigned)((nunit + 255) / 256)), dim3(256), 0, s, Zp,
-                     nks_z, GTp, nks_c, c, V, nks_zt, nunit, lse_c, labels_c, ii, sc);
+hipError_t launch_dlogits_bf16(uint16_t *Zp, int64_t nks_z, int c, int V, const float *lse_c,
+                               const int64_t *labels_c, int64_t ii, const Scalars *sc,
+                               hipStream_t s) {
+  // 16-byte slots over the row tiles that cover [0, c), every slice of Zp
+  const int64_t nslot = (int64_t)((c + 255) / 256) * nks_z * 1024;
+  hipLaunchKernelGGL(dlogits_kernel, dim3((unsigned)((nslot + 255) / 256)), dim3(256), 0, s, Zp,
+                     nks_z, c, V, nslot, lse_c, labels_c, ii, sc);
   return hipGetLastError();
 }
 
-hipError_t launch_dx_bf16(const uint16_t *Gp, int64_t nks_z, const uint16_t *W, int c, int H,
-                          int V, int splitk, int64_t ksplit, float *dxp, hipStream_t s) {
+hipError_t launch_dx_bf16(const uint16_t *Gp, int64_t nks_z, const uint16_t *Wp, int64_t nks_h,
+                          int c, int H, int V, int splitk, int64_t ksplit, float *dxp,
+                          hipStream_t s) {
   const int nmt = (c + DxTile::BM - 1) / DxTile::BM, nnt = (H + DxTile::BN - 1) / DxTile::BN;
-  hipLaunchKernelGGL(dx_kernel, dim3(splitk * nmt * nnt), dim3(NTHREADS), 0, s, Gp, nks_z, W, c,
-                     H, V, ksplit, nmt, nnt, dxp);
+  hipLaunchKernelGGL(dx_kernel, dim3(splitk * nmt * nnt), dim3(NTHREADS), 0, s, Gp, nks_z, Wp,
+                     nks_h, c, H, V, ksplit, nmt, nnt, dxp);
   return hipGetLastError();
 }
 
@@ -688,11 +653,11 @@ hipError_t launch_dx_reduce_bf16(const float *dxp, int splitk, int c, int H, uin
   return hipGetLastError();
 }
 
-hipError_t launch_dw_bf16(const uint16_t *GTp, const uint16_t *XTp, int64_t nks_c, int c, int H,
-                          int V, float *dW, bool accumulate, hipStream_t s) {
+hipError_t launch_dw_bf16(const uint16_t *Gp, int64_t nks_z, const uint16_t *Xp, int64_t nks_h,
+                          int c, int H, int V, float *dW, bool accumulate, hipStream_t s) {
   const int nvt = (V + DwTile::BM - 1) / DwTile::BM, nht = (H + DwTile::BN - 1) / DwTile::BN;
-  hipLaunchKernelGGL(dw_kernel, dim3(nvt * nht), dim3(NTHREADS), 0, s, GTp, XTp, nks_c, c, H, V,
-                     nht, dW, accumulate ? 1 : 0);
+  hipLaunchKernelGGL((dw_kernel<DwTile, kDwOcc>), dim3(nvt * nht), dim3(NTHREADS), 0, s, Gp, nks_z, Xp, nks_h, c, H,
+                     V, nht, dW, accumulate ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -114,18 +114,38 @@ def test_workspace_bounded_by_chunk_not_N():
     sizes = [fl.flce_workspace_bytes(16384, H, V, fl.FLCE_BF16, c) for c in (512, 1024, 4096)]
     assert sizes[0] < sizes[1] < sizes[2]
     for c, s in zip((512, 1024, 4096), sizes):
-        assert s >= c * V * 2                                  # the bf16 logits chunk
-        # plus its transposed copy, the packed X chunk, partials and split-K sums
-        assert s < c * V * 2 * 3.5 + V * H * 2.2   # and W packed once per call
+        assert s >= c * V * 2 + V * H * 2          # the bf16 logits chunk and W packed once
+        # plus the packed X chunk, log-sum-exp partials and split-K sums
+        assert s < c * V * 2 * 2 + V * H * 2.2
     full_logits = 16384 * V * 2
     assert sizes[1] - V * H * 2 < full_logits / 5
 
 
+def _wp_bytes(H, V):
+    """The packed copy of W: rows and columns padded to 256, bf16."""
+    return (V + 255) // 256 * 256 * ((H + 255) // 256 * 256) * 2
+
+
+def _largest_fitting_chunk(N, H, V, budget):
+    """The rule flce_plan states: the largest power-of-two multiple of 256 tokens
+    (at most N) whose chunk-dependent scratch (workspace minus packed W) fits."""
+    best, c = None, 256
+    while True:
+        cc = min(c, N)
+        if fl.flce_workspace_bytes(N, H, V, fl.FLCE_BF16, cc) - _wp_bytes(H, V) > budget:
+            return best
+        best = cc
+        if c >= N:
+            return best
+        c *= 2
+
+
 def test_plan_auto_and_explicit():
     st, c, peak = fl.flce_plan(8192, 2304, 256000, fl.FLCE_BF16)      # large-vocabulary head
-    assert st == fl.FLCE_OK and c == 2048
+    assert st == fl.FLCE_OK and c == _largest_fitting_chunk(8192, 2304, 256000, 3 << 30)
+    assert c in (2048, 4096)
     assert peak == fl.flce_workspace_bytes(8192, 2304, 256000, fl.FLCE_BF16, 0)
-    assert peak - 256000 * 2304 * 2 <= 3 << 30
+    assert peak - _wp_bytes(2304, 256000) <= 3 << 30
     st, c, peak = fl.flce_plan(8192, 4096, 128256, fl.FLCE_BF16, chunk_tokens=1024)
     assert st == fl.FLCE_OK and c == 1024
     assert peak == fl.flce_workspace_bytes(8192, 4096, 128256, fl.FLCE_BF16, 1024)
@@ -135,8 +155,12 @@ def test_plan_auto_and_explicit():
     assert st == fl.FLCE_OK and c == 100
     st, c, _ = fl.flce_plan(8192, 4096, 128256, fl.FLCE_BF16, scratch_budget_bytes=1 << 20)
     assert st == fl.FLCE_EWORKSPACE and c == 256                          # smallest chunk reported
-    st, c, _ = fl.flce_plan(8192, 4096, 128256, fl.FLCE_BF16, scratch_budget_bytes=800 << 20)
-    assert st == fl.FLCE_OK and c == 1024                     # 1024 fits 800 MB, 2048 does not
+    for budget in (300 << 20, 800 << 20, 1500 << 20):
+        st, c, _ = fl.flce_plan(8192, 4096, 128256, fl.FLCE_BF16, scratch_budget_bytes=budget)
+        assert st == fl.FLCE_OK and c == _largest_fitting_chunk(8192, 4096, 128256, budget)
+        if c < 8192:       # the next chunk up does not fit
+            nxt = fl.flce_workspace_bytes(8192, 4096, 128256, fl.FLCE_BF16, 2 * c)
+            assert nxt - _wp_bytes(4096, 128256) > budget
     st, c, peak = fl.flce_plan(0, 64, 100, fl.FLCE_BF16)
     assert st == fl.FLCE_OK and c == 0 and peak > 0
 
