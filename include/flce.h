@@ -76,7 +76,8 @@ size_t flce_workspace_bytes(int64_t N, int64_t H, int64_t V, int dtype, int64_t 
  * (<= 0: choose the largest power-of-two multiple of 256 tokens, at most N,
  * whose chunk scratch fits scratch_budget_bytes; 0 budget = the default).
  * The budget bounds the scratch that grows with the chunk; on the bf16 path a
- * packed copy of W (V x H bf16, both rounded up to 256) comes on top of it.
+ * pair of packed copies of W (as is and transposed, each V x H bf16 with both
+ * rounded up to 256) comes on top of it.
  * On return *chunk_tokens holds the chunk that will be used and
  * *peak_scratch_bytes (may be NULL) the whole workspace it needs, which is the
  * peak device scratch of a call.  Host only; no device call.

@@ -176,9 +176,13 @@ int run(bool bwd, const void *X, const void *W, const int64_t *labels, int64_t N
   LAUNCH(FLCE_K_LABELS, launch_label_check(labels, N, V, ii, sc, s));
   if (bwd && N == 0) LAUNCH(FLCE_K_FINAL, launch_fill_f32(dW, V * H, 0.f, s));
 
-  if (dtype == FLCE_BF16 && N > 0)
+  if (dtype == FLCE_BF16 && N > 0) {
     LAUNCH(FLCE_K_PACK, launch_pack_bf16((const uint16_t *)W, Vi, Hi, (uint16_t *)(ws + p.off_wp),
                                          p.nks_h, s));
+    if (bwd)
+      LAUNCH(FLCE_K_PACK, launch_pack_t_bf16((const uint16_t *)W, Vi, Hi,
+                                             (uint16_t *)(ws + p.off_wtp), p.nks_z, s));
+  }
   for (int64_t c0 = 0; c0 < N; c0 += C) {
     const int c = (int)std::min(C, N - c0);
     const int64_t *lab = labels + c0;
@@ -196,8 +200,8 @@ int run(bool bwd, const void *X, const void *W, const int64_t *labels, int64_t N
       if (bwd) {
         LAUNCH(FLCE_K_DLOGITS, launch_dlogits_bf16(Zp, p.nks_z, c, Vi, lse, lab, ii, sc, s));
         float *dxp = (float *)(ws + p.off_dxp);
-        LAUNCH(FLCE_K_DX_GEMM, launch_dx_bf16(Zp, p.nks_z, Wp, p.nks_h, c, Hi, Vi, p.splitk,
-                                              p.ksplit, dxp, s));
+        LAUNCH(FLCE_K_DX_GEMM, launch_dx_bf16(Zp, p.nks_z, (const uint16_t *)(ws + p.off_wtp), c,
+                                              Hi, Vi, p.splitk, p.ksplit, dxp, s));
         LAUNCH(FLCE_K_DX_REDUCE,
                launch_dx_reduce_bf16(dxp, p.splitk, c, Hi, (uint16_t *)dX + c0 * H, s));
         LAUNCH(FLCE_K_DW_GEMM, launch_dw_bf16(Zp, p.nks_z, Xp, p.nks_h, c, Hi, Vi, dW, c0 > 0, s));
@@ -275,9 +279,12 @@ void make_plan(int64_t N, int64_t H, int64_t V, int dtype, int64_t C, Plan *p) {
     // packed layouts: rows and columns padded to 256 (see flce_internal.h)
     p->nks_z = cdiv(V, 256) * 8;
     p->nks_h = cdiv(H, 256) * 8;
-    const size_t cpad = (size_t)round_up(C, 256), vpad = (size_t)round_up(V, 256);
+    const size_t cpad = (size_t)round_up(C, 256), vpad = (size_t)round_up(V, 256),
+                 hpad = (size_t)round_up(H, 256);
     p->off_wp = o;                       // W packed once per call (rows = vocabulary)
     o += align256(vpad * p->nks_h * 64);
+    p->off_wtp = o;                      // and transposed (rows = hidden), for dX
+    o += align256(hpad * p->nks_z * 64);
     p->off_z = o;                        // logits, then G, of the chunk (rows = tokens)
     o += align256(cpad * p->nks_z * 64);
     p->off_xp = o;                       // the chunk's X (rows = tokens)

@@ -34,7 +34,7 @@ struct Plan {
   int64_t nvt = 0;      // vocabulary tiles = log-sum-exp partials per token
   int splitk = 0;       // K-splits of the dX GEMM (0: the fp32 path writes dX directly)
   int64_t ksplit = 0;   // vocabulary rows per split (multiple of 64)
-  size_t off_wp = 0, off_z = 0, off_xp = 0, off_pm = 0, off_ps = 0, off_zy = 0, off_lse = 0,
+  size_t off_wp = 0, off_wtp = 0, off_z = 0, off_xp = 0, off_pm = 0, off_ps = 0, off_zy = 0, off_lse = 0,
          off_rowloss = 0, off_dxp = 0, off_scal = 0, total = 0;
 };
 
@@ -68,9 +68,12 @@ hipError_t launch_fwd_tile_bf16(const uint16_t *Wp, const uint16_t *Xp, int64_t 
 hipError_t launch_dlogits_bf16(uint16_t *Zp, int64_t nks_z, int c, int V, const float *lse_c,
                                const int64_t *labels_c, int64_t ii, const Scalars *sc,
                                hipStream_t s);
-hipError_t launch_dx_bf16(const uint16_t *Gp, int64_t nks_z, const uint16_t *Wp, int64_t nks_h,
-                          int c, int H, int V, int splitk, int64_t ksplit, float *dxp,
-                          hipStream_t s);
+// Pack the transpose of a row-major [R][K] matrix into PT (rows K padded to
+// 256, nks_t column slices covering R).
+hipError_t launch_pack_t_bf16(const uint16_t *src, int R, int K, uint16_t *PT, int64_t nks_t,
+                              hipStream_t s);
+hipError_t launch_dx_bf16(const uint16_t *Gp, int64_t nks_z, const uint16_t *WTp, int c, int H,
+                          int V, int splitk, int64_t ksplit, float *dxp, hipStream_t s);
 hipError_t launch_dx_reduce_bf16(const float *dxp, int splitk, int c, int H, uint16_t *dXc,
                                  hipStream_t s);
 hipError_t launch_dw_bf16(const uint16_t *Gp, int64_t nks_z, const uint16_t *Xp, int64_t nks_h,

@@ -10,7 +10,9 @@
 //               the target logit, and the bf16 logits into Zp (rows = tokens,
 //               k = vocabulary);
 //   dlogits   Zp rewritten in place into G = (softmax - onehot) / N_valid;
-//   dX        dX_c  = G_c W        M = c, N = H, K = V (split-K, fp32 partials)
+//   dX        dX_c  = G_c W        M = c, N = H, K = V (split-K, fp32 partials),
+//             W from WTp, a second packed copy of W made once per call (rows =
+//             hidden, k = vocabulary);
 //   dW        dW   (+)= G_c^T X_c  M = V, N = H, K = c (fp32)
 //
 // GEMM tiles: a workgroup of 4 waves (2 x 2) computes a BM x BN fp32 tile with
@@ -81,6 +83,20 @@ __device__ __forceinline__ int xcd_remap(int b, int nb) {
   int xcd = b & 7, idx = b >> 3;
   int per = nb >> 3, rem = nb & 7;
   return xcd * per + (xcd < rem ? xcd : rem) + idx;
+}
+
+// Grouped order of an nrow x ncol tile grid: logical tiles run down a group
+// of G rows, then on to the next column, so that the tiles resident on one
+// XCD at a time form a G x (slots / G) block whose row and column operand
+// strips both stay in its L2.  Bijective.
+template <int G>
+__device__ __forceinline__ void grouped(int t, int nrow, int ncol, int &row, int &col) {
+  const int g = t / (G * ncol);
+  const int r0 = g * G;
+  const int gs = min(G, nrow - r0);
+  const int l = t - g * G * ncol;
+  row = r0 + l % gs;
+  col = l / gs;
 }
 
 template <int BM_, int BN_, int STAGES_, int KA_, int KB_>
@@ -162,10 +178,11 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-// s_waitcnt vmcnt(groups * PER) for a runtime number of groups in 0..2.
+// s_waitcnt vmcnt(groups * PER) for a runtime number of groups in 0..3.
 template <int PER>
 __device__ __forceinline__ void wait_groups(int groups) {
-  if (groups >= 2) wait_vm<2 * PER>();
+  if (groups >= 3) wait_vm<3 * PER>();
+  else if (groups == 2) wait_vm<2 * PER>();
   else if (groups == 1) wait_vm<PER>();
   else wait_vm<0>();
 }
@@ -266,7 +283,7 @@ __device__ __forceinline__ float bf16_lo(uint32_t u) { return __builtin_bit_cast
 __device__ __forceinline__ float bf16_hi(uint32_t u) { return __builtin_bit_cast(float, u & 0xFFFF0000u); }
 
 using FwdTile = Tile<256, 256, 4, PACKED, PACKED>;     // A = Wp, B = Xp
-using DxTile = Tile<256, 256, 4, PACKED, PACKED_T>;    // A = G (Zp), B = Wp read transposed
+using DxTile = Tile<256, 256, 4, PACKED, PACKED>;      // A = G (Zp), B = WTp
 using DwTile = Tile<256, 128, 3, PACKED_T, PACKED_T>;  // A = G (Zp), B = Xp, both transposed
 constexpr int kDwOcc = 2;                              // dW workgroups per CU
 
@@ -299,6 +316,59 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint16_t *__restrict__ 
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int q = i * 256 + threadIdx.x;
+    *(u32x4 *)(dst + q * 8) = *(const u32x4 *)(lds + q * 16);
+  }
+}
+
+// Transpose an 8 x 8 block of 16-bit values held as 8 rows of 16 bytes:
+// out[j] holds element j of rows 0..7, two per dword, low half first.
+__device__ __forceinline__ void transpose8x8(const u32x4 (&in)[8], u32x4 (&out)[8]) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int pp = 0; pp < 4; ++pp) {
+      const uint32_t lo = in[2 * pp][j >> 1], hi = in[2 * pp + 1][j >> 1];
+      out[j][pp] = (j & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
+    }
+}
+
+// Transposed packing: the packed matrix PT has the columns of a row-major
+// bf16 [R][K] source as rows (rows = K, columns = R, nks_t column slices).
+// One workgroup per 256 rows x 64 columns of PT (two blocks, 32 KB): thread t
+// loads the 8 x 8 source block at source rows 64 p + 8 (t / 32) and columns
+// 256 rt + 8 (t % 32) (a wave reads 2 source rows x 512 contiguous bytes per
+// instruction), transposes it in registers, places its 8 row pieces in LDS in
+// packed order and the workgroup writes both blocks as one 32 KB copy.
+__global__ __launch_bounds__(256) void pack_t_kernel(const uint16_t *__restrict__ src, int R,
+                                                    int K, uint16_t *__restrict__ PT,
+                                                    int64_t nks_t) {
+  __shared__ __attribute__((aligned(1024))) char lds[32768];
+  const int npair = (int)(nks_t >> 1);
+  const int rt = blockIdx.x / npair;                  // row tile of PT = 256 source columns
+  const int kp = blockIdx.x - rt * npair;             // pair of PT column slices = 64 source rows
+  const int t = threadIdx.x;
+  const int r0 = kp * 64 + (t >> 5) * 8;              // source rows r0..r0+7 = PT columns
+  const int c0 = rt * 256 + (t & 31) * 8;             // source columns c0..c0+7 = PT rows
+  u32x4 in[8], out[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    in[i] = (r0 + i < R && c0 < K) ? *(const u32x4 *)(src + (int64_t)(r0 + i) * K + c0)
+                                   : u32x4{0u, 0u, 0u, 0u};
+  transpose8x8(in, out);
+  const int k = (t >> 5) * 8;                         // PT column within the pair, 0..56
+  const int kk = k & 31;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int r = (t & 31) * 8 + j;                   // PT row within the tile
+    const int off = ((k >> 5) << 14) + ((((r >> 5) << 1) + (kk >> 4)) << 10) +
+                    (pk_slot(r & 31, (kk >> 3) & 1, kk >> 4) << 4);
+    *(u32x4 *)(lds + off) = out[j];
+  }
+  __syncthreads();
+  uint16_t *dst = PT + (((int64_t)rt * nks_t + 2 * kp) << 13);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int q = i * 256 + t;
     *(u32x4 *)(dst + q * 8) = *(const u32x4 *)(lds + q * 16);
   }
 }
@@ -453,23 +523,25 @@ __global__ __launch_bounds__(256) void dlogits_kernel(
 
 // ---------------------------------------------------------------- dX (split-K)
 // Unit (s, mt, nt): dxp[s][tok][h] = sum over vocabulary in split s of
-// G[tok][v] W[v][h].  G from Zp (rows = tokens), W from Wp read transposed.
+// G[tok][v] W[v][h].  G from Zp (rows = tokens), W from WTp (rows = hidden),
+// both with the vocabulary along k.
 __global__ __launch_bounds__(NTHREADS, 1) void dx_kernel(
-    const uint16_t *__restrict__ Gp, int64_t nks_z, const uint16_t *__restrict__ Wp,
-    int64_t nks_h, int c, int H, int V, int64_t ksplit, int nmt, int nnt, float *__restrict__ dxp) {
+    const uint16_t *__restrict__ Gp, int64_t nks_z, const uint16_t *__restrict__ WTp,
+    int c, int H, int V, int64_t ksplit, int nmt, int nnt, float *__restrict__ dxp) {
   using T = DxTile;
   __shared__ __attribute__((aligned(1024))) char smem[T::LDS];
   const int unit = xcd_remap(blockIdx.x, gridDim.x);
   const int per = nmt * nnt;
+  // token tile fastest: the few token tiles of a split share each W block
   const int s = unit / per, rem = unit - s * per;
-  const int mt = rem / nnt, nt = rem - mt * nnt;
+  const int nt = rem / nmt, mt = rem - nt * nmt;
   const int m0 = mt * T::BM, n0 = nt * T::BN;
   const int64_t kb = (int64_t)s * ksplit;
   const int64_t ke = kb + ksplit < V ? kb + ksplit : V;
   const int klen = (int)(ke - kb);
 
   const Op a{Gp + ((int64_t)mt * nks_z + (kb >> 5)) * 8192, 0, 0};
-  const Op b{Wp + (int64_t)(n0 >> 5) * 8192, nks_h * 8192, kb};
+  const Op b{WTp + ((int64_t)nt * nks_z + (kb >> 5)) * 8192, 0, 0};
   f32x16 acc[4][4];
   zero_acc<T>(acc);
   mainloop<T>(a, b, klen, smem, acc);
@@ -529,10 +601,10 @@ __device__ __forceinline__ int dwst_off(int r, int col) {   // bytes
 template <class T, int OCC>
 __global__ __launch_bounds__(NTHREADS, OCC) void dw_kernel(
     const uint16_t *__restrict__ Gp, int64_t nks_z, const uint16_t *__restrict__ Xp,
-    int64_t nks_h, int c, int H, int V, int nht, float *__restrict__ dW, int accumulate) {
+    int64_t nks_h, int c, int H, int V, int nvt, int nht, float *__restrict__ dW, int accumulate) {
   __shared__ __attribute__((aligned(1024))) char smem[T::LDS];
-  const int tile = xcd_remap(blockIdx.x, gridDim.x);
-  const int vt = tile / nht, ht = tile - vt * nht;
+  int vt, ht;
+  grouped<8>(xcd_remap(blockIdx.x, gridDim.x), nvt, nht, vt, ht);
   const int m0 = vt * T::BM, n0 = ht * T::BN;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int wm = w >> 1, wn = w & 1;
@@ -636,12 +708,19 @@ hipError_t launch_dlogits_bf16(uint16_t *Zp, int64_t nks_z, int c, int V, const 
   return hipGetLastError();
 }
 
-hipError_t launch_dx_bf16(const uint16_t *Gp, int64_t nks_z, const uint16_t *Wp, int64_t nks_h,
-                          int c, int H, int V, int splitk, int64_t ksplit, float *dxp,
-                          hipStream_t s) {
+hipError_t launch_pack_t_bf16(const uint16_t *src, int R, int K, uint16_t *PT, int64_t nks_t,
+                              hipStream_t s) {
+  // nks_t is a multiple of 8, so column pairs of slices tile it exactly
+  const int64_t nwg = (int64_t)(K + 255) / 256 * (nks_t / 2);
+  hipLaunchKernelGGL(pack_t_kernel, dim3((unsigned)nwg), dim3(256), 0, s, src, R, K, PT, nks_t);
+  return hipGetLastError();
+}
+
+hipError_t launch_dx_bf16(const uint16_t *Gp, int64_t nks_z, const uint16_t *WTp, int c, int H,
+                          int V, int splitk, int64_t ksplit, float *dxp, hipStream_t s) {
   const int nmt = (c + DxTile::BM - 1) / DxTile::BM, nnt = (H + DxTile::BN - 1) / DxTile::BN;
-  hipLaunchKernelGGL(dx_kernel, dim3(splitk * nmt * nnt), dim3(NTHREADS), 0, s, Gp, nks_z, Wp,
-                     nks_h, c, H, V, ksplit, nmt, nnt, dxp);
+  hipLaunchKernelGGL(dx_kernel, dim3(splitk * nmt * nnt), dim3(NTHREADS), 0, s, Gp, nks_z, WTp,
+                     c, H, V, ksplit, nmt, nnt, dxp);
   return hipGetLastError();
 }
 
@@ -657,7 +736,7 @@ hipError_t launch_dw_bf16(const uint16_t *Gp, int64_t nks_z, const uint16_t *Xp,
                           int c, int H, int V, float *dW, bool accumulate, hipStream_t s) {
   const int nvt = (V + DwTile::BM - 1) / DwTile::BM, nht = (H + DwTile::BN - 1) / DwTile::BN;
   hipLaunchKernelGGL((dw_kernel<DwTile, kDwOcc>), dim3(nvt * nht), dim3(NTHREADS), 0, s, Gp, nks_z, Xp, nks_h, c, H,
-                     V, nht, dW, accumulate ? 1 : 0);
+                     V, nvt, nht, dW, accumulate ? 1 : 0);
   return hipGetLastError();
 }
 

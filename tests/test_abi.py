@@ -114,16 +114,17 @@ def test_workspace_bounded_by_chunk_not_N():
     sizes = [fl.flce_workspace_bytes(16384, H, V, fl.FLCE_BF16, c) for c in (512, 1024, 4096)]
     assert sizes[0] < sizes[1] < sizes[2]
     for c, s in zip((512, 1024, 4096), sizes):
-        assert s >= c * V * 2 + V * H * 2          # the bf16 logits chunk and W packed once
+        assert s >= c * V * 2 + V * H * 4          # the bf16 logits chunk and W packed twice
         # plus the packed X chunk, log-sum-exp partials and split-K sums
-        assert s < c * V * 2 * 2 + V * H * 2.2
+        assert s < c * V * 2 * 2 + V * H * 4.4
     full_logits = 16384 * V * 2
-    assert sizes[1] - V * H * 2 < full_logits / 5
+    assert sizes[1] - V * H * 4 < full_logits / 5
 
 
 def _wp_bytes(H, V):
-    """The packed copy of W: rows and columns padded to 256, bf16."""
-    return (V + 255) // 256 * 256 * ((H + 255) // 256 * 256) * 2
+    """The two packed copies of W (as is and transposed): rows and columns
+    padded to 256, bf16."""
+    return 2 * ((V + 255) // 256 * 256) * ((H + 255) // 256 * 256) * 2
 
 
 def _largest_fitting_chunk(N, H, V, budget):
