@@ -52,6 +52,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
@@ -638,23 +639,23 @@ __global__ __launch_bounds__(NTHREADS, OCC) void dw_kernel(
     const int col = (threadIdx.x % TPR) * 4;
     const int h = n0 + col;
     const int rb = threadIdx.x / TPR;
-    float4 old[NQ];
+    // dW is touched once per chunk: non-temporal accesses keep it from
+    // evicting the G and X strips that the next tiles reuse from L2
+    f32x4 old[NQ];
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
       const int v = m0 + half * 128 + rb + RPP * q;
       const bool ok = v < V && h < H;            // H % 8 == 0: a started piece fits
-      old[q] = (accumulate && ok) ? *(const float4 *)(dW + (int64_t)v * H + h)
-                                  : make_float4(0.f, 0.f, 0.f, 0.f);
+      old[q] = (accumulate && ok) ? __builtin_nontemporal_load((const f32x4 *)(dW + (int64_t)v * H + h))
+                                  : f32x4{0.f, 0.f, 0.f, 0.f};
     }
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
       const int r = rb + RPP * q;
       const int v = m0 + half * 128 + r;
       if (v < V && h < H) {
-        const float4 add = *(const float4 *)(smem + dwst_off<T::BN>(r, col));
-        float4 o = old[q];
-        o.x += add.x; o.y += add.y; o.z += add.z; o.w += add.w;
-        *(float4 *)(dW + (int64_t)v * H + h) = o;
+        const f32x4 add = *(const f32x4 *)(smem + dwst_off<T::BN>(r, col));
+        __builtin_nontemporal_store(old[q] + add, (f32x4 *)(dW + (int64_t)v * H + h));
       }
     }
     __syncthreads();

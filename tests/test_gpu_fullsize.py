@@ -81,8 +81,14 @@ def test_fullsize(wid, chunk):
     ign = torch.from_numpy(ref["ign"]).to(dX_t.device)
     assert bool((dX_t[ign] == 0).all())
     assert bool(torch.isfinite(dW_t).all()) and bool(torch.isfinite(dX_t.float()).all())
-    # every dlogits row sums to ~0, so the columns of dW sum to ~0
-    col = dW_t.double().sum(dim=0).abs().max().item()
-    assert col <= 2e-2 * dW_t.abs().max().item()
+    # Every dlogits row sums to 0, so the columns of dW sum to 0 up to the
+    # rounding of G to bf16 (relative 2^-9 per element): a row's sum is then at
+    # most 2^-9 sum_v |G| <= 2^-8 / N_valid, hence
+    #   |sum_v dW[v, h]| <= 2^-8 / N_valid * sum_{valid t} |X[t, h]|
+    # (plus fp32 accumulation, far below it).
+    col = dW_t.double().sum(dim=0).abs().cpu().numpy()
+    valid = inp.labels != -100
+    bound = 2.0 ** -8 / valid.sum() * np.abs(inp.X_f64()[valid]).sum(axis=0)
+    assert np.all(col <= bound + 1e-6 * dW_t.abs().max().item())
     del g
     torch.cuda.empty_cache()
