@@ -12,16 +12,25 @@ FLOPs are counted as 6 N H V per step (three GEMMs of 2 N H V each).
 
 Printed: one JSON line on stdout.  ``roofline`` describes the kernel class
 with the largest total time, from HIP events recorded around each launch on
-the launch stream during the timed steps; ``cpu_baseline`` times the fp64
-oracle on a bounded sample of the same workload on the host cores.
+the launch stream during the timed steps.  Its ``traffic`` is the HBM bytes
+per launch of that kernel measured by rocprofv3 counters (FETCH_SIZE and
+WRITE_SIZE, each scaled by what the counter reads for a plain copy of known
+size), taken from the summary under profiles/ for this workload; it is null
+when no summary covers the kernel or the kernel source has changed since the
+counters were taken (the summary records the source's SHA-256).
+``cpu_baseline`` times the fp64 oracle on a bounded sample of the same
+workload on the host cores.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
 import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
 
 METRIC = "FLCE fwd+bwd tokens/s and TFLOP/s (% bf16 MFMA peak), Llama-3-8B head"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
@@ -32,22 +41,49 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_work(name, chunks, H, V, ldz):
+def kernel_work(name, chunks, H, V):
     """Algorithmic work of one kernel class summed over a step's launches.
 
-    Returns (bound, amount, unit): flops for the GEMMs, bytes for the rest."""
+    Returns (bound, amount, unit): flops for the GEMM tiles whose roofline is
+    MFMA, bytes for the rest (each array read or written once)."""
     if name in ("fwd_tile", "dx_gemm"):
         return "mfma", sum(2.0 * c * H * V for c in chunks), "flop"
     if name == "dw_gemm":
-        # fp32 dW read-modify-write (store only on the first chunk) + G + X reads
+        # 2 c H V flops against the fp32 dW read-modify-write (a store only on
+        # the first chunk) plus G and X: below the MFMA ridge, so bytes bound it
         b = sum((4.0 if i == 0 else 8.0) * V * H + 2.0 * c * V + 2.0 * c * H
                 for i, c in enumerate(chunks))
         return "hbm", b, "byte"
-    if name == "dlogits":
-        return "hbm", sum(4.0 * c * ldz for c in chunks), "byte"
-    if name == "dx_reduce":
-        return "hbm", None, "byte"
+    if name == "dlogits":                      # bf16 logits read, G written in place
+        return "hbm", sum(4.0 * c * V for c in chunks), "byte"
+    if name == "pack_x":                       # bf16 X chunk read and written packed
+        return "hbm", sum(4.0 * c * H for c in chunks), "byte"
+    if name == "pack_w":                       # W read and written packed, twice
+        return "hbm", 2 * 4.0 * V * H, "byte"
     return "hbm", None, "byte"
+
+
+def counter_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` from profiles/traffic_<workload>.txt,
+    or None if absent or if the kernel source changed since it was measured."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if line.startswith("#") or ":" not in line:
+                continue
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    src = os.path.join(ROOT, fields.get("source", ""))
+    if not os.path.isfile(src):
+        return None
+    with open(src, "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest() != fields.get("source_sha256"):
+            return None
+    v = fields.get(f"{kernel}.traffic_bytes_per_launch")
+    return float(v) if v else None
 
 
 def cpu_baseline(inp, n_tok):
@@ -78,7 +114,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=1, help="workload id (datagen.WORKLOADS)")
     ap.add_argument("--chunk", type=int, default=None, help="chunk tokens (default: the workload's)")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=192)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=4096)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-reference-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (a known-size "
@@ -159,7 +195,6 @@ def main():
     flops = 6.0 * N * H * V
     tflops = flops / (ms * 1e-3) / 1e12
     chunks = [min(C, N - c0) for c0 in range(0, N, C)]
-    ldz = (V + 7) // 8 * 8 if dt == fl.FLCE_BF16 else (V + 3) // 4 * 4
 
     kernels = {}
     for name, (tot, n) in prof.items():
@@ -167,7 +202,7 @@ def main():
             continue
         steps_n = n / args.steps
         avg = tot / n
-        bound, amount, unit = kernel_work(name, chunks, H, V, ldz)
+        bound, amount, unit = kernel_work(name, chunks, H, V)
         k = {"avg_ms": round(avg, 5), "launches_per_step": steps_n,
              "ms_per_step": round(tot / args.steps, 4)}
         if amount is not None:
@@ -178,16 +213,17 @@ def main():
                 k["gbps"] = round(per_launch / (avg * 1e-3) / 1e9, 1)
         kernels[name] = k
     dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
-    bound, amount, unit = kernel_work(dom, chunks, H, V, ldz)
+    bound, amount, unit = kernel_work(dom, chunks, H, V)
     if amount is not None and unit == "flop":
         ach = kernels[dom]["tflops"]
         roof = {"kernel": dom, "bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None}
+                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                "traffic": counter_traffic(dom, wl.name)}
     else:
         ach = kernels[dom].get("gbps")
         roof = {"kernel": dom, "bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4) if ach else None,
-                "traffic": None}
+                "traffic": counter_traffic(dom, wl.name)}
 
     out = {
         "metric": METRIC,

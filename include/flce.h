@@ -139,8 +139,9 @@ enum {
   FLCE_K_DX_REDUCE = 5,   /* dX split-K reduction */
   FLCE_K_DW_GEMM = 6,     /* dW GEMM */
   FLCE_K_FINAL = 7,       /* final mean loss, fills */
-  FLCE_K_PACK = 8,        /* per-chunk packing of X into the GEMM operand layouts */
-  FLCE_K_COUNT = 9
+  FLCE_K_PACK = 8,        /* per-chunk packing of X into the GEMM operand layout */
+  FLCE_K_PACK_W = 9,      /* per-call packing of W (as is and transposed) */
+  FLCE_K_COUNT = 10
 };
 int flce_profile_enable(int enable);
 int flce_profile_read(double *ms, int64_t *launches, int n);

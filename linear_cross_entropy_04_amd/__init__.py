@@ -89,7 +89,7 @@ def flce_last_error() -> str:
     return _load().flce_last_error().decode()
 
 
-KERNEL_CLASSES = 9
+KERNEL_CLASSES = 10
 
 
 def flce_profile_enable(enable: bool = True) -> None:

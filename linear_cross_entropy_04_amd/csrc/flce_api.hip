@@ -177,10 +177,10 @@ int run(bool bwd, const void *X, const void *W, const int64_t *labels, int64_t N
   if (bwd && N == 0) LAUNCH(FLCE_K_FINAL, launch_fill_f32(dW, V * H, 0.f, s));
 
   if (dtype == FLCE_BF16 && N > 0) {
-    LAUNCH(FLCE_K_PACK, launch_pack_bf16((const uint16_t *)W, Vi, Hi, (uint16_t *)(ws + p.off_wp),
+    LAUNCH(FLCE_K_PACK_W, launch_pack_bf16((const uint16_t *)W, Vi, Hi, (uint16_t *)(ws + p.off_wp),
                                          p.nks_h, s));
     if (bwd)
-      LAUNCH(FLCE_K_PACK, launch_pack_t_bf16((const uint16_t *)W, Vi, Hi,
+      LAUNCH(FLCE_K_PACK_W, launch_pack_t_bf16((const uint16_t *)W, Vi, Hi,
                                              (uint16_t *)(ws + p.off_wtp), p.nks_z, s));
   }
   for (int64_t c0 = 0; c0 < N; c0 += C) {
@@ -392,7 +392,7 @@ FLCE_API int flce_profile_read(double *ms, int64_t *launches, int n) {
 FLCE_API const char *flce_kernel_name(int k) {
   static const char *names[FLCE_K_COUNT] = {"label_check", "fwd_tile", "lse_combine", "dlogits",
                                             "dx_gemm", "dx_reduce", "dw_gemm", "final",
-                                            "pack_x"};
+                                            "pack_x", "pack_w"};
   return (k >= 0 && k < FLCE_K_COUNT) ? names[k] : "";
 }
 
