@@ -248,19 +248,23 @@ __device__ __forceinline__ void mainloop(const Op &a, const Op &b, int klen, cha
     bar();
     bf16x8 fa0[T::MI], fb0[T::NI], fa1[T::MI], fb1[T::NI];
     load_frags<T>(smem, 0, fa0, fb0);
-    for (int t = 0; t < nk; ++t) {
+    // the last slice is peeled so that the loop body has one path: the
+    // fragment reads of slice t+1 then never merge with a path without them,
+    // and the second half-step's MFMAs wait only for their own fragments
+    for (int t = 0; t < nk - 1; ++t) {
       const char *st = smem + (t % T::STAGES) * T::STAGE_BYTES;
       load_frags<T>(st, 1, fa1, fb1);
       mfma_block<T>(fa0, fb0, acc);
-      if (t + 1 < nk) {
-        // slice t+1 must have landed; slices up to t+STAGES-2 may stay in flight
-        wait_groups<T::NPER>(min(t + T::STAGES - 2, nk - 1) - (t + 1));
-        bar();
-        if (t + T::STAGES - 1 < nk) issue_stage<T>(a, b, t + T::STAGES - 1, smem);
-        load_frags<T>(smem + ((t + 1) % T::STAGES) * T::STAGE_BYTES, 0, fa0, fb0);
-      }
+      // slice t+1 must have landed; slices up to t+STAGES-2 may stay in flight
+      wait_groups<T::NPER>(min(t + T::STAGES - 2, nk - 1) - (t + 1));
+      bar();
+      if (t + T::STAGES - 1 < nk) issue_stage<T>(a, b, t + T::STAGES - 1, smem);
+      load_frags<T>(smem + ((t + 1) % T::STAGES) * T::STAGE_BYTES, 0, fa0, fb0);
       mfma_block<T>(fa1, fb1, acc);
     }
+    load_frags<T>(smem + ((nk - 1) % T::STAGES) * T::STAGE_BYTES, 1, fa1, fb1);
+    mfma_block<T>(fa0, fb0, acc);
+    mfma_block<T>(fa1, fb1, acc);
   }
   bar();    // every wave is done with the LDS slices; the caller may reuse LDS
 }
