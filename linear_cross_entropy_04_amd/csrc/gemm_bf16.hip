@@ -62,6 +62,10 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 enum Kind { PACKED = 0, PACKED_T = 1 };
 
+// 1 KB of zeros: the source of the copies a pipeline issues past its last
+// slice, so that every iteration issues the same copies.
+__device__ const uint4 g_zero_kb[64] = {};
+
 // ---------------------------------------------------------------- packed layout
 // 16-byte slot of row r32 = r % 32, column half h = (k / 8) % 2 and fragment
 // half f = (k / 16) % 2 inside a 1 KB fragment.
@@ -127,7 +131,7 @@ struct Op {
 // ROWS rows into LDS: ROWS / 16 pieces of 1 KB, piece b at tile + 1 KB b.
 // PACKED_T pieces 2q, 2q+1 are the two fragments of operand rows 32q..32q+31.
 template <int KIND, int ROWS>
-__device__ __forceinline__ void issue_tile(const Op &op, int k0, char *tile) {
+__device__ __forceinline__ void issue_tile(const Op &op, int k0, char *tile, bool live) {
   constexpr int N = ROWS * BK * 2 / 4096;
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
   const uint16_t *base;
@@ -145,6 +149,7 @@ __device__ __forceinline__ void issue_tile(const Op &op, int k0, char *tile) {
       src = base + blk * 512 + l * 8;
     else
       src = base + (blk >> 1) * 8192 + (blk & 1) * 512 + l * 8;
+    if (!live) src = (const uint16_t *)g_zero_kb + l * 8;
     __builtin_amdgcn_global_load_lds(src, tile + blk * 1024, 16, 0, 0);
   }
 }
@@ -218,11 +223,42 @@ __device__ __forceinline__ void mfma_block(const bf16x8 (&fa)[T::MI], const bf16
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
 }
 
+// Copies of slice `step`; past the last slice (step >= nk) they read zeros
+// into a ring slot that is not read again.
 template <class T>
-__device__ __forceinline__ void issue_stage(const Op &a, const Op &b, int step, char *smem) {
+__device__ __forceinline__ void issue_stage(const Op &a, const Op &b, int step, int nk,
+                                            char *smem) {
   char *st = smem + (step % T::STAGES) * T::STAGE_BYTES;
-  issue_tile<T::KA, T::BM>(a, step * BK, st);
-  issue_tile<T::KB, T::BN>(b, step * BK, st + T::A_BYTES);
+  const bool live = step < nk;
+  issue_tile<T::KA, T::BM>(a, live ? step * BK : 0, st, live);
+  issue_tile<T::KB, T::BN>(b, live ? step * BK : 0, st + T::A_BYTES, live);
+}
+
+// Instruction-group order for the scheduler (sched_group_barrier masks:
+// 0x008 MFMA, 0x010 VMEM, 0x100 DS read).  Before the barrier: each of the
+// half-step's MFMAs is followed by one fragment read of the next half-step.
+// After it: each MFMA is followed by one fragment read, then by one slice
+// copy, so the reads start first and the MFMA pipe never waits on issue.
+template <class T>
+__device__ __forceinline__ void order_first_half() {
+  constexpr int M = T::MI * T::NI, R = T::MI + T::NI;
+#pragma unroll
+  for (int i = 0; i < M; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if (i < R) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+}
+
+template <class T>
+__device__ __forceinline__ void order_second_half() {
+  constexpr int M = T::MI * T::NI, R = T::MI + T::NI, G = T::NPER;
+#pragma unroll
+  for (int i = 0; i < M; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if (i < R) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    else if (i < R + G) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+  }
+  if (R + G > M) __builtin_amdgcn_sched_group_barrier(0x010, R + G - M, 0);
 }
 
 // acc[i][j] is the 32 x 32 block (i, j) of the wave's quarter.  Lane l of
@@ -234,39 +270,185 @@ __device__ __forceinline__ void issue_stage(const Op &a, const Op &b, int step, 
 // the fragments of slice t+1's first half-step are read from LDS while the
 // MFMAs of slice t's second half-step run, and the barrier itself waits with
 // MFMAs in flight.  Slice t+STAGES-1 is copied into the buffer of slice t-1,
-// whose reads every wave finished before that barrier.  Packed operands carry
-// zero padding up to whole slices, so no copy needs a bounds check.
+// whose reads every wave finished before that barrier.  Every iteration
+// issues one slice of copies (zeros past the end), so the wait is always for
+// all but the newest STAGES-3 slices, and the last slice is peeled: the loop
+// body is one straight path.  Packed operands carry zero padding up to whole
+// slices, so no copy needs a bounds check.
 template <class T>
 __device__ __forceinline__ void mainloop(const Op &a, const Op &b, int klen, char *smem,
                                          f32x16 (&acc)[T::MI][T::NI]) {
   const int nk = (klen + BK - 1) / BK;
   if (nk > 0) {
 #pragma unroll
-    for (int s = 0; s < T::STAGES - 1; ++s)
-      if (s < nk) issue_stage<T>(a, b, s, smem);
-    wait_groups<T::NPER>(min(T::STAGES - 2, nk - 1));
+    for (int s = 0; s < T::STAGES - 1; ++s) issue_stage<T>(a, b, s, nk, smem);
+    wait_vm<(T::STAGES - 2) * T::NPER>();
     bar();
     bf16x8 fa0[T::MI], fb0[T::NI], fa1[T::MI], fb1[T::NI];
     load_frags<T>(smem, 0, fa0, fb0);
-    // the last slice is peeled so that the loop body has one path: the
-    // fragment reads of slice t+1 then never merge with a path without them,
-    // and the second half-step's MFMAs wait only for their own fragments
     for (int t = 0; t < nk - 1; ++t) {
       const char *st = smem + (t % T::STAGES) * T::STAGE_BYTES;
       load_frags<T>(st, 1, fa1, fb1);
       mfma_block<T>(fa0, fb0, acc);
-      // slice t+1 must have landed; slices up to t+STAGES-2 may stay in flight
-      wait_groups<T::NPER>(min(t + T::STAGES - 2, nk - 1) - (t + 1));
+      order_first_half<T>();
+      // slice t+1 must have landed; slices t+2 .. t+STAGES-2 may stay in flight
+      wait_vm<(T::STAGES - 3) * T::NPER>();
       bar();
-      if (t + T::STAGES - 1 < nk) issue_stage<T>(a, b, t + T::STAGES - 1, smem);
       load_frags<T>(smem + ((t + 1) % T::STAGES) * T::STAGE_BYTES, 0, fa0, fb0);
+      issue_stage<T>(a, b, t + T::STAGES - 1, nk, smem);
       mfma_block<T>(fa1, fb1, acc);
+      order_second_half<T>();
     }
     load_frags<T>(smem + ((nk - 1) % T::STAGES) * T::STAGE_BYTES, 1, fa1, fb1);
     mfma_block<T>(fa0, fb0, acc);
     mfma_block<T>(fa1, fb1, acc);
   }
-  bar();    // every wave is done with the LDS slices; the caller may reuse LDS
+  // every wave is done with the LDS slices and no copy is still writing them;
+  // the caller may reuse LDS
+  wait_vm<0>();
+  bar();
+}
+
+// ---------------------------------------------------------------- transposed main loop
+// Main loop of a tile whose operands are both read transposed (dW).  The
+// compiler guards every ds_read_b64_tr_b16 it emits with a wait for all
+// direct-to-LDS copies in flight, which would drain the copy pipeline once
+// per slice; so here the transposing reads are issued as inline asm, their
+// completion is awaited explicitly (s_waitcnt lgkmcnt(0), tied to the
+// fragment registers so no MFMA can move above it), and the source order of
+// reads, copies and MFMAs is the issue order (volatile asm statements keep
+// their order).  Same pipeline as mainloop: the wait and barrier admitting
+// slice t+1 sit between the half-steps of slice t.
+struct TrFrag {
+  i16x4 lo, hi;
+};
+
+__device__ __forceinline__ void tr_read(i16x4 &dst, const char *p) {
+  const uint32_t a = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)p;
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(dst) : "v"(a));
+}
+
+// LDS addresses of the two transposing reads of this lane for the fragment
+// of operand rows r0..r0+31, half-step kk (see frag<PACKED_T>).
+__device__ __forceinline__ void tr_addrs(const char *tile, int r0, int kk, const char *&lo,
+                                         const char *&hi) {
+  const int l = threadIdx.x & 63;
+  const int g = l >> 4, j = l & 15;
+  const int r = r0 + ((g & 1) << 4) + ((j & 3) << 2);
+  const int k = kk * 16 + ((g >> 1) << 3) + (j >> 2);
+  const int h = (r >> 3) & 1, f = (r >> 4) & 1;
+  const char *p = tile + ((((r >> 5) << 1) + f) << 10) + ((r & 7) << 1);
+  lo = p + (pk_slot(k, h, f) << 4);
+  hi = p + (pk_slot(k + 4, h, f) << 4);
+}
+
+// Read q (0 .. 2 (MI + NI) - 1) of a half-step: fragment q/2 (A fragments
+// first), low or high half.
+template <class T>
+__device__ __forceinline__ void tr_issue(const char *sa, const char *sb, int kk, int q,
+                                         TrFrag (&fa)[T::MI], TrFrag (&fb)[T::NI]) {
+  const int w = threadIdx.x >> 6;
+  const int wm = w >> 1, wn = w & 1;
+  const int fi = q >> 1;
+  const char *lo, *hi;
+  if (fi < T::MI) {
+    tr_addrs(sa, wm * T::WM + 32 * fi, kk, lo, hi);
+    if (q & 1) tr_read(fa[fi].hi, hi);
+    else tr_read(fa[fi].lo, lo);
+  } else {
+    tr_addrs(sb, wn * T::WN + 32 * (fi - T::MI), kk, lo, hi);
+    if (q & 1) tr_read(fb[fi - T::MI].hi, hi);
+    else tr_read(fb[fi - T::MI].lo, lo);
+  }
+}
+
+// Wait for every LDS read of this wave and tie the fragments to the wait.
+template <class T>
+__device__ __forceinline__ void tr_wait(TrFrag (&fa)[T::MI], TrFrag (&fb)[T::NI]) {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int i = 0; i < T::MI; ++i) asm volatile("" : "+v"(fa[i].lo), "+v"(fa[i].hi));
+#pragma unroll
+  for (int j = 0; j < T::NI; ++j) asm volatile("" : "+v"(fb[j].lo), "+v"(fb[j].hi));
+}
+
+__device__ __forceinline__ bf16x8 tr_join(const TrFrag &f) {
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(f.lo, f.hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// One MFMA of a half-step, fenced so that the scheduler keeps the source
+// order of MFMAs, reads and copies.
+template <class T>
+__device__ __forceinline__ void tr_mfma(int i, const TrFrag (&fa)[T::MI], const TrFrag (&fb)[T::NI],
+                                        f32x16 (&acc)[T::MI][T::NI]) {
+  const int a = i / T::NI, b = i % T::NI;
+  __builtin_amdgcn_sched_barrier(0);
+  acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_join(fa[a]), tr_join(fb[b]), acc[a][b], 0,
+                                                      0, 0);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <class T>
+__device__ __forceinline__ void mainloop_tt(const Op &a, const Op &b, int klen, char *smem,
+                                            f32x16 (&acc)[T::MI][T::NI]) {
+  static_assert(T::KA == PACKED_T && T::KB == PACKED_T, "transposed operands only");
+  constexpr int M = T::MI * T::NI;             // MFMAs per half-step
+  constexpr int R = 2 * (T::MI + T::NI);       // transposing reads per half-step
+  const int nk = (klen + BK - 1) / BK;
+  if (nk > 0) {
+#pragma unroll
+    for (int s = 0; s < T::STAGES - 1; ++s) issue_stage<T>(a, b, s, nk, smem);
+    wait_vm<(T::STAGES - 2) * T::NPER>();
+    bar();
+    TrFrag fa0[T::MI], fb0[T::NI], fa1[T::MI], fb1[T::NI];
+#pragma unroll
+    for (int q = 0; q < R; ++q) tr_issue<T>(smem, smem + T::A_BYTES, 0, q, fa0, fb0);
+    // the last slice is peeled so that the loop body is one straight path
+    for (int t = 0; t < nk - 1; ++t) {
+      const char *st = smem + (t % T::STAGES) * T::STAGE_BYTES;
+      const char *sn = smem + ((t + 1) % T::STAGES) * T::STAGE_BYTES;
+      tr_wait<T>(fa0, fb0);
+      // first half-step; the reads of the second go out between its MFMAs
+#pragma unroll
+      for (int i = 0; i < M; ++i) {
+        tr_mfma<T>(i, fa0, fb0, acc);
+#pragma unroll
+        for (int q = i * R / M; q < (i + 1) * R / M; ++q)
+          tr_issue<T>(st, st + T::A_BYTES, 1, q, fa1, fb1);
+      }
+      // slice t+1 must have landed; slices t+2 .. t+STAGES-2 may stay in flight
+      wait_vm<(T::STAGES - 3) * T::NPER>();
+      bar();
+      tr_wait<T>(fa1, fb1);
+      // second half-step: the next copies after its first MFMA, then the
+      // next slice's first reads between the rest
+      tr_mfma<T>(0, fa1, fb1, acc);
+      issue_stage<T>(a, b, t + T::STAGES - 1, nk, smem);
+#pragma unroll
+      for (int i = 1; i < M; ++i) {
+        tr_mfma<T>(i, fa1, fb1, acc);
+#pragma unroll
+        for (int q = (i - 1) * R / (M - 1); q < i * R / (M - 1); ++q)
+          tr_issue<T>(sn, sn + T::A_BYTES, 0, q, fa0, fb0);
+      }
+    }
+    const char *st = smem + ((nk - 1) % T::STAGES) * T::STAGE_BYTES;
+    tr_wait<T>(fa0, fb0);
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+      tr_mfma<T>(i, fa0, fb0, acc);
+#pragma unroll
+      for (int q = i * R / M; q < (i + 1) * R / M; ++q)
+        tr_issue<T>(st, st + T::A_BYTES, 1, q, fa1, fb1);
+    }
+    tr_wait<T>(fa1, fb1);
+#pragma unroll
+    for (int i = 0; i < M; ++i) tr_mfma<T>(i, fa1, fb1, acc);
+  }
+  // every wave is done with the LDS slices and no copy is still writing them;
+  // the caller may reuse LDS
+  wait_vm<0>();
+  bar();
 }
 
 template <class T>
@@ -618,7 +800,7 @@ __global__ __launch_bounds__(NTHREADS, OCC) void dw_kernel(
   zero_acc<T>(acc);
   const Op a{Gp + (int64_t)(m0 >> 5) * 8192, nks_z * 8192, 0};
   const Op b{Xp + (int64_t)(n0 >> 5) * 8192, nks_h * 8192, 0};
-  mainloop<T>(a, b, c, smem, acc);
+  mainloop_tt<T>(a, b, c, smem, acc);
 
   constexpr int TPR = T::BN / 4;            // threads per row: one 16-byte piece each
   constexpr int RPP = NTHREADS / TPR;       // rows per pass of the workgroup
