@@ -568,14 +568,8 @@ __global__ __launch_bounds__(256) void pack_t_kernel(const uint16_t *__restrict_
 // Epilogue, wave by wave: each wave reduces its own 128 vocabulary rows, so a
 // token gets one (max, sum of exp) partial per 128 vocabulary ids, at index
 // 2 vt + wm.  The target logit is taken from the fp32 accumulators by the
-// lane that holds it.  The bf16 logits tile is laid out in LDS in Zp's packed
-// order (it is 8 consecutive blocks of Zp) and leaves as one 128 KB copy.
-__device__ __forceinline__ int zst_off(int r, int v) {     // bytes, tile-local
-  const int kk = v & 31;
-  return ((v >> 5) << 14) + ((((r >> 5) << 1) + (kk >> 4)) << 10) +
-         (pk_slot(r & 31, (kk >> 3) & 1, kk >> 4) << 4) + ((kk & 7) << 1);
-}
-
+// lane that holds it.  The bf16 logits tile (8 consecutive blocks of Zp) is
+// stored straight from the accumulators in 512-byte half-fragments.
 template <bool VTAIL>
 __global__ __launch_bounds__(NTHREADS, 1) void fwd_tile_kernel(
     const uint16_t *__restrict__ Wp, const uint16_t *__restrict__ Xp, int64_t nks_h,
@@ -638,28 +632,27 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_tile_kernel(
   }
 
   if (store_z) {
-    // rows past V hold products with Wp's zero padding; dlogits zeroes them
+    // Straight from the accumulators: for one (i, j, g) the lanes hold 32
+    // consecutive tokens x 4 consecutive vocabulary ids each (lanes 32..63
+    // the next 4), i.e. the 32 slots of one half of a Zp fragment, so each
+    // store instruction writes 512 contiguous bytes.  Rows past V hold
+    // products with Wp's zero padding; dlogits zeroes them.
+    uint16_t *zt = Zp + ((int64_t)ct * nks_z + 8 * (int64_t)vt) * 8192 + 4 * (lane >> 5);
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      // vocabulary v = wm 128 + 32 i + 8 g + 4 (lane / 32) + 0..3, token r =
-      // wn 128 + 32 j + lane % 32: the lane's part of the LDS offset for this g
-      const int lo = zst_off(lane & 31, 8 * g + 4 * (lane >> 5));
+      const int h = g & 1, f = g >> 1;
+      uint16_t *zg = zt + (f << 9) + (pk_slot(lane & 31, h, f) << 3);
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
+          // vocabulary slice wm 4 + i of the tile, token row group wn 4 + j
           uint2 pk;
           pk.x = pack_bf16x2(acc[i][j][4 * g], acc[i][j][4 * g + 1]);
           pk.y = pack_bf16x2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
-          // + token row group (wn 4 + j) x 2 KB, + vocabulary slice (wm 4 + i) x 16 KB
-          *(uint2 *)(smem + lo + ((wn * 4 + j) << 11) + ((wm * 4 + i) << 14)) = pk;
+          *(uint2 *)(zg + ((wm * 4 + i) << 13) + ((wn * 4 + j) << 10)) = pk;
         }
     }
-    __syncthreads();
-    // blocks (ct, 8 vt + s), s < 8, of Zp (whose slices cover V padded to 256)
-    uint16_t *dst = Zp + ((int64_t)ct * nks_z + 8 * (int64_t)vt) * 8192;
-    for (int q = threadIdx.x; q < 8 * 1024; q += NTHREADS)
-      *(u32x4 *)(dst + q * 8) = *(const u32x4 *)(smem + q * 16);
   }
 }
 
