@@ -58,6 +58,13 @@ typedef enum {
   FLCE_BF16 = 1          /* X, W, dX in bf16; fp32 accumulation; logits/dlogits scratch in bf16 */
 } flce_dtype;
 
+/* How the per-token losses l_i = lse_i - z_{i,y_i} of valid tokens are reduced. */
+typedef enum {
+  FLCE_REDUCE_MEAN = 0,  /* loss = sum_i l_i / max(N_valid, 1) (flce_fwd_bwd, flce_fwd) */
+  FLCE_REDUCE_SUM = 1,   /* loss = sum_i l_i */
+  FLCE_REDUCE_NONE = 2   /* the output is the vector l (row_loss); loss = sum_i l_i */
+} flce_reduction;
+
 /* Default scratch budget used when chunk_tokens <= 0 (auto): 3 GiB. */
 #define FLCE_DEFAULT_SCRATCH_BUDGET ((size_t)3 << 30)
 
@@ -114,6 +121,47 @@ int flce_fwd(const void *X, const void *W, const int64_t *labels,
              int64_t ignore_index, int64_t chunk_tokens,
              float *loss, float *row_loss, float *row_lse,
              void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Forward and backward with a choice of reduction and extra per-token
+ * outputs: the differentiated objective is L = sum_i w_i l_i over valid
+ * tokens, with
+ *   w_i = 1 / max(N_valid, 1)               reduction FLCE_REDUCE_MEAN
+ *   w_i = 1                                 reduction FLCE_REDUCE_SUM
+ *   w_i = grad_rows[i] (1 if grad_rows is NULL)   reduction FLCE_REDUCE_NONE
+ * (for FLCE_REDUCE_NONE, grad_rows is the upstream gradient of the per-token
+ * loss vector), so G_i = w_i (softmax(Z_i) - onehot(y_i)), dX = G W, dW = G^T X.
+ * The per-token log-probabilities of the targets feed token-level losses
+ * built on top of this one (project overview page, "Exemplo de Uso de Perda
+ * de Pós-Treinamento").
+ *   reduction      flce_reduction
+ *   grad_rows      device [N] fp32 or NULL  only with FLCE_REDUCE_NONE (else FLCE_EINVAL)
+ *   accumulate_dw  0: dW = dL/dW;  1: dW += dL/dW (dW holds valid fp32 values on entry)
+ *   loss           host float               as flce_reduction says
+ *   row_loss       device [N] fp32          per-token loss; required for FLCE_REDUCE_NONE (N > 0)
+ *   row_lse        device [N] fp32 or NULL  per-token log-sum-exp
+ *   logprob        device [N] fp32 or NULL  per-token z_{i,y_i} - lse_i (0 if ignored)
+ * Other arguments and behaviour as for flce_fwd_bwd (with reduction MEAN,
+ * grad_rows NULL, accumulate_dw 0 and logprob NULL it is flce_fwd_bwd).
+ * N == 0: loss = 0; dW = 0, or unchanged when accumulating.
+ */
+int flce_fwd_bwd_ex(const void *X, const void *W, const int64_t *labels,
+                    int64_t N, int64_t H, int64_t V, int dtype,
+                    int64_t ignore_index, int64_t chunk_tokens,
+                    int reduction, const float *grad_rows, int accumulate_dw,
+                    float *loss, void *dX, float *dW,
+                    float *row_loss, float *row_lse, float *logprob,
+                    void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Forward only, with a choice of reduction and the per-token outputs of
+ * flce_fwd_bwd_ex (row_loss is required for FLCE_REDUCE_NONE).
+ */
+int flce_fwd_ex(const void *X, const void *W, const int64_t *labels,
+                int64_t N, int64_t H, int64_t V, int dtype,
+                int64_t ignore_index, int64_t chunk_tokens, int reduction,
+                float *loss, float *row_loss, float *row_lse, float *logprob,
+                void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * buf[i] *= *scale for i < n, in place, on the stream (no sync).  buf is a

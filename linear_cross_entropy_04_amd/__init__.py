@@ -6,8 +6,9 @@ kernels; there is no Python or CPU fallback, and a missing library raises.
 
 The operation is the one the Liger Kernel pages call as
 ``loss_fn(weight, input, target)`` (project overview page, "Método de API de
-Baixo Nível"): the LM-head projection fused with mean cross-entropy over
-tokens whose target is not ``ignore_index``.
+Baixo Nível"): the LM-head projection fused with cross-entropy over tokens
+whose target is not ``ignore_index`` -- their mean, their sum, or the
+per-token losses with an upstream gradient per token.
 """
 from __future__ import annotations
 
@@ -18,7 +19,7 @@ import torch
 
 __all__ = [
     "FLCE_F32", "FLCE_BF16", "FLCEError", "flce_workspace_bytes", "flce_plan", "flce_fwd_bwd",
-    "flce_fwd", "flce_scale_inplace", "flce_status_string", "flce_last_error", "lib_path",
+    "flce_fwd", "flce_fwd_bwd_ex", "flce_fwd_ex", "REDUCTIONS", "flce_scale_inplace", "flce_status_string", "flce_last_error", "lib_path",
     "flce_profile_enable", "flce_profile_read",
     "workspace", "loss", "FusedLinearCrossEntropyLoss",
 ]
@@ -26,6 +27,7 @@ __all__ = [
 FLCE_F32 = 0
 FLCE_BF16 = 1
 FLCE_OK, FLCE_EINVAL, FLCE_ELABEL, FLCE_EWORKSPACE, FLCE_EHIP, FLCE_EUNSUPPORTED = range(6)
+REDUCTIONS = {"mean": 0, "sum": 1, "none": 2}        # flce_reduction
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libflce.so")
 _lib = None
@@ -65,6 +67,13 @@ def _load():
     l.flce_fwd.argtypes = [_p, _p, _p, _i64, _i64, _i64, _i32, _i64, _i64,
                            ctypes.POINTER(ctypes.c_float), _p, _p, _p, _sz, _p]
     l.flce_fwd.restype = _i32
+    l.flce_fwd_bwd_ex.argtypes = [_p, _p, _p, _i64, _i64, _i64, _i32, _i64, _i64, _i32, _p, _i32,
+                                  ctypes.POINTER(ctypes.c_float), _p, _p, _p, _p, _p, _p, _sz,
+                                  _p]
+    l.flce_fwd_bwd_ex.restype = _i32
+    l.flce_fwd_ex.argtypes = [_p, _p, _p, _i64, _i64, _i64, _i32, _i64, _i64, _i32,
+                              ctypes.POINTER(ctypes.c_float), _p, _p, _p, _p, _sz, _p]
+    l.flce_fwd_ex.restype = _i32
     l.flce_scale_inplace.argtypes = [_p, _i64, _i32, _p, _p]
     l.flce_scale_inplace.restype = _i32
     l.flce_status_string.argtypes = [_i32]
@@ -211,6 +220,66 @@ def flce_fwd(X: torch.Tensor, W: torch.Tensor, labels: torch.Tensor, ignore_inde
     return float(loss.value)
 
 
+def _reduction_code(reduction: str) -> int:
+    if reduction not in REDUCTIONS:
+        raise ValueError(f"reduction must be one of {tuple(REDUCTIONS)}, got {reduction!r}")
+    return REDUCTIONS[reduction]
+
+
+def flce_fwd_bwd_ex(X: torch.Tensor, W: torch.Tensor, labels: torch.Tensor, ignore_index: int,
+                    chunk_tokens: int, dX: torch.Tensor, dW: torch.Tensor,
+                    workspace: torch.Tensor, reduction: str = "mean",
+                    grad_rows: torch.Tensor | None = None, accumulate_dw: bool = False,
+                    row_loss: torch.Tensor | None = None, row_lse: torch.Tensor | None = None,
+                    logprob: torch.Tensor | None = None, stream=None) -> float:
+    """Call libflce's flce_fwd_bwd_ex on device tensors; returns the loss."""
+    N, H = X.shape
+    V = W.shape[0]
+    dt = _dtype_code(X)
+    _dev(X, "X")
+    _dev(W, "W", X.dtype, (V, H))
+    _dev(labels, "labels", torch.int64, (N,))
+    _dev(dX, "dX", X.dtype, (N, H))
+    _dev(dW, "dW", torch.float32, (V, H))
+    _dev(workspace, "workspace")
+    for t, name in ((grad_rows, "grad_rows"), (row_loss, "row_loss"), (row_lse, "row_lse"),
+                    (logprob, "logprob")):
+        _dev(t, name, torch.float32, (N,))
+    loss = ctypes.c_float(0.0)
+    st = _load().flce_fwd_bwd_ex(_ptr(X), _ptr(W), _ptr(labels), N, H, V, dt, ignore_index,
+                                 chunk_tokens, _reduction_code(reduction), _ptr(grad_rows),
+                                 1 if accumulate_dw else 0, ctypes.byref(loss), _ptr(dX),
+                                 _ptr(dW), _ptr(row_loss), _ptr(row_lse), _ptr(logprob),
+                                 _ptr(workspace), workspace.numel(), _stream(stream, X.device))
+    if st != FLCE_OK:
+        raise FLCEError(st, "flce_fwd_bwd_ex")
+    return float(loss.value)
+
+
+def flce_fwd_ex(X: torch.Tensor, W: torch.Tensor, labels: torch.Tensor, ignore_index: int,
+                chunk_tokens: int, workspace: torch.Tensor, reduction: str = "mean",
+                row_loss: torch.Tensor | None = None, row_lse: torch.Tensor | None = None,
+                logprob: torch.Tensor | None = None, stream=None) -> float:
+    """Call libflce's flce_fwd_ex on device tensors; returns the loss."""
+    N, H = X.shape
+    V = W.shape[0]
+    dt = _dtype_code(X)
+    _dev(X, "X")
+    _dev(W, "W", X.dtype, (V, H))
+    _dev(labels, "labels", torch.int64, (N,))
+    _dev(workspace, "workspace")
+    for t, name in ((row_loss, "row_loss"), (row_lse, "row_lse"), (logprob, "logprob")):
+        _dev(t, name, torch.float32, (N,))
+    loss = ctypes.c_float(0.0)
+    st = _load().flce_fwd_ex(_ptr(X), _ptr(W), _ptr(labels), N, H, V, dt, ignore_index,
+                             chunk_tokens, _reduction_code(reduction), ctypes.byref(loss),
+                             _ptr(row_loss), _ptr(row_lse), _ptr(logprob), _ptr(workspace),
+                             workspace.numel(), _stream(stream, X.device))
+    if st != FLCE_OK:
+        raise FLCEError(st, "flce_fwd_ex")
+    return float(loss.value)
+
+
 def flce_scale_inplace(buf: torch.Tensor, scale: torch.Tensor, stream=None) -> None:
     """buf *= scale (a one-element fp32 device tensor), in place, on the stream."""
     _dev(buf, "buf")
@@ -226,8 +295,11 @@ def flce_scale_inplace(buf: torch.Tensor, scale: torch.Tensor, stream=None) -> N
 # ------------------------------------------------------------------ autograd
 
 class _FLCEFunction(torch.autograd.Function):
+    """Mean or sum: the gradients are computed with the loss (one call) and
+    scaled by the upstream gradient in backward."""
+
     @staticmethod
-    def forward(ctx, weight, input, target, ignore_index, chunk_tokens):
+    def forward(ctx, weight, input, target, ignore_index, chunk_tokens, reduction):
         N, H = input.shape
         V = weight.shape[0]
         dt = _dtype_code(input)
@@ -236,10 +308,12 @@ class _FLCEFunction(torch.autograd.Function):
         if need:
             dX = torch.empty_like(input)
             dW = torch.empty((V, H), dtype=torch.float32, device=input.device)
-            val = flce_fwd_bwd(input, weight, target, ignore_index, chunk_tokens, dX, dW, ws)
+            val = flce_fwd_bwd_ex(input, weight, target, ignore_index, chunk_tokens, dX, dW, ws,
+                                  reduction=reduction)
             ctx.save_for_backward(dX, dW)
         else:
-            val = flce_fwd(input, weight, target, ignore_index, chunk_tokens, ws)
+            val = flce_fwd_ex(input, weight, target, ignore_index, chunk_tokens, ws,
+                              reduction=reduction)
         ctx.wdtype = weight.dtype
         return torch.tensor(val, dtype=torch.float32, device=input.device)
 
@@ -250,25 +324,65 @@ class _FLCEFunction(torch.autograd.Function):
         flce_scale_inplace(dX, g)
         flce_scale_inplace(dW, g)
         gw = dW if ctx.wdtype == torch.float32 else dW.to(ctx.wdtype)
+        return gw, dX, None, None, None, None
+
+
+class _FLCETokenFunction(torch.autograd.Function):
+    """Per-token losses: the forward returns the loss vector; the backward
+    runs the fused forward and backward again with the upstream gradient of
+    each token as its weight."""
+
+    @staticmethod
+    def forward(ctx, weight, input, target, ignore_index, chunk_tokens):
+        N, H = input.shape
+        V = weight.shape[0]
+        ws = workspace(N, H, V, _dtype_code(input), chunk_tokens, device=input.device)
+        row = torch.empty(N, dtype=torch.float32, device=input.device)
+        flce_fwd_ex(input, weight, target, ignore_index, chunk_tokens, ws, reduction="none",
+                    row_loss=row)
+        ctx.save_for_backward(weight, input, target)
+        ctx.ignore_index, ctx.chunk_tokens = ignore_index, chunk_tokens
+        return row
+
+    @staticmethod
+    def backward(ctx, grad_rows):
+        weight, input, target = ctx.saved_tensors
+        N, H = input.shape
+        V = weight.shape[0]
+        ws = workspace(N, H, V, _dtype_code(input), ctx.chunk_tokens, device=input.device)
+        dX = torch.empty_like(input)
+        dW = torch.empty((V, H), dtype=torch.float32, device=input.device)
+        row = torch.empty(N, dtype=torch.float32, device=input.device)
+        g = grad_rows.detach().to(torch.float32).contiguous()
+        flce_fwd_bwd_ex(input, weight, target, ctx.ignore_index, ctx.chunk_tokens, dX, dW, ws,
+                        reduction="none", grad_rows=g, row_loss=row)
+        gw = dW if weight.dtype == torch.float32 else dW.to(weight.dtype)
         return gw, dX, None, None, None
 
 
 def loss(weight: torch.Tensor, input: torch.Tensor, target: torch.Tensor,
-         ignore_index: int = -100, chunk_tokens: int = 0) -> torch.Tensor:
-    """Mean cross-entropy of input @ weight.T against target, fused and chunked.
+         ignore_index: int = -100, chunk_tokens: int = 0,
+         reduction: str = "mean") -> torch.Tensor:
+    """Cross-entropy of input @ weight.T against target, fused and chunked.
 
     weight [V, H], input [N, H] (both bf16 or both fp32, contiguous, on the
-    GPU), target [N] int64.  Gradients flow to weight and input."""
-    return _FLCEFunction.apply(weight, input, target, ignore_index, chunk_tokens)
+    GPU), target [N] int64.  reduction "mean" (over tokens whose target is not
+    ignore_index) or "sum" returns a scalar; "none" returns the per-token
+    losses [N] (0 on ignored tokens).  Gradients flow to weight and input."""
+    _reduction_code(reduction)
+    if reduction == "none":
+        return _FLCETokenFunction.apply(weight, input, target, ignore_index, chunk_tokens)
+    return _FLCEFunction.apply(weight, input, target, ignore_index, chunk_tokens, reduction)
 
 
 class FusedLinearCrossEntropyLoss(torch.nn.Module):
     """Module form of :func:`loss`: ``loss_fn(weight, input, target)``."""
 
-    def __init__(self, ignore_index: int = -100, chunk_tokens: int = 0):
+    def __init__(self, ignore_index: int = -100, chunk_tokens: int = 0, reduction: str = "mean"):
         super().__init__()
         self.ignore_index = ignore_index
         self.chunk_tokens = chunk_tokens
+        self.reduction = reduction
 
     def forward(self, weight, input, target):
-        return loss(weight, input, target, self.ignore_index, self.chunk_tokens)
+        return loss(weight, input, target, self.ignore_index, self.chunk_tokens, self.reduction)

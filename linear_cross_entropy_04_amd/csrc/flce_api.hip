@@ -142,12 +142,28 @@ hipError_t timed(int cls, hipStream_t s, F &&launch) {
 
 #define LAUNCH(cls, call) CK(timed(cls, s, [&]() { return (call); }))
 
+// How the per-token losses are reduced and what else a call returns.
+struct Options {
+  int reduction = kReduceMean;
+  const float *grad_rows = nullptr;   // per-token upstream gradient (reduction none)
+  bool accumulate_dw = false;         // dW += instead of dW =
+  float *logprob = nullptr;           // per-token z_y - lse
+};
+
 int run(bool bwd, const void *X, const void *W, const int64_t *labels, int64_t N, int64_t H,
         int64_t V, int dtype, int64_t ii, int64_t chunk_tokens, float *loss, void *dX, float *dW,
-        float *row_loss, float *row_lse, void *workspace, size_t workspace_bytes, void *stream) {
+        float *row_loss, float *row_lse, const Options &o, void *workspace,
+        size_t workspace_bytes, void *stream) {
   int st = check_sizes(N, H, V, dtype);
   if (st != FLCE_OK) return st;
   if (!loss || !W || !workspace) return FLCE_EINVAL;
+  if (o.reduction != kReduceMean && o.reduction != kReduceSum && o.reduction != kReduceNone)
+    return FLCE_EINVAL;
+  if (o.grad_rows && (o.reduction != kReduceNone || !bwd)) return FLCE_EINVAL;
+  if (o.reduction == kReduceNone && N > 0 && !row_loss) return FLCE_EINVAL;
+  if (misaligned(o.grad_rows, 4) || misaligned(o.logprob, 4) || misaligned(row_loss, 4) ||
+      misaligned(row_lse, 4))
+    return FLCE_EINVAL;
   if (N > 0 && (!X || !labels)) return FLCE_EINVAL;
   if (bwd && (!dW || (N > 0 && !dX))) return FLCE_EINVAL;
   if (misaligned(workspace, 256)) return FLCE_EINVAL;
@@ -173,8 +189,8 @@ int run(bool bwd, const void *X, const void *W, const int64_t *labels, int64_t N
   float *rowloss = row_loss ? row_loss : (float *)(ws + p.off_rowloss);
   const int Hi = (int)H, Vi = (int)V;
 
-  LAUNCH(FLCE_K_LABELS, launch_label_check(labels, N, V, ii, sc, s));
-  if (bwd && N == 0) LAUNCH(FLCE_K_FINAL, launch_fill_f32(dW, V * H, 0.f, s));
+  LAUNCH(FLCE_K_LABELS, launch_label_check(labels, N, V, ii, o.reduction, sc, s));
+  if (bwd && N == 0 && !o.accumulate_dw) LAUNCH(FLCE_K_FINAL, launch_fill_f32(dW, V * H, 0.f, s));
 
   if (dtype == FLCE_BF16 && N > 0) {
     LAUNCH(FLCE_K_PACK_W, launch_pack_bf16((const uint16_t *)W, Vi, Hi, (uint16_t *)(ws + p.off_wp),
@@ -188,6 +204,9 @@ int run(bool bwd, const void *X, const void *W, const int64_t *labels, int64_t N
     const int64_t *lab = labels + c0;
     float *rl = rowloss + c0;
     float *rs = row_lse ? row_lse + c0 : nullptr;
+    float *lp = o.logprob ? o.logprob + c0 : nullptr;
+    const float *wr = o.grad_rows ? o.grad_rows + c0 : nullptr;
+    const bool acc_dw = c0 > 0 || o.accumulate_dw;
     if (dtype == FLCE_BF16) {
       const uint16_t *Wp = (const uint16_t *)(ws + p.off_wp);
       const uint16_t *Xc = (const uint16_t *)X + c0 * H;
@@ -196,30 +215,30 @@ int run(bool bwd, const void *X, const void *W, const int64_t *labels, int64_t N
       LAUNCH(FLCE_K_PACK, launch_pack_bf16(Xc, c, Hi, Xp, p.nks_h, s));
       LAUNCH(FLCE_K_FWD_TILE, launch_fwd_tile_bf16(Wp, Xp, p.nks_h, lab, ii, c, Hi, Vi, Zp,
                                                    p.nks_z, pm, ps, zy, p.nvt, bwd, s));
-      LAUNCH(FLCE_K_LSE_COMBINE, launch_lse_combine(pm, ps, zy, lab, ii, c, p.nvt, lse, rl, rs, s));
+      LAUNCH(FLCE_K_LSE_COMBINE, launch_lse_combine(pm, ps, zy, lab, ii, c, p.nvt, lse, rl, rs, lp, s));
       if (bwd) {
-        LAUNCH(FLCE_K_DLOGITS, launch_dlogits_bf16(Zp, p.nks_z, c, Vi, lse, lab, ii, sc, s));
+        LAUNCH(FLCE_K_DLOGITS, launch_dlogits_bf16(Zp, p.nks_z, c, Vi, lse, lab, ii, wr, sc, s));
         float *dxp = (float *)(ws + p.off_dxp);
         LAUNCH(FLCE_K_DX_GEMM, launch_dx_bf16(Zp, p.nks_z, (const uint16_t *)(ws + p.off_wtp), c,
                                               Hi, Vi, p.splitk, p.ksplit, dxp, s));
         LAUNCH(FLCE_K_DX_REDUCE,
                launch_dx_reduce_bf16(dxp, p.splitk, c, Hi, (uint16_t *)dX + c0 * H, s));
-        LAUNCH(FLCE_K_DW_GEMM, launch_dw_bf16(Zp, p.nks_z, Xp, p.nks_h, c, Hi, Vi, dW, c0 > 0, s));
+        LAUNCH(FLCE_K_DW_GEMM, launch_dw_bf16(Zp, p.nks_z, Xp, p.nks_h, c, Hi, Vi, dW, acc_dw, s));
       }
     } else {
       const float *Wf = (const float *)W;
       const float *Xc = (const float *)X + c0 * H;
       float *z = (float *)(ws + p.off_z);
       LAUNCH(FLCE_K_FWD_TILE, launch_fwd_tile_f32(Wf, Xc, lab, ii, c, Hi, Vi, z, p.ldz, pm, ps, zy, p.nvt, bwd, s));
-      LAUNCH(FLCE_K_LSE_COMBINE, launch_lse_combine(pm, ps, zy, lab, ii, c, p.nvt, lse, rl, rs, s));
+      LAUNCH(FLCE_K_LSE_COMBINE, launch_lse_combine(pm, ps, zy, lab, ii, c, p.nvt, lse, rl, rs, lp, s));
       if (bwd) {
-        LAUNCH(FLCE_K_DLOGITS, launch_dlogits_f32(z, p.ldz, c, Vi, lse, lab, ii, sc, s));
+        LAUNCH(FLCE_K_DLOGITS, launch_dlogits_f32(z, p.ldz, c, Vi, lse, lab, ii, wr, sc, s));
         LAUNCH(FLCE_K_DX_GEMM, launch_dx_f32(z, p.ldz, Wf, c, Hi, Vi, (float *)dX + c0 * H, s));
-        LAUNCH(FLCE_K_DW_GEMM, launch_dw_f32(z, p.ldz, Xc, c, Hi, Vi, dW, c0 > 0, s));
+        LAUNCH(FLCE_K_DW_GEMM, launch_dw_f32(z, p.ldz, Xc, c, Hi, Vi, dW, acc_dw, s));
       }
     }
   }
-  LAUNCH(FLCE_K_FINAL, launch_final_loss(rowloss, N, sc, s));
+  LAUNCH(FLCE_K_FINAL, launch_final_loss(rowloss, N, o.reduction, sc, s));
   float host[2];
   CK(hipMemcpyAsync(host, sc, sizeof(host), hipMemcpyDeviceToHost, s));
   CK(hipStreamSynchronize(s));
@@ -341,7 +360,7 @@ FLCE_API int flce_fwd_bwd(const void *X, const void *W, const int64_t *labels, i
                           int64_t chunk_tokens, float *loss, void *dX, float *dW, float *row_loss,
                           float *row_lse, void *workspace, size_t workspace_bytes, void *stream) {
   return run(true, X, W, labels, N, H, V, dtype, ignore_index, chunk_tokens, loss, dX, dW,
-             row_loss, row_lse, workspace, workspace_bytes, stream);
+             row_loss, row_lse, Options{}, workspace, workspace_bytes, stream);
 }
 
 FLCE_API int flce_fwd(const void *X, const void *W, const int64_t *labels, int64_t N, int64_t H,
@@ -349,7 +368,34 @@ FLCE_API int flce_fwd(const void *X, const void *W, const int64_t *labels, int64
                       float *loss, float *row_loss, float *row_lse, void *workspace,
                       size_t workspace_bytes, void *stream) {
   return run(false, X, W, labels, N, H, V, dtype, ignore_index, chunk_tokens, loss, nullptr,
-             nullptr, row_loss, row_lse, workspace, workspace_bytes, stream);
+             nullptr, row_loss, row_lse, Options{}, workspace, workspace_bytes, stream);
+}
+
+FLCE_API int flce_fwd_bwd_ex(const void *X, const void *W, const int64_t *labels, int64_t N,
+                             int64_t H, int64_t V, int dtype, int64_t ignore_index,
+                             int64_t chunk_tokens, int reduction, const float *grad_rows,
+                             int accumulate_dw, float *loss, void *dX, float *dW,
+                             float *row_loss, float *row_lse, float *logprob, void *workspace,
+                             size_t workspace_bytes, void *stream) {
+  Options o;
+  o.reduction = reduction;
+  o.grad_rows = grad_rows;
+  o.accumulate_dw = accumulate_dw != 0;
+  o.logprob = logprob;
+  return run(true, X, W, labels, N, H, V, dtype, ignore_index, chunk_tokens, loss, dX, dW,
+             row_loss, row_lse, o, workspace, workspace_bytes, stream);
+}
+
+FLCE_API int flce_fwd_ex(const void *X, const void *W, const int64_t *labels, int64_t N,
+                         int64_t H, int64_t V, int dtype, int64_t ignore_index,
+                         int64_t chunk_tokens, int reduction, float *loss, float *row_loss,
+                         float *row_lse, float *logprob, void *workspace,
+                         size_t workspace_bytes, void *stream) {
+  Options o;
+  o.reduction = reduction;
+  o.logprob = logprob;
+  return run(false, X, W, labels, N, H, V, dtype, ignore_index, chunk_tokens, loss, nullptr,
+             nullptr, row_loss, row_lse, o, workspace, workspace_bytes, stream);
 }
 
 FLCE_API int flce_scale_inplace(void *buf, int64_t n, int dtype, const float *scale,

@@ -18,11 +18,15 @@ constexpr int kMaxSplitK = 32;
 // Device-side scalars kept in the workspace.  loss and flag sit first so a
 // single 8-byte copy returns both to the host.
 struct Scalars {
-  float loss;        // final mean loss
+  float loss;        // final loss (mean, or sum of the per-token losses)
   int flag;          // 1 if a label was neither ignore_index nor in [0, V)
   int nvalid;        // number of non-ignored labels
   float inv_nvalid;  // 1 / max(nvalid, 1)
+  float scale;       // weight of a valid token's loss: 1 / max(nvalid, 1) for the mean, else 1
 };
+
+// Reductions of the per-token losses (values of flce_reduction).
+constexpr int kReduceMean = 0, kReduceSum = 1, kReduceNone = 2;
 
 // Sizes and workspace layout of one call.
 struct Plan {
@@ -45,11 +49,13 @@ int choose_splitk(int64_t C, int64_t H, int64_t V);
 
 // ---------------------------------------------------------------- common kernels
 hipError_t launch_label_check(const int64_t *labels, int64_t N, int64_t V, int64_t ii,
-                              Scalars *sc, hipStream_t s);
+                              int reduction, Scalars *sc, hipStream_t s);
 hipError_t launch_lse_combine(const float *pm, const float *ps, const float *zy,
                               const int64_t *labels_c, int64_t ii, int c, int64_t nvt,
-                              float *lse_c, float *rowloss_c, float *rowlse_c, hipStream_t s);
-hipError_t launch_final_loss(const float *rowloss, int64_t N, Scalars *sc, hipStream_t s);
+                              float *lse_c, float *rowloss_c, float *rowlse_c,
+                              float *logprob_c, hipStream_t s);
+hipError_t launch_final_loss(const float *rowloss, int64_t N, int reduction, Scalars *sc,
+                             hipStream_t s);
 hipError_t launch_fill_f32(float *p, int64_t n, float v, hipStream_t s);
 hipError_t launch_scale(void *buf, int64_t n, int dtype, const float *scale, hipStream_t s);
 
@@ -65,9 +71,11 @@ hipError_t launch_fwd_tile_bf16(const uint16_t *Wp, const uint16_t *Xp, int64_t 
                                 const int64_t *labels_c, int64_t ii, int c, int H, int V,
                                 uint16_t *Zp, int64_t nks_z, float *pm, float *ps, float *zy,
                                 int64_t nvt, bool store_z, hipStream_t s);
+// wrow_c (may be null): per-token weight of the loss (the upstream gradient
+// of a per-token loss vector); null: sc->scale for every valid token.
 hipError_t launch_dlogits_bf16(uint16_t *Zp, int64_t nks_z, int c, int V, const float *lse_c,
-                               const int64_t *labels_c, int64_t ii, const Scalars *sc,
-                               hipStream_t s);
+                               const int64_t *labels_c, int64_t ii, const float *wrow_c,
+                               const Scalars *sc, hipStream_t s);
 // Pack the transpose of a row-major [R][K] matrix into PT (rows K padded to
 // 256, nks_t column slices covering R).
 hipError_t launch_pack_t_bf16(const uint16_t *src, int R, int K, uint16_t *PT, int64_t nks_t,
@@ -85,8 +93,8 @@ hipError_t launch_fwd_tile_f32(const float *W, const float *Xc, const int64_t *l
                                float *pm, float *ps, float *zy, int64_t nvt, bool store_z,
                                hipStream_t s);
 hipError_t launch_dlogits_f32(float *zbuf, int64_t ldz, int c, int V, const float *lse_c,
-                              const int64_t *labels_c, int64_t ii, const Scalars *sc,
-                              hipStream_t s);
+                              const int64_t *labels_c, int64_t ii, const float *wrow_c,
+                              const Scalars *sc, hipStream_t s);
 hipError_t launch_dx_f32(const float *G, int64_t ldz, const float *W, int c, int H, int V,
                          float *dXc, hipStream_t s);
 hipError_t launch_dw_f32(const float *G, int64_t ldz, const float *Xc, int c, int H, int V,

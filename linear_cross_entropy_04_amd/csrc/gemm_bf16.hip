@@ -660,12 +660,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_tile_kernel(
 // One thread per 16-byte slot of Zp (one token, 8 consecutive vocabulary
 // columns), in memory order, so a wave reads and writes 1 KB contiguous and
 // its 64 lanes cover 32 consecutive tokens.  In place:
-// G = (exp(Z - lse) - onehot(y)) / N_valid on valid tokens, 0 on ignored
-// tokens and outside [0, c) x [0, V).
+// G = w_r (exp(Z - lse) - onehot(y)) on valid tokens, 0 on ignored tokens and
+// outside [0, c) x [0, V); w_r = wrow_c[r] if given, else sc->scale
+// (1 / N_valid for the mean loss).
 __global__ __launch_bounds__(256) void dlogits_kernel(
     uint16_t *__restrict__ Zp, int64_t nks_z, int c, int V, int64_t nslot,
     const float *__restrict__ lse_c, const int64_t *__restrict__ labels_c, int64_t ii,
-    const Scalars *__restrict__ sc) {
+    const float *__restrict__ wrow_c, const Scalars *__restrict__ sc) {
   const int64_t u = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
   if (u >= nslot) return;
   // u = ((rt * nks_z + ks) * 16 + f) * 64 + slot, slot = 32 h + (r % 32 ^ 4 h ^ 8 (f % 2))
@@ -676,13 +677,13 @@ __global__ __launch_bounds__(256) void dlogits_kernel(
   const int r = (int)(rt * 256) + (f >> 1) * 32 + ((sl & 31) ^ (h << 2) ^ ((f & 1) << 3));
   const int v0 = (int)(ks * 32) + (f & 1) * 16 + h * 8;
   int64_t y = ii;
-  float l2 = 0.f;
+  float l2 = 0.f, inv = 0.f;
   if (r < c) {
     y = labels_c[r];
     l2 = lse_c[r] * kLog2e;
+    inv = wrow_c ? wrow_c[r] : sc->scale;
   }
   const bool valid = r < c && y != ii;
-  const float inv = sc->inv_nvalid;
   uint16_t *zu = Zp + (u << 3);
   const u32x4 z = *(const u32x4 *)zu;
   u32x4 g;
@@ -879,12 +880,12 @@ hipError_t launch_fwd_tile_bf16(const uint16_t *Wp, const uint16_t *Xp, int64_t 
 }
 
 hipError_t launch_dlogits_bf16(uint16_t *Zp, int64_t nks_z, int c, int V, const float *lse_c,
-                               const int64_t *labels_c, int64_t ii, const Scalars *sc,
-                               hipStream_t s) {
+                               const int64_t *labels_c, int64_t ii, const float *wrow_c,
+                               const Scalars *sc, hipStream_t s) {
   // 16-byte slots over the row tiles that cover [0, c), every slice of Zp
   const int64_t nslot = (int64_t)((c + 255) / 256) * nks_z * 1024;
   hipLaunchKernelGGL(dlogits_kernel, dim3((unsigned)((nslot + 255) / 256)), dim3(256), 0, s, Zp,
-                     nks_z, c, V, nslot, lse_c, labels_c, ii, sc);
+                     nks_z, c, V, nslot, lse_c, labels_c, ii, wrow_c, sc);
   return hipGetLastError();
 }
 

@@ -1,5 +1,5 @@
 // Small kernels shared by both precisions: the label pre-pass, the
-// log-sum-exp combine over vocabulary tiles, the final mean, fills, scaling.
+// log-sum-exp combine over vocabulary tiles, the final loss, fills, scaling.
 // All reductions use a fixed order, so results are bitwise reproducible.
 #include "flce_internal.h"
 
@@ -11,8 +11,11 @@ constexpr float kLn2 = 0.6931471805599453f;
 
 // N_valid = #{i : y_i != ii}; flag if a valid label lies outside [0, V).
 // One workgroup of 1024 threads.
+// scale = the weight of each valid token's loss: 1 / max(N_valid, 1) for the
+// mean, 1 for the sum (and for per-token losses without upstream weights).
 __global__ __launch_bounds__(1024) void label_check_kernel(const int64_t *__restrict__ labels,
                                                            int64_t N, int64_t V, int64_t ii,
+                                                           int reduction,
                                                            Scalars *__restrict__ sc) {
   __shared__ int s_cnt[16], s_bad[16];
   int cnt = 0, bad = 0;
@@ -42,17 +45,20 @@ __global__ __launch_bounds__(1024) void label_check_kernel(const int64_t *__rest
     }
     sc->nvalid = c;
     sc->inv_nvalid = 1.0f / (float)(c > 0 ? c : 1);
+    sc->scale = reduction == kReduceMean ? sc->inv_nvalid : 1.0f;
     sc->flag = b;
     sc->loss = 0.f;
   }
 }
 
 // One wave per token: lse = M + ln sum_t s_t exp(m_t - M) over the token's
-// vocabulary-tile partials (m_t = tile max, s_t = sum of exp(z - m_t)).
+// vocabulary-tile partials (m_t = tile max, s_t = sum of exp(z - m_t)); the
+// token's loss lse - z_y and, if asked, its log-probability z_y - lse (both
+// 0 on ignored tokens).
 __global__ __launch_bounds__(256) void lse_combine_kernel(
     const float *__restrict__ pm, const float *__restrict__ ps, const float *__restrict__ zy,
     const int64_t *__restrict__ labels_c, int64_t ii, int c, int64_t nvt, float *__restrict__ lse_c,
-    float *__restrict__ rowloss_c, float *__restrict__ rowlse_c) {
+    float *__restrict__ rowloss_c, float *__restrict__ rowlse_c, float *__restrict__ logprob_c) {
   const int tok = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (tok >= c) return;
@@ -72,12 +78,15 @@ __global__ __launch_bounds__(256) void lse_combine_kernel(
     lse_c[tok] = lse;
     rowloss_c[tok] = (y != ii) ? lse - zy[tok] : 0.f;
     if (rowlse_c) rowlse_c[tok] = lse;
+    if (logprob_c) logprob_c[tok] = (y != ii) ? zy[tok] - lse : 0.f;
   }
 }
 
-// loss = sum_i rowloss_i / max(N_valid, 1), summed in fp64 in a fixed tree.
+// loss = sum_i rowloss_i, divided by max(N_valid, 1) for the mean; summed in
+// fp64 in a fixed tree.
 __global__ __launch_bounds__(1024) void final_loss_kernel(const float *__restrict__ rowloss,
-                                                          int64_t N, Scalars *__restrict__ sc) {
+                                                          int64_t N, int reduction,
+                                                          Scalars *__restrict__ sc) {
   __shared__ double part[1024];
   double acc = 0.0;
   for (int64_t i = threadIdx.x; i < N; i += 1024) acc += (double)rowloss[i];
@@ -89,7 +98,8 @@ __global__ __launch_bounds__(1024) void final_loss_kernel(const float *__restric
   }
   if (threadIdx.x == 0) {
     const int nv = sc->nvalid;
-    sc->loss = (float)(part[0] / (double)(nv > 0 ? nv : 1));
+    sc->loss = reduction == kReduceMean ? (float)(part[0] / (double)(nv > 0 ? nv : 1))
+                                        : (float)part[0];
   }
 }
 
@@ -124,21 +134,24 @@ inline int grid_for(int64_t n, int block, int cap) {
 }  // namespace
 
 hipError_t launch_label_check(const int64_t *labels, int64_t N, int64_t V, int64_t ii,
-                              Scalars *sc, hipStream_t s) {
-  hipLaunchKernelGGL(label_check_kernel, dim3(1), dim3(1024), 0, s, labels, N, V, ii, sc);
+                              int reduction, Scalars *sc, hipStream_t s) {
+  hipLaunchKernelGGL(label_check_kernel, dim3(1), dim3(1024), 0, s, labels, N, V, ii, reduction,
+                     sc);
   return hipGetLastError();
 }
 
 hipError_t launch_lse_combine(const float *pm, const float *ps, const float *zy,
                               const int64_t *labels_c, int64_t ii, int c, int64_t nvt,
-                              float *lse_c, float *rowloss_c, float *rowlse_c, hipStream_t s) {
+                              float *lse_c, float *rowloss_c, float *rowlse_c,
+                              float *logprob_c, hipStream_t s) {
   hipLaunchKernelGGL(lse_combine_kernel, dim3((c + 3) / 4), dim3(256), 0, s, pm, ps, zy, labels_c,
-                     ii, c, nvt, lse_c, rowloss_c, rowlse_c);
+                     ii, c, nvt, lse_c, rowloss_c, rowlse_c, logprob_c);
   return hipGetLastError();
 }
 
-hipError_t launch_final_loss(const float *rowloss, int64_t N, Scalars *sc, hipStream_t s) {
-  hipLaunchKernelGGL(final_loss_kernel, dim3(1), dim3(1024), 0, s, rowloss, N, sc);
+hipError_t launch_final_loss(const float *rowloss, int64_t N, int reduction, Scalars *sc,
+                             hipStream_t s) {
+  hipLaunchKernelGGL(final_loss_kernel, dim3(1), dim3(1024), 0, s, rowloss, N, reduction, sc);
   return hipGetLastError();
 }
 

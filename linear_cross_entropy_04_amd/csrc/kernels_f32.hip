@@ -160,13 +160,15 @@ __global__ __launch_bounds__(256) void dw_f32_kernel(const float *__restrict__ G
     }
 }
 
-// G = (exp(Z - lse) - onehot(y)) / N_valid in place; 0 on ignored rows and padding.
+// G = w_r (exp(Z - lse) - onehot(y)) in place, w_r = wrow_c[r] if given, else
+// sc->scale; 0 on ignored rows and padding.
 __global__ void dlogits_f32_kernel(float *__restrict__ z, int64_t ldz, int c, int V,
                                    const float *__restrict__ lse_c,
                                    const int64_t *__restrict__ labels_c, int64_t ii,
+                                   const float *__restrict__ wrow_c,
                                    const Scalars *__restrict__ sc) {
   const int64_t n = (int64_t)c * ldz;
-  const float inv = sc->inv_nvalid;
+  const float scale = sc->scale;
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
        i += (int64_t)gridDim.x * blockDim.x) {
     const int64_t r = i / ldz;
@@ -174,7 +176,8 @@ __global__ void dlogits_f32_kernel(float *__restrict__ z, int64_t ldz, int c, in
     const int64_t y = labels_c[r];
     float g = 0.f;
     if (y != ii && v < V)
-      g = (__builtin_amdgcn_exp2f((z[i] - lse_c[r]) * kLog2e) - ((int64_t)v == y ? 1.f : 0.f)) * inv;
+      g = (__builtin_amdgcn_exp2f((z[i] - lse_c[r]) * kLog2e) - ((int64_t)v == y ? 1.f : 0.f)) *
+          (wrow_c ? wrow_c[r] : scale);
     z[i] = g;
   }
 }
@@ -192,13 +195,13 @@ hipError_t launch_fwd_tile_f32(const float *W, const float *Xc, const int64_t *l
 }
 
 hipError_t launch_dlogits_f32(float *zbuf, int64_t ldz, int c, int V, const float *lse_c,
-                              const int64_t *labels_c, int64_t ii, const Scalars *sc,
-                              hipStream_t s) {
+                              const int64_t *labels_c, int64_t ii, const float *wrow_c,
+                              const Scalars *sc, hipStream_t s) {
   const int64_t n = (int64_t)c * ldz;
   int64_t g = (n + 255) / 256;
   if (g > 256 * 64) g = 256 * 64;
   hipLaunchKernelGGL(dlogits_f32_kernel, dim3((int)g), dim3(256), 0, s, zbuf, ldz, c, V, lse_c,
-                     labels_c, ii, sc);
+                     labels_c, ii, wrow_c, sc);
   return hipGetLastError();
 }
 

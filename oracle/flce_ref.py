@@ -143,6 +143,82 @@ def flce(X, W, labels, ignore_index: int = IGNORE_INDEX, grads: bool = True) -> 
     return Result(loss, grad_input(G, W), grad_weight(G, X), lse, rl, n_valid)
 
 
+# ------------------------------------------------------------------ other reductions
+# The loss that chunked post-training losses build on (the project overview
+# page, "Exemplo de Uso de Perda de Pós-Treinamento") is a weighted sum of the
+# per-token losses: L = sum_i w_i l_i over valid tokens.  The mean above is
+# w_i = 1 / N_valid; the sum is w_i = 1; with the per-token loss vector as the
+# output ("none"), w_i is the upstream gradient of that vector.
+
+REDUCTIONS = ("mean", "sum", "none")
+
+
+def token_weights(valid: np.ndarray, n_valid: int, reduction: str,
+                  grad_rows=None) -> np.ndarray:
+    """w_i of L = sum_i w_i l_i: 1/N_valid (mean), 1 (sum), grad_rows[i] or 1
+    (none); 0 on ignored tokens."""
+    if reduction == "mean":
+        w = np.full(valid.shape, 1.0 / max(n_valid, 1))
+    elif reduction == "sum":
+        w = np.ones(valid.shape)
+    elif reduction == "none":
+        w = np.ones(valid.shape) if grad_rows is None else np.asarray(grad_rows, dtype=np.float64)
+    else:
+        raise ValueError(f"unknown reduction {reduction!r}")
+    return np.where(valid, w, 0.0)
+
+
+def dlogits_weighted(Z: np.ndarray, lse: np.ndarray, labels: np.ndarray, weights: np.ndarray,
+                     col_ids: np.ndarray | None = None) -> np.ndarray:
+    """dL/dZ for L = sum_i w_i l_i: row i is w_i (softmax(Z_i) - onehot(y_i))."""
+    if col_ids is None:
+        col_ids = np.arange(Z.shape[1])
+    P = np.exp(Z - lse[:, None])
+    onehot = (labels[:, None] == col_ids[None, :]).astype(np.float64)
+    return weights[:, None] * (P - onehot)
+
+
+def log_probs(lse: np.ndarray, zy: np.ndarray, valid: np.ndarray) -> np.ndarray:
+    """log softmax(z_i)_{y_i} = z_{i,y_i} - lse_i on valid rows, 0 elsewhere."""
+    return np.where(valid, zy - lse, 0.0)
+
+
+@dataclasses.dataclass
+class ResultEx:
+    loss: float                # mean, or sum of the per-token losses (sum and none)
+    row_loss: np.ndarray       # [N] l_i, 0 on ignored rows
+    logprob: np.ndarray        # [N] z_{i,y_i} - lse_i, 0 on ignored rows
+    lse: np.ndarray
+    dX: np.ndarray | None      # dL/dX for L = sum_i w_i l_i
+    dW: np.ndarray | None
+    n_valid: int
+
+
+def flce_ex(X, W, labels, ignore_index: int = IGNORE_INDEX, reduction: str = "mean",
+            grad_rows=None, grads: bool = True) -> ResultEx:
+    """The definition with a choice of reduction; grad_rows is the upstream
+    gradient of the per-token loss vector (reduction "none" only)."""
+    if grad_rows is not None and reduction != "none":
+        raise ValueError("grad_rows goes with reduction 'none'")
+    X = np.asarray(X, dtype=np.float64)
+    W = np.asarray(W, dtype=np.float64)
+    labels = np.asarray(labels, dtype=np.int64)
+    V = W.shape[0]
+    valid = valid_mask(labels, V, ignore_index)
+    n_valid = int(valid.sum())
+    Z = logits(X, W)
+    lse = row_logsumexp(Z)
+    zy = target_logit(Z, labels, valid)
+    rl = row_losses(lse, zy, valid)
+    loss = mean_loss(rl, n_valid) if reduction == "mean" else float(rl.sum())
+    w = token_weights(valid, n_valid, reduction, grad_rows)
+    if not grads:
+        return ResultEx(loss, rl, log_probs(lse, zy, valid), lse, None, None, n_valid)
+    G = dlogits_weighted(Z, lse, labels, w)
+    return ResultEx(loss, rl, log_probs(lse, zy, valid), lse, grad_input(G, W),
+                    grad_weight(G, X), n_valid)
+
+
 # ------------------------------------------------------------------ the same definition on parts
 # For workloads whose N x V logits do not fit in host memory: each function
 # below evaluates the definition above for a subset of outputs, still with

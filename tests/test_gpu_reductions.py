@@ -1,0 +1,142 @@
+"""GPU parity of the extended entry points (flce_fwd_bwd_ex / flce_fwd_ex)
+against the fp64 oracle's flce_ex: sum and per-token ("none") reductions with
+an upstream gradient per token, per-token log-probabilities, accumulation into
+dW, their argument checks, and the autograd binding of reduction="none"."""
+import numpy as np
+import pytest
+import torch
+
+import datagen
+import linear_cross_entropy_04_amd as fl
+import oracle
+from _gpu_common import DEV, TOL, check_grad, check_loss, say, to_device
+
+pytestmark = pytest.mark.gpu
+II = -100
+
+
+def _grad_rows(N, seed):
+    return np.random.default_rng(seed).standard_normal(N).astype(np.float32)
+
+
+def _run_ex(inp, chunk, reduction, grad_rows=None, dW0=None):
+    X, W, y = to_device(inp)
+    N, H = X.shape
+    V = W.shape[0]
+    dt = fl.FLCE_BF16 if X.dtype == torch.bfloat16 else fl.FLCE_F32
+    ws = fl.workspace(N, H, V, dt, chunk, device=DEV)
+    ws.fill_(255)
+    dX = torch.full_like(X, float("nan"))
+    if dW0 is None:
+        dW = torch.full((V, H), float("nan"), dtype=torch.float32, device=DEV)
+    else:
+        dW = torch.from_numpy(dW0).to(DEV)
+    rl = torch.full((N,), float("nan"), dtype=torch.float32, device=DEV)
+    lp = torch.full((N,), float("nan"), dtype=torch.float32, device=DEV)
+    g = None if grad_rows is None else torch.from_numpy(grad_rows).to(DEV)
+    say(f"  gpu ex call: N={N} H={H} V={V} chunk={chunk} reduction={reduction} "
+        f"grad_rows={'yes' if g is not None else 'no'} accumulate={dW0 is not None}")
+    loss = fl.flce_fwd_bwd_ex(X, W, y, II, chunk, dX, dW, ws, reduction=reduction, grad_rows=g,
+                              accumulate_dw=dW0 is not None, row_loss=rl, logprob=lp)
+    torch.cuda.synchronize()
+    return (loss, dX.double().cpu().numpy(), dW.double().cpu().numpy(),
+            rl.double().cpu().numpy(), lp.double().cpu().numpy())
+
+
+CASES = [("bf16", 1000, 200, 1001, 384), ("bf16", 513, 256, 257, 512), ("f32", 77, 33, 130, 32)]
+
+
+@pytest.mark.parametrize("kind,N,H,V,chunk", CASES)
+@pytest.mark.parametrize("reduction", ["sum", "none"])
+def test_reduction(kind, N, H, V, chunk, reduction):
+    inp = datagen.make_custom(N, H, V, kind, seed=3 * N + V, ignore_frac=0.1)
+    gr = _grad_rows(N, N) if reduction == "none" else None
+    loss, dX, dW, rl, lp = _run_ex(inp, chunk, reduction, gr)
+    r = oracle.flce_ex(inp.X_f64(), inp.W_f64(), inp.labels, II, reduction,
+                       grad_rows=None if gr is None else gr.astype(np.float64))
+    check_loss(loss, r.loss, kind)
+    check_grad(dX, r.dX, kind, "dX")
+    check_grad(dW, r.dW, kind, "dW")
+    tol = 1e-3 if kind == "bf16" else 1e-5
+    scale = np.max(np.abs(r.lse))
+    assert np.max(np.abs(rl - r.row_loss)) <= tol * scale
+    assert np.max(np.abs(lp - r.logprob)) <= tol * scale
+    valid = inp.labels != II
+    assert np.all(rl[~valid] == 0.0) and np.all(lp[~valid] == 0.0)
+    assert np.all(dX[~valid] == 0.0)
+
+
+def test_accumulate_into_dw():
+    inp = datagen.make_custom(600, 512, 3000, "bf16", seed=17, ignore_frac=0.1)
+    dW0 = np.random.default_rng(5).standard_normal((3000, 512)).astype(np.float32) * 1e-3
+    loss, dX, dW, _, _ = _run_ex(inp, 256, "mean", dW0=dW0)
+    r = oracle.flce(inp.X_f64(), inp.W_f64(), inp.labels, II)
+    check_loss(loss, r.loss, "bf16")
+    # the accumulated result against the exact sum, measured on dL/dW's scale
+    e = np.max(np.abs((dW - dW0.astype(np.float64)) - r.dW)) / np.max(np.abs(r.dW))
+    say(f"    accumulated dW: max|err|/max|ref| = {e:.3e}")
+    assert e <= TOL["bf16"]["grad"]
+
+
+def test_empty_input_accumulate_keeps_dw():
+    X = torch.zeros((0, 64), dtype=torch.bfloat16, device=DEV)
+    W = torch.randn((100, 64), device=DEV).to(torch.bfloat16)
+    y = torch.zeros((0,), dtype=torch.int64, device=DEV)
+    dW = torch.full((100, 64), 3.0, dtype=torch.float32, device=DEV)
+    ws = fl.workspace(0, 64, 100, fl.FLCE_BF16, 0, device=DEV)
+    loss = fl.flce_fwd_bwd_ex(X, W, y, II, 0, torch.empty_like(X), dW, ws, reduction="sum",
+                              accumulate_dw=True)
+    torch.cuda.synchronize()
+    assert loss == 0.0 and bool((dW == 3.0).all())
+
+
+def test_argument_checks():
+    inp = datagen.make_custom(64, 64, 100, "bf16", seed=1)
+    X, W, y = to_device(inp)
+    ws = fl.workspace(64, 64, 100, fl.FLCE_BF16, 0, device=DEV)
+    dX, dW = torch.empty_like(X), torch.empty((100, 64), dtype=torch.float32, device=DEV)
+    g = torch.ones(64, dtype=torch.float32, device=DEV)
+    with pytest.raises(fl.FLCEError) as e:            # grad_rows only with reduction none
+        fl.flce_fwd_bwd_ex(X, W, y, II, 0, dX, dW, ws, reduction="mean", grad_rows=g)
+    assert e.value.status == fl.FLCE_EINVAL
+    with pytest.raises(fl.FLCEError) as e:            # reduction none needs row_loss
+        fl.flce_fwd_bwd_ex(X, W, y, II, 0, dX, dW, ws, reduction="none")
+    assert e.value.status == fl.FLCE_EINVAL
+    with pytest.raises(ValueError):
+        fl.flce_fwd_bwd_ex(X, W, y, II, 0, dX, dW, ws, reduction="max")
+
+
+def test_fwd_ex_matches():
+    inp = datagen.make_custom(700, 256, 2000, "bf16", seed=9, ignore_frac=0.2)
+    X, W, y = to_device(inp)
+    ws = fl.workspace(700, 256, 2000, fl.FLCE_BF16, 256, device=DEV)
+    rl = torch.empty(700, dtype=torch.float32, device=DEV)
+    lp = torch.empty(700, dtype=torch.float32, device=DEV)
+    loss = fl.flce_fwd_ex(X, W, y, II, 256, ws, reduction="sum", row_loss=rl, logprob=lp)
+    r = oracle.flce_ex(inp.X_f64(), inp.W_f64(), inp.labels, II, "sum", grads=False)
+    check_loss(loss, r.loss, "bf16")
+    assert np.max(np.abs(lp.double().cpu().numpy() - r.logprob)) <= 1e-3 * np.max(np.abs(r.lse))
+
+
+@pytest.mark.parametrize("reduction", ["sum", "none"])
+def test_autograd_reductions(reduction):
+    inp = datagen.make_custom(300, 128, 900, "f32", seed=11, ignore_frac=0.1)
+    X, W, y = to_device(inp)
+    Xg = X.clone().requires_grad_(True)
+    Wg = W.clone().requires_grad_(True)
+    out = fl.loss(Wg, Xg, y, reduction=reduction, chunk_tokens=128)
+    if reduction == "none":
+        g = _grad_rows(300, 2)
+        (out * torch.from_numpy(g).to(DEV)).sum().backward()
+        r = oracle.flce_ex(inp.X_f64(), inp.W_f64(), inp.labels, II, "none",
+                           grad_rows=g.astype(np.float64))
+        assert np.max(np.abs(out.detach().double().cpu().numpy() - r.row_loss)) <= \
+            1e-5 * np.max(np.abs(r.lse))
+    else:
+        (2.5 * out).backward()
+        r = oracle.flce_ex(inp.X_f64(), inp.W_f64(), inp.labels, II, "sum")
+        check_loss(float(out), r.loss, "f32")
+        r.dX *= 2.5
+        r.dW *= 2.5
+    check_grad(Xg.grad.double().cpu().numpy(), r.dX, "f32", "dX")
+    check_grad(Wg.grad.double().cpu().numpy(), r.dW, "f32", "dW")
