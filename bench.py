@@ -107,6 +107,85 @@ def cpu_baseline(inp, n_tok):
                       f"V={inp.wl.V}), fp64 loss + dX + dW on the host"}
 
 
+CE_N, CE_V = 8192, 128256     # the Llama-3-8B head's logits: 8 x 1024 tokens x vocabulary
+
+
+def bench_ce(args):
+    """Cross-entropy on given bf16 logits [8192, 128256], in place: one step
+    is one flce_ce_fwd_bwd (label pass, row kernel, final loss, sync).  The
+    call overwrites the logits with their gradient, so after the first step
+    the rows hold gradient values; the work per step does not depend on
+    them.  Roofline: HBM, 3 N V 2 bytes (the row read twice, written once)."""
+    import numpy as np
+    import torch
+    import datagen
+    import linear_cross_entropy_04_amd as fl
+    import oracle
+
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    Zraw, y_np = datagen.make_logits(CE_N, CE_V, "bf16", seed=20270)
+    log(f"logits {CE_N} x {CE_V} bf16 drawn in {time.time() - t0:.1f}s")
+    L = torch.from_numpy(Zraw.view(np.int16)).to(dev).view(torch.bfloat16)
+    y = torch.from_numpy(y_np).to(dev)
+    ws = torch.empty(fl.flce_ce_workspace_bytes(CE_N), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    loss0 = fl.flce_ce_fwd_bwd(L, y, -100, ws, stream=stream)      # on the drawn logits
+    for _ in range(max(args.warmup - 1, 0)):
+        fl.flce_ce_fwd_bwd(L, y, -100, ws, stream=stream)
+    torch.cuda.synchronize()
+    fl.flce_profile_enable(True)
+    fl.flce_profile_read()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for _ in range(args.steps):
+        fl.flce_ce_fwd_bwd(L, y, -100, ws, stream=stream)
+    torch.cuda.synchronize()
+    ms = 1e3 * (time.perf_counter() - t1) / args.steps
+    prof = fl.flce_profile_read()
+    fl.flce_profile_enable(False)
+    tot, n = prof["ce_rows"]
+    k_ms = tot / n
+    traffic = 3.0 * CE_N * CE_V * 2
+    gbps = traffic / (k_ms * 1e-3) / 1e9
+    out = {
+        "metric": "cross-entropy on given logits fwd+bwd tokens/s, Llama-3-8B head logits",
+        "value": round(CE_N / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded; logits ~ N(0, 1.28^2), uniform labels, 5% ignored)",
+        "config": {"workload": "llama3-8b-head-logits", "N": CE_N, "V": CE_V},
+        "loss": loss0,
+        "kernels": {"ce_rows": {"avg_ms": round(k_ms, 5), "gbps": round(gbps, 1)}},
+        "roofline": {"kernel": "ce_rows", "bound": "hbm", "achieved": round(gbps, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbps / PEAK_HBM_GBS, 4),
+                     "traffic": counter_traffic("ce_rows", "llama3-8b-head-logits")},
+    }
+    if not args.no_cpu_baseline:
+        n_tok = 1024
+        Z64 = datagen.bf16_bits_to_f32(Zraw[:n_tok]).astype(np.float64)
+        t2 = time.perf_counter()
+        oracle.cross_entropy(Z64, y_np[:n_tok])
+        dt = time.perf_counter() - t2
+        out["cpu_baseline"] = {"value": n_tok / dt, "unit": "tokens/s",
+                               "cores": _blas_threads(), "kind": "oracle",
+                               "seconds": round(dt, 3),
+                               "sample": f"first {n_tok} rows of the logits, fp64 loss + gradient"}
+    else:
+        out["cpu_baseline"] = None
+    log(f"ce: {ms:.3f} ms/step, kernel {k_ms:.3f} ms at {gbps:.0f} GB/s, loss={loss0:.6f}")
+    print(json.dumps(out), flush=True)
+
+
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max((i.get("num_threads", 1) for i in threadpool_info()
+                    if i.get("user_api") == "blas"), default=1)
+    except Exception:       # pragma: no cover - informational only
+        return os.cpu_count() or 1
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -116,6 +195,9 @@ def main():
     ap.add_argument("--chunk", type=int, default=None, help="chunk tokens (default: the workload's)")
     ap.add_argument("--cpu-sample-tokens", type=int, default=4096)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--op", choices=("flce", "ce"), default="flce",
+                    help="flce: the fused linear cross-entropy step (default); ce: cross-entropy "
+                         "on given logits of the Llama-3-8B head's size")
     ap.add_argument("--copy-reference-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (a known-size "
                          "reference for hardware byte counters)")
@@ -125,6 +207,10 @@ def main():
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the multi-GPU "
               "sharding of this path is a design only)", file=sys.stderr)
         sys.exit(2)
+
+    if args.op == "ce":
+        bench_ce(args)
+        return
 
     import numpy as np
     import torch

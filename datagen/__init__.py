@@ -202,6 +202,24 @@ def make_custom(N: int, H: int, V: int, dtype: str = "bf16", seed: int = 1,
     return draw(Workload("custom", N, H, V, dtype, chunk_tokens, **kw), seed)
 
 
+def make_logits(N: int, V: int, dtype: str = "bf16", seed: int = 1, std: float = 1.28,
+                ignore_frac: float = 0.05) -> tuple[np.ndarray, np.ndarray]:
+    """Logits and labels for cross-entropy on given logits.
+
+    Z ~ N(0, std^2) in fp32 (the default 1.28 = sqrt(4096) * 0.02 is the
+    spread of x.w for x ~ N(0, 1), w ~ N(0, 0.02^2) at H = 4096, i.e. the
+    Llama-3-8B head's logits at initialisation), bf16 rounded to nearest even
+    (returned as uint16 bits); labels uniform with exactly round(p N) ignored.
+    Draw order: Z, labels, ignored positions."""
+    ss = np.random.SeedSequence(seed)
+    s_z, s_y, s_i = ss.spawn(3)
+    Z = np.random.default_rng(s_z).standard_normal((N, V), dtype=np.float32)
+    Z *= np.float32(std)
+    y = _draw_labels(np.random.default_rng(s_y), N, V, "uniform", 0.0)
+    y[_ignore_positions(np.random.default_rng(s_i), N, "random", ignore_frac)] = IGNORE_INDEX
+    return (f32_to_bf16_bits(Z) if dtype == "bf16" else Z), y
+
+
 def sample_rows(n_total: int, k: int, seed: int, must: tuple = ()) -> np.ndarray:
     """Seeded sorted sample of k distinct row indices, always holding ``must``."""
     rng = np.random.default_rng(seed)

@@ -164,6 +164,35 @@ int flce_fwd_ex(const void *X, const void *W, const int64_t *labels,
                 void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Cross-entropy on given logits (no projection), the plain cross-entropy loss
+ * the Liger Kernel pages list beside the fused one (project overview page,
+ * "Modelos e Operações"); its gradient overwrites the logits (overview page,
+ * "Princípios Técnicos", in-place operations):
+ *     loss = reduce_i (lse(logits_i) - logits_{i,y_i})   over valid tokens
+ *     logits_i := w_i (softmax(logits_i) - onehot(y_i))  (0 on ignored rows)
+ * with reduce and w_i as for flce_fwd_bwd_ex.
+ *   logits     device [N, V] (dtype)         flce_ce_fwd_bwd: read, then overwritten
+ *                                            with dL/dlogits; flce_ce_fwd: read only
+ *   labels     device [N] int64              read only
+ *   reduction  flce_reduction; grad_rows as for flce_fwd_bwd_ex
+ *   loss       host float
+ *   row_loss, row_lse, logprob   device [N] fp32 or NULL (row_loss required for NONE)
+ *   workspace  device, >= flce_ce_workspace_bytes(N) bytes, 256-byte aligned
+ * logits must be aligned to its element size; 16-byte alignment with V a
+ * multiple of 16 bytes' worth of elements takes the vector path.  On
+ * FLCE_ELABEL the logits are already overwritten (unspecified).
+ */
+size_t flce_ce_workspace_bytes(int64_t N);
+int flce_ce_fwd_bwd(void *logits, const int64_t *labels, int64_t N, int64_t V, int dtype,
+                    int64_t ignore_index, int reduction, const float *grad_rows,
+                    float *loss, float *row_loss, float *row_lse, float *logprob,
+                    void *workspace, size_t workspace_bytes, void *stream);
+int flce_ce_fwd(const void *logits, const int64_t *labels, int64_t N, int64_t V, int dtype,
+                int64_t ignore_index, int reduction,
+                float *loss, float *row_loss, float *row_lse, float *logprob,
+                void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * buf[i] *= *scale for i < n, in place, on the stream (no sync).  buf is a
  * device array of dtype (FLCE_F32 or FLCE_BF16); scale is a device fp32
  * scalar.  Used to apply an upstream gradient d(out)/d(loss) != 1 to dX, dW.
@@ -189,7 +218,8 @@ enum {
   FLCE_K_FINAL = 7,       /* final mean loss, fills */
   FLCE_K_PACK = 8,        /* per-chunk packing of X into the GEMM operand layout */
   FLCE_K_PACK_W = 9,      /* per-call packing of W (as is and transposed) */
-  FLCE_K_COUNT = 10
+  FLCE_K_CE_ROWS = 10,    /* cross-entropy on given logits, one workgroup per row */
+  FLCE_K_COUNT = 11
 };
 int flce_profile_enable(int enable);
 int flce_profile_read(double *ms, int64_t *launches, int n);

@@ -22,6 +22,7 @@ __all__ = [
     "flce_fwd", "flce_fwd_bwd_ex", "flce_fwd_ex", "REDUCTIONS", "flce_scale_inplace", "flce_status_string", "flce_last_error", "lib_path",
     "flce_profile_enable", "flce_profile_read",
     "workspace", "loss", "FusedLinearCrossEntropyLoss",
+    "flce_ce_workspace_bytes", "flce_ce_fwd_bwd", "flce_ce_fwd", "cross_entropy",
 ]
 
 FLCE_F32 = 0
@@ -74,6 +75,14 @@ def _load():
     l.flce_fwd_ex.argtypes = [_p, _p, _p, _i64, _i64, _i64, _i32, _i64, _i64, _i32,
                               ctypes.POINTER(ctypes.c_float), _p, _p, _p, _p, _sz, _p]
     l.flce_fwd_ex.restype = _i32
+    l.flce_ce_workspace_bytes.argtypes = [_i64]
+    l.flce_ce_workspace_bytes.restype = _sz
+    l.flce_ce_fwd_bwd.argtypes = [_p, _p, _i64, _i64, _i32, _i64, _i32, _p,
+                                  ctypes.POINTER(ctypes.c_float), _p, _p, _p, _p, _sz, _p]
+    l.flce_ce_fwd_bwd.restype = _i32
+    l.flce_ce_fwd.argtypes = [_p, _p, _i64, _i64, _i32, _i64, _i32,
+                              ctypes.POINTER(ctypes.c_float), _p, _p, _p, _p, _sz, _p]
+    l.flce_ce_fwd.restype = _i32
     l.flce_scale_inplace.argtypes = [_p, _i64, _i32, _p, _p]
     l.flce_scale_inplace.restype = _i32
     l.flce_status_string.argtypes = [_i32]
@@ -98,7 +107,7 @@ def flce_last_error() -> str:
     return _load().flce_last_error().decode()
 
 
-KERNEL_CLASSES = 10
+KERNEL_CLASSES = 11
 
 
 def flce_profile_enable(enable: bool = True) -> None:
@@ -280,6 +289,55 @@ def flce_fwd_ex(X: torch.Tensor, W: torch.Tensor, labels: torch.Tensor, ignore_i
     return float(loss.value)
 
 
+def flce_ce_workspace_bytes(N: int) -> int:
+    return int(_load().flce_ce_workspace_bytes(N))
+
+
+def _ce_args(logits, labels, workspace, grad_rows, row_loss, row_lse, logprob):
+    N, V = logits.shape
+    _dev(logits, "logits")
+    _dev(labels, "labels", torch.int64, (N,))
+    _dev(workspace, "workspace")
+    for t, name in ((grad_rows, "grad_rows"), (row_loss, "row_loss"), (row_lse, "row_lse"),
+                    (logprob, "logprob")):
+        _dev(t, name, torch.float32, (N,))
+    return N, V, _dtype_code(logits)
+
+
+def flce_ce_fwd_bwd(logits: torch.Tensor, labels: torch.Tensor, ignore_index: int,
+                    workspace: torch.Tensor, reduction: str = "mean",
+                    grad_rows: torch.Tensor | None = None, row_loss: torch.Tensor | None = None,
+                    row_lse: torch.Tensor | None = None, logprob: torch.Tensor | None = None,
+                    stream=None) -> float:
+    """Call libflce's flce_ce_fwd_bwd: returns the loss; logits is overwritten
+    with dL/dlogits."""
+    N, V, dt = _ce_args(logits, labels, workspace, grad_rows, row_loss, row_lse, logprob)
+    loss = ctypes.c_float(0.0)
+    st = _load().flce_ce_fwd_bwd(_ptr(logits), _ptr(labels), N, V, dt, ignore_index,
+                                 _reduction_code(reduction), _ptr(grad_rows), ctypes.byref(loss),
+                                 _ptr(row_loss), _ptr(row_lse), _ptr(logprob), _ptr(workspace),
+                                 workspace.numel(), _stream(stream, logits.device))
+    if st != FLCE_OK:
+        raise FLCEError(st, "flce_ce_fwd_bwd")
+    return float(loss.value)
+
+
+def flce_ce_fwd(logits: torch.Tensor, labels: torch.Tensor, ignore_index: int,
+                workspace: torch.Tensor, reduction: str = "mean",
+                row_loss: torch.Tensor | None = None, row_lse: torch.Tensor | None = None,
+                logprob: torch.Tensor | None = None, stream=None) -> float:
+    """Call libflce's flce_ce_fwd (logits read only); returns the loss."""
+    N, V, dt = _ce_args(logits, labels, workspace, None, row_loss, row_lse, logprob)
+    loss = ctypes.c_float(0.0)
+    st = _load().flce_ce_fwd(_ptr(logits), _ptr(labels), N, V, dt, ignore_index,
+                             _reduction_code(reduction), ctypes.byref(loss), _ptr(row_loss),
+                             _ptr(row_lse), _ptr(logprob), _ptr(workspace), workspace.numel(),
+                             _stream(stream, logits.device))
+    if st != FLCE_OK:
+        raise FLCEError(st, "flce_ce_fwd")
+    return float(loss.value)
+
+
 def flce_scale_inplace(buf: torch.Tensor, scale: torch.Tensor, stream=None) -> None:
     """buf *= scale (a one-element fp32 device tensor), in place, on the stream."""
     _dev(buf, "buf")
@@ -386,3 +444,40 @@ class FusedLinearCrossEntropyLoss(torch.nn.Module):
 
     def forward(self, weight, input, target):
         return loss(weight, input, target, self.ignore_index, self.chunk_tokens, self.reduction)
+
+
+class _CEFunction(torch.autograd.Function):
+    """Cross-entropy on given logits, mean or sum.  With gradients, the
+    logits buffer (or its copy, when not in place) receives dL/dlogits in
+    the forward; backward scales it by the upstream gradient."""
+
+    @staticmethod
+    def forward(ctx, logits, target, ignore_index, reduction, inplace):
+        N = logits.shape[0]
+        ws = torch.empty(flce_ce_workspace_bytes(N), dtype=torch.uint8, device=logits.device)
+        if ctx.needs_input_grad[0]:
+            buf = logits if inplace else logits.detach().clone()
+            val = flce_ce_fwd_bwd(buf, target, ignore_index, ws, reduction=reduction)
+            ctx.save_for_backward(buf)
+        else:
+            val = flce_ce_fwd(logits, target, ignore_index, ws, reduction=reduction)
+        return torch.tensor(val, dtype=torch.float32, device=logits.device)
+
+    @staticmethod
+    def backward(ctx, grad_out):
+        (buf,) = ctx.saved_tensors
+        g = grad_out.detach().to(torch.float32).reshape(1).contiguous()
+        flce_scale_inplace(buf, g)
+        return buf, None, None, None, None
+
+
+def cross_entropy(logits: torch.Tensor, target: torch.Tensor, ignore_index: int = -100,
+                  reduction: str = "mean", inplace: bool = True) -> torch.Tensor:
+    """Cross-entropy of given logits [N, V] (bf16 or fp32) against target [N].
+
+    reduction "mean" or "sum".  With inplace (the default, as the pages'
+    in-place operations), a logits tensor that requires grad is overwritten
+    with its own gradient during the forward, so it must not be used again."""
+    if reduction not in ("mean", "sum"):
+        raise ValueError("cross_entropy supports reduction 'mean' or 'sum'")
+    return _CEFunction.apply(logits, target, ignore_index, reduction, inplace)

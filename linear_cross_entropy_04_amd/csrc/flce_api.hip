@@ -398,6 +398,74 @@ FLCE_API int flce_fwd_ex(const void *X, const void *W, const int64_t *labels, in
              nullptr, row_loss, row_lse, o, workspace, workspace_bytes, stream);
 }
 
+// ---------------------------------------------------------------- cross-entropy on given logits
+
+namespace flce {
+namespace {
+
+constexpr size_t kCeRowLossOffset = 256;
+
+int run_ce(bool grad, void *logits, const int64_t *labels, int64_t N, int64_t V, int dtype,
+           int64_t ii, int reduction, const float *grad_rows, float *loss, float *row_loss,
+           float *row_lse, float *logprob, void *workspace, size_t workspace_bytes,
+           void *stream) {
+  if (dtype != FLCE_F32 && dtype != FLCE_BF16) return FLCE_EINVAL;
+  if (N < 0 || V <= 0 || !loss || !workspace) return FLCE_EINVAL;
+  if (N > kMaxN || V > ((int64_t)1 << 31)) return FLCE_EUNSUPPORTED;
+  if (N > 0 && (!logits || !labels)) return FLCE_EINVAL;
+  if (reduction != kReduceMean && reduction != kReduceSum && reduction != kReduceNone)
+    return FLCE_EINVAL;
+  if (grad_rows && (reduction != kReduceNone || !grad)) return FLCE_EINVAL;
+  if (reduction == kReduceNone && N > 0 && !row_loss) return FLCE_EINVAL;
+  if (misaligned(workspace, 256) || misaligned(labels, 8) ||
+      misaligned(logits, dtype == FLCE_F32 ? 4 : 2) || misaligned(grad_rows, 4) ||
+      misaligned(row_loss, 4) || misaligned(row_lse, 4) || misaligned(logprob, 4))
+    return FLCE_EINVAL;
+  if (workspace_bytes < flce_ce_workspace_bytes(N)) return FLCE_EWORKSPACE;
+
+  hipStream_t s = (hipStream_t)stream;
+  char *ws = (char *)workspace;
+  Scalars *sc = (Scalars *)ws;
+  float *rl = row_loss ? row_loss : (float *)(ws + kCeRowLossOffset);
+  LAUNCH(FLCE_K_LABELS, launch_label_check(labels, N, V, ii, reduction, sc, s));
+  LAUNCH(FLCE_K_CE_ROWS, launch_ce_rows(logits, N, V, dtype, labels, ii, grad, grad_rows, sc, rl,
+                                        row_lse, logprob, s));
+  LAUNCH(FLCE_K_FINAL, launch_final_loss(rl, N, reduction, sc, s));
+  float host[2];
+  CK(hipMemcpyAsync(host, sc, sizeof(host), hipMemcpyDeviceToHost, s));
+  CK(hipStreamSynchronize(s));
+  int flag;
+  std::memcpy(&flag, &host[1], sizeof(flag));
+  if (flag) return FLCE_ELABEL;
+  *loss = host[0];
+  return FLCE_OK;
+}
+
+}  // namespace
+}  // namespace flce
+
+FLCE_API size_t flce_ce_workspace_bytes(int64_t N) {
+  if (N < 0) return 0;
+  return flce::kCeRowLossOffset + flce::align256((size_t)N * 4);
+}
+
+FLCE_API int flce_ce_fwd_bwd(void *logits, const int64_t *labels, int64_t N, int64_t V, int dtype,
+                             int64_t ignore_index, int reduction, const float *grad_rows,
+                             float *loss, float *row_loss, float *row_lse, float *logprob,
+                             void *workspace, size_t workspace_bytes, void *stream) {
+  return flce::run_ce(true, logits, labels, N, V, dtype, ignore_index, reduction, grad_rows, loss,
+                      row_loss, row_lse, logprob, workspace, workspace_bytes, stream);
+}
+
+FLCE_API int flce_ce_fwd(const void *logits, const int64_t *labels, int64_t N, int64_t V,
+                         int dtype, int64_t ignore_index, int reduction, float *loss,
+                         float *row_loss, float *row_lse, float *logprob, void *workspace,
+                         size_t workspace_bytes, void *stream) {
+  return flce::run_ce(false, const_cast<void *>(logits), labels, N, V, dtype, ignore_index,
+                      reduction, nullptr, loss, row_loss, row_lse, logprob, workspace,
+                      workspace_bytes, stream);
+}
+
 FLCE_API int flce_scale_inplace(void *buf, int64_t n, int dtype, const float *scale,
                                 void *stream) {
   if (dtype != FLCE_F32 && dtype != FLCE_BF16) return FLCE_EINVAL;
@@ -438,7 +506,7 @@ FLCE_API int flce_profile_read(double *ms, int64_t *launches, int n) {
 FLCE_API const char *flce_kernel_name(int k) {
   static const char *names[FLCE_K_COUNT] = {"label_check", "fwd_tile", "lse_combine", "dlogits",
                                             "dx_gemm", "dx_reduce", "dw_gemm", "final",
-                                            "pack_x", "pack_w"};
+                                            "pack_x", "pack_w", "ce_rows"};
   return (k >= 0 && k < FLCE_K_COUNT) ? names[k] : "";
 }
 

@@ -87,6 +87,14 @@ hipError_t launch_dx_reduce_bf16(const float *dxp, int splitk, int c, int H, uin
 hipError_t launch_dw_bf16(const uint16_t *Gp, int64_t nks_z, const uint16_t *Xp, int64_t nks_h,
                           int c, int H, int V, float *dW, bool accumulate, hipStream_t s);
 
+// ---------------------------------------------------------------- cross-entropy on given logits
+// One workgroup per row of logits [N][V] (dtype 0 = fp32, 1 = bf16): lse,
+// per-token loss / log-sum-exp / log-probability (each may be null), and with
+// grad the gradient written over the row (wrow: per-token weights or null).
+hipError_t launch_ce_rows(void *logits, int64_t N, int64_t V, int dtype, const int64_t *labels,
+                          int64_t ii, bool grad, const float *wrow, const Scalars *sc,
+                          float *row_loss, float *row_lse, float *logprob, hipStream_t s);
+
 // ---------------------------------------------------------------- fp32 path (SIMT)
 hipError_t launch_fwd_tile_f32(const float *W, const float *Xc, const int64_t *labels_c,
                                int64_t ii, int c, int H, int V, float *zbuf, int64_t ldz,

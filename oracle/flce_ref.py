@@ -219,6 +219,40 @@ def flce_ex(X, W, labels, ignore_index: int = IGNORE_INDEX, reduction: str = "me
                     grad_weight(G, X), n_valid)
 
 
+# ------------------------------------------------------------------ cross-entropy on given logits
+# The plain cross-entropy loss the pages list beside the fused one (project
+# overview page, "Modelos e Operações"): the same steps with the logits given
+# instead of computed from X and W.
+
+@dataclasses.dataclass
+class CEResult:
+    loss: float
+    row_loss: np.ndarray
+    logprob: np.ndarray
+    lse: np.ndarray
+    dZ: np.ndarray | None      # dL/dlogits
+    n_valid: int
+
+
+def cross_entropy(Z, labels, ignore_index: int = IGNORE_INDEX, reduction: str = "mean",
+                  grad_rows=None, grads: bool = True) -> CEResult:
+    """Cross-entropy of logits Z [N, V] against labels, with its gradient."""
+    if grad_rows is not None and reduction != "none":
+        raise ValueError("grad_rows goes with reduction 'none'")
+    Z = np.asarray(Z, dtype=np.float64)
+    labels = np.asarray(labels, dtype=np.int64)
+    valid = valid_mask(labels, Z.shape[1], ignore_index)
+    n_valid = int(valid.sum())
+    lse = row_logsumexp(Z)
+    zy = target_logit(Z, labels, valid)
+    rl = row_losses(lse, zy, valid)
+    loss = mean_loss(rl, n_valid) if reduction == "mean" else float(rl.sum())
+    dZ = None
+    if grads:
+        dZ = dlogits_weighted(Z, lse, labels, token_weights(valid, n_valid, reduction, grad_rows))
+    return CEResult(loss, rl, log_probs(lse, zy, valid), lse, dZ, n_valid)
+
+
 # ------------------------------------------------------------------ the same definition on parts
 # For workloads whose N x V logits do not fit in host memory: each function
 # below evaluates the definition above for a subset of outputs, still with

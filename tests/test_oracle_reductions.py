@@ -189,3 +189,43 @@ def test_planted_mistakes_ex(monkeypatch, step, mistake):
         except (AssertionError, ValueError, IndexError, FloatingPointError):
             caught.append(pin.__name__)
     assert caught, f"no pin catches the planted mistake {mistake.__name__}"
+
+
+# ------------------------------------------------------------------ cross-entropy on given logits
+
+def _torch_ce(Z, y, reduction, g=None):
+    import torch
+    Zt = torch.tensor(Z, dtype=torch.float64, requires_grad=True)
+    out = torch.nn.functional.cross_entropy(Zt, torch.tensor(y), ignore_index=II,
+                                            reduction=reduction)
+    if reduction == "none":
+        (out * torch.tensor(g if g is not None else np.ones(len(y)))).sum().backward()
+        return float(out.sum()), out.detach().numpy(), Zt.grad.numpy()
+    out.backward()
+    return out.item(), None, Zt.grad.numpy()
+
+
+@pytest.mark.parametrize("reduction", ["mean", "sum", "none"])
+def test_cross_entropy_against_torch(reduction):
+    rng = np.random.default_rng(21)
+    Z = rng.standard_normal((13, 29)) * 3.0
+    y = rng.integers(0, 29, size=13)
+    y[[2, 7]] = II
+    g = rng.standard_normal(13) if reduction == "none" else None
+    r = oracle.cross_entropy(Z, y, II, reduction, grad_rows=g)
+    loss, rl, dZ = _torch_ce(Z, y, reduction, g)
+    assert abs(r.loss - loss) <= 1e-12 * abs(loss)
+    assert _rel(r.dZ, dZ) <= 1e-12
+    if rl is not None:
+        assert _rel(r.row_loss, rl) <= 1e-12
+
+
+def test_cross_entropy_is_flce_on_logits():
+    """Given Z = X W^T, the cross-entropy of Z has the loss of the fused
+    definition and dX = dZ W, dW = dZ^T X."""
+    X, W, y, g = _rand(8, 5, 11, 22)
+    for red, gr in (("mean", None), ("none", g)):
+        a = oracle.cross_entropy(X @ W.T, y, II, red, grad_rows=gr)
+        b = oracle.flce_ex(X, W, y, II, red, grad_rows=gr)
+        assert abs(a.loss - b.loss) <= 1e-12 * abs(b.loss)
+        assert _rel(a.dZ @ W, b.dX) <= 1e-12 and _rel(a.dZ.T @ X, b.dW) <= 1e-12
