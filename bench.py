@@ -58,8 +58,8 @@ def kernel_work(name, chunks, H, V):
         return "hbm", sum(4.0 * c * V for c in chunks), "byte"
     if name == "pack_x":                       # bf16 X chunk read and written packed
         return "hbm", sum(4.0 * c * H for c in chunks), "byte"
-    if name == "pack_w":                       # W read and written packed, twice
-        return "hbm", 2 * 4.0 * V * H, "byte"
+    if name == "pack_w":                       # W read once, written packed twice
+        return "hbm", 6.0 * V * H, "byte"
     return "hbm", None, "byte"
 
 

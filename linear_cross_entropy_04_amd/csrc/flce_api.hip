@@ -193,11 +193,13 @@ int run(bool bwd, const void *X, const void *W, const int64_t *labels, int64_t N
   if (bwd && N == 0 && !o.accumulate_dw) LAUNCH(FLCE_K_FINAL, launch_fill_f32(dW, V * H, 0.f, s));
 
   if (dtype == FLCE_BF16 && N > 0) {
-    LAUNCH(FLCE_K_PACK_W, launch_pack_bf16((const uint16_t *)W, Vi, Hi, (uint16_t *)(ws + p.off_wp),
-                                         p.nks_h, s));
-    if (bwd)
+    if (bwd)      // Wp and WTp from one read of W
       LAUNCH(FLCE_K_PACK_W, launch_pack_t_bf16((const uint16_t *)W, Vi, Hi,
-                                             (uint16_t *)(ws + p.off_wtp), p.nks_z, s));
+                                               (uint16_t *)(ws + p.off_wtp), p.nks_z,
+                                               (uint16_t *)(ws + p.off_wp), p.nks_h, s));
+    else
+      LAUNCH(FLCE_K_PACK_W, launch_pack_bf16((const uint16_t *)W, Vi, Hi,
+                                             (uint16_t *)(ws + p.off_wp), p.nks_h, s));
   }
   for (int64_t c0 = 0; c0 < N; c0 += C) {
     const int c = (int)std::min(C, N - c0);

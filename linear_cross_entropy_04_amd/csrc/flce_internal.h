@@ -77,9 +77,10 @@ hipError_t launch_dlogits_bf16(uint16_t *Zp, int64_t nks_z, int c, int V, const 
                                const int64_t *labels_c, int64_t ii, const float *wrow_c,
                                const Scalars *sc, hipStream_t s);
 // Pack the transpose of a row-major [R][K] matrix into PT (rows K padded to
-// 256, nks_t column slices covering R).
+// 256, nks_t column slices covering R) and, if P is not null, the matrix
+// itself into P (rows R padded to 256, nks_p slices), reading it once.
 hipError_t launch_pack_t_bf16(const uint16_t *src, int R, int K, uint16_t *PT, int64_t nks_t,
-                              hipStream_t s);
+                              uint16_t *P, int64_t nks_p, hipStream_t s);
 hipError_t launch_dx_bf16(const uint16_t *Gp, int64_t nks_z, const uint16_t *WTp, int c, int H,
                           int V, int splitk, int64_t ksplit, float *dxp, hipStream_t s);
 hipError_t launch_dx_reduce_bf16(const float *dxp, int splitk, int c, int H, uint16_t *dXc,
