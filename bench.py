@@ -110,6 +110,19 @@ def cpu_baseline(inp, n_tok):
 CE_N, CE_V = 8192, 128256     # the Llama-3-8B head's logits: 8 x 1024 tokens x vocabulary
 
 
+def copy_reference(mib, dev):
+    """One plain device copy of `mib` MiB: a transfer of known size that the
+    hardware byte counters of the same run can be scaled by."""
+    import torch
+    src = torch.empty(mib << 18, dtype=torch.float32, device=dev)
+    src.fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def bench_ce(args):
     """Cross-entropy on given bf16 logits [8192, 128256], in place: one step
     is one flce_ce_fwd_bwd (label pass, row kernel, final loss, sync).  The
@@ -130,6 +143,8 @@ def bench_ce(args):
     y = torch.from_numpy(y_np).to(dev)
     ws = torch.empty(fl.flce_ce_workspace_bytes(CE_N), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
+    if args.copy_reference_mib:
+        copy_reference(args.copy_reference_mib, dev)
     loss0 = fl.flce_ce_fwd_bwd(L, y, -100, ws, stream=stream)      # on the drawn logits
     for _ in range(max(args.warmup - 1, 0)):
         fl.flce_ce_fwd_bwd(L, y, -100, ws, stream=stream)
@@ -242,13 +257,7 @@ def main():
     stream = torch.cuda.current_stream(dev)
 
     if args.copy_reference_mib:
-        src = torch.empty(args.copy_reference_mib << 18, dtype=torch.float32, device=dev)
-        src.fill_(1.0)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        copy_reference(args.copy_reference_mib, dev)
 
     def step():
         return fl.flce_fwd_bwd(X, W, y, -100, chunk, dX, dW, ws, stream=stream)
