@@ -308,3 +308,108 @@ def dW_rows(X, W, labels, lse, vrows, ignore_index: int = IGNORE_INDEX) -> np.nd
     Zc = logits(Xd, np.asarray(W[vrows], dtype=np.float64))   # [N, k] columns vrows of Z
     G = dlogits(Zc, np.asarray(lse, dtype=np.float64), labels, valid, n_valid, col_ids=vrows)
     return grad_weight(G, Xd)
+
+
+# ------------------------------------------------------------------ odds-ratio preference loss
+# The project overview page lists fused-linear post-training losses built on
+# the same chunked projection ("Kernels de Pós-Treinamento") and calls the
+# ORPO one as orpo_loss(lm_head.weight, x, target) ("Exemplo de Uso de Perda
+# de Pós-Treinamento").  The pages give no formula; this is the published
+# definition of Odds Ratio Preference Optimization (Hong, Lee and Thorne,
+# 2024) on top of the per-token log-probabilities above:
+#   a_s   = mean over the valid tokens t of sequence s of log p(y_t)
+#   odds  = p / (1 - p) with p = exp(a_s), so log odds(a) = a - log(1 - e^a)
+#   d_i   = log odds(a_chosen_i) - log odds(a_rejected_i)
+#   L_OR  = mean over pairs of -log sigmoid(d_i)
+#   L_SFT = mean over the chosen sequences' valid tokens of -log p(y_t)
+#   L     = L_SFT + beta L_OR
+# Layout (read from the call form): the rows of X are 2B sequences of T
+# tokens, the B chosen sequences first, then the B rejected ones, pair i =
+# (sequence i, sequence B + i); ignore_index marks the tokens that are not
+# scored (prompt, padding).  A pair with an empty sequence adds nothing to
+# L_OR (the mean still divides by B).
+
+@dataclasses.dataclass
+class ORPOResult:
+    loss: float
+    nll: float                   # L_SFT
+    or_loss: float               # L_OR (before beta)
+    chosen_logp: np.ndarray      # [B] a of each chosen sequence (0 if empty)
+    rejected_logp: np.ndarray    # [B]
+    log_odds_ratio: np.ndarray   # [B] d_i (0 for pairs with an empty sequence)
+    dX: np.ndarray | None
+    dW: np.ndarray | None
+
+
+def sequence_logp(lp: np.ndarray, valid: np.ndarray, n_seq: int):
+    """Mean log-probability over each sequence's valid tokens and the number
+    of valid tokens; lp and valid are [n_seq * T], sequence-major."""
+    lp = lp.reshape(n_seq, -1)
+    valid = valid.reshape(n_seq, -1)
+    n = valid.sum(axis=1)
+    a = np.where(n > 0, np.where(valid, lp, 0.0).sum(axis=1) / np.maximum(n, 1), 0.0)
+    return a, n
+
+
+def log_odds(a: np.ndarray) -> np.ndarray:
+    """log(p / (1 - p)) for log p = a < 0."""
+    return a - np.log(-np.expm1(a))
+
+
+def odds_ratio_loss(d: np.ndarray, live: np.ndarray) -> np.ndarray:
+    """-log sigmoid(d) = log(1 + e^-d) per pair, 0 where the pair is not live."""
+    return np.where(live, np.logaddexp(0.0, -d), 0.0)
+
+
+def orpo_token_weights(a_c, n_c, a_r, n_r, d, live, valid, n_pairs: int, n_chosen_valid: int,
+                       beta: float) -> np.ndarray:
+    """w_t = -dL/d log p(y_t) for every token (sequence-major [2B * T]): the
+    loss above as L = sum_t w_t l_t in the per-token losses l_t = -log p(y_t).
+
+    dL_SFT/d lp_t = -1/N_c on chosen valid tokens; through a_s = mean of lp,
+    dL_OR,i/d a_c = -sigmoid(-d_i) / (1 - e^{a_c}) and
+    dL_OR,i/d a_r = +sigmoid(-d_i) / (1 - e^{a_r}), each spread as 1/n_s over
+    the sequence's valid tokens, and L_OR is their mean over B pairs."""
+    s = np.where(live, 1.0 / (1.0 + np.exp(d)), 0.0)                # sigmoid(-d)
+    a_c = np.where(live, a_c, -1.0)                                 # pairs not live: s = 0
+    a_r = np.where(live, a_r, -1.0)
+    gc = -beta / n_pairs * s / (-np.expm1(a_c)) / np.maximum(n_c, 1)
+    gr = beta / n_pairs * s / (-np.expm1(a_r)) / np.maximum(n_r, 1)
+    T = valid.size // (2 * n_pairs)
+    v = valid.reshape(2 * n_pairs, T)
+    dlp = np.zeros((2 * n_pairs, T))
+    dlp[:n_pairs] = -1.0 / max(n_chosen_valid, 1) + gc[:, None]
+    dlp[n_pairs:] = gr[:, None]
+    return np.where(v, -dlp, 0.0).reshape(-1)
+
+
+def orpo(X, W, labels, n_pairs: int, ignore_index: int = IGNORE_INDEX, beta: float = 0.1,
+         grads: bool = True) -> ORPOResult:
+    """ORPO loss of 2 * n_pairs sequences (rows of X sequence-major, chosen
+    first) and its gradients."""
+    X = np.asarray(X, dtype=np.float64)
+    W = np.asarray(W, dtype=np.float64)
+    labels = np.asarray(labels, dtype=np.int64)
+    N, V = X.shape[0], W.shape[0]
+    if n_pairs <= 0 or N % (2 * n_pairs) != 0:
+        raise ValueError("X must hold 2 * n_pairs sequences of equal length")
+    valid = valid_mask(labels, V, ignore_index)
+    Z = logits(X, W)
+    lse = row_logsumexp(Z)
+    zy = target_logit(Z, labels, valid)
+    lp = log_probs(lse, zy, valid)
+    a, n = sequence_logp(lp, valid, 2 * n_pairs)
+    a_c, a_r, n_c, n_r = a[:n_pairs], a[n_pairs:], n[:n_pairs], n[n_pairs:]
+    live = (n_c > 0) & (n_r > 0)
+    d = np.where(live, log_odds(np.where(live, a_c, -1.0)) - log_odds(np.where(live, a_r, -1.0)),
+                 0.0)
+    half = N // 2
+    n_chosen_valid = int(valid[:half].sum())
+    nll = float(-lp[:half].sum() / max(n_chosen_valid, 1))
+    or_loss = float(odds_ratio_loss(d, live).sum() / n_pairs)
+    loss = nll + beta * or_loss
+    if not grads:
+        return ORPOResult(loss, nll, or_loss, a_c, a_r, d, None, None)
+    w = orpo_token_weights(a_c, n_c, a_r, n_r, d, live, valid, n_pairs, n_chosen_valid, beta)
+    G = dlogits_weighted(Z, lse, labels, w)
+    return ORPOResult(loss, nll, or_loss, a_c, a_r, d, grad_input(G, W), grad_weight(G, X))
