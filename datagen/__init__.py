@@ -220,6 +220,33 @@ def make_logits(N: int, V: int, dtype: str = "bf16", seed: int = 1, std: float =
     return (f32_to_bf16_bits(Z) if dtype == "bf16" else Z), y
 
 
+def make_pairs(n_pairs: int, T: int, H: int, V: int, dtype: str = "bf16", seed: int = 1,
+               w_std: float = 0.02) -> Inputs:
+    """Preference batch: 2 n_pairs sequences of T tokens as rows of X (the
+    n_pairs chosen sequences first, then the rejected ones; pair i is
+    sequence i and sequence n_pairs + i).
+
+    Each pair shares a prompt of P ~ U{ceil(T/8) .. floor(T/2)} tokens, and
+    each sequence ends with D ~ U{0 .. floor(T/4)} padding tokens; prompt and
+    padding are ignore_index, the response tokens between them get uniform
+    labels.  X ~ N(0, 1), W ~ N(0, w_std^2) as in the other workloads.  Draw
+    order: X, W, labels, prompt lengths, padding lengths."""
+    N = 2 * n_pairs * T
+    wl = Workload("pairs", N, H, V, dtype, 0, ignore_mode="none", w_std=w_std)
+    ss = np.random.SeedSequence(seed)
+    s_x, s_w, s_y, s_p, s_d = ss.spawn(5)
+    X = _draw_X(np.random.default_rng(s_x), N, H, "normal", dtype)
+    W = _draw_W(s_w, V, H, w_std, dtype)
+    y = _draw_labels(np.random.default_rng(s_y), N, V, "uniform", 0.0).reshape(2 * n_pairs, T)
+    P = np.random.default_rng(s_p).integers(-(-T // 8), T // 2 + 1, size=n_pairs)
+    D = np.random.default_rng(s_d).integers(0, T // 4 + 1, size=2 * n_pairs)
+    for s_ in range(2 * n_pairs):
+        y[s_, :P[s_ % n_pairs]] = IGNORE_INDEX
+        if D[s_]:
+            y[s_, T - D[s_]:] = IGNORE_INDEX
+    return Inputs(wl, X, W, y.reshape(-1), seed)
+
+
 def sample_rows(n_total: int, k: int, seed: int, must: tuple = ()) -> np.ndarray:
     """Seeded sorted sample of k distinct row indices, always holding ``must``."""
     rng = np.random.default_rng(seed)

@@ -193,6 +193,47 @@ int flce_ce_fwd(const void *logits, const int64_t *labels, int64_t N, int64_t V,
                 void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Odds-ratio preference loss (ORPO) on the fused projection, one of the
+ * fused-linear post-training losses of the Liger Kernel pages (project
+ * overview page, "Kernels de Pós-Treinamento"; called as
+ * orpo_loss(lm_head.weight, x, target) in "Exemplo de Uso de Perda de
+ * Pós-Treinamento").  The pages give no formula; this is the published
+ * definition (Hong, Lee and Thorne, 2024):
+ *     a_s   = mean of log p(y_t) over the scored tokens of sequence s
+ *     d_i   = log odds(a_chosen_i) - log odds(a_rejected_i),  log odds(a) = a - log(1 - e^a)
+ *     loss  = NLL + beta * (1 / n_pairs) sum_i -log sigmoid(d_i)
+ *     NLL   = mean of -log p(y_t) over the chosen sequences' scored tokens
+ * with p = softmax(x_t W^T).  A pair with a sequence that has no scored token
+ * adds nothing to the odds-ratio term.
+ *   X          device [2 n_pairs T, H] (dtype)  2 n_pairs sequences of T rows: the
+ *                                               n_pairs chosen ones, then the rejected
+ *                                               ones; pair i = (sequence i, n_pairs + i)
+ *   labels     device [2 n_pairs T] int64       ignore_index marks unscored tokens
+ *   W          device [V, H] (dtype)
+ *   beta       weight of the odds-ratio term
+ *   chunk_pairs  pairs per chunk (a chunk holds both sequences of each of its
+ *              pairs: 2 chunk_pairs T rows); <= 0: the largest count with at
+ *              most 4096 rows (at least 1)
+ *   loss, nll  host float (nll may be NULL)
+ *   dX         device [2 n_pairs T, H] (dtype), overwritten; dW device [V, H] fp32, overwritten
+ *   chosen_logp, rejected_logp, log_odds_ratio   device [n_pairs] fp32 or NULL
+ *   workspace  device, >= flce_orpo_workspace_bytes(...) bytes, 256-byte aligned
+ * Same alignment rules and errors as flce_fwd_bwd; n_pairs, T >= 1.
+ */
+size_t flce_orpo_workspace_bytes(int64_t n_pairs, int64_t T, int64_t H, int64_t V, int dtype,
+                                 int64_t chunk_pairs);
+int flce_orpo_fwd_bwd(const void *X, const void *W, const int64_t *labels, int64_t n_pairs,
+                      int64_t T, int64_t H, int64_t V, int dtype, int64_t ignore_index, float beta,
+                      int64_t chunk_pairs, float *loss, float *nll, void *dX, float *dW,
+                      float *chosen_logp, float *rejected_logp, float *log_odds_ratio,
+                      void *workspace, size_t workspace_bytes, void *stream);
+int flce_orpo_fwd(const void *X, const void *W, const int64_t *labels, int64_t n_pairs, int64_t T,
+                  int64_t H, int64_t V, int dtype, int64_t ignore_index, float beta,
+                  int64_t chunk_pairs, float *loss, float *nll, float *chosen_logp,
+                  float *rejected_logp, float *log_odds_ratio, void *workspace,
+                  size_t workspace_bytes, void *stream);
+
+/*
  * buf[i] *= *scale for i < n, in place, on the stream (no sync).  buf is a
  * device array of dtype (FLCE_F32 or FLCE_BF16); scale is a device fp32
  * scalar.  Used to apply an upstream gradient d(out)/d(loss) != 1 to dX, dW.
@@ -219,7 +260,9 @@ enum {
   FLCE_K_PACK = 8,        /* per-chunk packing of X into the GEMM operand layout */
   FLCE_K_PACK_W = 9,      /* per-call packing of W (as is and transposed) */
   FLCE_K_CE_ROWS = 10,    /* cross-entropy on given logits, one workgroup per row */
-  FLCE_K_COUNT = 11
+  FLCE_K_ORPO = 11,       /* preference loss: label pass, per-pair step, final loss */
+  FLCE_K_ROWS = 12,       /* preference loss: gathering a chunk's rows, scattering dX */
+  FLCE_K_COUNT = 13
 };
 int flce_profile_enable(int enable);
 int flce_profile_read(double *ms, int64_t *launches, int n);

@@ -23,6 +23,8 @@ __all__ = [
     "flce_profile_enable", "flce_profile_read",
     "workspace", "loss", "FusedLinearCrossEntropyLoss",
     "flce_ce_workspace_bytes", "flce_ce_fwd_bwd", "flce_ce_fwd", "cross_entropy",
+    "flce_orpo_workspace_bytes", "flce_orpo_fwd_bwd", "flce_orpo_fwd", "orpo_loss",
+    "FusedLinearORPOLoss",
 ]
 
 FLCE_F32 = 0
@@ -83,6 +85,17 @@ def _load():
     l.flce_ce_fwd.argtypes = [_p, _p, _i64, _i64, _i32, _i64, _i32,
                               ctypes.POINTER(ctypes.c_float), _p, _p, _p, _p, _sz, _p]
     l.flce_ce_fwd.restype = _i32
+    l.flce_orpo_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64, _i32, _i64]
+    l.flce_orpo_workspace_bytes.restype = _sz
+    l.flce_orpo_fwd_bwd.argtypes = [_p, _p, _p, _i64, _i64, _i64, _i64, _i32, _i64,
+                                    ctypes.c_float, _i64, ctypes.POINTER(ctypes.c_float),
+                                    ctypes.POINTER(ctypes.c_float), _p, _p, _p, _p, _p, _p, _sz,
+                                    _p]
+    l.flce_orpo_fwd_bwd.restype = _i32
+    l.flce_orpo_fwd.argtypes = [_p, _p, _p, _i64, _i64, _i64, _i64, _i32, _i64, ctypes.c_float,
+                                _i64, ctypes.POINTER(ctypes.c_float),
+                                ctypes.POINTER(ctypes.c_float), _p, _p, _p, _p, _sz, _p]
+    l.flce_orpo_fwd.restype = _i32
     l.flce_scale_inplace.argtypes = [_p, _i64, _i32, _p, _p]
     l.flce_scale_inplace.restype = _i32
     l.flce_status_string.argtypes = [_i32]
@@ -107,7 +120,7 @@ def flce_last_error() -> str:
     return _load().flce_last_error().decode()
 
 
-KERNEL_CLASSES = 11
+KERNEL_CLASSES = 13
 
 
 def flce_profile_enable(enable: bool = True) -> None:
@@ -338,6 +351,70 @@ def flce_ce_fwd(logits: torch.Tensor, labels: torch.Tensor, ignore_index: int,
     return float(loss.value)
 
 
+def flce_orpo_workspace_bytes(n_pairs: int, T: int, H: int, V: int, dtype: int,
+                              chunk_pairs: int = 0) -> int:
+    return int(_load().flce_orpo_workspace_bytes(n_pairs, T, H, V, dtype, chunk_pairs))
+
+
+def _orpo_args(X, W, labels, n_pairs, workspace, chosen_logp, rejected_logp, log_odds_ratio):
+    N, H = X.shape
+    V = W.shape[0]
+    if n_pairs <= 0 or N % (2 * n_pairs) != 0:
+        raise ValueError(f"X has {N} rows: not 2 * n_pairs = {2 * n_pairs} equal sequences")
+    _dev(X, "X")
+    _dev(W, "W", X.dtype, (V, H))
+    _dev(labels, "labels", torch.int64, (N,))
+    _dev(workspace, "workspace")
+    for t, name in ((chosen_logp, "chosen_logp"), (rejected_logp, "rejected_logp"),
+                    (log_odds_ratio, "log_odds_ratio")):
+        _dev(t, name, torch.float32, (n_pairs,))
+    return N // (2 * n_pairs), H, V, _dtype_code(X)
+
+
+def flce_orpo_fwd_bwd(X: torch.Tensor, W: torch.Tensor, labels: torch.Tensor, n_pairs: int,
+                      ignore_index: int, beta: float, chunk_pairs: int, dX: torch.Tensor,
+                      dW: torch.Tensor, workspace: torch.Tensor,
+                      chosen_logp: torch.Tensor | None = None,
+                      rejected_logp: torch.Tensor | None = None,
+                      log_odds_ratio: torch.Tensor | None = None,
+                      stream=None) -> tuple[float, float]:
+    """Call libflce's flce_orpo_fwd_bwd: X holds 2 n_pairs sequences (chosen
+    first) as rows; returns (loss, nll)."""
+    T, H, V, dt = _orpo_args(X, W, labels, n_pairs, workspace, chosen_logp, rejected_logp,
+                             log_odds_ratio)
+    _dev(dX, "dX", X.dtype, tuple(X.shape))
+    _dev(dW, "dW", torch.float32, (V, H))
+    loss, nll = ctypes.c_float(0.0), ctypes.c_float(0.0)
+    st = _load().flce_orpo_fwd_bwd(_ptr(X), _ptr(W), _ptr(labels), n_pairs, T, H, V, dt,
+                                   ignore_index, float(beta), chunk_pairs, ctypes.byref(loss),
+                                   ctypes.byref(nll), _ptr(dX), _ptr(dW), _ptr(chosen_logp),
+                                   _ptr(rejected_logp), _ptr(log_odds_ratio), _ptr(workspace),
+                                   workspace.numel(), _stream(stream, X.device))
+    if st != FLCE_OK:
+        raise FLCEError(st, "flce_orpo_fwd_bwd")
+    return float(loss.value), float(nll.value)
+
+
+def flce_orpo_fwd(X: torch.Tensor, W: torch.Tensor, labels: torch.Tensor, n_pairs: int,
+                  ignore_index: int, beta: float, chunk_pairs: int, workspace: torch.Tensor,
+                  chosen_logp: torch.Tensor | None = None,
+                  rejected_logp: torch.Tensor | None = None,
+                  log_odds_ratio: torch.Tensor | None = None,
+                  stream=None) -> tuple[float, float]:
+    """Call libflce's flce_orpo_fwd; returns (loss, nll)."""
+    T, H, V, dt = _orpo_args(X, W, labels, n_pairs, workspace, chosen_logp, rejected_logp,
+                             log_odds_ratio)
+    loss, nll = ctypes.c_float(0.0), ctypes.c_float(0.0)
+    st = _load().flce_orpo_fwd(_ptr(X), _ptr(W), _ptr(labels), n_pairs, T, H, V, dt,
+                               ignore_index, float(beta), chunk_pairs, ctypes.byref(loss),
+                               ctypes.byref(nll), _ptr(chosen_logp), _ptr(rejected_logp),
+                               _ptr(log_odds_ratio), _ptr(workspace), workspace.numel(),
+                               _stream(stream, X.device))
+    if st != FLCE_OK:
+        raise FLCEError(st, "flce_orpo_fwd")
+    return float(loss.value), float(nll.value)
+
+
 def flce_scale_inplace(buf: torch.Tensor, scale: torch.Tensor, stream=None) -> None:
     """buf *= scale (a one-element fp32 device tensor), in place, on the stream."""
     _dev(buf, "buf")
@@ -481,3 +558,67 @@ def cross_entropy(logits: torch.Tensor, target: torch.Tensor, ignore_index: int 
     if reduction not in ("mean", "sum"):
         raise ValueError("cross_entropy supports reduction 'mean' or 'sum'")
     return _CEFunction.apply(logits, target, ignore_index, reduction, inplace)
+
+
+class _ORPOFunction(torch.autograd.Function):
+    """Odds-ratio preference loss: the gradients are computed with the loss
+    (one call) and scaled by the upstream gradient in backward."""
+
+    @staticmethod
+    def forward(ctx, weight, input, target, n_pairs, ignore_index, beta, chunk_pairs):
+        N, H = input.shape
+        V = weight.shape[0]
+        T = N // (2 * n_pairs) if n_pairs > 0 else 0
+        nbytes = flce_orpo_workspace_bytes(n_pairs, T, H, V, _dtype_code(input), chunk_pairs)
+        if nbytes == 0:
+            raise FLCEError(FLCE_EINVAL, "flce_orpo_workspace_bytes")
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=input.device)
+        if ctx.needs_input_grad[0] or ctx.needs_input_grad[1]:
+            dX = torch.empty_like(input)
+            dW = torch.empty((V, H), dtype=torch.float32, device=input.device)
+            val, _ = flce_orpo_fwd_bwd(input, weight, target, n_pairs, ignore_index, beta,
+                                       chunk_pairs, dX, dW, ws)
+            ctx.save_for_backward(dX, dW)
+        else:
+            val, _ = flce_orpo_fwd(input, weight, target, n_pairs, ignore_index, beta,
+                                   chunk_pairs, ws)
+        ctx.wdtype = weight.dtype
+        return torch.tensor(val, dtype=torch.float32, device=input.device)
+
+    @staticmethod
+    def backward(ctx, grad_out):
+        dX, dW = ctx.saved_tensors
+        g = grad_out.detach().to(torch.float32).reshape(1).contiguous()
+        flce_scale_inplace(dX, g)
+        flce_scale_inplace(dW, g)
+        gw = dW if ctx.wdtype == torch.float32 else dW.to(ctx.wdtype)
+        return gw, dX, None, None, None, None, None
+
+
+def orpo_loss(weight: torch.Tensor, input: torch.Tensor, target: torch.Tensor,
+              ignore_index: int = -100, beta: float = 0.1, chunk_pairs: int = 0) -> torch.Tensor:
+    """ORPO loss in the pages' call form orpo_loss(lm_head.weight, x, target).
+
+    input [2B, T, H] (or [2B * T, H] with target [2B, T]): the B chosen
+    sequences, then the B rejected ones; target [2B, T] with ignore_index on
+    unscored tokens.  Returns NLL of the chosen tokens + beta * mean over pairs
+    of -log sigmoid(log odds ratio)."""
+    if target.dim() != 2 or target.shape[0] % 2 != 0:
+        raise ValueError("target must be [2B, T] (chosen sequences first)")
+    n_pairs = target.shape[0] // 2
+    x = input.reshape(-1, input.shape[-1])
+    if x.shape[0] != target.numel():
+        raise ValueError(f"input has {x.shape[0]} rows, target {target.numel()} tokens")
+    return _ORPOFunction.apply(weight, x, target.reshape(-1).contiguous(), n_pairs, ignore_index,
+                               beta, chunk_pairs)
+
+
+class FusedLinearORPOLoss(torch.nn.Module):
+    """Module form: FusedLinearORPOLoss(beta)(lm_head.weight, x, target)."""
+
+    def __init__(self, ignore_index: int = -100, beta: float = 0.1, chunk_pairs: int = 0):
+        super().__init__()
+        self.ignore_index, self.beta, self.chunk_pairs = ignore_index, beta, chunk_pairs
+
+    def forward(self, weight, input, target):
+        return orpo_loss(weight, input, target, self.ignore_index, self.beta, self.chunk_pairs)

@@ -150,6 +150,86 @@ struct Options {
   float *logprob = nullptr;           // per-token z_y - lse
 };
 
+// One chunk's rows, contiguous in memory, and where its per-row outputs go.
+struct ChunkIO {
+  const void *Xc = nullptr;        // [c, H] rows of X (dtype of the plan)
+  const int64_t *lab = nullptr;    // [c] labels
+  int c = 0;
+  float *rl = nullptr;             // [c] per-token loss (required)
+  float *rs = nullptr;             // [c] log-sum-exp or null
+  float *lp = nullptr;             // [c] log-probability of the target or null
+  const float *wr = nullptr;       // [c] per-token loss weights, or null for sc->scale
+  bool acc_dw = false;             // dW += (else dW =)
+  void *dXc = nullptr;             // [c, H] rows of dX (backward)
+};
+
+// Forward of one chunk: pack X_c (bf16), logits tile GEMM with the LSE
+// epilogue (Z_c kept when the backward follows), per-token lse and loss.
+int chunk_forward(const Plan &p, char *ws, const void *W, int64_t ii, bool keep_z,
+                  const ChunkIO &io, hipStream_t s) {
+  const int Hi = (int)p.H, Vi = (int)p.V;
+  float *pm = (float *)(ws + p.off_pm);
+  float *ps = (float *)(ws + p.off_ps);
+  float *zy = (float *)(ws + p.off_zy);
+  float *lse = (float *)(ws + p.off_lse);
+  if (p.dtype == FLCE_BF16) {
+    const uint16_t *Wp = (const uint16_t *)(ws + p.off_wp);
+    uint16_t *Zp = (uint16_t *)(ws + p.off_z);
+    uint16_t *Xp = (uint16_t *)(ws + p.off_xp);
+    LAUNCH(FLCE_K_PACK, launch_pack_bf16((const uint16_t *)io.Xc, io.c, Hi, Xp, p.nks_h, s));
+    LAUNCH(FLCE_K_FWD_TILE, launch_fwd_tile_bf16(Wp, Xp, p.nks_h, io.lab, ii, io.c, Hi, Vi, Zp,
+                                                 p.nks_z, pm, ps, zy, p.nvt, keep_z, s));
+  } else {
+    float *z = (float *)(ws + p.off_z);
+    LAUNCH(FLCE_K_FWD_TILE, launch_fwd_tile_f32((const float *)W, (const float *)io.Xc, io.lab,
+                                                ii, io.c, Hi, Vi, z, p.ldz, pm, ps, zy, p.nvt,
+                                                keep_z, s));
+  }
+  LAUNCH(FLCE_K_LSE_COMBINE, launch_lse_combine(pm, ps, zy, io.lab, ii, io.c, p.nvt, lse, io.rl,
+                                                io.rs, io.lp, s));
+  return FLCE_OK;
+}
+
+// Backward of one chunk after chunk_forward: G_c in place, dX_c, dW.
+int chunk_backward(const Plan &p, char *ws, const void *W, int64_t ii, const ChunkIO &io,
+                   float *dW, const Scalars *sc, hipStream_t s) {
+  const int Hi = (int)p.H, Vi = (int)p.V;
+  const float *lse = (const float *)(ws + p.off_lse);
+  if (p.dtype == FLCE_BF16) {
+    uint16_t *Zp = (uint16_t *)(ws + p.off_z);
+    const uint16_t *Xp = (const uint16_t *)(ws + p.off_xp);
+    float *dxp = (float *)(ws + p.off_dxp);
+    LAUNCH(FLCE_K_DLOGITS, launch_dlogits_bf16(Zp, p.nks_z, io.c, Vi, lse, io.lab, ii, io.wr, sc,
+                                               s));
+    LAUNCH(FLCE_K_DX_GEMM, launch_dx_bf16(Zp, p.nks_z, (const uint16_t *)(ws + p.off_wtp), io.c,
+                                          Hi, Vi, p.splitk, p.ksplit, dxp, s));
+    LAUNCH(FLCE_K_DX_REDUCE, launch_dx_reduce_bf16(dxp, p.splitk, io.c, Hi, (uint16_t *)io.dXc, s));
+    LAUNCH(FLCE_K_DW_GEMM, launch_dw_bf16(Zp, p.nks_z, Xp, p.nks_h, io.c, Hi, Vi, dW, io.acc_dw, s));
+  } else {
+    const float *Wf = (const float *)W;
+    float *z = (float *)(ws + p.off_z);
+    LAUNCH(FLCE_K_DLOGITS, launch_dlogits_f32(z, p.ldz, io.c, Vi, lse, io.lab, ii, io.wr, sc, s));
+    LAUNCH(FLCE_K_DX_GEMM, launch_dx_f32(z, p.ldz, Wf, io.c, Hi, Vi, (float *)io.dXc, s));
+    LAUNCH(FLCE_K_DW_GEMM, launch_dw_f32(z, p.ldz, (const float *)io.Xc, io.c, Hi, Vi, dW,
+                                         io.acc_dw, s));
+  }
+  return FLCE_OK;
+}
+
+// Pack W once per call (bf16 path): Wp, and WTp too when a backward follows.
+int pack_weight(const Plan &p, char *ws, const void *W, bool bwd, hipStream_t s) {
+  if (p.dtype != FLCE_BF16) return FLCE_OK;
+  const int Hi = (int)p.H, Vi = (int)p.V;
+  if (bwd)      // Wp and WTp from one read of W
+    LAUNCH(FLCE_K_PACK_W, launch_pack_t_bf16((const uint16_t *)W, Vi, Hi,
+                                             (uint16_t *)(ws + p.off_wtp), p.nks_z,
+                                             (uint16_t *)(ws + p.off_wp), p.nks_h, s));
+  else
+    LAUNCH(FLCE_K_PACK_W, launch_pack_bf16((const uint16_t *)W, Vi, Hi,
+                                           (uint16_t *)(ws + p.off_wp), p.nks_h, s));
+  return FLCE_OK;
+}
+
 int run(bool bwd, const void *X, const void *W, const int64_t *labels, int64_t N, int64_t H,
         int64_t V, int dtype, int64_t ii, int64_t chunk_tokens, float *loss, void *dX, float *dW,
         float *row_loss, float *row_lse, const Options &o, void *workspace,
@@ -182,62 +262,31 @@ int run(bool bwd, const void *X, const void *W, const int64_t *labels, int64_t N
   hipStream_t s = (hipStream_t)stream;
   char *ws = (char *)workspace;
   Scalars *sc = (Scalars *)(ws + p.off_scal);
-  float *pm = (float *)(ws + p.off_pm);
-  float *ps = (float *)(ws + p.off_ps);
-  float *zy = (float *)(ws + p.off_zy);
-  float *lse = (float *)(ws + p.off_lse);
   float *rowloss = row_loss ? row_loss : (float *)(ws + p.off_rowloss);
-  const int Hi = (int)H, Vi = (int)V;
 
   LAUNCH(FLCE_K_LABELS, launch_label_check(labels, N, V, ii, o.reduction, sc, s));
   if (bwd && N == 0 && !o.accumulate_dw) LAUNCH(FLCE_K_FINAL, launch_fill_f32(dW, V * H, 0.f, s));
 
-  if (dtype == FLCE_BF16 && N > 0) {
-    if (bwd)      // Wp and WTp from one read of W
-      LAUNCH(FLCE_K_PACK_W, launch_pack_t_bf16((const uint16_t *)W, Vi, Hi,
-                                               (uint16_t *)(ws + p.off_wtp), p.nks_z,
-                                               (uint16_t *)(ws + p.off_wp), p.nks_h, s));
-    else
-      LAUNCH(FLCE_K_PACK_W, launch_pack_bf16((const uint16_t *)W, Vi, Hi,
-                                             (uint16_t *)(ws + p.off_wp), p.nks_h, s));
+  if (N > 0) {
+    st = pack_weight(p, ws, W, bwd, s);
+    if (st != FLCE_OK) return st;
   }
   for (int64_t c0 = 0; c0 < N; c0 += C) {
-    const int c = (int)std::min(C, N - c0);
-    const int64_t *lab = labels + c0;
-    float *rl = rowloss + c0;
-    float *rs = row_lse ? row_lse + c0 : nullptr;
-    float *lp = o.logprob ? o.logprob + c0 : nullptr;
-    const float *wr = o.grad_rows ? o.grad_rows + c0 : nullptr;
-    const bool acc_dw = c0 > 0 || o.accumulate_dw;
-    if (dtype == FLCE_BF16) {
-      const uint16_t *Wp = (const uint16_t *)(ws + p.off_wp);
-      const uint16_t *Xc = (const uint16_t *)X + c0 * H;
-      uint16_t *Zp = (uint16_t *)(ws + p.off_z);
-      uint16_t *Xp = (uint16_t *)(ws + p.off_xp);
-      LAUNCH(FLCE_K_PACK, launch_pack_bf16(Xc, c, Hi, Xp, p.nks_h, s));
-      LAUNCH(FLCE_K_FWD_TILE, launch_fwd_tile_bf16(Wp, Xp, p.nks_h, lab, ii, c, Hi, Vi, Zp,
-                                                   p.nks_z, pm, ps, zy, p.nvt, bwd, s));
-      LAUNCH(FLCE_K_LSE_COMBINE, launch_lse_combine(pm, ps, zy, lab, ii, c, p.nvt, lse, rl, rs, lp, s));
-      if (bwd) {
-        LAUNCH(FLCE_K_DLOGITS, launch_dlogits_bf16(Zp, p.nks_z, c, Vi, lse, lab, ii, wr, sc, s));
-        float *dxp = (float *)(ws + p.off_dxp);
-        LAUNCH(FLCE_K_DX_GEMM, launch_dx_bf16(Zp, p.nks_z, (const uint16_t *)(ws + p.off_wtp), c,
-                                              Hi, Vi, p.splitk, p.ksplit, dxp, s));
-        LAUNCH(FLCE_K_DX_REDUCE,
-               launch_dx_reduce_bf16(dxp, p.splitk, c, Hi, (uint16_t *)dX + c0 * H, s));
-        LAUNCH(FLCE_K_DW_GEMM, launch_dw_bf16(Zp, p.nks_z, Xp, p.nks_h, c, Hi, Vi, dW, acc_dw, s));
-      }
-    } else {
-      const float *Wf = (const float *)W;
-      const float *Xc = (const float *)X + c0 * H;
-      float *z = (float *)(ws + p.off_z);
-      LAUNCH(FLCE_K_FWD_TILE, launch_fwd_tile_f32(Wf, Xc, lab, ii, c, Hi, Vi, z, p.ldz, pm, ps, zy, p.nvt, bwd, s));
-      LAUNCH(FLCE_K_LSE_COMBINE, launch_lse_combine(pm, ps, zy, lab, ii, c, p.nvt, lse, rl, rs, lp, s));
-      if (bwd) {
-        LAUNCH(FLCE_K_DLOGITS, launch_dlogits_f32(z, p.ldz, c, Vi, lse, lab, ii, wr, sc, s));
-        LAUNCH(FLCE_K_DX_GEMM, launch_dx_f32(z, p.ldz, Wf, c, Hi, Vi, (float *)dX + c0 * H, s));
-        LAUNCH(FLCE_K_DW_GEMM, launch_dw_f32(z, p.ldz, Xc, c, Hi, Vi, dW, acc_dw, s));
-      }
+    ChunkIO io;
+    io.c = (int)std::min(C, N - c0);
+    io.Xc = (const char *)X + c0 * H * (dtype == FLCE_BF16 ? 2 : 4);
+    io.lab = labels + c0;
+    io.rl = rowloss + c0;
+    io.rs = row_lse ? row_lse + c0 : nullptr;
+    io.lp = o.logprob ? o.logprob + c0 : nullptr;
+    io.wr = o.grad_rows ? o.grad_rows + c0 : nullptr;
+    io.acc_dw = c0 > 0 || o.accumulate_dw;
+    io.dXc = bwd ? (char *)dX + c0 * H * (dtype == FLCE_BF16 ? 2 : 4) : nullptr;
+    st = chunk_forward(p, ws, W, ii, bwd, io, s);
+    if (st != FLCE_OK) return st;
+    if (bwd) {
+      st = chunk_backward(p, ws, W, ii, io, dW, sc, s);
+      if (st != FLCE_OK) return st;
     }
   }
   LAUNCH(FLCE_K_FINAL, launch_final_loss(rowloss, N, o.reduction, sc, s));
@@ -468,6 +517,171 @@ FLCE_API int flce_ce_fwd(const void *logits, const int64_t *labels, int64_t N, i
                       workspace_bytes, stream);
 }
 
+// ---------------------------------------------------------------- odds-ratio preference loss
+// A chunk holds k whole pairs: their chosen rows, then their rejected rows,
+// gathered from the two halves of X into one contiguous chunk, so the fused
+// pipeline runs on it unchanged.  Between its forward and its backward the
+// per-pair step turns the chunk's per-token log-probabilities into the loss
+// terms and the per-token weights of the backward (orpo_kernels.hip).
+
+namespace flce {
+namespace {
+
+constexpr int64_t kOrpoAutoRows = 4096;
+
+struct OrpoLayout {
+  Plan p;                 // the fused pipeline for chunks of C = 2 k T rows
+  int64_t k = 0;          // pairs per chunk
+  size_t off_x = 0, off_lab = 0, off_lp = 0, off_w = 0, off_dx = 0, off_nll = 0, off_or = 0,
+         off_clp = 0, off_rlp = 0, off_lor = 0, total = 0;
+};
+
+int orpo_check(int64_t B, int64_t T, int64_t H, int64_t V, int dtype) {
+  if (B <= 0 || T <= 0) return FLCE_EINVAL;
+  if (T > ((int64_t)1 << 29) || B > kMaxN / (2 * T)) return FLCE_EUNSUPPORTED;
+  return check_sizes(2 * B * T, H, V, dtype);
+}
+
+void orpo_layout(int64_t B, int64_t T, int64_t H, int64_t V, int dtype, int64_t chunk_pairs,
+                 OrpoLayout *L) {
+  int64_t k = chunk_pairs > 0 ? chunk_pairs : kOrpoAutoRows / (2 * T);
+  k = std::max<int64_t>(1, std::min(k, B));
+  const int64_t C = 2 * k * T;
+  const size_t esz = dtype == FLCE_BF16 ? 2 : 4;
+  make_plan(C, H, V, dtype, C, &L->p);       // its per-token loss array holds one chunk
+  L->k = k;
+  size_t o = L->p.total;
+  L->off_x = o;
+  o += align256((size_t)C * H * esz);
+  L->off_lab = o;
+  o += align256((size_t)C * 8);
+  L->off_lp = o;
+  o += align256((size_t)C * 4);
+  L->off_w = o;
+  o += align256((size_t)C * 4);
+  L->off_dx = o;
+  o += align256((size_t)C * H * esz);
+  size_t *pair_arrays[5] = {&L->off_nll, &L->off_or, &L->off_clp, &L->off_rlp, &L->off_lor};
+  for (size_t *q : pair_arrays) {
+    *q = o;
+    o += align256((size_t)B * 4);
+  }
+  L->total = o;
+}
+
+int run_orpo(bool bwd, const void *X, const void *W, const int64_t *labels, int64_t B, int64_t T,
+             int64_t H, int64_t V, int dtype, int64_t ii, float beta, int64_t chunk_pairs,
+             float *loss, float *nll, void *dX, float *dW, float *chosen_logp,
+             float *rejected_logp, float *log_odds_ratio, void *workspace,
+             size_t workspace_bytes, void *stream) {
+  int st = orpo_check(B, T, H, V, dtype);
+  if (st != FLCE_OK) return st;
+  if (!loss || !X || !W || !labels || !workspace) return FLCE_EINVAL;
+  if (bwd && (!dX || !dW)) return FLCE_EINVAL;
+  if (misaligned(workspace, 256) || misaligned(labels, 8) || misaligned(chosen_logp, 4) ||
+      misaligned(rejected_logp, 4) || misaligned(log_odds_ratio, 4))
+    return FLCE_EINVAL;
+  if (dtype == FLCE_BF16 && (misaligned(X, 16) || misaligned(W, 16) || (bwd && misaligned(dX, 16))))
+    return FLCE_EUNSUPPORTED;
+  if (dtype == FLCE_F32 && (misaligned(X, 4) || misaligned(W, 4) || (bwd && misaligned(dX, 4))))
+    return FLCE_EINVAL;
+  if (bwd && misaligned(dW, 4)) return FLCE_EINVAL;
+  OrpoLayout L;
+  orpo_layout(B, T, H, V, dtype, chunk_pairs, &L);
+  if (workspace_bytes < L.total) return FLCE_EWORKSPACE;
+
+  const Plan &p = L.p;
+  hipStream_t s = (hipStream_t)stream;
+  char *ws = (char *)workspace;
+  Scalars *sc = (Scalars *)(ws + p.off_scal);
+  const int64_t esz = dtype == FLCE_BF16 ? 2 : 4;
+  const int64_t half = B * T;                        // rows of each half of X
+  char *xbuf = ws + L.off_x, *dxbuf = ws + L.off_dx;
+  int64_t *lab = (int64_t *)(ws + L.off_lab);
+  float *rl = (float *)(ws + p.off_rowloss), *lp = (float *)(ws + L.off_lp);
+  float *wrow = (float *)(ws + L.off_w);
+  float *nll_sum = (float *)(ws + L.off_nll), *or_term = (float *)(ws + L.off_or);
+  float *clp = chosen_logp ? chosen_logp : (float *)(ws + L.off_clp);
+  float *rlp = rejected_logp ? rejected_logp : (float *)(ws + L.off_rlp);
+  float *lor = log_odds_ratio ? log_odds_ratio : (float *)(ws + L.off_lor);
+
+  LAUNCH(FLCE_K_ORPO, launch_orpo_labels(labels, 2 * half, half, V, ii, sc, s));
+  st = pack_weight(p, ws, W, bwd, s);
+  if (st != FLCE_OK) return st;
+  for (int64_t p0 = 0; p0 < B; p0 += L.k) {
+    const int64_t kk = std::min(L.k, B - p0);
+    const int64_t rows = kk * T;                     // rows of each half in this chunk
+    const int64_t rb = rows * H * esz;
+    const char *xc = (const char *)X + p0 * T * H * esz;
+    const char *xr = (const char *)X + (half + p0 * T) * H * esz;
+    LAUNCH(FLCE_K_ROWS, launch_copy_bytes(xbuf, xc, rb, s));
+    LAUNCH(FLCE_K_ROWS, launch_copy_bytes(xbuf + rb, xr, rb, s));
+    LAUNCH(FLCE_K_ROWS, launch_copy_bytes(lab, labels + p0 * T, rows * 8, s));
+    LAUNCH(FLCE_K_ROWS, launch_copy_bytes(lab + rows, labels + half + p0 * T, rows * 8, s));
+    ChunkIO io;
+    io.Xc = xbuf;
+    io.lab = lab;
+    io.c = (int)(2 * rows);
+    io.rl = rl;
+    io.lp = lp;
+    io.wr = bwd ? wrow : nullptr;
+    io.acc_dw = p0 > 0;
+    io.dXc = dxbuf;
+    st = chunk_forward(p, ws, W, ii, bwd, io, s);
+    if (st != FLCE_OK) return st;
+    LAUNCH(FLCE_K_ORPO, launch_orpo_pairs(lp, rl, lab, ii, T, (int)kk, p0, B, beta, sc,
+                                          bwd ? wrow : nullptr, nll_sum, or_term, clp, rlp, lor,
+                                          s));
+    if (bwd) {
+      st = chunk_backward(p, ws, W, ii, io, dW, sc, s);
+      if (st != FLCE_OK) return st;
+      LAUNCH(FLCE_K_ROWS, launch_copy_bytes((char *)dX + p0 * T * H * esz, dxbuf, rb, s));
+      LAUNCH(FLCE_K_ROWS,
+             launch_copy_bytes((char *)dX + (half + p0 * T) * H * esz, dxbuf + rb, rb, s));
+    }
+  }
+  LAUNCH(FLCE_K_ORPO, launch_orpo_final(nll_sum, or_term, B, beta, sc, s));
+  Scalars host;
+  CK(hipMemcpyAsync(&host, sc, sizeof(host), hipMemcpyDeviceToHost, s));
+  CK(hipStreamSynchronize(s));
+  if (host.flag) return FLCE_ELABEL;
+  *loss = host.loss;
+  if (nll) *nll = host.aux;
+  return FLCE_OK;
+}
+
+}  // namespace
+}  // namespace flce
+
+FLCE_API size_t flce_orpo_workspace_bytes(int64_t n_pairs, int64_t T, int64_t H, int64_t V,
+                                          int dtype, int64_t chunk_pairs) {
+  if (flce::orpo_check(n_pairs, T, H, V, dtype) != FLCE_OK) return 0;
+  flce::OrpoLayout L;
+  flce::orpo_layout(n_pairs, T, H, V, dtype, chunk_pairs, &L);
+  return L.total;
+}
+
+FLCE_API int flce_orpo_fwd_bwd(const void *X, const void *W, const int64_t *labels,
+                               int64_t n_pairs, int64_t T, int64_t H, int64_t V, int dtype,
+                               int64_t ignore_index, float beta, int64_t chunk_pairs, float *loss,
+                               float *nll, void *dX, float *dW, float *chosen_logp,
+                               float *rejected_logp, float *log_odds_ratio, void *workspace,
+                               size_t workspace_bytes, void *stream) {
+  return flce::run_orpo(true, X, W, labels, n_pairs, T, H, V, dtype, ignore_index, beta,
+                        chunk_pairs, loss, nll, dX, dW, chosen_logp, rejected_logp,
+                        log_odds_ratio, workspace, workspace_bytes, stream);
+}
+
+FLCE_API int flce_orpo_fwd(const void *X, const void *W, const int64_t *labels, int64_t n_pairs,
+                           int64_t T, int64_t H, int64_t V, int dtype, int64_t ignore_index,
+                           float beta, int64_t chunk_pairs, float *loss, float *nll,
+                           float *chosen_logp, float *rejected_logp, float *log_odds_ratio,
+                           void *workspace, size_t workspace_bytes, void *stream) {
+  return flce::run_orpo(false, X, W, labels, n_pairs, T, H, V, dtype, ignore_index, beta,
+                        chunk_pairs, loss, nll, nullptr, nullptr, chosen_logp, rejected_logp,
+                        log_odds_ratio, workspace, workspace_bytes, stream);
+}
+
 FLCE_API int flce_scale_inplace(void *buf, int64_t n, int dtype, const float *scale,
                                 void *stream) {
   if (dtype != FLCE_F32 && dtype != FLCE_BF16) return FLCE_EINVAL;
@@ -508,7 +722,8 @@ FLCE_API int flce_profile_read(double *ms, int64_t *launches, int n) {
 FLCE_API const char *flce_kernel_name(int k) {
   static const char *names[FLCE_K_COUNT] = {"label_check", "fwd_tile", "lse_combine", "dlogits",
                                             "dx_gemm", "dx_reduce", "dw_gemm", "final",
-                                            "pack_x", "pack_w", "ce_rows"};
+                                            "pack_x", "pack_w", "ce_rows", "orpo",
+                                            "orpo_rows"};
   return (k >= 0 && k < FLCE_K_COUNT) ? names[k] : "";
 }
 

@@ -23,6 +23,7 @@ struct Scalars {
   int nvalid;        // number of non-ignored labels
   float inv_nvalid;  // 1 / max(nvalid, 1)
   float scale;       // weight of a valid token's loss: 1 / max(nvalid, 1) for the mean, else 1
+  float aux;         // a second result of the call (the preference loss: its NLL term)
 };
 
 // Reductions of the per-token losses (values of flce_reduction).
@@ -95,6 +96,25 @@ hipError_t launch_dw_bf16(const uint16_t *Gp, int64_t nks_z, const uint16_t *Xp,
 hipError_t launch_ce_rows(void *logits, int64_t N, int64_t V, int dtype, const int64_t *labels,
                           int64_t ii, bool grad, const float *wrow, const Scalars *sc,
                           float *row_loss, float *row_lse, float *logprob, hipStream_t s);
+
+// ---------------------------------------------------------------- odds-ratio preference loss
+// Label pass: N_c = scored tokens among rows < n_chosen_rows, label flag.
+hipError_t launch_orpo_labels(const int64_t *labels, int64_t N, int64_t n_chosen_rows, int64_t V,
+                              int64_t ii, Scalars *sc, hipStream_t s);
+// Device copy of a whole number of 4-byte words.
+hipError_t launch_copy_bytes(void *dst, const void *src, int64_t bytes, hipStream_t s);
+// Per pair of a chunk of k pairs (chosen rows first, then rejected, T rows
+// each): sequence log-probabilities, log odds ratio, the pair's NLL sum and
+// odds-ratio term at pair p0 + j, and (wrow not null) the per-row weights
+// w = -dL/dlogp of the backward.
+hipError_t launch_orpo_pairs(const float *lp, const float *rl, const int64_t *labels_c, int64_t ii,
+                             int64_t T, int k, int64_t p0, int64_t n_pairs, float beta,
+                             const Scalars *sc, float *wrow, float *nll_sum, float *or_term,
+                             float *chosen_logp, float *rejected_logp, float *log_odds_ratio,
+                             hipStream_t s);
+// sc->loss = NLL + beta * mean odds-ratio term, sc->aux = NLL.
+hipError_t launch_orpo_final(const float *nll_sum, const float *or_term, int64_t n_pairs,
+                             float beta, Scalars *sc, hipStream_t s);
 
 // ---------------------------------------------------------------- fp32 path (SIMT)
 hipError_t launch_fwd_tile_f32(const float *W, const float *Xc, const int64_t *labels_c,

@@ -1,0 +1,221 @@
+// Odds-ratio preference loss (ORPO) on the fused projection: the per-pair
+// step between a chunk's forward and its backward.  The project overview
+// page lists this loss among the fused-linear post-training kernels ("Kernels
+// de Pós-Treinamento") and calls it as orpo_loss(lm_head.weight, x, target)
+// ("Exemplo de Uso de Perda de Pós-Treinamento"); the pages give no formula,
+// so it follows the published definition (Hong, Lee and Thorne, 2024):
+//   a_s   = mean log-probability of sequence s over its scored tokens
+//   d     = log odds(a_chosen) - log odds(a_rejected),  log odds(a) = a - log(1 - e^a)
+//   L     = L_SFT + beta * mean over pairs of -log sigmoid(d)
+//   L_SFT = mean over the chosen sequences' scored tokens of -log p(y_t)
+// Its gradient reaches the logits through the per-token log-probabilities
+// only, so the backward is the fused one with the per-token weight
+//   w_t = -dL / d log p(y_t)
+// and every GEMM of the chunk pipeline is reused unchanged.
+#include "flce_internal.h"
+
+namespace flce {
+namespace {
+
+constexpr int kPairThreads = 256;
+
+// One workgroup: N_c = scored tokens of the chosen half (rows < n_chosen_rows)
+// and the flag for a label that is neither ignore_index nor in [0, V).
+__global__ __launch_bounds__(1024) void orpo_labels_kernel(const int64_t *__restrict__ labels,
+                                                           int64_t N, int64_t n_chosen_rows,
+                                                           int64_t V, int64_t ii,
+                                                           Scalars *__restrict__ sc) {
+  __shared__ int s_cnt[16], s_bad[16];
+  int cnt = 0, bad = 0;
+  for (int64_t i = threadIdx.x; i < N; i += 1024) {
+    const int64_t y = labels[i];
+    if (y != ii) {
+      cnt += i < n_chosen_rows ? 1 : 0;
+      bad |= (y < 0 || y >= V) ? 1 : 0;
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    cnt += __shfl_xor(cnt, o);
+    bad |= __shfl_xor(bad, o);
+  }
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    s_cnt[w] = cnt;
+    s_bad[w] = bad;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int c = 0, b = 0;
+    for (int q = 0; q < 16; ++q) {
+      c += s_cnt[q];
+      b |= s_bad[q];
+    }
+    sc->nvalid = c;
+    sc->inv_nvalid = 1.0f / (float)(c > 0 ? c : 1);
+    sc->scale = sc->inv_nvalid;
+    sc->flag = b;
+    sc->loss = 0.f;
+    sc->aux = 0.f;
+  }
+}
+
+// dst[i] = src[i] for n 4-byte words, 16 bytes per thread where possible.
+__global__ __launch_bounds__(256) void copy_words_kernel(uint32_t *__restrict__ dst,
+                                                         const uint32_t *__restrict__ src,
+                                                         int64_t n, int vec) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (vec) {
+    const int64_t n4 = n >> 2;
+    for (int64_t j = i; j < n4; j += stride) ((uint4 *)dst)[j] = ((const uint4 *)src)[j];
+    for (int64_t j = (n4 << 2) + i; j < n; j += stride) dst[j] = src[j];
+  } else {
+    for (int64_t j = i; j < n; j += stride) dst[j] = src[j];
+  }
+}
+
+// Sum over a workgroup of kPairThreads; every thread gets the total.
+__device__ __forceinline__ float block_sum(float v, float *red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float t = 0.f;
+#pragma unroll
+  for (int q = 0; q < kPairThreads / 64; ++q) t += red[q];
+  return t;
+}
+
+// One workgroup per pair j of a chunk of k pairs: the chosen sequence is
+// chunk rows j T .. j T + T - 1, the rejected one rows k T + j T ...; lp and
+// rl are the rows' log-probabilities and losses (0 on unscored rows).
+__global__ __launch_bounds__(kPairThreads) void orpo_pairs_kernel(
+    const float *__restrict__ lp, const float *__restrict__ rl,
+    const int64_t *__restrict__ labels_c, int64_t ii, int64_t T, int k, int64_t p0,
+    int64_t n_pairs, float beta, const Scalars *__restrict__ sc, float *__restrict__ wrow,
+    float *__restrict__ nll_sum, float *__restrict__ or_term, float *__restrict__ chosen_logp,
+    float *__restrict__ rejected_logp, float *__restrict__ log_odds_ratio) {
+  __shared__ float red[kPairThreads / 64];
+  const int j = blockIdx.x;
+  const int64_t rc = (int64_t)j * T, rr = (int64_t)k * T + rc;
+  float sc_lp = 0.f, sc_n = 0.f, sc_rl = 0.f, sr_lp = 0.f, sr_n = 0.f;
+  for (int64_t t = threadIdx.x; t < T; t += kPairThreads) {
+    if (labels_c[rc + t] != ii) {
+      sc_lp += lp[rc + t];
+      sc_rl += rl[rc + t];
+      sc_n += 1.f;
+    }
+    if (labels_c[rr + t] != ii) {
+      sr_lp += lp[rr + t];
+      sr_n += 1.f;
+    }
+  }
+  sc_lp = block_sum(sc_lp, red);
+  sc_rl = block_sum(sc_rl, red);
+  sc_n = block_sum(sc_n, red);
+  sr_lp = block_sum(sr_lp, red);
+  sr_n = block_sum(sr_n, red);
+
+  const bool live = sc_n > 0.f && sr_n > 0.f;
+  const float ac = sc_n > 0.f ? sc_lp / sc_n : 0.f;
+  const float ar = sr_n > 0.f ? sr_lp / sr_n : 0.f;
+  float d = 0.f, orl = 0.f, gc = 0.f, gr = 0.f;
+  if (live) {
+    const float omc = -expm1f(ac), omr = -expm1f(ar);           // 1 - p
+    d = (ac - logf(omc)) - (ar - logf(omr));
+    orl = fmaxf(-d, 0.f) + log1pf(expf(-fabsf(d)));              // -log sigmoid(d)
+    const float sg = 1.f / (1.f + expf(d));                      // sigmoid(-d)
+    const float f = beta / (float)n_pairs * sg;
+    gc = -f / omc / sc_n;                                        // dL / d lp, chosen token
+    gr = f / omr / sr_n;                                         // dL / d lp, rejected token
+  }
+  if (threadIdx.x == 0) {
+    nll_sum[p0 + j] = sc_rl;
+    or_term[p0 + j] = orl;
+    if (chosen_logp) chosen_logp[p0 + j] = ac;
+    if (rejected_logp) rejected_logp[p0 + j] = ar;
+    if (log_odds_ratio) log_odds_ratio[p0 + j] = d;
+  }
+  if (wrow) {
+    const float wc = sc->inv_nvalid - gc, wr = -gr;              // w = -dL/d lp
+    for (int64_t t = threadIdx.x; t < T; t += kPairThreads) {
+      wrow[rc + t] = labels_c[rc + t] != ii ? wc : 0.f;
+      wrow[rr + t] = labels_c[rr + t] != ii ? wr : 0.f;
+    }
+  }
+}
+
+// loss = (sum of the chosen tokens' losses) / N_c + beta * mean_i L_OR,i;
+// aux = the first term.  One workgroup; fixed summation order.
+__global__ __launch_bounds__(256) void orpo_final_kernel(const float *__restrict__ nll_sum,
+                                                         const float *__restrict__ or_term,
+                                                         int64_t n_pairs, float beta,
+                                                         Scalars *__restrict__ sc) {
+  __shared__ float red[4];
+  float a = 0.f, b = 0.f;
+  for (int64_t i = threadIdx.x; i < n_pairs; i += 256) {
+    a += nll_sum[i];
+    b += or_term[i];
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    a += __shfl_xor(a, o);
+    b += __shfl_xor(b, o);
+  }
+  __shared__ float red2[4];
+  if ((threadIdx.x & 63) == 0) {
+    red[threadIdx.x >> 6] = a;
+    red2[threadIdx.x >> 6] = b;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const float nll = (red[0] + red[1] + red[2] + red[3]) * sc->inv_nvalid;
+    const float orl = (red2[0] + red2[1] + red2[2] + red2[3]) / (float)n_pairs;
+    sc->aux = nll;
+    sc->loss = nll + beta * orl;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_orpo_labels(const int64_t *labels, int64_t N, int64_t n_chosen_rows, int64_t V,
+                              int64_t ii, Scalars *sc, hipStream_t s) {
+  hipLaunchKernelGGL(orpo_labels_kernel, dim3(1), dim3(1024), 0, s, labels, N, n_chosen_rows, V,
+                     ii, sc);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_bytes(void *dst, const void *src, int64_t bytes, hipStream_t s) {
+  if (bytes <= 0) return hipSuccess;
+  const int64_t n = bytes / 4;                 // every caller copies whole 4-byte words
+  const int vec = ((uintptr_t)dst % 16 == 0 && (uintptr_t)src % 16 == 0) ? 1 : 0;
+  int64_t g = ((vec ? (n + 3) / 4 : n) + 255) / 256;
+  if (g > 256 * 16) g = 256 * 16;
+  if (g < 1) g = 1;
+  hipLaunchKernelGGL(copy_words_kernel, dim3((unsigned)g), dim3(256), 0, s, (uint32_t *)dst,
+                     (const uint32_t *)src, n, vec);
+  return hipGetLastError();
+}
+
+hipError_t launch_orpo_pairs(const float *lp, const float *rl, const int64_t *labels_c, int64_t ii,
+                             int64_t T, int k, int64_t p0, int64_t n_pairs, float beta,
+                             const Scalars *sc, float *wrow, float *nll_sum, float *or_term,
+                             float *chosen_logp, float *rejected_logp, float *log_odds_ratio,
+                             hipStream_t s) {
+  if (k <= 0) return hipSuccess;
+  hipLaunchKernelGGL(orpo_pairs_kernel, dim3((unsigned)k), dim3(kPairThreads), 0, s, lp, rl,
+                     labels_c, ii, T, k, p0, n_pairs, beta, sc, wrow, nll_sum, or_term,
+                     chosen_logp, rejected_logp, log_odds_ratio);
+  return hipGetLastError();
+}
+
+hipError_t launch_orpo_final(const float *nll_sum, const float *or_term, int64_t n_pairs,
+                             float beta, Scalars *sc, hipStream_t s) {
+  hipLaunchKernelGGL(orpo_final_kernel, dim3(1), dim3(256), 0, s, nll_sum, or_term, n_pairs, beta,
+                     sc);
+  return hipGetLastError();
+}
+
+}  // namespace flce

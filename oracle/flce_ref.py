@@ -383,6 +383,28 @@ def orpo_token_weights(a_c, n_c, a_r, n_r, d, live, valid, n_pairs: int, n_chose
     return np.where(v, -dlp, 0.0).reshape(-1)
 
 
+def orpo_terms(lp: np.ndarray, valid: np.ndarray, n_pairs: int, beta: float):
+    """From the per-token log-probabilities (sequence-major, 0 on unscored
+    tokens): loss, NLL, L_OR, a_chosen, a_rejected, d and the per-token
+    weights of the backward."""
+    a, n = sequence_logp(lp, valid, 2 * n_pairs)
+    a_c, a_r, n_c, n_r = a[:n_pairs], a[n_pairs:], n[:n_pairs], n[n_pairs:]
+    live = (n_c > 0) & (n_r > 0)
+    d = np.where(live, log_odds(np.where(live, a_c, -1.0)) - log_odds(np.where(live, a_r, -1.0)),
+                 0.0)
+    half = lp.size // 2
+    n_chosen_valid = int(valid[:half].sum())
+    nll = float(-lp[:half].sum() / max(n_chosen_valid, 1))
+    or_loss = float(odds_ratio_loss(d, live).sum() / n_pairs)
+    w = orpo_token_weights(a_c, n_c, a_r, n_r, d, live, valid, n_pairs, n_chosen_valid, beta)
+    return nll + beta * or_loss, nll, or_loss, a_c, a_r, d, w
+
+
+def _orpo_shape(N: int, n_pairs: int):
+    if n_pairs <= 0 or N % (2 * n_pairs) != 0:
+        raise ValueError("X must hold 2 * n_pairs sequences of equal length")
+
+
 def orpo(X, W, labels, n_pairs: int, ignore_index: int = IGNORE_INDEX, beta: float = 0.1,
          grads: bool = True) -> ORPOResult:
     """ORPO loss of 2 * n_pairs sequences (rows of X sequence-major, chosen
@@ -390,26 +412,35 @@ def orpo(X, W, labels, n_pairs: int, ignore_index: int = IGNORE_INDEX, beta: flo
     X = np.asarray(X, dtype=np.float64)
     W = np.asarray(W, dtype=np.float64)
     labels = np.asarray(labels, dtype=np.int64)
-    N, V = X.shape[0], W.shape[0]
-    if n_pairs <= 0 or N % (2 * n_pairs) != 0:
-        raise ValueError("X must hold 2 * n_pairs sequences of equal length")
-    valid = valid_mask(labels, V, ignore_index)
+    _orpo_shape(X.shape[0], n_pairs)
+    valid = valid_mask(labels, W.shape[0], ignore_index)
     Z = logits(X, W)
     lse = row_logsumexp(Z)
-    zy = target_logit(Z, labels, valid)
-    lp = log_probs(lse, zy, valid)
-    a, n = sequence_logp(lp, valid, 2 * n_pairs)
-    a_c, a_r, n_c, n_r = a[:n_pairs], a[n_pairs:], n[:n_pairs], n[n_pairs:]
-    live = (n_c > 0) & (n_r > 0)
-    d = np.where(live, log_odds(np.where(live, a_c, -1.0)) - log_odds(np.where(live, a_r, -1.0)),
-                 0.0)
-    half = N // 2
-    n_chosen_valid = int(valid[:half].sum())
-    nll = float(-lp[:half].sum() / max(n_chosen_valid, 1))
-    or_loss = float(odds_ratio_loss(d, live).sum() / n_pairs)
-    loss = nll + beta * or_loss
+    lp = log_probs(lse, target_logit(Z, labels, valid), valid)
+    loss, nll, or_loss, a_c, a_r, d, w = orpo_terms(lp, valid, n_pairs, beta)
     if not grads:
         return ORPOResult(loss, nll, or_loss, a_c, a_r, d, None, None)
-    w = orpo_token_weights(a_c, n_c, a_r, n_r, d, live, valid, n_pairs, n_chosen_valid, beta)
     G = dlogits_weighted(Z, lse, labels, w)
     return ORPOResult(loss, nll, or_loss, a_c, a_r, d, grad_input(G, W), grad_weight(G, X))
+
+
+def orpo_rows(X, W, labels, n_pairs: int, rows, vrows, ignore_index: int = IGNORE_INDEX,
+              beta: float = 0.1, block: int = 256) -> ORPOResult:
+    """The same loss for workloads whose logits do not fit in host memory:
+    every token's log-probability from complete logits rows in blocks, and
+    dX only for ``rows``, dW only for vocabulary rows ``vrows``."""
+    labels = np.asarray(labels, dtype=np.int64)
+    Wd = np.asarray(W, dtype=np.float64)
+    _orpo_shape(X.shape[0], n_pairs)
+    valid = valid_mask(labels, Wd.shape[0], ignore_index)
+    lse, rl, _ = forward_rows(X, Wd, labels, None, ignore_index, block)
+    lp = np.where(valid, -rl, 0.0)
+    loss, nll, or_loss, a_c, a_r, d, w = orpo_terms(lp, valid, n_pairs, beta)
+    rows = np.asarray(rows, dtype=np.int64)
+    Z = logits(np.asarray(X[rows], dtype=np.float64), Wd)
+    dX = grad_input(dlogits_weighted(Z, row_logsumexp(Z), labels[rows], w[rows]), Wd)
+    vrows = np.asarray(vrows, dtype=np.int64)
+    Xd = np.asarray(X, dtype=np.float64)
+    Zc = logits(Xd, Wd[vrows])
+    dW = grad_weight(dlogits_weighted(Zc, lse, labels, w, col_ids=vrows), Xd)
+    return ORPOResult(loss, nll, or_loss, a_c, a_r, d, dX, dW)

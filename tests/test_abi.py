@@ -92,6 +92,35 @@ def test_fwd_validation(lib):
     assert st == fl.FLCE_EINVAL
 
 
+def _orpo(lib, X=FAKE, W=FAKE, labels=FAKE, B=2, T=8, H=64, V=100, dt=fl.FLCE_BF16,
+          chunk_pairs=1, loss=True, dX=FAKE, dW=FAKE, ws=FAKE, ws_bytes=1 << 40):
+    lv = ctypes.c_float(0)
+    return lib.flce_orpo_fwd_bwd(X, W, labels, B, T, H, V, dt, -100, 0.1, chunk_pairs,
+                                 ctypes.byref(lv) if loss else None, None, dX, dW, None, None,
+                                 None, ws, ws_bytes, None)
+
+
+def test_orpo_validation(lib):
+    assert _orpo(lib, B=0) == fl.FLCE_EINVAL
+    assert _orpo(lib, T=0) == fl.FLCE_EINVAL
+    assert _orpo(lib, dt=5) == fl.FLCE_EINVAL
+    assert _orpo(lib, loss=False) == fl.FLCE_EINVAL
+    assert _orpo(lib, X=None) == fl.FLCE_EINVAL
+    assert _orpo(lib, dX=None) == fl.FLCE_EINVAL
+    assert _orpo(lib, ws=FAKE_ODD) == fl.FLCE_EINVAL
+    assert _orpo(lib, H=12) == fl.FLCE_EUNSUPPORTED              # bf16 needs H % 8 == 0
+    assert _orpo(lib, X=FAKE_ODD) == fl.FLCE_EUNSUPPORTED
+    need = fl.flce_orpo_workspace_bytes(2, 8, 64, 100, fl.FLCE_BF16, 1)
+    assert need > 0
+    assert _orpo(lib, ws_bytes=need - 1) == fl.FLCE_EWORKSPACE
+    assert fl.flce_orpo_workspace_bytes(0, 8, 64, 100, fl.FLCE_BF16, 1) == 0
+    # a chunk holds whole pairs: more pairs per chunk, more scratch; auto stops at 4096 rows
+    sizes = [fl.flce_orpo_workspace_bytes(8, 512, 4096, 128256, fl.FLCE_BF16, k)
+             for k in (1, 2, 4)]
+    assert sizes[0] < sizes[1] < sizes[2]
+    assert fl.flce_orpo_workspace_bytes(8, 512, 4096, 128256, fl.FLCE_BF16, 0) == sizes[2]
+
+
 def test_scale_validation(lib):
     assert lib.flce_scale_inplace(FAKE, 10, 5, FAKE, None) == fl.FLCE_EINVAL
     assert lib.flce_scale_inplace(FAKE, -1, 0, FAKE, None) == fl.FLCE_EINVAL

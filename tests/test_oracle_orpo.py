@@ -167,6 +167,17 @@ def test_pin_orpo(pin):
     pin(oracle.orpo)
 
 
+def test_rows_form_matches_whole():
+    B, T = 3, 6
+    X, W, y = _batch(B, T, 5, 17, 8, prompt=2)
+    r = oracle.orpo(X, W, y, B, II, beta=0.4)
+    rows, vrows = np.array([0, 5, 17, 30]), np.array([1, 8, 16])
+    q = oracle.orpo_rows(X, W, y, B, rows, vrows, II, beta=0.4, block=7)
+    assert abs(q.loss - r.loss) <= 1e-13 * abs(r.loss) and abs(q.nll - r.nll) <= 1e-13 * r.nll
+    assert _rel(q.log_odds_ratio, r.log_odds_ratio) <= 1e-12
+    assert _rel(q.dX, r.dX[rows]) <= 1e-12 and _rel(q.dW, r.dW[vrows]) <= 1e-12
+
+
 def test_layout_checked():
     X, W, y = _batch(2, 4, 3, 5, 7)
     with pytest.raises(ValueError):
