@@ -60,6 +60,8 @@ def kernel_work(name, chunks, H, V):
         return "hbm", sum(4.0 * c * H for c in chunks), "byte"
     if name == "pack_w":                       # W read once, written packed twice
         return "hbm", 6.0 * V * H, "byte"
+    if name == "orpo_rows":                    # X rows gathered, dX rows scattered (bf16)
+        return "hbm", sum(8.0 * c * H for c in chunks), "byte"
     return "hbm", None, "byte"
 
 
@@ -108,6 +110,40 @@ def cpu_baseline(inp, n_tok):
 
 
 CE_N, CE_V = 8192, 128256     # the Llama-3-8B head's logits: 8 x 1024 tokens x vocabulary
+
+
+def kernel_summary(prof, steps, chunks, H, V, workload):
+    """Per-kernel-class times of the timed steps and the roofline of the
+    class with the largest share of the step."""
+    kernels = {}
+    for name, (tot, n) in prof.items():
+        if n == 0:
+            continue
+        steps_n = n / steps
+        avg = tot / n
+        bound, amount, unit = kernel_work(name, chunks, H, V)
+        k = {"avg_ms": round(avg, 5), "launches_per_step": steps_n,
+             "ms_per_step": round(tot / steps, 4)}
+        if amount is not None:
+            per_launch = amount / steps_n
+            if unit == "flop":
+                k["tflops"] = round(per_launch / (avg * 1e-3) / 1e12, 2)
+            else:
+                k["gbps"] = round(per_launch / (avg * 1e-3) / 1e9, 1)
+        kernels[name] = k
+    dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
+    bound, amount, unit = kernel_work(dom, chunks, H, V)
+    if amount is not None and unit == "flop":
+        ach = kernels[dom]["tflops"]
+        roof = {"kernel": dom, "bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                "traffic": counter_traffic(dom, workload)}
+    else:
+        ach = kernels[dom].get("gbps")
+        roof = {"kernel": dom, "bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4) if ach else None,
+                "traffic": counter_traffic(dom, workload)}
+    return kernels, roof
 
 
 def copy_reference(mib, dev):
@@ -192,6 +228,90 @@ def bench_ce(args):
     print(json.dumps(out), flush=True)
 
 
+ORPO_PAIRS, ORPO_T = 8, 512   # 8 pairs of 512-token sequences: 8192 rows on the Llama-3-8B head
+
+
+def bench_orpo(args):
+    """ORPO loss on the Llama-3-8B head: 8 preference pairs of 512-token
+    sequences (8192 rows, H = 4096, V = 128256, bf16), one pair (1024 rows)
+    per chunk; one step is one flce_orpo_fwd_bwd.  FLOPs 6 N H V as for the
+    fused loss (the same three GEMMs over every row)."""
+    import numpy as np
+    import torch
+    import datagen
+    import linear_cross_entropy_04_amd as fl
+
+    dev = torch.device("cuda:0")
+    B, T, H, V = ORPO_PAIRS, ORPO_T, 4096, 128256
+    chunk_pairs = 1
+    t0 = time.time()
+    inp = datagen.make_pairs(B, T, H, V, "bf16", seed=20280)
+    log(f"preference batch {B} pairs x {T} tokens drawn in {time.time() - t0:.1f}s")
+    N = 2 * B * T
+    X = torch.from_numpy(inp.X.view(np.int16)).to(dev).view(torch.bfloat16)
+    W = torch.from_numpy(inp.W.view(np.int16)).to(dev).view(torch.bfloat16)
+    y = torch.from_numpy(inp.labels).to(dev)
+    dX = torch.empty_like(X)
+    dW = torch.empty((V, H), dtype=torch.float32, device=dev)
+    nbytes = fl.flce_orpo_workspace_bytes(B, T, H, V, fl.FLCE_BF16, chunk_pairs)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    if args.copy_reference_mib:
+        copy_reference(args.copy_reference_mib, dev)
+
+    def step():
+        return fl.flce_orpo_fwd_bwd(X, W, y, B, -100, 0.1, chunk_pairs, dX, dW, ws, stream=stream)
+
+    for _ in range(args.warmup):
+        loss, nll = step()
+    torch.cuda.synchronize()
+    fl.flce_profile_enable(True)
+    fl.flce_profile_read()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for _ in range(args.steps):
+        loss, nll = step()
+    torch.cuda.synchronize()
+    ms = 1e3 * (time.perf_counter() - t1) / args.steps
+    prof = fl.flce_profile_read()
+    fl.flce_profile_enable(False)
+    tflops = 6.0 * N * H * V / (ms * 1e-3) / 1e12
+    chunks = [2 * chunk_pairs * T] * (B // chunk_pairs)
+    kernels, roof = kernel_summary(prof, args.steps, chunks, H, V, "llama3-8b-head-orpo")
+    out = {
+        "metric": "ORPO fused-linear preference loss fwd+bwd tokens/s, Llama-3-8B head",
+        "value": round(N / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded; X ~ N(0,1), W ~ N(0,0.02^2); per pair a shared prompt of "
+                "T/8..T/2 unscored tokens, per sequence 0..T/4 unscored padding tokens, "
+                "uniform response labels)",
+        "config": {"workload": "llama3-8b-head-orpo", "pairs": B, "T": T, "N": N, "H": H, "V": V,
+                   "chunk_pairs": chunk_pairs, "beta": 0.1, "workspace_bytes": nbytes},
+        "tflops": round(tflops, 2), "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        "loss": loss, "nll": nll, "kernels": kernels, "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        n_pairs = 4                                  # the first four pairs: 4096 rows
+        rows = np.concatenate([np.arange(0, n_pairs * T), np.arange(B * T, (B + n_pairs) * T)])
+        X64, W64 = inp.X_f64()[rows], inp.W_f64()
+        t2 = time.perf_counter()
+        oracle.orpo(X64, W64, inp.labels[rows], n_pairs, -100, 0.1)
+        dt = time.perf_counter() - t2
+        out["cpu_baseline"] = {"value": rows.size / dt, "unit": "tokens/s",
+                               "cores": _blas_threads(), "kind": "oracle",
+                               "seconds": round(dt, 3),
+                               "sample": f"the first {n_pairs} pairs ({rows.size} rows), fp64 "
+                                         "loss + dX + dW on the host"}
+    else:
+        out["cpu_baseline"] = None
+    log(f"orpo: {ms:.3f} ms/step  {tflops:.1f} TFLOP/s  loss={loss:.6f} nll={nll:.6f}")
+    for name, k in kernels.items():
+        log(f"  {name:12s} {k}")
+    print(json.dumps(out), flush=True)
+
+
 def _blas_threads():
     try:
         from threadpoolctl import threadpool_info
@@ -210,9 +330,10 @@ def main():
     ap.add_argument("--chunk", type=int, default=None, help="chunk tokens (default: the workload's)")
     ap.add_argument("--cpu-sample-tokens", type=int, default=4096)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--op", choices=("flce", "ce"), default="flce",
+    ap.add_argument("--op", choices=("flce", "ce", "orpo"), default="flce",
                     help="flce: the fused linear cross-entropy step (default); ce: cross-entropy "
-                         "on given logits of the Llama-3-8B head's size")
+                         "on given logits of the Llama-3-8B head's size; orpo: the fused-linear "
+                         "ORPO loss on 8 pairs of 512-token sequences on the same head")
     ap.add_argument("--copy-reference-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (a known-size "
                          "reference for hardware byte counters)")
@@ -225,6 +346,9 @@ def main():
 
     if args.op == "ce":
         bench_ce(args)
+        return
+    if args.op == "orpo":
+        bench_orpo(args)
         return
 
     import numpy as np
@@ -291,34 +415,7 @@ def main():
     tflops = flops / (ms * 1e-3) / 1e12
     chunks = [min(C, N - c0) for c0 in range(0, N, C)]
 
-    kernels = {}
-    for name, (tot, n) in prof.items():
-        if n == 0:
-            continue
-        steps_n = n / args.steps
-        avg = tot / n
-        bound, amount, unit = kernel_work(name, chunks, H, V)
-        k = {"avg_ms": round(avg, 5), "launches_per_step": steps_n,
-             "ms_per_step": round(tot / args.steps, 4)}
-        if amount is not None:
-            per_launch = amount / steps_n
-            if unit == "flop":
-                k["tflops"] = round(per_launch / (avg * 1e-3) / 1e12, 2)
-            else:
-                k["gbps"] = round(per_launch / (avg * 1e-3) / 1e9, 1)
-        kernels[name] = k
-    dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
-    bound, amount, unit = kernel_work(dom, chunks, H, V)
-    if amount is not None and unit == "flop":
-        ach = kernels[dom]["tflops"]
-        roof = {"kernel": dom, "bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
-                "traffic": counter_traffic(dom, wl.name)}
-    else:
-        ach = kernels[dom].get("gbps")
-        roof = {"kernel": dom, "bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4) if ach else None,
-                "traffic": counter_traffic(dom, wl.name)}
+    kernels, roof = kernel_summary(prof, args.steps, chunks, H, V, wl.name)
 
     out = {
         "metric": METRIC,

@@ -614,10 +614,11 @@ int run_orpo(bool bwd, const void *X, const void *W, const int64_t *labels, int6
     const int64_t rb = rows * H * esz;
     const char *xc = (const char *)X + p0 * T * H * esz;
     const char *xr = (const char *)X + (half + p0 * T) * H * esz;
-    LAUNCH(FLCE_K_ROWS, launch_copy_bytes(xbuf, xc, rb, s));
-    LAUNCH(FLCE_K_ROWS, launch_copy_bytes(xbuf + rb, xr, rb, s));
-    LAUNCH(FLCE_K_ROWS, launch_copy_bytes(lab, labels + p0 * T, rows * 8, s));
-    LAUNCH(FLCE_K_ROWS, launch_copy_bytes(lab + rows, labels + half + p0 * T, rows * 8, s));
+    const CopySeg gather[4] = {{xbuf, xc, rb},
+                               {xbuf + rb, xr, rb},
+                               {lab, labels + p0 * T, rows * 8},
+                               {lab + rows, labels + half + p0 * T, rows * 8}};
+    LAUNCH(FLCE_K_ROWS, launch_copy_segments(gather, 4, s));
     ChunkIO io;
     io.Xc = xbuf;
     io.lab = lab;
@@ -635,9 +636,9 @@ int run_orpo(bool bwd, const void *X, const void *W, const int64_t *labels, int6
     if (bwd) {
       st = chunk_backward(p, ws, W, ii, io, dW, sc, s);
       if (st != FLCE_OK) return st;
-      LAUNCH(FLCE_K_ROWS, launch_copy_bytes((char *)dX + p0 * T * H * esz, dxbuf, rb, s));
-      LAUNCH(FLCE_K_ROWS,
-             launch_copy_bytes((char *)dX + (half + p0 * T) * H * esz, dxbuf + rb, rb, s));
+      const CopySeg scatter[2] = {{(char *)dX + p0 * T * H * esz, dxbuf, rb},
+                                  {(char *)dX + (half + p0 * T) * H * esz, dxbuf + rb, rb}};
+      LAUNCH(FLCE_K_ROWS, launch_copy_segments(scatter, 2, s));
     }
   }
   LAUNCH(FLCE_K_ORPO, launch_orpo_final(nll_sum, or_term, B, beta, sc, s));

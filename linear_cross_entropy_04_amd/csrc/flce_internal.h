@@ -101,8 +101,13 @@ hipError_t launch_ce_rows(void *logits, int64_t N, int64_t V, int dtype, const i
 // Label pass: N_c = scored tokens among rows < n_chosen_rows, label flag.
 hipError_t launch_orpo_labels(const int64_t *labels, int64_t N, int64_t n_chosen_rows, int64_t V,
                               int64_t ii, Scalars *sc, hipStream_t s);
-// Device copy of a whole number of 4-byte words.
-hipError_t launch_copy_bytes(void *dst, const void *src, int64_t bytes, hipStream_t s);
+// Up to 4 device copies of whole numbers of 4-byte words, in one launch.
+struct CopySeg {
+  void *dst;
+  const void *src;
+  int64_t bytes;
+};
+hipError_t launch_copy_segments(const CopySeg *segs, int nseg, hipStream_t s);
 // Per pair of a chunk of k pairs (chosen rows first, then rejected, T rows
 // each): sequence log-probabilities, log odds ratio, the pair's NLL sum and
 // odds-ratio term at pair p0 + j, and (wrow not null) the per-row weights

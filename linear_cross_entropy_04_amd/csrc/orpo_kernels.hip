@@ -18,6 +18,7 @@ namespace flce {
 namespace {
 
 constexpr int kPairThreads = 256;
+constexpr int kMaxSegs = 4;
 
 // One workgroup: N_c = scored tokens of the chosen half (rows < n_chosen_rows)
 // and the flag for a label that is neither ignore_index nor in [0, V).
@@ -60,13 +61,24 @@ __global__ __launch_bounds__(1024) void orpo_labels_kernel(const int64_t *__rest
   }
 }
 
-// dst[i] = src[i] for n 4-byte words, 16 bytes per thread where possible.
-__global__ __launch_bounds__(256) void copy_words_kernel(uint32_t *__restrict__ dst,
-                                                         const uint32_t *__restrict__ src,
-                                                         int64_t n, int vec) {
+// Up to kMaxSegs independent copies in one launch: blockIdx.y picks the
+// segment; dst[i] = src[i] for its n 4-byte words, 16 bytes per thread where
+// both ends are 16-byte aligned.
+struct CopySegs {
+  uint32_t *dst[kMaxSegs];
+  const uint32_t *src[kMaxSegs];
+  int64_t n[kMaxSegs];
+  int vec[kMaxSegs];
+};
+
+__global__ __launch_bounds__(256) void copy_segments_kernel(CopySegs segs) {
+  const int q = blockIdx.y;
+  uint32_t *__restrict__ dst = segs.dst[q];
+  const uint32_t *__restrict__ src = segs.src[q];
+  const int64_t n = segs.n[q];
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-  if (vec) {
+  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (segs.vec[q]) {
     const int64_t n4 = n >> 2;
     for (int64_t j = i; j < n4; j += stride) ((uint4 *)dst)[j] = ((const uint4 *)src)[j];
     for (int64_t j = (n4 << 2) + i; j < n; j += stride) dst[j] = src[j];
@@ -187,15 +199,22 @@ hipError_t launch_orpo_labels(const int64_t *labels, int64_t N, int64_t n_chosen
   return hipGetLastError();
 }
 
-hipError_t launch_copy_bytes(void *dst, const void *src, int64_t bytes, hipStream_t s) {
-  if (bytes <= 0) return hipSuccess;
-  const int64_t n = bytes / 4;                 // every caller copies whole 4-byte words
-  const int vec = ((uintptr_t)dst % 16 == 0 && (uintptr_t)src % 16 == 0) ? 1 : 0;
-  int64_t g = ((vec ? (n + 3) / 4 : n) + 255) / 256;
-  if (g > 256 * 16) g = 256 * 16;
-  if (g < 1) g = 1;
-  hipLaunchKernelGGL(copy_words_kernel, dim3((unsigned)g), dim3(256), 0, s, (uint32_t *)dst,
-                     (const uint32_t *)src, n, vec);
+hipError_t launch_copy_segments(const CopySeg *segs, int nseg, hipStream_t s) {
+  if (nseg <= 0 || nseg > kMaxSegs) return hipErrorInvalidValue;
+  CopySegs a = {};
+  int64_t most = 0;
+  for (int q = 0; q < nseg; ++q) {
+    a.dst[q] = (uint32_t *)segs[q].dst;
+    a.src[q] = (const uint32_t *)segs[q].src;
+    a.n[q] = segs[q].bytes / 4;                  // every caller copies whole 4-byte words
+    a.vec[q] = ((uintptr_t)segs[q].dst % 16 == 0 && (uintptr_t)segs[q].src % 16 == 0) ? 1 : 0;
+    const int64_t work = a.vec[q] ? (a.n[q] + 3) / 4 : a.n[q];
+    most = work > most ? work : most;
+  }
+  if (most == 0) return hipSuccess;
+  int64_t g = (most + 255) / 256;
+  if (g > 2048) g = 2048;
+  hipLaunchKernelGGL(copy_segments_kernel, dim3((unsigned)g, (unsigned)nseg), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
