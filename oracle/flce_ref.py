@@ -444,3 +444,117 @@ def orpo_rows(X, W, labels, n_pairs: int, rows, vrows, ignore_index: int = IGNOR
     Zc = logits(Xd, Wd[vrows])
     dW = grad_weight(dlogits_weighted(Zc, lse, labels, w, col_ids=vrows), Xd)
     return ORPOResult(loss, nll, or_loss, a_c, a_r, d, dX, dW)
+
+
+# ------------------------------------------------------------------ other pairwise preference losses
+# The same page lists DPO, CPO and SimPO beside ORPO ("Kernels de
+# Pós-Treinamento"), again without formulas.  Each is its published pairwise
+# form on the same batch layout: with S_s = sum and a_s = S_s / n_s = mean of
+# log p(y_t) over sequence s's scored tokens,
+#   SimPO (Meng, Xia and Chen, 2024):      z = beta (a_c - a_r) - gamma
+#   CPO   (Xu et al., 2024):               z = beta (S_c - S_r)
+#   DPO   (Rafailov et al., 2023):         z = beta ((S_c - R_c) - (S_r - R_r)),
+#         R_s the reference model's sequence log-probability (an input)
+#   L = alpha NLL + mean over pairs of -log sigmoid(z_i)
+# with NLL the token-level mean of -log p over the chosen half, as for ORPO.
+# ORPO is the same shape with z = log odds(a_c) - log odds(a_r), alpha = 1
+# and beta weighting the pair term.  A pair with an empty sequence adds
+# nothing to the pair term.
+
+PAIR_KINDS = ("orpo", "simpo", "cpo", "dpo")
+
+
+@dataclasses.dataclass
+class PreferenceResult:
+    loss: float
+    nll: float                   # token-level mean of -log p over the chosen half
+    pair_loss: float             # mean over pairs of -log sigmoid(z_i)
+    chosen_logp: np.ndarray      # [B] the sequence log-probability the loss uses (a or S)
+    rejected_logp: np.ndarray    # [B]
+    pair_logit: np.ndarray       # [B] z_i (0 for pairs with an empty sequence)
+    dX: np.ndarray | None
+    dW: np.ndarray | None
+
+
+def sequence_sums(lp: np.ndarray, valid: np.ndarray, n_seq: int):
+    """Sum of log p over each sequence's scored tokens, and their number."""
+    lp = lp.reshape(n_seq, -1)
+    valid = valid.reshape(n_seq, -1)
+    return np.where(valid, lp, 0.0).sum(axis=1), valid.sum(axis=1)
+
+
+def pair_logit(kind: str, S_c, n_c, S_r, n_r, beta: float, gamma: float, ref_c, ref_r):
+    """z_i and its derivatives dz/dS_c, dz/dS_r (live pairs: n_c, n_r > 0)."""
+    nc, nr = np.maximum(n_c, 1), np.maximum(n_r, 1)
+    if kind == "simpo":
+        return beta * (S_c / nc - S_r / nr) - gamma, beta / nc, -beta / nr
+    if kind == "cpo":
+        return beta * (S_c - S_r), np.full(S_c.shape, beta), np.full(S_c.shape, -beta)
+    if kind == "dpo":
+        return (beta * ((S_c - ref_c) - (S_r - ref_r)), np.full(S_c.shape, beta),
+                np.full(S_c.shape, -beta))
+    if kind == "orpo":
+        a_c, a_r = np.minimum(S_c / nc, -1e-300), np.minimum(S_r / nr, -1e-300)
+        return (log_odds(a_c) - log_odds(a_r), 1.0 / (-np.expm1(a_c)) / nc,
+                -1.0 / (-np.expm1(a_r)) / nr)
+    raise ValueError(f"unknown preference loss {kind!r}")
+
+
+def preference_token_weights(dz_c, dz_r, z, live, valid, n_pairs: int, n_chosen_valid: int,
+                             alpha: float, lam: float) -> np.ndarray:
+    """w_t = -dL/d log p(y_t): dL/dz_i = -lam sigmoid(-z_i) / B, reaching each
+    token of the pair's sequences through dz/dS; the NLL adds -alpha / N_c on
+    chosen scored tokens."""
+    g = np.where(live, -lam / n_pairs / (1.0 + np.exp(z)), 0.0)      # dL/dz
+    T = valid.size // (2 * n_pairs)
+    v = valid.reshape(2 * n_pairs, T)
+    dlp = np.zeros((2 * n_pairs, T))
+    dlp[:n_pairs] = -alpha / max(n_chosen_valid, 1) + (g * dz_c)[:, None]
+    dlp[n_pairs:] = (g * dz_r)[:, None]
+    return np.where(v, -dlp, 0.0).reshape(-1)
+
+
+def preference_terms(kind: str, lp, valid, n_pairs: int, beta: float, gamma: float,
+                     alpha: float, ref_c=None, ref_r=None):
+    """Loss, NLL, pair loss, sequence scores, z and the backward's per-token
+    weights from the per-token log-probabilities."""
+    S, n = sequence_sums(lp, valid, 2 * n_pairs)
+    S_c, S_r, n_c, n_r = S[:n_pairs], S[n_pairs:], n[:n_pairs], n[n_pairs:]
+    live = (n_c > 0) & (n_r > 0)
+    if kind == "dpo" and (ref_c is None or ref_r is None):
+        raise ValueError("DPO needs the reference sequence log-probabilities")
+    ref_c = np.zeros(n_pairs) if ref_c is None else np.asarray(ref_c, dtype=np.float64)
+    ref_r = np.zeros(n_pairs) if ref_r is None else np.asarray(ref_r, dtype=np.float64)
+    z, dz_c, dz_r = pair_logit(kind, S_c, n_c, S_r, n_r, beta, gamma, ref_c, ref_r)
+    z = np.where(live, z, 0.0)
+    lam = beta if kind == "orpo" else 1.0
+    half = lp.size // 2
+    n_chosen_valid = int(valid[:half].sum())
+    nll = float(-lp[:half].sum() / max(n_chosen_valid, 1))
+    pair_loss = float(np.where(live, np.logaddexp(0.0, -z), 0.0).sum() / n_pairs)
+    w = preference_token_weights(dz_c, dz_r, z, live, valid, n_pairs, n_chosen_valid, alpha, lam)
+    mean_based = kind in ("orpo", "simpo")
+    u_c = np.where(n_c > 0, S_c / np.maximum(n_c, 1), 0.0) if mean_based else S_c
+    u_r = np.where(n_r > 0, S_r / np.maximum(n_r, 1), 0.0) if mean_based else S_r
+    return alpha * nll + lam * pair_loss, nll, pair_loss, u_c, u_r, z, w
+
+
+def preference(kind: str, X, W, labels, n_pairs: int, ignore_index: int = IGNORE_INDEX,
+               beta: float = 0.1, gamma: float = 0.0, alpha: float = 0.0, ref_chosen=None,
+               ref_rejected=None, grads: bool = True) -> PreferenceResult:
+    """A pairwise preference loss of 2 * n_pairs sequences (rows of X
+    sequence-major, chosen first) and its gradients."""
+    X = np.asarray(X, dtype=np.float64)
+    W = np.asarray(W, dtype=np.float64)
+    labels = np.asarray(labels, dtype=np.int64)
+    _orpo_shape(X.shape[0], n_pairs)
+    valid = valid_mask(labels, W.shape[0], ignore_index)
+    Z = logits(X, W)
+    lse = row_logsumexp(Z)
+    lp = log_probs(lse, target_logit(Z, labels, valid), valid)
+    loss, nll, pl, u_c, u_r, z, w = preference_terms(kind, lp, valid, n_pairs, beta, gamma, alpha,
+                                                     ref_chosen, ref_rejected)
+    if not grads:
+        return PreferenceResult(loss, nll, pl, u_c, u_r, z, None, None)
+    G = dlogits_weighted(Z, lse, labels, w)
+    return PreferenceResult(loss, nll, pl, u_c, u_r, z, grad_input(G, W), grad_weight(G, X))
