@@ -60,7 +60,7 @@ def kernel_work(name, chunks, H, V):
         return "hbm", sum(4.0 * c * H for c in chunks), "byte"
     if name == "pack_w":                       # W read once, written packed twice
         return "hbm", 6.0 * V * H, "byte"
-    if name == "orpo_rows":                    # X rows gathered, dX rows scattered (bf16)
+    if name == "pair_rows":                    # X rows gathered, dX rows scattered (bf16)
         return "hbm", sum(8.0 * c * H for c in chunks), "byte"
     return "hbm", None, "byte"
 

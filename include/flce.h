@@ -234,6 +234,43 @@ int flce_orpo_fwd(const void *X, const void *W, const int64_t *labels, int64_t n
                   size_t workspace_bytes, void *stream);
 
 /*
+ * The other pairwise preference losses of the same list (project overview
+ * page, "Kernels de Pós-Treinamento"), each in its published form, on the
+ * batch layout, chunking and outputs of flce_orpo_fwd_bwd.  With S = sum and
+ * a = S / n = mean of log p(y_t) over a sequence's n scored tokens:
+ *   FLCE_PAIR_ORPO   z = log odds(a_c) - log odds(a_r)            (lambda = beta)
+ *   FLCE_PAIR_SIMPO  z = beta (a_c - a_r) - gamma                 (Meng, Xia and Chen, 2024)
+ *   FLCE_PAIR_CPO    z = beta (S_c - S_r)                         (Xu et al., 2024)
+ *   FLCE_PAIR_DPO    z = beta ((S_c - R_c) - (S_r - R_r))         (Rafailov et al., 2023)
+ *   loss = alpha NLL + lambda (1 / n_pairs) sum_i -log sigmoid(z_i),  lambda = 1 unless ORPO
+ * R_c, R_r: device [n_pairs] fp32, the reference model's sequence log-probability sums
+ * (required for DPO, ignored otherwise).  chosen_logp / rejected_logp receive the
+ * sequence log-probability the loss uses (a for ORPO and SimPO, S for CPO and DPO),
+ * pair_logit receives z.  An unknown kind is FLCE_EINVAL.
+ */
+typedef enum {
+  FLCE_PAIR_ORPO = 0,
+  FLCE_PAIR_SIMPO = 1,
+  FLCE_PAIR_CPO = 2,
+  FLCE_PAIR_DPO = 3
+} flce_pair_loss;
+size_t flce_pair_workspace_bytes(int64_t n_pairs, int64_t T, int64_t H, int64_t V, int dtype,
+                                 int64_t chunk_pairs);
+int flce_pair_fwd_bwd(int kind, const void *X, const void *W, const int64_t *labels,
+                      int64_t n_pairs, int64_t T, int64_t H, int64_t V, int dtype,
+                      int64_t ignore_index, float beta, float gamma, float alpha,
+                      const float *ref_chosen_logp, const float *ref_rejected_logp,
+                      int64_t chunk_pairs, float *loss, float *nll, void *dX, float *dW,
+                      float *chosen_logp, float *rejected_logp, float *pair_logit,
+                      void *workspace, size_t workspace_bytes, void *stream);
+int flce_pair_fwd(int kind, const void *X, const void *W, const int64_t *labels, int64_t n_pairs,
+                  int64_t T, int64_t H, int64_t V, int dtype, int64_t ignore_index, float beta,
+                  float gamma, float alpha, const float *ref_chosen_logp,
+                  const float *ref_rejected_logp, int64_t chunk_pairs, float *loss, float *nll,
+                  float *chosen_logp, float *rejected_logp, float *pair_logit, void *workspace,
+                  size_t workspace_bytes, void *stream);
+
+/*
  * buf[i] *= *scale for i < n, in place, on the stream (no sync).  buf is a
  * device array of dtype (FLCE_F32 or FLCE_BF16); scale is a device fp32
  * scalar.  Used to apply an upstream gradient d(out)/d(loss) != 1 to dX, dW.
@@ -260,8 +297,8 @@ enum {
   FLCE_K_PACK = 8,        /* per-chunk packing of X into the GEMM operand layout */
   FLCE_K_PACK_W = 9,      /* per-call packing of W (as is and transposed) */
   FLCE_K_CE_ROWS = 10,    /* cross-entropy on given logits, one workgroup per row */
-  FLCE_K_ORPO = 11,       /* preference loss: label pass, per-pair step, final loss */
-  FLCE_K_ROWS = 12,       /* preference loss: gathering a chunk's rows, scattering dX */
+  FLCE_K_PAIRS = 11,      /* preference losses: label pass, per-pair step, final loss */
+  FLCE_K_PAIR_ROWS = 12,  /* preference losses: gathering a chunk's rows, scattering dX */
   FLCE_K_COUNT = 13
 };
 int flce_profile_enable(int enable);

@@ -24,7 +24,9 @@ __all__ = [
     "workspace", "loss", "FusedLinearCrossEntropyLoss",
     "flce_ce_workspace_bytes", "flce_ce_fwd_bwd", "flce_ce_fwd", "cross_entropy",
     "flce_orpo_workspace_bytes", "flce_orpo_fwd_bwd", "flce_orpo_fwd", "orpo_loss",
-    "FusedLinearORPOLoss",
+    "FusedLinearORPOLoss", "PAIR_KINDS", "flce_pair_workspace_bytes", "flce_pair_fwd_bwd",
+    "flce_pair_fwd", "preference_loss", "sequence_logps", "FusedLinearSimPOLoss",
+    "FusedLinearCPOLoss", "FusedLinearDPOLoss",
 ]
 
 FLCE_F32 = 0
@@ -96,6 +98,17 @@ def _load():
                                 _i64, ctypes.POINTER(ctypes.c_float),
                                 ctypes.POINTER(ctypes.c_float), _p, _p, _p, _p, _sz, _p]
     l.flce_orpo_fwd.restype = _i32
+    l.flce_pair_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64, _i32, _i64]
+    l.flce_pair_workspace_bytes.restype = _sz
+    _f = ctypes.c_float
+    l.flce_pair_fwd_bwd.argtypes = [_i32, _p, _p, _p, _i64, _i64, _i64, _i64, _i32, _i64, _f, _f,
+                                    _f, _p, _p, _i64, ctypes.POINTER(_f), ctypes.POINTER(_f), _p,
+                                    _p, _p, _p, _p, _p, _sz, _p]
+    l.flce_pair_fwd_bwd.restype = _i32
+    l.flce_pair_fwd.argtypes = [_i32, _p, _p, _p, _i64, _i64, _i64, _i64, _i32, _i64, _f, _f, _f,
+                                _p, _p, _i64, ctypes.POINTER(_f), ctypes.POINTER(_f), _p, _p, _p,
+                                _p, _sz, _p]
+    l.flce_pair_fwd.restype = _i32
     l.flce_scale_inplace.argtypes = [_p, _i64, _i32, _p, _p]
     l.flce_scale_inplace.restype = _i32
     l.flce_status_string.argtypes = [_i32]
@@ -415,6 +428,73 @@ def flce_orpo_fwd(X: torch.Tensor, W: torch.Tensor, labels: torch.Tensor, n_pair
     return float(loss.value), float(nll.value)
 
 
+PAIR_KINDS = {"orpo": 0, "simpo": 1, "cpo": 2, "dpo": 3}          # flce_pair_loss
+
+
+def _pair_kind(kind: str) -> int:
+    if kind not in PAIR_KINDS:
+        raise ValueError(f"kind must be one of {tuple(PAIR_KINDS)}, got {kind!r}")
+    return PAIR_KINDS[kind]
+
+
+def flce_pair_workspace_bytes(n_pairs: int, T: int, H: int, V: int, dtype: int,
+                              chunk_pairs: int = 0) -> int:
+    return int(_load().flce_pair_workspace_bytes(n_pairs, T, H, V, dtype, chunk_pairs))
+
+
+def flce_pair_fwd_bwd(kind: str, X: torch.Tensor, W: torch.Tensor, labels: torch.Tensor,
+                      n_pairs: int, ignore_index: int, beta: float, gamma: float, alpha: float,
+                      chunk_pairs: int, dX: torch.Tensor, dW: torch.Tensor,
+                      workspace: torch.Tensor, ref_chosen_logp: torch.Tensor | None = None,
+                      ref_rejected_logp: torch.Tensor | None = None,
+                      chosen_logp: torch.Tensor | None = None,
+                      rejected_logp: torch.Tensor | None = None,
+                      pair_logit: torch.Tensor | None = None, stream=None) -> tuple[float, float]:
+    """Call libflce's flce_pair_fwd_bwd; returns (loss, nll)."""
+    T, H, V, dt = _orpo_args(X, W, labels, n_pairs, workspace, chosen_logp, rejected_logp,
+                             pair_logit)
+    _dev(dX, "dX", X.dtype, tuple(X.shape))
+    _dev(dW, "dW", torch.float32, (V, H))
+    _dev(ref_chosen_logp, "ref_chosen_logp", torch.float32, (n_pairs,))
+    _dev(ref_rejected_logp, "ref_rejected_logp", torch.float32, (n_pairs,))
+    loss, nll = ctypes.c_float(0.0), ctypes.c_float(0.0)
+    st = _load().flce_pair_fwd_bwd(_pair_kind(kind), _ptr(X), _ptr(W), _ptr(labels), n_pairs, T,
+                                   H, V, dt, ignore_index, float(beta), float(gamma),
+                                   float(alpha), _ptr(ref_chosen_logp), _ptr(ref_rejected_logp),
+                                   chunk_pairs, ctypes.byref(loss), ctypes.byref(nll), _ptr(dX),
+                                   _ptr(dW), _ptr(chosen_logp), _ptr(rejected_logp),
+                                   _ptr(pair_logit), _ptr(workspace), workspace.numel(),
+                                   _stream(stream, X.device))
+    if st != FLCE_OK:
+        raise FLCEError(st, "flce_pair_fwd_bwd")
+    return float(loss.value), float(nll.value)
+
+
+def flce_pair_fwd(kind: str, X: torch.Tensor, W: torch.Tensor, labels: torch.Tensor,
+                  n_pairs: int, ignore_index: int, beta: float, gamma: float, alpha: float,
+                  chunk_pairs: int, workspace: torch.Tensor,
+                  ref_chosen_logp: torch.Tensor | None = None,
+                  ref_rejected_logp: torch.Tensor | None = None,
+                  chosen_logp: torch.Tensor | None = None,
+                  rejected_logp: torch.Tensor | None = None,
+                  pair_logit: torch.Tensor | None = None, stream=None) -> tuple[float, float]:
+    """Call libflce's flce_pair_fwd; returns (loss, nll)."""
+    T, H, V, dt = _orpo_args(X, W, labels, n_pairs, workspace, chosen_logp, rejected_logp,
+                             pair_logit)
+    _dev(ref_chosen_logp, "ref_chosen_logp", torch.float32, (n_pairs,))
+    _dev(ref_rejected_logp, "ref_rejected_logp", torch.float32, (n_pairs,))
+    loss, nll = ctypes.c_float(0.0), ctypes.c_float(0.0)
+    st = _load().flce_pair_fwd(_pair_kind(kind), _ptr(X), _ptr(W), _ptr(labels), n_pairs, T, H, V,
+                               dt, ignore_index, float(beta), float(gamma), float(alpha),
+                               _ptr(ref_chosen_logp), _ptr(ref_rejected_logp), chunk_pairs,
+                               ctypes.byref(loss), ctypes.byref(nll), _ptr(chosen_logp),
+                               _ptr(rejected_logp), _ptr(pair_logit), _ptr(workspace),
+                               workspace.numel(), _stream(stream, X.device))
+    if st != FLCE_OK:
+        raise FLCEError(st, "flce_pair_fwd")
+    return float(loss.value), float(nll.value)
+
+
 def flce_scale_inplace(buf: torch.Tensor, scale: torch.Tensor, stream=None) -> None:
     """buf *= scale (a one-element fp32 device tensor), in place, on the stream."""
     _dev(buf, "buf")
@@ -622,3 +702,135 @@ class FusedLinearORPOLoss(torch.nn.Module):
 
     def forward(self, weight, input, target):
         return orpo_loss(weight, input, target, self.ignore_index, self.beta, self.chunk_pairs)
+
+
+class _PairFunction(torch.autograd.Function):
+    """A pairwise preference loss: gradients computed with the loss (one
+    call), scaled by the upstream gradient in backward."""
+
+    @staticmethod
+    def forward(ctx, weight, input, target, kind, n_pairs, ignore_index, beta, gamma, alpha,
+                ref_c, ref_r, chunk_pairs):
+        N, H = input.shape
+        V = weight.shape[0]
+        T = N // (2 * n_pairs) if n_pairs > 0 else 0
+        nbytes = flce_pair_workspace_bytes(n_pairs, T, H, V, _dtype_code(input), chunk_pairs)
+        if nbytes == 0:
+            raise FLCEError(FLCE_EINVAL, "flce_pair_workspace_bytes")
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=input.device)
+        if ctx.needs_input_grad[0] or ctx.needs_input_grad[1]:
+            dX = torch.empty_like(input)
+            dW = torch.empty((V, H), dtype=torch.float32, device=input.device)
+            val, _ = flce_pair_fwd_bwd(kind, input, weight, target, n_pairs, ignore_index, beta,
+                                       gamma, alpha, chunk_pairs, dX, dW, ws, ref_c, ref_r)
+            ctx.save_for_backward(dX, dW)
+        else:
+            val, _ = flce_pair_fwd(kind, input, weight, target, n_pairs, ignore_index, beta,
+                                   gamma, alpha, chunk_pairs, ws, ref_c, ref_r)
+        ctx.wdtype = weight.dtype
+        return torch.tensor(val, dtype=torch.float32, device=input.device)
+
+    @staticmethod
+    def backward(ctx, grad_out):
+        dX, dW = ctx.saved_tensors
+        g = grad_out.detach().to(torch.float32).reshape(1).contiguous()
+        flce_scale_inplace(dX, g)
+        flce_scale_inplace(dW, g)
+        gw = dW if ctx.wdtype == torch.float32 else dW.to(ctx.wdtype)
+        return gw, dX, None, None, None, None, None, None, None, None, None, None
+
+
+def _pair_rows(input, target):
+    if target.dim() != 2 or target.shape[0] % 2 != 0:
+        raise ValueError("target must be [2B, T] (chosen sequences first)")
+    x = input.reshape(-1, input.shape[-1])
+    if x.shape[0] != target.numel():
+        raise ValueError(f"input has {x.shape[0]} rows, target {target.numel()} tokens")
+    return x, target.reshape(-1).contiguous(), target.shape[0] // 2
+
+
+def preference_loss(kind: str, weight: torch.Tensor, input: torch.Tensor, target: torch.Tensor,
+                    beta: float, gamma: float = 0.0, alpha: float = 0.0,
+                    ref_chosen_logp: torch.Tensor | None = None,
+                    ref_rejected_logp: torch.Tensor | None = None, ignore_index: int = -100,
+                    chunk_pairs: int = 0) -> torch.Tensor:
+    """A pairwise preference loss ("orpo", "simpo", "cpo", "dpo") of the B
+    chosen sequences then the B rejected ones in input [2B, T, H] (or
+    [2B * T, H]), target [2B, T]; see flce_pair_fwd_bwd in include/flce.h."""
+    x, y, n_pairs = _pair_rows(input, target)
+    if kind == "orpo":
+        return _ORPOFunction.apply(weight, x, y, n_pairs, ignore_index, beta, chunk_pairs)
+    return _PairFunction.apply(weight, x, y, kind, n_pairs, ignore_index, beta, gamma, alpha,
+                               ref_chosen_logp, ref_rejected_logp, chunk_pairs)
+
+
+@torch.no_grad()
+def sequence_logps(weight: torch.Tensor, input: torch.Tensor, target: torch.Tensor,
+                   ignore_index: int = -100, chunk_pairs: int = 0):
+    """Sums of log p(y_t) over each chosen and each rejected sequence's scored
+    tokens (forward only), e.g. a reference model's for DPO: (chosen [B],
+    rejected [B]) fp32."""
+    x, y, n_pairs = _pair_rows(input, target)
+    N, H = x.shape
+    nbytes = flce_pair_workspace_bytes(n_pairs, N // (2 * n_pairs), H, weight.shape[0],
+                                       _dtype_code(x), chunk_pairs)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=x.device)
+    c = torch.empty(n_pairs, dtype=torch.float32, device=x.device)
+    r = torch.empty(n_pairs, dtype=torch.float32, device=x.device)
+    flce_pair_fwd("cpo", x.contiguous(), weight.contiguous(), y, n_pairs, ignore_index, 0.0, 0.0,
+                  0.0, chunk_pairs, ws, chosen_logp=c, rejected_logp=r)
+    return c, r
+
+
+class FusedLinearSimPOLoss(torch.nn.Module):
+    """SimPO: -log sigmoid(beta (a_c - a_r) - gamma) with a the mean token
+    log-probability, plus alpha times the chosen NLL."""
+
+    def __init__(self, beta: float = 2.0, gamma: float = 1.0, alpha: float = 0.0,
+                 ignore_index: int = -100, chunk_pairs: int = 0):
+        super().__init__()
+        self.beta, self.gamma, self.alpha = beta, gamma, alpha
+        self.ignore_index, self.chunk_pairs = ignore_index, chunk_pairs
+
+    def forward(self, weight, input, target):
+        return preference_loss("simpo", weight, input, target, self.beta, self.gamma, self.alpha,
+                               ignore_index=self.ignore_index, chunk_pairs=self.chunk_pairs)
+
+
+class FusedLinearCPOLoss(torch.nn.Module):
+    """CPO: -log sigmoid(beta (S_c - S_r)) with S the summed token
+    log-probability, plus alpha times the chosen NLL."""
+
+    def __init__(self, beta: float = 0.1, alpha: float = 1.0, ignore_index: int = -100,
+                 chunk_pairs: int = 0):
+        super().__init__()
+        self.beta, self.alpha = beta, alpha
+        self.ignore_index, self.chunk_pairs = ignore_index, chunk_pairs
+
+    def forward(self, weight, input, target):
+        return preference_loss("cpo", weight, input, target, self.beta, 0.0, self.alpha,
+                               ignore_index=self.ignore_index, chunk_pairs=self.chunk_pairs)
+
+
+class FusedLinearDPOLoss(torch.nn.Module):
+    """DPO: -log sigmoid(beta ((S_c - R_c) - (S_r - R_r))), R the reference
+    model's summed log-probabilities: given directly, or computed (forward
+    only) from ref_weight and ref_input (default: input)."""
+
+    def __init__(self, beta: float = 0.1, alpha: float = 0.0, ignore_index: int = -100,
+                 chunk_pairs: int = 0):
+        super().__init__()
+        self.beta, self.alpha = beta, alpha
+        self.ignore_index, self.chunk_pairs = ignore_index, chunk_pairs
+
+    def forward(self, weight, input, target, ref_weight=None, ref_input=None,
+                ref_chosen_logp=None, ref_rejected_logp=None):
+        if ref_chosen_logp is None or ref_rejected_logp is None:
+            if ref_weight is None:
+                raise ValueError("DPO needs ref_weight or the reference log-probabilities")
+            ref_chosen_logp, ref_rejected_logp = sequence_logps(
+                ref_weight.detach(), (input if ref_input is None else ref_input).detach(), target,
+                self.ignore_index, self.chunk_pairs)
+        return preference_loss("dpo", weight, input, target, self.beta, 0.0, self.alpha,
+                               ref_chosen_logp, ref_rejected_logp, self.ignore_index,
+                               self.chunk_pairs)

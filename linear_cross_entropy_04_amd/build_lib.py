@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libflce.so")
 SOURCES = ["flce_api.hip", "gemm_bf16.hip", "kernels_f32.hip", "kernels_common.hip",
-           "ce_kernels.hip", "orpo_kernels.hip"]
+           "ce_kernels.hip", "pair_kernels.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 instructions are disabled for the device code (the host pass

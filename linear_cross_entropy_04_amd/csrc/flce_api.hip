@@ -517,12 +517,12 @@ FLCE_API int flce_ce_fwd(const void *logits, const int64_t *labels, int64_t N, i
                       workspace_bytes, stream);
 }
 
-// ---------------------------------------------------------------- odds-ratio preference loss
+// ---------------------------------------------------------------- pairwise preference losses
 // A chunk holds k whole pairs: their chosen rows, then their rejected rows,
 // gathered from the two halves of X into one contiguous chunk, so the fused
 // pipeline runs on it unchanged.  Between its forward and its backward the
 // per-pair step turns the chunk's per-token log-probabilities into the loss
-// terms and the per-token weights of the backward (orpo_kernels.hip).
+// terms and the per-token weights of the backward (pair_kernels.hip).
 
 namespace flce {
 namespace {
@@ -569,13 +569,17 @@ void orpo_layout(int64_t B, int64_t T, int64_t H, int64_t V, int dtype, int64_t 
   L->total = o;
 }
 
-int run_orpo(bool bwd, const void *X, const void *W, const int64_t *labels, int64_t B, int64_t T,
-             int64_t H, int64_t V, int dtype, int64_t ii, float beta, int64_t chunk_pairs,
-             float *loss, float *nll, void *dX, float *dW, float *chosen_logp,
-             float *rejected_logp, float *log_odds_ratio, void *workspace,
-             size_t workspace_bytes, void *stream) {
+int run_pairs(bool bwd, int kind, const void *X, const void *W, const int64_t *labels, int64_t B,
+              int64_t T, int64_t H, int64_t V, int dtype, int64_t ii, const PairParams &pp,
+              int64_t chunk_pairs, float *loss, float *nll, void *dX, float *dW,
+              float *chosen_logp, float *rejected_logp, float *log_odds_ratio, void *workspace,
+              size_t workspace_bytes, void *stream) {
   int st = orpo_check(B, T, H, V, dtype);
   if (st != FLCE_OK) return st;
+  if (kind != kPairOrpo && kind != kPairSimpo && kind != kPairCpo && kind != kPairDpo)
+    return FLCE_EINVAL;
+  if (kind == kPairDpo && (!pp.ref_c || !pp.ref_r)) return FLCE_EINVAL;
+  if (misaligned(pp.ref_c, 4) || misaligned(pp.ref_r, 4)) return FLCE_EINVAL;
   if (!loss || !X || !W || !labels || !workspace) return FLCE_EINVAL;
   if (bwd && (!dX || !dW)) return FLCE_EINVAL;
   if (misaligned(workspace, 256) || misaligned(labels, 8) || misaligned(chosen_logp, 4) ||
@@ -605,7 +609,7 @@ int run_orpo(bool bwd, const void *X, const void *W, const int64_t *labels, int6
   float *rlp = rejected_logp ? rejected_logp : (float *)(ws + L.off_rlp);
   float *lor = log_odds_ratio ? log_odds_ratio : (float *)(ws + L.off_lor);
 
-  LAUNCH(FLCE_K_ORPO, launch_orpo_labels(labels, 2 * half, half, V, ii, sc, s));
+  LAUNCH(FLCE_K_PAIRS, launch_pairs_labels(labels, 2 * half, half, V, ii, sc, s));
   st = pack_weight(p, ws, W, bwd, s);
   if (st != FLCE_OK) return st;
   for (int64_t p0 = 0; p0 < B; p0 += L.k) {
@@ -618,7 +622,7 @@ int run_orpo(bool bwd, const void *X, const void *W, const int64_t *labels, int6
                                {xbuf + rb, xr, rb},
                                {lab, labels + p0 * T, rows * 8},
                                {lab + rows, labels + half + p0 * T, rows * 8}};
-    LAUNCH(FLCE_K_ROWS, launch_copy_segments(gather, 4, s));
+    LAUNCH(FLCE_K_PAIR_ROWS, launch_copy_segments(gather, 4, s));
     ChunkIO io;
     io.Xc = xbuf;
     io.lab = lab;
@@ -630,18 +634,17 @@ int run_orpo(bool bwd, const void *X, const void *W, const int64_t *labels, int6
     io.dXc = dxbuf;
     st = chunk_forward(p, ws, W, ii, bwd, io, s);
     if (st != FLCE_OK) return st;
-    LAUNCH(FLCE_K_ORPO, launch_orpo_pairs(lp, rl, lab, ii, T, (int)kk, p0, B, beta, sc,
-                                          bwd ? wrow : nullptr, nll_sum, or_term, clp, rlp, lor,
-                                          s));
+    LAUNCH(FLCE_K_PAIRS, launch_pairs(kind, lp, rl, lab, ii, T, (int)kk, p0, B, pp, sc,
+                                      bwd ? wrow : nullptr, nll_sum, or_term, clp, rlp, lor, s));
     if (bwd) {
       st = chunk_backward(p, ws, W, ii, io, dW, sc, s);
       if (st != FLCE_OK) return st;
       const CopySeg scatter[2] = {{(char *)dX + p0 * T * H * esz, dxbuf, rb},
                                   {(char *)dX + (half + p0 * T) * H * esz, dxbuf + rb, rb}};
-      LAUNCH(FLCE_K_ROWS, launch_copy_segments(scatter, 2, s));
+      LAUNCH(FLCE_K_PAIR_ROWS, launch_copy_segments(scatter, 2, s));
     }
   }
-  LAUNCH(FLCE_K_ORPO, launch_orpo_final(nll_sum, or_term, B, beta, sc, s));
+  LAUNCH(FLCE_K_PAIRS, launch_pairs_final(nll_sum, or_term, B, pp.alpha, pp.lambda, sc, s));
   Scalars host;
   CK(hipMemcpyAsync(&host, sc, sizeof(host), hipMemcpyDeviceToHost, s));
   CK(hipStreamSynchronize(s));
@@ -654,12 +657,71 @@ int run_orpo(bool bwd, const void *X, const void *W, const int64_t *labels, int6
 }  // namespace
 }  // namespace flce
 
-FLCE_API size_t flce_orpo_workspace_bytes(int64_t n_pairs, int64_t T, int64_t H, int64_t V,
+namespace flce {
+namespace {
+
+PairParams orpo_params(float beta) {
+  PairParams pp{};
+  pp.beta = beta;
+  pp.alpha = 1.f;
+  pp.lambda = beta;
+  return pp;
+}
+
+PairParams pair_params(int kind, float beta, float gamma, float alpha, const float *ref_c,
+                       const float *ref_r) {
+  PairParams pp{};
+  pp.beta = beta;
+  pp.gamma = gamma;
+  pp.alpha = alpha;
+  pp.lambda = kind == kPairOrpo ? beta : 1.f;
+  pp.ref_c = ref_c;
+  pp.ref_r = ref_r;
+  return pp;
+}
+
+}  // namespace
+}  // namespace flce
+
+FLCE_API size_t flce_pair_workspace_bytes(int64_t n_pairs, int64_t T, int64_t H, int64_t V,
                                           int dtype, int64_t chunk_pairs) {
   if (flce::orpo_check(n_pairs, T, H, V, dtype) != FLCE_OK) return 0;
   flce::OrpoLayout L;
   flce::orpo_layout(n_pairs, T, H, V, dtype, chunk_pairs, &L);
   return L.total;
+}
+
+FLCE_API size_t flce_orpo_workspace_bytes(int64_t n_pairs, int64_t T, int64_t H, int64_t V,
+                                          int dtype, int64_t chunk_pairs) {
+  return flce_pair_workspace_bytes(n_pairs, T, H, V, dtype, chunk_pairs);
+}
+
+FLCE_API int flce_pair_fwd_bwd(int kind, const void *X, const void *W, const int64_t *labels,
+                               int64_t n_pairs, int64_t T, int64_t H, int64_t V, int dtype,
+                               int64_t ignore_index, float beta, float gamma, float alpha,
+                               const float *ref_chosen_logp, const float *ref_rejected_logp,
+                               int64_t chunk_pairs, float *loss, float *nll, void *dX, float *dW,
+                               float *chosen_logp, float *rejected_logp, float *pair_logit,
+                               void *workspace, size_t workspace_bytes, void *stream) {
+  return flce::run_pairs(true, kind, X, W, labels, n_pairs, T, H, V, dtype, ignore_index,
+                         flce::pair_params(kind, beta, gamma, alpha, ref_chosen_logp,
+                                           ref_rejected_logp),
+                         chunk_pairs, loss, nll, dX, dW, chosen_logp, rejected_logp, pair_logit,
+                         workspace, workspace_bytes, stream);
+}
+
+FLCE_API int flce_pair_fwd(int kind, const void *X, const void *W, const int64_t *labels,
+                           int64_t n_pairs, int64_t T, int64_t H, int64_t V, int dtype,
+                           int64_t ignore_index, float beta, float gamma, float alpha,
+                           const float *ref_chosen_logp, const float *ref_rejected_logp,
+                           int64_t chunk_pairs, float *loss, float *nll, float *chosen_logp,
+                           float *rejected_logp, float *pair_logit, void *workspace,
+                           size_t workspace_bytes, void *stream) {
+  return flce::run_pairs(false, kind, X, W, labels, n_pairs, T, H, V, dtype, ignore_index,
+                         flce::pair_params(kind, beta, gamma, alpha, ref_chosen_logp,
+                                           ref_rejected_logp),
+                         chunk_pairs, loss, nll, nullptr, nullptr, chosen_logp, rejected_logp,
+                         pair_logit, workspace, workspace_bytes, stream);
 }
 
 FLCE_API int flce_orpo_fwd_bwd(const void *X, const void *W, const int64_t *labels,
@@ -668,9 +730,10 @@ FLCE_API int flce_orpo_fwd_bwd(const void *X, const void *W, const int64_t *labe
                                float *nll, void *dX, float *dW, float *chosen_logp,
                                float *rejected_logp, float *log_odds_ratio, void *workspace,
                                size_t workspace_bytes, void *stream) {
-  return flce::run_orpo(true, X, W, labels, n_pairs, T, H, V, dtype, ignore_index, beta,
-                        chunk_pairs, loss, nll, dX, dW, chosen_logp, rejected_logp,
-                        log_odds_ratio, workspace, workspace_bytes, stream);
+  return flce::run_pairs(true, flce::kPairOrpo, X, W, labels, n_pairs, T, H, V, dtype,
+                         ignore_index, flce::orpo_params(beta), chunk_pairs, loss, nll, dX, dW,
+                         chosen_logp, rejected_logp, log_odds_ratio, workspace, workspace_bytes,
+                         stream);
 }
 
 FLCE_API int flce_orpo_fwd(const void *X, const void *W, const int64_t *labels, int64_t n_pairs,
@@ -678,9 +741,10 @@ FLCE_API int flce_orpo_fwd(const void *X, const void *W, const int64_t *labels, 
                            float beta, int64_t chunk_pairs, float *loss, float *nll,
                            float *chosen_logp, float *rejected_logp, float *log_odds_ratio,
                            void *workspace, size_t workspace_bytes, void *stream) {
-  return flce::run_orpo(false, X, W, labels, n_pairs, T, H, V, dtype, ignore_index, beta,
-                        chunk_pairs, loss, nll, nullptr, nullptr, chosen_logp, rejected_logp,
-                        log_odds_ratio, workspace, workspace_bytes, stream);
+  return flce::run_pairs(false, flce::kPairOrpo, X, W, labels, n_pairs, T, H, V, dtype,
+                         ignore_index, flce::orpo_params(beta), chunk_pairs, loss, nll, nullptr,
+                         nullptr, chosen_logp, rejected_logp, log_odds_ratio, workspace,
+                         workspace_bytes, stream);
 }
 
 FLCE_API int flce_scale_inplace(void *buf, int64_t n, int dtype, const float *scale,
@@ -723,8 +787,8 @@ FLCE_API int flce_profile_read(double *ms, int64_t *launches, int n) {
 FLCE_API const char *flce_kernel_name(int k) {
   static const char *names[FLCE_K_COUNT] = {"label_check", "fwd_tile", "lse_combine", "dlogits",
                                             "dx_gemm", "dx_reduce", "dw_gemm", "final",
-                                            "pack_x", "pack_w", "ce_rows", "orpo",
-                                            "orpo_rows"};
+                                            "pack_x", "pack_w", "ce_rows", "pairs",
+                                            "pair_rows"};
   return (k >= 0 && k < FLCE_K_COUNT) ? names[k] : "";
 }
 

@@ -97,10 +97,16 @@ hipError_t launch_ce_rows(void *logits, int64_t N, int64_t V, int dtype, const i
                           int64_t ii, bool grad, const float *wrow, const Scalars *sc,
                           float *row_loss, float *row_lse, float *logprob, hipStream_t s);
 
-// ---------------------------------------------------------------- odds-ratio preference loss
+// ---------------------------------------------------------------- pairwise preference losses
+// Kinds (values of flce_pair_loss).
+constexpr int kPairOrpo = 0, kPairSimpo = 1, kPairCpo = 2, kPairDpo = 3;
+struct PairParams {
+  float beta, gamma, alpha, lambda;   // lambda: weight of the pair term (beta for ORPO, else 1)
+  const float *ref_c, *ref_r;         // DPO: the reference model's sequence log-probabilities
+};
 // Label pass: N_c = scored tokens among rows < n_chosen_rows, label flag.
-hipError_t launch_orpo_labels(const int64_t *labels, int64_t N, int64_t n_chosen_rows, int64_t V,
-                              int64_t ii, Scalars *sc, hipStream_t s);
+hipError_t launch_pairs_labels(const int64_t *labels, int64_t N, int64_t n_chosen_rows, int64_t V,
+                               int64_t ii, Scalars *sc, hipStream_t s);
 // Up to 4 device copies of whole numbers of 4-byte words, in one launch.
 struct CopySeg {
   void *dst;
@@ -109,17 +115,17 @@ struct CopySeg {
 };
 hipError_t launch_copy_segments(const CopySeg *segs, int nseg, hipStream_t s);
 // Per pair of a chunk of k pairs (chosen rows first, then rejected, T rows
-// each): sequence log-probabilities, log odds ratio, the pair's NLL sum and
-// odds-ratio term at pair p0 + j, and (wrow not null) the per-row weights
-// w = -dL/dlogp of the backward.
-hipError_t launch_orpo_pairs(const float *lp, const float *rl, const int64_t *labels_c, int64_t ii,
-                             int64_t T, int k, int64_t p0, int64_t n_pairs, float beta,
-                             const Scalars *sc, float *wrow, float *nll_sum, float *or_term,
-                             float *chosen_logp, float *rejected_logp, float *log_odds_ratio,
-                             hipStream_t s);
-// sc->loss = NLL + beta * mean odds-ratio term, sc->aux = NLL.
-hipError_t launch_orpo_final(const float *nll_sum, const float *or_term, int64_t n_pairs,
-                             float beta, Scalars *sc, hipStream_t s);
+// each): the sequence log-probabilities the loss uses, the pair logit z, the
+// pair's NLL sum and pair term at pair p0 + j, and (wrow not null) the
+// per-row weights w = -dL/dlogp of the backward.
+hipError_t launch_pairs(int kind, const float *lp, const float *rl, const int64_t *labels_c,
+                        int64_t ii, int64_t T, int k, int64_t p0, int64_t n_pairs,
+                        const PairParams &pp, const Scalars *sc, float *wrow, float *nll_sum,
+                        float *pair_term, float *chosen_logp, float *rejected_logp,
+                        float *pair_logit, hipStream_t s);
+// sc->loss = alpha NLL + lambda mean pair term, sc->aux = NLL.
+hipError_t launch_pairs_final(const float *nll_sum, const float *pair_term, int64_t n_pairs,
+                              float alpha, float lambda, Scalars *sc, hipStream_t s);
 
 // ---------------------------------------------------------------- fp32 path (SIMT)
 hipError_t launch_fwd_tile_f32(const float *W, const float *Xc, const int64_t *labels_c,

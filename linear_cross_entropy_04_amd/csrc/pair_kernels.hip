@@ -1,15 +1,22 @@
-// Odds-ratio preference loss (ORPO) on the fused projection: the per-pair
-// step between a chunk's forward and its backward.  The project overview
-// page lists this loss among the fused-linear post-training kernels ("Kernels
-// de Pós-Treinamento") and calls it as orpo_loss(lm_head.weight, x, target)
-// ("Exemplo de Uso de Perda de Pós-Treinamento"); the pages give no formula,
-// so it follows the published definition (Hong, Lee and Thorne, 2024):
-//   a_s   = mean log-probability of sequence s over its scored tokens
-//   d     = log odds(a_chosen) - log odds(a_rejected),  log odds(a) = a - log(1 - e^a)
-//   L     = L_SFT + beta * mean over pairs of -log sigmoid(d)
-//   L_SFT = mean over the chosen sequences' scored tokens of -log p(y_t)
-// Its gradient reaches the logits through the per-token log-probabilities
-// only, so the backward is the fused one with the per-token weight
+// Pairwise preference losses on the fused projection: the per-pair step
+// between a chunk's forward and its backward.  The project overview page
+// lists fused-linear post-training losses ("Kernels de Pós-Treinamento":
+// DPO, ORPO, CPO, SimPO, KTO) and calls the ORPO one as
+// orpo_loss(lm_head.weight, x, target) ("Exemplo de Uso de Perda de
+// Pós-Treinamento"); the pages give no formula, so each follows its published
+// pairwise form.  With S = sum and a = S / n = mean of log p(y_t) over a
+// sequence's n scored tokens (c: chosen, r: rejected):
+//   ORPO  (Hong, Lee and Thorne, 2024)  z = log odds(a_c) - log odds(a_r),
+//                                         log odds(a) = a - log(1 - e^a)
+//   SimPO (Meng, Xia and Chen, 2024)    z = beta (a_c - a_r) - gamma
+//   CPO   (Xu et al., 2024)             z = beta (S_c - S_r)
+//   DPO   (Rafailov et al., 2023)       z = beta ((S_c - R_c) - (S_r - R_r)),
+//                                         R the reference model's S (input)
+//   L = alpha NLL + lambda mean over pairs of -log sigmoid(z)
+// with NLL the mean of -log p over the chosen half's scored tokens, lambda =
+// beta for ORPO (its weight of the odds-ratio term) and 1 otherwise.  The
+// gradient reaches the logits through the per-token log-probabilities only,
+// so the backward is the fused one with the per-token weight
 //   w_t = -dL / d log p(y_t)
 // and every GEMM of the chunk pipeline is reused unchanged.
 #include "flce_internal.h"
@@ -22,7 +29,7 @@ constexpr int kMaxSegs = 4;
 
 // One workgroup: N_c = scored tokens of the chosen half (rows < n_chosen_rows)
 // and the flag for a label that is neither ignore_index nor in [0, V).
-__global__ __launch_bounds__(1024) void orpo_labels_kernel(const int64_t *__restrict__ labels,
+__global__ __launch_bounds__(1024) void pairs_labels_kernel(const int64_t *__restrict__ labels,
                                                            int64_t N, int64_t n_chosen_rows,
                                                            int64_t V, int64_t ii,
                                                            Scalars *__restrict__ sc) {
@@ -103,12 +110,12 @@ __device__ __forceinline__ float block_sum(float v, float *red) {
 // One workgroup per pair j of a chunk of k pairs: the chosen sequence is
 // chunk rows j T .. j T + T - 1, the rejected one rows k T + j T ...; lp and
 // rl are the rows' log-probabilities and losses (0 on unscored rows).
-__global__ __launch_bounds__(kPairThreads) void orpo_pairs_kernel(
-    const float *__restrict__ lp, const float *__restrict__ rl,
+__global__ __launch_bounds__(kPairThreads) void pairs_kernel(
+    int kind, const float *__restrict__ lp, const float *__restrict__ rl,
     const int64_t *__restrict__ labels_c, int64_t ii, int64_t T, int k, int64_t p0,
-    int64_t n_pairs, float beta, const Scalars *__restrict__ sc, float *__restrict__ wrow,
-    float *__restrict__ nll_sum, float *__restrict__ or_term, float *__restrict__ chosen_logp,
-    float *__restrict__ rejected_logp, float *__restrict__ log_odds_ratio) {
+    int64_t n_pairs, PairParams pp, const Scalars *__restrict__ sc, float *__restrict__ wrow,
+    float *__restrict__ nll_sum, float *__restrict__ pair_term, float *__restrict__ chosen_logp,
+    float *__restrict__ rejected_logp, float *__restrict__ pair_logit) {
   __shared__ float red[kPairThreads / 64];
   const int j = blockIdx.x;
   const int64_t rc = (int64_t)j * T, rr = (int64_t)k * T + rc;
@@ -133,25 +140,38 @@ __global__ __launch_bounds__(kPairThreads) void orpo_pairs_kernel(
   const bool live = sc_n > 0.f && sr_n > 0.f;
   const float ac = sc_n > 0.f ? sc_lp / sc_n : 0.f;
   const float ar = sr_n > 0.f ? sr_lp / sr_n : 0.f;
-  float d = 0.f, orl = 0.f, gc = 0.f, gr = 0.f;
+  const bool mean_based = kind == kPairOrpo || kind == kPairSimpo;
+  float z = 0.f, term = 0.f, dzc = 0.f, dzr = 0.f;
   if (live) {
-    const float omc = -expm1f(ac), omr = -expm1f(ar);           // 1 - p
-    d = (ac - logf(omc)) - (ar - logf(omr));
-    orl = fmaxf(-d, 0.f) + log1pf(expf(-fabsf(d)));              // -log sigmoid(d)
-    const float sg = 1.f / (1.f + expf(d));                      // sigmoid(-d)
-    const float f = beta / (float)n_pairs * sg;
-    gc = -f / omc / sc_n;                                        // dL / d lp, chosen token
-    gr = f / omr / sr_n;                                         // dL / d lp, rejected token
+    if (kind == kPairOrpo) {
+      const float omc = -expm1f(ac), omr = -expm1f(ar);         // 1 - p
+      z = (ac - logf(omc)) - (ar - logf(omr));
+      dzc = 1.f / omc / sc_n;
+      dzr = -1.f / omr / sr_n;
+    } else if (kind == kPairSimpo) {
+      z = pp.beta * (ac - ar) - pp.gamma;
+      dzc = pp.beta / sc_n;
+      dzr = -pp.beta / sr_n;
+    } else {
+      const float rc_ref = kind == kPairDpo ? pp.ref_c[p0 + j] : 0.f;
+      const float rr_ref = kind == kPairDpo ? pp.ref_r[p0 + j] : 0.f;
+      z = pp.beta * ((sc_lp - rc_ref) - (sr_lp - rr_ref));
+      dzc = pp.beta;
+      dzr = -pp.beta;
+    }
+    term = fmaxf(-z, 0.f) + log1pf(expf(-fabsf(z)));             // -log sigmoid(z)
   }
+  // dL/dz = -lambda sigmoid(-z) / n_pairs
+  const float g = live ? -pp.lambda / (float)n_pairs / (1.f + expf(z)) : 0.f;
   if (threadIdx.x == 0) {
     nll_sum[p0 + j] = sc_rl;
-    or_term[p0 + j] = orl;
-    if (chosen_logp) chosen_logp[p0 + j] = ac;
-    if (rejected_logp) rejected_logp[p0 + j] = ar;
-    if (log_odds_ratio) log_odds_ratio[p0 + j] = d;
+    pair_term[p0 + j] = term;
+    if (chosen_logp) chosen_logp[p0 + j] = mean_based ? ac : sc_lp;
+    if (rejected_logp) rejected_logp[p0 + j] = mean_based ? ar : sr_lp;
+    if (pair_logit) pair_logit[p0 + j] = z;
   }
   if (wrow) {
-    const float wc = sc->inv_nvalid - gc, wr = -gr;              // w = -dL/d lp
+    const float wc = pp.alpha * sc->inv_nvalid - g * dzc, wr = -g * dzr;   // w = -dL/d lp
     for (int64_t t = threadIdx.x; t < T; t += kPairThreads) {
       wrow[rc + t] = labels_c[rc + t] != ii ? wc : 0.f;
       wrow[rr + t] = labels_c[rr + t] != ii ? wr : 0.f;
@@ -159,12 +179,13 @@ __global__ __launch_bounds__(kPairThreads) void orpo_pairs_kernel(
   }
 }
 
-// loss = (sum of the chosen tokens' losses) / N_c + beta * mean_i L_OR,i;
-// aux = the first term.  One workgroup; fixed summation order.
-__global__ __launch_bounds__(256) void orpo_final_kernel(const float *__restrict__ nll_sum,
-                                                         const float *__restrict__ or_term,
-                                                         int64_t n_pairs, float beta,
-                                                         Scalars *__restrict__ sc) {
+// loss = alpha (sum of the chosen tokens' losses) / N_c + lambda mean_i of
+// the pair terms; aux = the NLL.  One workgroup; fixed summation order.
+__global__ __launch_bounds__(256) void pairs_final_kernel(const float *__restrict__ nll_sum,
+                                                          const float *__restrict__ or_term,
+                                                          int64_t n_pairs, float alpha,
+                                                          float lambda,
+                                                          Scalars *__restrict__ sc) {
   __shared__ float red[4];
   float a = 0.f, b = 0.f;
   for (int64_t i = threadIdx.x; i < n_pairs; i += 256) {
@@ -186,15 +207,15 @@ __global__ __launch_bounds__(256) void orpo_final_kernel(const float *__restrict
     const float nll = (red[0] + red[1] + red[2] + red[3]) * sc->inv_nvalid;
     const float orl = (red2[0] + red2[1] + red2[2] + red2[3]) / (float)n_pairs;
     sc->aux = nll;
-    sc->loss = nll + beta * orl;
+    sc->loss = alpha * nll + lambda * orl;
   }
 }
 
 }  // namespace
 
-hipError_t launch_orpo_labels(const int64_t *labels, int64_t N, int64_t n_chosen_rows, int64_t V,
+hipError_t launch_pairs_labels(const int64_t *labels, int64_t N, int64_t n_chosen_rows, int64_t V,
                               int64_t ii, Scalars *sc, hipStream_t s) {
-  hipLaunchKernelGGL(orpo_labels_kernel, dim3(1), dim3(1024), 0, s, labels, N, n_chosen_rows, V,
+  hipLaunchKernelGGL(pairs_labels_kernel, dim3(1), dim3(1024), 0, s, labels, N, n_chosen_rows, V,
                      ii, sc);
   return hipGetLastError();
 }
@@ -218,22 +239,22 @@ hipError_t launch_copy_segments(const CopySeg *segs, int nseg, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_orpo_pairs(const float *lp, const float *rl, const int64_t *labels_c, int64_t ii,
-                             int64_t T, int k, int64_t p0, int64_t n_pairs, float beta,
-                             const Scalars *sc, float *wrow, float *nll_sum, float *or_term,
-                             float *chosen_logp, float *rejected_logp, float *log_odds_ratio,
-                             hipStream_t s) {
+hipError_t launch_pairs(int kind, const float *lp, const float *rl, const int64_t *labels_c,
+                        int64_t ii, int64_t T, int k, int64_t p0, int64_t n_pairs,
+                        const PairParams &pp, const Scalars *sc, float *wrow, float *nll_sum,
+                        float *pair_term, float *chosen_logp, float *rejected_logp,
+                        float *pair_logit, hipStream_t s) {
   if (k <= 0) return hipSuccess;
-  hipLaunchKernelGGL(orpo_pairs_kernel, dim3((unsigned)k), dim3(kPairThreads), 0, s, lp, rl,
-                     labels_c, ii, T, k, p0, n_pairs, beta, sc, wrow, nll_sum, or_term,
-                     chosen_logp, rejected_logp, log_odds_ratio);
+  hipLaunchKernelGGL(pairs_kernel, dim3((unsigned)k), dim3(kPairThreads), 0, s, kind, lp, rl,
+                     labels_c, ii, T, k, p0, n_pairs, pp, sc, wrow, nll_sum, pair_term,
+                     chosen_logp, rejected_logp, pair_logit);
   return hipGetLastError();
 }
 
-hipError_t launch_orpo_final(const float *nll_sum, const float *or_term, int64_t n_pairs,
-                             float beta, Scalars *sc, hipStream_t s) {
-  hipLaunchKernelGGL(orpo_final_kernel, dim3(1), dim3(256), 0, s, nll_sum, or_term, n_pairs, beta,
-                     sc);
+hipError_t launch_pairs_final(const float *nll_sum, const float *pair_term, int64_t n_pairs,
+                              float alpha, float lambda, Scalars *sc, hipStream_t s) {
+  hipLaunchKernelGGL(pairs_final_kernel, dim3(1), dim3(256), 0, s, nll_sum, pair_term, n_pairs,
+                     alpha, lambda, sc);
   return hipGetLastError();
 }
 

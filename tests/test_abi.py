@@ -121,6 +121,23 @@ def test_orpo_validation(lib):
     assert fl.flce_orpo_workspace_bytes(8, 512, 4096, 128256, fl.FLCE_BF16, 0) == sizes[2]
 
 
+def test_pair_validation(lib):
+    lv, nv = ctypes.c_float(0), ctypes.c_float(0)
+
+    def call(kind, ref=FAKE):
+        return lib.flce_pair_fwd_bwd(kind, FAKE, FAKE, FAKE, 2, 8, 64, 100, fl.FLCE_BF16, -100,
+                                     0.1, 0.0, 0.0, ref, ref, 1, ctypes.byref(lv),
+                                     ctypes.byref(nv), FAKE, FAKE, None, None, None, FAKE, 10,
+                                     None)
+    assert call(4) == fl.FLCE_EINVAL                       # unknown kind
+    assert call(-1) == fl.FLCE_EINVAL
+    assert call(fl.PAIR_KINDS["dpo"], ref=None) == fl.FLCE_EINVAL     # DPO needs references
+    for k in ("orpo", "simpo", "cpo", "dpo"):              # valid: stops at the small workspace
+        assert call(fl.PAIR_KINDS[k]) == fl.FLCE_EWORKSPACE
+    assert fl.flce_pair_workspace_bytes(2, 8, 64, 100, fl.FLCE_BF16, 1) == \
+        fl.flce_orpo_workspace_bytes(2, 8, 64, 100, fl.FLCE_BF16, 1)
+
+
 def test_scale_validation(lib):
     assert lib.flce_scale_inplace(FAKE, 10, 5, FAKE, None) == fl.FLCE_EINVAL
     assert lib.flce_scale_inplace(FAKE, -1, 0, FAKE, None) == fl.FLCE_EINVAL
