@@ -231,11 +231,19 @@ def bench_ce(args):
 ORPO_PAIRS, ORPO_T = 8, 512   # 8 pairs of 512-token sequences: 8192 rows on the Llama-3-8B head
 
 
+PAIR_PARAMS = {"orpo": dict(beta=0.1, gamma=0.0, alpha=1.0),
+               "simpo": dict(beta=2.0, gamma=1.0, alpha=0.0),
+               "cpo": dict(beta=0.1, gamma=0.0, alpha=1.0),
+               "dpo": dict(beta=0.1, gamma=0.0, alpha=0.0)}
+
+
 def bench_orpo(args):
-    """ORPO loss on the Llama-3-8B head: 8 preference pairs of 512-token
-    sequences (8192 rows, H = 4096, V = 128256, bf16), one pair (1024 rows)
-    per chunk; one step is one flce_orpo_fwd_bwd.  FLOPs 6 N H V as for the
-    fused loss (the same three GEMMs over every row)."""
+    """A pairwise preference loss (--op orpo, simpo, cpo or dpo) on the
+    Llama-3-8B head: 8 preference pairs of 512-token sequences (8192 rows,
+    H = 4096, V = 128256, bf16), one pair (1024 rows) per chunk; one step is
+    one flce_pair_fwd_bwd (DPO with fixed reference log-probabilities).
+    FLOPs 6 N H V as for the fused loss (the same three GEMMs over every
+    row)."""
     import numpy as np
     import torch
     import datagen
@@ -259,8 +267,16 @@ def bench_orpo(args):
     if args.copy_reference_mib:
         copy_reference(args.copy_reference_mib, dev)
 
+    kind = args.op
+    pp = PAIR_PARAMS[kind]
+    ref = [None, None]
+    if kind == "dpo":     # a reference head's sequence log-probabilities (not timed)
+        Wref = (W.float() * 1.01).to(torch.bfloat16)
+        ref = list(fl.sequence_logps(Wref, X, y.view(2 * B, T), chunk_pairs=chunk_pairs))
+
     def step():
-        return fl.flce_orpo_fwd_bwd(X, W, y, B, -100, 0.1, chunk_pairs, dX, dW, ws, stream=stream)
+        return fl.flce_pair_fwd_bwd(kind, X, W, y, B, -100, pp["beta"], pp["gamma"], pp["alpha"],
+                                    chunk_pairs, dX, dW, ws, ref[0], ref[1], stream=stream)
 
     for _ in range(args.warmup):
         loss, nll = step()
@@ -277,17 +293,17 @@ def bench_orpo(args):
     fl.flce_profile_enable(False)
     tflops = 6.0 * N * H * V / (ms * 1e-3) / 1e12
     chunks = [2 * chunk_pairs * T] * (B // chunk_pairs)
-    kernels, roof = kernel_summary(prof, args.steps, chunks, H, V, "llama3-8b-head-orpo")
+    kernels, roof = kernel_summary(prof, args.steps, chunks, H, V, f"llama3-8b-head-{kind}")
     out = {
-        "metric": "ORPO fused-linear preference loss fwd+bwd tokens/s, Llama-3-8B head",
+        "metric": f"{kind.upper()} fused-linear preference loss fwd+bwd tokens/s, Llama-3-8B head",
         "value": round(N / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded; X ~ N(0,1), W ~ N(0,0.02^2); per pair a shared prompt of "
                 "T/8..T/2 unscored tokens, per sequence 0..T/4 unscored padding tokens, "
                 "uniform response labels)",
-        "config": {"workload": "llama3-8b-head-orpo", "pairs": B, "T": T, "N": N, "H": H, "V": V,
-                   "chunk_pairs": chunk_pairs, "beta": 0.1, "workspace_bytes": nbytes},
+        "config": {"workload": f"llama3-8b-head-{kind}", "pairs": B, "T": T, "N": N, "H": H,
+                   "V": V, "chunk_pairs": chunk_pairs, **pp, "workspace_bytes": nbytes},
         "tflops": round(tflops, 2), "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
         "loss": loss, "nll": nll, "kernels": kernels, "roofline": roof,
     }
@@ -296,8 +312,13 @@ def bench_orpo(args):
         n_pairs = 4                                  # the first four pairs: 4096 rows
         rows = np.concatenate([np.arange(0, n_pairs * T), np.arange(B * T, (B + n_pairs) * T)])
         X64, W64 = inp.X_f64()[rows], inp.W_f64()
+        rr = None
+        if kind == "dpo":
+            rr = [r.double().cpu().numpy()[:n_pairs] for r in ref]
         t2 = time.perf_counter()
-        oracle.orpo(X64, W64, inp.labels[rows], n_pairs, -100, 0.1)
+        oracle.preference(kind, X64, W64, inp.labels[rows], n_pairs, -100,
+                          ref_chosen=rr[0] if rr else None, ref_rejected=rr[1] if rr else None,
+                          **pp)
         dt = time.perf_counter() - t2
         out["cpu_baseline"] = {"value": rows.size / dt, "unit": "tokens/s",
                                "cores": _blas_threads(), "kind": "oracle",
@@ -306,7 +327,7 @@ def bench_orpo(args):
                                          "loss + dX + dW on the host"}
     else:
         out["cpu_baseline"] = None
-    log(f"orpo: {ms:.3f} ms/step  {tflops:.1f} TFLOP/s  loss={loss:.6f} nll={nll:.6f}")
+    log(f"{kind}: {ms:.3f} ms/step  {tflops:.1f} TFLOP/s  loss={loss:.6f} nll={nll:.6f}")
     for name, k in kernels.items():
         log(f"  {name:12s} {k}")
     print(json.dumps(out), flush=True)
@@ -330,10 +351,12 @@ def main():
     ap.add_argument("--chunk", type=int, default=None, help="chunk tokens (default: the workload's)")
     ap.add_argument("--cpu-sample-tokens", type=int, default=4096)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--op", choices=("flce", "ce", "orpo"), default="flce",
+    ap.add_argument("--op", choices=("flce", "ce", "orpo", "simpo", "cpo", "dpo"),
+                    default="flce",
                     help="flce: the fused linear cross-entropy step (default); ce: cross-entropy "
-                         "on given logits of the Llama-3-8B head's size; orpo: the fused-linear "
-                         "ORPO loss on 8 pairs of 512-token sequences on the same head")
+                         "on given logits of the Llama-3-8B head's size; orpo, simpo, cpo, dpo: "
+                         "a fused-linear preference loss on 8 pairs of 512-token sequences on "
+                         "the same head")
     ap.add_argument("--copy-reference-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (a known-size "
                          "reference for hardware byte counters)")
@@ -347,7 +370,7 @@ def main():
     if args.op == "ce":
         bench_ce(args)
         return
-    if args.op == "orpo":
+    if args.op in PAIR_PARAMS:
         bench_orpo(args)
         return
 
