@@ -558,3 +558,67 @@ def preference(kind: str, X, W, labels, n_pairs: int, ignore_index: int = IGNORE
         return PreferenceResult(loss, nll, pl, u_c, u_r, z, None, None)
     G = dlogits_weighted(Z, lse, labels, w)
     return PreferenceResult(loss, nll, pl, u_c, u_r, z, grad_input(G, W), grad_weight(G, X))
+
+
+# ------------------------------------------------------------------ unpaired preference loss (KTO)
+# The last of the page's post-training list ("Kernels de Pós-Treinamento"),
+# again without a formula: Kahneman-Tversky Optimization (Ethayarajh et al.,
+# 2024).  Sequences are unpaired, each marked desirable or undesirable; with
+# S the sum of log p(y_t) over a sequence's scored tokens, R the reference
+# model's (an input) and r = S - R,
+#   desirable:    l = lambda_d (1 - sigmoid(beta (r - z0)))
+#   undesirable:  l = lambda_u (1 - sigmoid(beta (z0 - r)))
+#   L = mean over sequences of l
+# z0 is the reference point (the KL term of the paper), an input through
+# which no gradient flows.  Layout: the rows of X are n_seq sequences of T
+# tokens; ignore_index marks unscored tokens.
+
+@dataclasses.dataclass
+class KTOResult:
+    loss: float
+    logp: np.ndarray             # [n_seq] S
+    reward: np.ndarray           # [n_seq] r = S - R
+    dX: np.ndarray | None
+    dW: np.ndarray | None
+
+
+def kto_sequence_terms(r, desirable, beta: float, z0: float, lambda_d: float, lambda_u: float):
+    """Per-sequence loss l and dl/dr."""
+    u = np.where(desirable, beta * (r - z0), beta * (z0 - r))
+    sig = 1.0 / (1.0 + np.exp(-u))
+    lam = np.where(desirable, lambda_d, lambda_u)
+    l = lam * (1.0 - sig)
+    dl_du = -lam * sig * (1.0 - sig)
+    return l, dl_du * np.where(desirable, beta, -beta)
+
+
+def kto_token_weights(dl_dr, valid, n_seq: int) -> np.ndarray:
+    """w_t = -dL/d log p(y_t) = -(1/n_seq) dl/dr of the token's sequence."""
+    T = valid.size // n_seq
+    v = valid.reshape(n_seq, T)
+    return np.where(v, (-dl_dr / n_seq)[:, None], 0.0).reshape(-1)
+
+
+def kto(X, W, labels, n_seq: int, desirable, ref_logp, ignore_index: int = IGNORE_INDEX,
+        beta: float = 0.1, z0: float = 0.0, lambda_d: float = 1.0, lambda_u: float = 1.0,
+        grads: bool = True) -> KTOResult:
+    """KTO loss of n_seq sequences (rows of X sequence-major) and its gradients."""
+    X = np.asarray(X, dtype=np.float64)
+    W = np.asarray(W, dtype=np.float64)
+    labels = np.asarray(labels, dtype=np.int64)
+    if n_seq <= 0 or X.shape[0] % n_seq != 0:
+        raise ValueError("X must hold n_seq sequences of equal length")
+    desirable = np.asarray(desirable, dtype=bool)
+    ref_logp = np.asarray(ref_logp, dtype=np.float64)
+    valid = valid_mask(labels, W.shape[0], ignore_index)
+    Z = logits(X, W)
+    lse = row_logsumexp(Z)
+    lp = log_probs(lse, target_logit(Z, labels, valid), valid)
+    S, _ = sequence_sums(lp, valid, n_seq)
+    r = S - ref_logp
+    l, dl_dr = kto_sequence_terms(r, desirable, beta, z0, lambda_d, lambda_u)
+    loss = float(l.sum() / n_seq)
+    if not grads:
+        return KTOResult(loss, S, r, None, None)
+    G = dlogits_weighted(Z, lse, labels, kto_token_weights(dl_dr, valid, n_seq))
+    return KTOResult(loss, S, r, grad_input(G, W), grad_weight(G, X))
