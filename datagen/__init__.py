@@ -247,6 +247,37 @@ def make_pairs(n_pairs: int, T: int, H: int, V: int, dtype: str = "bf16", seed: 
     return Inputs(wl, X, W, y.reshape(-1), seed)
 
 
+def make_unpaired(n_seq: int, T: int, H: int, V: int, dtype: str = "bf16", seed: int = 1,
+                  w_std: float = 0.02):
+    """Unpaired preference batch: n_seq sequences of T tokens as rows of X,
+    each with its own prompt of U{ceil(T/8) .. floor(T/2)} and padding of
+    U{0 .. floor(T/4)} unscored tokens (labels as make_pairs), a desirability
+    flag (half of the sequences, by a seeded permutation) and a reference
+    log-probability sum R ~ N(-n_s (ln V + w_std^2 H / 2), (2 sqrt(n_s))^2)
+    for its n_s scored tokens: centred on what a head drawn this way gives
+    (logits of variance w_std^2 H), so rewards are of order sqrt(n_s).  Returns (Inputs, desirable int32 [n_seq], R float32 [n_seq]).
+    Draw order: X, W, labels, prompt lengths, padding lengths, flags, R."""
+    N = n_seq * T
+    wl = Workload("unpaired", N, H, V, dtype, 0, ignore_mode="none", w_std=w_std)
+    ss = np.random.SeedSequence(seed)
+    s_x, s_w, s_y, s_p, s_d, s_f, s_r = ss.spawn(7)
+    X = _draw_X(np.random.default_rng(s_x), N, H, "normal", dtype)
+    W = _draw_W(s_w, V, H, w_std, dtype)
+    y = _draw_labels(np.random.default_rng(s_y), N, V, "uniform", 0.0).reshape(n_seq, T)
+    P = np.random.default_rng(s_p).integers(-(-T // 8), T // 2 + 1, size=n_seq)
+    D = np.random.default_rng(s_d).integers(0, T // 4 + 1, size=n_seq)
+    for s_ in range(n_seq):
+        y[s_, :P[s_]] = IGNORE_INDEX
+        if D[s_]:
+            y[s_, T - D[s_]:] = IGNORE_INDEX
+    des = np.zeros(n_seq, dtype=np.int32)
+    des[np.random.default_rng(s_f).permutation(n_seq)[: n_seq // 2]] = 1
+    n_s = (y != IGNORE_INDEX).sum(axis=1)
+    R = (-(np.log(V) + 0.5 * w_std * w_std * H) * n_s + 2.0 * np.sqrt(n_s) *
+         np.random.default_rng(s_r).standard_normal(n_seq)).astype(np.float32)
+    return Inputs(wl, X, W, y.reshape(-1), seed), des, R
+
+
 def sample_rows(n_total: int, k: int, seed: int, must: tuple = ()) -> np.ndarray:
     """Seeded sorted sample of k distinct row indices, always holding ``must``."""
     rng = np.random.default_rng(seed)

@@ -271,6 +271,35 @@ int flce_pair_fwd(int kind, const void *X, const void *W, const int64_t *labels,
                   size_t workspace_bytes, void *stream);
 
 /*
+ * The unpaired loss of the same list: KTO (Ethayarajh et al., 2024).  The rows
+ * of X are n_seq sequences of T tokens (no pairing); with S the sum of
+ * log p(y_t) over a sequence's scored tokens, R its reference value and
+ * r = S - R,
+ *     desirable:    l = lambda_d (1 - sigmoid(beta (r - z0)))
+ *     undesirable:  l = lambda_u (1 - sigmoid(beta (z0 - r)))
+ *     loss = mean over sequences of l
+ * z0 is the reference point (a host value; no gradient flows through it).
+ *   desirable  device [n_seq] int32, nonzero marks a desirable sequence
+ *   ref_logp   device [n_seq] fp32, R (required)
+ *   chunk_seqs sequences per chunk; <= 0: the largest count with at most 4096 rows
+ *   logp, reward  device [n_seq] fp32 or NULL: S and r
+ * Other arguments, alignment and errors as for flce_orpo_fwd_bwd.
+ */
+size_t flce_kto_workspace_bytes(int64_t n_seq, int64_t T, int64_t H, int64_t V, int dtype,
+                                int64_t chunk_seqs);
+int flce_kto_fwd_bwd(const void *X, const void *W, const int64_t *labels, int64_t n_seq,
+                     int64_t T, int64_t H, int64_t V, int dtype, int64_t ignore_index,
+                     const int32_t *desirable, const float *ref_logp, float beta, float z0,
+                     float lambda_d, float lambda_u, int64_t chunk_seqs, float *loss, void *dX,
+                     float *dW, float *logp, float *reward, void *workspace,
+                     size_t workspace_bytes, void *stream);
+int flce_kto_fwd(const void *X, const void *W, const int64_t *labels, int64_t n_seq, int64_t T,
+                 int64_t H, int64_t V, int dtype, int64_t ignore_index, const int32_t *desirable,
+                 const float *ref_logp, float beta, float z0, float lambda_d, float lambda_u,
+                 int64_t chunk_seqs, float *loss, float *logp, float *reward, void *workspace,
+                 size_t workspace_bytes, void *stream);
+
+/*
  * buf[i] *= *scale for i < n, in place, on the stream (no sync).  buf is a
  * device array of dtype (FLCE_F32 or FLCE_BF16); scale is a device fp32
  * scalar.  Used to apply an upstream gradient d(out)/d(loss) != 1 to dX, dW.

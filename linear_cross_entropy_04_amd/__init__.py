@@ -26,7 +26,8 @@ __all__ = [
     "flce_orpo_workspace_bytes", "flce_orpo_fwd_bwd", "flce_orpo_fwd", "orpo_loss",
     "FusedLinearORPOLoss", "PAIR_KINDS", "flce_pair_workspace_bytes", "flce_pair_fwd_bwd",
     "flce_pair_fwd", "preference_loss", "sequence_logps", "FusedLinearSimPOLoss",
-    "FusedLinearCPOLoss", "FusedLinearDPOLoss",
+    "FusedLinearCPOLoss", "FusedLinearDPOLoss", "flce_kto_workspace_bytes", "flce_kto_fwd_bwd",
+    "flce_kto_fwd", "kto_loss", "FusedLinearKTOLoss",
 ]
 
 FLCE_F32 = 0
@@ -109,6 +110,14 @@ def _load():
                                 _p, _p, _i64, ctypes.POINTER(_f), ctypes.POINTER(_f), _p, _p, _p,
                                 _p, _sz, _p]
     l.flce_pair_fwd.restype = _i32
+    l.flce_kto_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64, _i32, _i64]
+    l.flce_kto_workspace_bytes.restype = _sz
+    l.flce_kto_fwd_bwd.argtypes = [_p, _p, _p, _i64, _i64, _i64, _i64, _i32, _i64, _p, _p, _f, _f,
+                                   _f, _f, _i64, ctypes.POINTER(_f), _p, _p, _p, _p, _p, _sz, _p]
+    l.flce_kto_fwd_bwd.restype = _i32
+    l.flce_kto_fwd.argtypes = [_p, _p, _p, _i64, _i64, _i64, _i64, _i32, _i64, _p, _p, _f, _f, _f,
+                               _f, _i64, ctypes.POINTER(_f), _p, _p, _p, _sz, _p]
+    l.flce_kto_fwd.restype = _i32
     l.flce_scale_inplace.argtypes = [_p, _i64, _i32, _p, _p]
     l.flce_scale_inplace.restype = _i32
     l.flce_status_string.argtypes = [_i32]
@@ -495,6 +504,67 @@ def flce_pair_fwd(kind: str, X: torch.Tensor, W: torch.Tensor, labels: torch.Ten
     return float(loss.value), float(nll.value)
 
 
+def flce_kto_workspace_bytes(n_seq: int, T: int, H: int, V: int, dtype: int,
+                             chunk_seqs: int = 0) -> int:
+    return int(_load().flce_kto_workspace_bytes(n_seq, T, H, V, dtype, chunk_seqs))
+
+
+def _kto_args(X, W, labels, n_seq, desirable, ref_logp, workspace, logp, reward):
+    N, H = X.shape
+    V = W.shape[0]
+    if n_seq <= 0 or N % n_seq != 0:
+        raise ValueError(f"X has {N} rows: not n_seq = {n_seq} equal sequences")
+    _dev(X, "X")
+    _dev(W, "W", X.dtype, (V, H))
+    _dev(labels, "labels", torch.int64, (N,))
+    _dev(desirable, "desirable", torch.int32, (n_seq,))
+    _dev(ref_logp, "ref_logp", torch.float32, (n_seq,))
+    _dev(workspace, "workspace")
+    for t, name in ((logp, "logp"), (reward, "reward")):
+        _dev(t, name, torch.float32, (n_seq,))
+    return N // n_seq, H, V, _dtype_code(X)
+
+
+def flce_kto_fwd_bwd(X: torch.Tensor, W: torch.Tensor, labels: torch.Tensor, n_seq: int,
+                     ignore_index: int, desirable: torch.Tensor, ref_logp: torch.Tensor,
+                     beta: float, z0: float, lambda_d: float, lambda_u: float, chunk_seqs: int,
+                     dX: torch.Tensor, dW: torch.Tensor, workspace: torch.Tensor,
+                     logp: torch.Tensor | None = None, reward: torch.Tensor | None = None,
+                     stream=None) -> float:
+    """Call libflce's flce_kto_fwd_bwd; returns the loss."""
+    T, H, V, dt = _kto_args(X, W, labels, n_seq, desirable, ref_logp, workspace, logp, reward)
+    _dev(dX, "dX", X.dtype, tuple(X.shape))
+    _dev(dW, "dW", torch.float32, (V, H))
+    loss = ctypes.c_float(0.0)
+    st = _load().flce_kto_fwd_bwd(_ptr(X), _ptr(W), _ptr(labels), n_seq, T, H, V, dt,
+                                  ignore_index, _ptr(desirable), _ptr(ref_logp), float(beta),
+                                  float(z0), float(lambda_d), float(lambda_u), chunk_seqs,
+                                  ctypes.byref(loss), _ptr(dX), _ptr(dW), _ptr(logp),
+                                  _ptr(reward), _ptr(workspace), workspace.numel(),
+                                  _stream(stream, X.device))
+    if st != FLCE_OK:
+        raise FLCEError(st, "flce_kto_fwd_bwd")
+    return float(loss.value)
+
+
+def flce_kto_fwd(X: torch.Tensor, W: torch.Tensor, labels: torch.Tensor, n_seq: int,
+                 ignore_index: int, desirable: torch.Tensor, ref_logp: torch.Tensor, beta: float,
+                 z0: float, lambda_d: float, lambda_u: float, chunk_seqs: int,
+                 workspace: torch.Tensor, logp: torch.Tensor | None = None,
+                 reward: torch.Tensor | None = None, stream=None) -> float:
+    """Call libflce's flce_kto_fwd; returns the loss."""
+    T, H, V, dt = _kto_args(X, W, labels, n_seq, desirable, ref_logp, workspace, logp, reward)
+    loss = ctypes.c_float(0.0)
+    st = _load().flce_kto_fwd(_ptr(X), _ptr(W), _ptr(labels), n_seq, T, H, V, dt, ignore_index,
+                              _ptr(desirable), _ptr(ref_logp), float(beta), float(z0),
+                              float(lambda_d), float(lambda_u), chunk_seqs, ctypes.byref(loss),
+                              _ptr(logp), _ptr(reward), _ptr(workspace), workspace.numel(),
+                              _stream(stream, X.device))
+    if st != FLCE_OK:
+        raise FLCEError(st, "flce_kto_fwd")
+    return float(loss.value)
+
+
 def flce_scale_inplace(buf: torch.Tensor, scale: torch.Tensor, stream=None) -> None:
     """buf *= scale (a one-element fp32 device tensor), in place, on the stream."""
     _dev(buf, "buf")
@@ -834,3 +904,92 @@ class FusedLinearDPOLoss(torch.nn.Module):
         return preference_loss("dpo", weight, input, target, self.beta, 0.0, self.alpha,
                                ref_chosen_logp, ref_rejected_logp, self.ignore_index,
                                self.chunk_pairs)
+
+
+def _kto_ws(x, weight, n_seq, chunk_seqs):
+    N, H = x.shape
+    nbytes = flce_kto_workspace_bytes(n_seq, N // n_seq, H, weight.shape[0], _dtype_code(x),
+                                      chunk_seqs)
+    if nbytes == 0:
+        raise FLCEError(FLCE_EINVAL, "flce_kto_workspace_bytes")
+    return torch.empty(nbytes, dtype=torch.uint8, device=x.device)
+
+
+class _KTOFunction(torch.autograd.Function):
+    """KTO: gradients computed with the loss (one call), scaled by the
+    upstream gradient in backward."""
+
+    @staticmethod
+    def forward(ctx, weight, input, target, n_seq, desirable, ref_logp, ignore_index, beta, z0,
+                lambda_d, lambda_u, chunk_seqs):
+        ws = _kto_ws(input, weight, n_seq, chunk_seqs)
+        args = (input, weight, target, n_seq, ignore_index, desirable, ref_logp, beta, z0,
+                lambda_d, lambda_u, chunk_seqs)
+        if ctx.needs_input_grad[0] or ctx.needs_input_grad[1]:
+            dX = torch.empty_like(input)
+            dW = torch.empty(tuple(weight.shape), dtype=torch.float32, device=input.device)
+            val = flce_kto_fwd_bwd(*args, dX, dW, ws)
+            ctx.save_for_backward(dX, dW)
+        else:
+            val = flce_kto_fwd(*args, ws)
+        ctx.wdtype = weight.dtype
+        return torch.tensor(val, dtype=torch.float32, device=input.device)
+
+    @staticmethod
+    def backward(ctx, grad_out):
+        dX, dW = ctx.saved_tensors
+        g = grad_out.detach().to(torch.float32).reshape(1).contiguous()
+        flce_scale_inplace(dX, g)
+        flce_scale_inplace(dW, g)
+        gw = dW if ctx.wdtype == torch.float32 else dW.to(ctx.wdtype)
+        return (gw, dX) + (None,) * 10
+
+
+def _kto_rows(input, target, desirable):
+    if target.dim() != 2:
+        raise ValueError("target must be [n_seq, T]")
+    x = input.reshape(-1, input.shape[-1])
+    if x.shape[0] != target.numel():
+        raise ValueError(f"input has {x.shape[0]} rows, target {target.numel()} tokens")
+    des = desirable.to(torch.int32).contiguous()
+    return x, target.reshape(-1).contiguous(), target.shape[0], des
+
+
+def kto_loss(weight: torch.Tensor, input: torch.Tensor, target: torch.Tensor,
+             desirable: torch.Tensor, ref_logp: torch.Tensor, beta: float = 0.1, z0: float = 0.0,
+             lambda_d: float = 1.0, lambda_u: float = 1.0, ignore_index: int = -100,
+             chunk_seqs: int = 0) -> torch.Tensor:
+    """KTO loss of input [n_seq, T, H] (or [n_seq * T, H]) against target
+    [n_seq, T]; desirable [n_seq] (bool or int), ref_logp [n_seq] the
+    reference model's summed log-probabilities, z0 the reference point."""
+    x, y, n_seq, des = _kto_rows(input, target, desirable)
+    return _KTOFunction.apply(weight, x, y, n_seq, des, ref_logp.float().contiguous(),
+                              ignore_index, beta, z0, lambda_d, lambda_u, chunk_seqs)
+
+
+class FusedLinearKTOLoss(torch.nn.Module):
+    """Module form of kto_loss; the reference log-probabilities are given, or
+    computed (forward only) from ref_weight and ref_input (default: input)."""
+
+    def __init__(self, beta: float = 0.1, lambda_d: float = 1.0, lambda_u: float = 1.0,
+                 ignore_index: int = -100, chunk_seqs: int = 0):
+        super().__init__()
+        self.beta, self.lambda_d, self.lambda_u = beta, lambda_d, lambda_u
+        self.ignore_index, self.chunk_seqs = ignore_index, chunk_seqs
+
+    def forward(self, weight, input, target, desirable, z0: float = 0.0, ref_logp=None,
+                ref_weight=None, ref_input=None):
+        if ref_logp is None:
+            if ref_weight is None:
+                raise ValueError("KTO needs ref_weight or the reference log-probabilities")
+            with torch.no_grad():
+                src = (input if ref_input is None else ref_input).detach()
+                x, y, n_seq, des = _kto_rows(src, target, desirable)
+                ref_logp = torch.empty(n_seq, dtype=torch.float32, device=x.device)
+                zeros = torch.zeros(n_seq, dtype=torch.float32, device=x.device)
+                flce_kto_fwd(x.contiguous(), ref_weight.detach().contiguous(), y, n_seq,
+                             self.ignore_index, des, zeros, self.beta, 0.0, 1.0, 1.0,
+                             self.chunk_seqs, _kto_ws(x, ref_weight, n_seq, self.chunk_seqs),
+                             logp=ref_logp)
+        return kto_loss(weight, input, target, desirable, ref_logp, self.beta, z0, self.lambda_d,
+                        self.lambda_u, self.ignore_index, self.chunk_seqs)

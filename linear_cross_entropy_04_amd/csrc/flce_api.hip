@@ -747,6 +747,154 @@ FLCE_API int flce_orpo_fwd(const void *X, const void *W, const int64_t *labels, 
                          workspace_bytes, stream);
 }
 
+// ---------------------------------------------------------------- unpaired preference loss (KTO)
+// A chunk holds k whole consecutive sequences, already contiguous in X; the
+// per-sequence step runs between the chunk's forward and backward.
+
+namespace flce {
+namespace {
+
+struct KtoLayout {
+  Plan p;
+  int64_t k = 0;          // sequences per chunk
+  size_t off_lp = 0, off_w = 0, off_term = 0, off_logp = 0, off_rew = 0, total = 0;
+};
+
+int kto_check(int64_t S, int64_t T, int64_t H, int64_t V, int dtype) {
+  if (S <= 0 || T <= 0) return FLCE_EINVAL;
+  if (T > ((int64_t)1 << 30) || S > kMaxN / T) return FLCE_EUNSUPPORTED;
+  return check_sizes(S * T, H, V, dtype);
+}
+
+void kto_layout(int64_t S, int64_t T, int64_t H, int64_t V, int dtype, int64_t chunk_seqs,
+                KtoLayout *L) {
+  int64_t k = chunk_seqs > 0 ? chunk_seqs : kOrpoAutoRows / T;
+  k = std::max<int64_t>(1, std::min(k, S));
+  const int64_t C = k * T;
+  make_plan(C, H, V, dtype, C, &L->p);
+  L->k = k;
+  size_t o = L->p.total;
+  L->off_lp = o;
+  o += align256((size_t)C * 4);
+  L->off_w = o;
+  o += align256((size_t)C * 4);
+  size_t *seq_arrays[3] = {&L->off_term, &L->off_logp, &L->off_rew};
+  for (size_t *q : seq_arrays) {
+    *q = o;
+    o += align256((size_t)S * 4);
+  }
+  L->total = o;
+}
+
+int run_kto(bool bwd, const void *X, const void *W, const int64_t *labels, int64_t S, int64_t T,
+            int64_t H, int64_t V, int dtype, int64_t ii, const KtoParams &kp, int64_t chunk_seqs,
+            float *loss, void *dX, float *dW, float *logp, float *reward, void *workspace,
+            size_t workspace_bytes, void *stream) {
+  int st = kto_check(S, T, H, V, dtype);
+  if (st != FLCE_OK) return st;
+  if (!loss || !X || !W || !labels || !workspace || !kp.desirable || !kp.ref) return FLCE_EINVAL;
+  if (bwd && (!dX || !dW)) return FLCE_EINVAL;
+  if (misaligned(workspace, 256) || misaligned(labels, 8) || misaligned(kp.desirable, 4) ||
+      misaligned(kp.ref, 4) || misaligned(logp, 4) || misaligned(reward, 4))
+    return FLCE_EINVAL;
+  if (dtype == FLCE_BF16 && (misaligned(X, 16) || misaligned(W, 16) || (bwd && misaligned(dX, 16))))
+    return FLCE_EUNSUPPORTED;
+  if (dtype == FLCE_F32 && (misaligned(X, 4) || misaligned(W, 4) || (bwd && misaligned(dX, 4))))
+    return FLCE_EINVAL;
+  if (bwd && misaligned(dW, 4)) return FLCE_EINVAL;
+  KtoLayout L;
+  kto_layout(S, T, H, V, dtype, chunk_seqs, &L);
+  if (workspace_bytes < L.total) return FLCE_EWORKSPACE;
+
+  const Plan &p = L.p;
+  hipStream_t s = (hipStream_t)stream;
+  char *ws = (char *)workspace;
+  Scalars *sc = (Scalars *)(ws + p.off_scal);
+  const int64_t esz = dtype == FLCE_BF16 ? 2 : 4;
+  float *rl = (float *)(ws + p.off_rowloss), *lp = (float *)(ws + L.off_lp);
+  float *wrow = (float *)(ws + L.off_w), *term = (float *)(ws + L.off_term);
+  float *lpo = logp ? logp : (float *)(ws + L.off_logp);
+  float *rwo = reward ? reward : (float *)(ws + L.off_rew);
+
+  LAUNCH(FLCE_K_PAIRS, launch_pairs_labels(labels, S * T, 0, V, ii, sc, s));
+  st = pack_weight(p, ws, W, bwd, s);
+  if (st != FLCE_OK) return st;
+  for (int64_t s0 = 0; s0 < S; s0 += L.k) {
+    const int64_t kk = std::min(L.k, S - s0);
+    ChunkIO io;
+    io.Xc = (const char *)X + s0 * T * H * esz;
+    io.lab = labels + s0 * T;
+    io.c = (int)(kk * T);
+    io.rl = rl;
+    io.lp = lp;
+    io.wr = bwd ? wrow : nullptr;
+    io.acc_dw = s0 > 0;
+    io.dXc = bwd ? (char *)dX + s0 * T * H * esz : nullptr;
+    st = chunk_forward(p, ws, W, ii, bwd, io, s);
+    if (st != FLCE_OK) return st;
+    LAUNCH(FLCE_K_PAIRS, launch_kto_seqs(lp, io.lab, ii, T, (int)kk, s0, S, kp,
+                                         bwd ? wrow : nullptr, term, lpo, rwo, s));
+    if (bwd) {
+      st = chunk_backward(p, ws, W, ii, io, dW, sc, s);
+      if (st != FLCE_OK) return st;
+    }
+  }
+  // loss = mean of the terms (no NLL term)
+  LAUNCH(FLCE_K_PAIRS, launch_pairs_final(term, term, S, 0.f, 1.f, sc, s));
+  Scalars host;
+  CK(hipMemcpyAsync(&host, sc, sizeof(host), hipMemcpyDeviceToHost, s));
+  CK(hipStreamSynchronize(s));
+  if (host.flag) return FLCE_ELABEL;
+  *loss = host.loss;
+  return FLCE_OK;
+}
+
+KtoParams kto_params(const int32_t *desirable, const float *ref, float beta, float z0,
+                     float lambda_d, float lambda_u) {
+  KtoParams kp{};
+  kp.beta = beta;
+  kp.z0 = z0;
+  kp.lambda_d = lambda_d;
+  kp.lambda_u = lambda_u;
+  kp.desirable = desirable;
+  kp.ref = ref;
+  return kp;
+}
+
+}  // namespace
+}  // namespace flce
+
+FLCE_API size_t flce_kto_workspace_bytes(int64_t n_seq, int64_t T, int64_t H, int64_t V,
+                                         int dtype, int64_t chunk_seqs) {
+  if (flce::kto_check(n_seq, T, H, V, dtype) != FLCE_OK) return 0;
+  flce::KtoLayout L;
+  flce::kto_layout(n_seq, T, H, V, dtype, chunk_seqs, &L);
+  return L.total;
+}
+
+FLCE_API int flce_kto_fwd_bwd(const void *X, const void *W, const int64_t *labels, int64_t n_seq,
+                              int64_t T, int64_t H, int64_t V, int dtype, int64_t ignore_index,
+                              const int32_t *desirable, const float *ref_logp, float beta,
+                              float z0, float lambda_d, float lambda_u, int64_t chunk_seqs,
+                              float *loss, void *dX, float *dW, float *logp, float *reward,
+                              void *workspace, size_t workspace_bytes, void *stream) {
+  return flce::run_kto(true, X, W, labels, n_seq, T, H, V, dtype, ignore_index,
+                       flce::kto_params(desirable, ref_logp, beta, z0, lambda_d, lambda_u),
+                       chunk_seqs, loss, dX, dW, logp, reward, workspace, workspace_bytes, stream);
+}
+
+FLCE_API int flce_kto_fwd(const void *X, const void *W, const int64_t *labels, int64_t n_seq,
+                          int64_t T, int64_t H, int64_t V, int dtype, int64_t ignore_index,
+                          const int32_t *desirable, const float *ref_logp, float beta, float z0,
+                          float lambda_d, float lambda_u, int64_t chunk_seqs, float *loss,
+                          float *logp, float *reward, void *workspace, size_t workspace_bytes,
+                          void *stream) {
+  return flce::run_kto(false, X, W, labels, n_seq, T, H, V, dtype, ignore_index,
+                       flce::kto_params(desirable, ref_logp, beta, z0, lambda_d, lambda_u),
+                       chunk_seqs, loss, nullptr, nullptr, logp, reward, workspace,
+                       workspace_bytes, stream);
+}
+
 FLCE_API int flce_scale_inplace(void *buf, int64_t n, int dtype, const float *scale,
                                 void *stream) {
   if (dtype != FLCE_F32 && dtype != FLCE_BF16) return FLCE_EINVAL;

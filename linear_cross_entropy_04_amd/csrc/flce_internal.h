@@ -123,6 +123,16 @@ hipError_t launch_pairs(int kind, const float *lp, const float *rl, const int64_
                         const PairParams &pp, const Scalars *sc, float *wrow, float *nll_sum,
                         float *pair_term, float *chosen_logp, float *rejected_logp,
                         float *pair_logit, hipStream_t s);
+// KTO: per sequence of a chunk of k sequences (T rows each): S, r = S - R, the
+// loss term at s0 + j and (wrow not null) the per-row backward weights.
+struct KtoParams {
+  float beta, z0, lambda_d, lambda_u;
+  const int32_t *desirable;   // [n_seq], nonzero: desirable
+  const float *ref;           // [n_seq] the reference model's S
+};
+hipError_t launch_kto_seqs(const float *lp, const int64_t *labels_c, int64_t ii, int64_t T,
+                          int k, int64_t s0, int64_t n_seq, const KtoParams &kp, float *wrow,
+                          float *term, float *logp, float *reward, hipStream_t s);
 // sc->loss = alpha NLL + lambda mean pair term, sc->aux = NLL.
 hipError_t launch_pairs_final(const float *nll_sum, const float *pair_term, int64_t n_pairs,
                               float alpha, float lambda, Scalars *sc, hipStream_t s);

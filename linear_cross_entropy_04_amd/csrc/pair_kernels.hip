@@ -179,6 +179,45 @@ __global__ __launch_bounds__(kPairThreads) void pairs_kernel(
   }
 }
 
+// KTO (Ethayarajh et al., 2024), the unpaired loss of the same list: one
+// workgroup per sequence j of a chunk (rows j T .. j T + T - 1) forms S = the
+// sum of its tokens' log-probabilities, the reward r = S - R (R the
+// reference model's, an input) and its loss term against the reference
+// point z0 (an input taking no gradient),
+//   desirable:    lambda_d (1 - sigmoid(beta (r - z0)))
+//   undesirable:  lambda_u (1 - sigmoid(beta (z0 - r)))
+// and every scored row's weight w = -(dl/dr) / n_seq for the backward.
+__global__ __launch_bounds__(kPairThreads) void kto_seq_kernel(
+    const float *__restrict__ lp, const int64_t *__restrict__ labels_c, int64_t ii, int64_t T,
+    int64_t s0, int64_t n_seq, KtoParams kp, float *__restrict__ wrow, float *__restrict__ term,
+    float *__restrict__ logp, float *__restrict__ reward) {
+  __shared__ float red[kPairThreads / 64];
+  const int j = blockIdx.x;
+  const int64_t r0 = (int64_t)j * T;
+  float sum = 0.f;
+  for (int64_t t = threadIdx.x; t < T; t += kPairThreads)
+    if (labels_c[r0 + t] != ii) sum += lp[r0 + t];
+  const float S = block_sum(sum, red);
+  const float r = S - kp.ref[s0 + j];
+  const bool des = kp.desirable[s0 + j] != 0;
+  const float u = des ? kp.beta * (r - kp.z0) : kp.beta * (kp.z0 - r);
+  // sigmoid(u) and 1 - sigmoid(u) = sigmoid(-u), each from its own exp so
+  // that neither loses its digits when the other rounds to 1
+  const float sg = 1.f / (1.f + expf(-u)), sgn = 1.f / (1.f + expf(u));
+  const float lam = des ? kp.lambda_d : kp.lambda_u;
+  const float dl_dr = -lam * sg * sgn * (des ? kp.beta : -kp.beta);
+  if (threadIdx.x == 0) {
+    term[s0 + j] = lam * sgn;
+    if (logp) logp[s0 + j] = S;
+    if (reward) reward[s0 + j] = r;
+  }
+  if (wrow) {
+    const float w = -dl_dr / (float)n_seq;
+    for (int64_t t = threadIdx.x; t < T; t += kPairThreads)
+      wrow[r0 + t] = labels_c[r0 + t] != ii ? w : 0.f;
+  }
+}
+
 // loss = alpha (sum of the chosen tokens' losses) / N_c + lambda mean_i of
 // the pair terms; aux = the NLL.  One workgroup; fixed summation order.
 __global__ __launch_bounds__(256) void pairs_final_kernel(const float *__restrict__ nll_sum,
@@ -248,6 +287,15 @@ hipError_t launch_pairs(int kind, const float *lp, const float *rl, const int64_
   hipLaunchKernelGGL(pairs_kernel, dim3((unsigned)k), dim3(kPairThreads), 0, s, kind, lp, rl,
                      labels_c, ii, T, k, p0, n_pairs, pp, sc, wrow, nll_sum, pair_term,
                      chosen_logp, rejected_logp, pair_logit);
+  return hipGetLastError();
+}
+
+hipError_t launch_kto_seqs(const float *lp, const int64_t *labels_c, int64_t ii, int64_t T,
+                          int k, int64_t s0, int64_t n_seq, const KtoParams &kp, float *wrow,
+                          float *term, float *logp, float *reward, hipStream_t s) {
+  if (k <= 0) return hipSuccess;
+  hipLaunchKernelGGL(kto_seq_kernel, dim3((unsigned)k), dim3(kPairThreads), 0, s, lp, labels_c,
+                     ii, T, s0, n_seq, kp, wrow, term, logp, reward);
   return hipGetLastError();
 }
 

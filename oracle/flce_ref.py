@@ -586,9 +586,10 @@ def kto_sequence_terms(r, desirable, beta: float, z0: float, lambda_d: float, la
     """Per-sequence loss l and dl/dr."""
     u = np.where(desirable, beta * (r - z0), beta * (z0 - r))
     sig = 1.0 / (1.0 + np.exp(-u))
+    sig_neg = 1.0 / (1.0 + np.exp(u))                # 1 - sigmoid(u), without cancellation
     lam = np.where(desirable, lambda_d, lambda_u)
-    l = lam * (1.0 - sig)
-    dl_du = -lam * sig * (1.0 - sig)
+    l = lam * sig_neg
+    dl_du = -lam * sig * sig_neg
     return l, dl_du * np.where(desirable, beta, -beta)
 
 
