@@ -333,6 +333,95 @@ def bench_orpo(args):
     print(json.dumps(out), flush=True)
 
 
+KTO_SEQS, KTO_T = 16, 512     # 16 unpaired 512-token sequences: 8192 rows on the Llama-3-8B head
+
+
+def bench_kto(args):
+    """KTO on the Llama-3-8B head: 16 unpaired sequences of 512 tokens (8192
+    rows, H = 4096, V = 128256, bf16), two sequences (1024 rows) per chunk,
+    fixed reference log-probabilities; one step is one flce_kto_fwd_bwd.
+    FLOPs 6 N H V."""
+    import numpy as np
+    import torch
+    import datagen
+    import linear_cross_entropy_04_amd as fl
+
+    dev = torch.device("cuda:0")
+    S, T, H, V = KTO_SEQS, KTO_T, 4096, 128256
+    chunk_seqs = 2
+    pp = dict(beta=0.1, z0=0.0, lambda_d=1.0, lambda_u=1.0)
+    t0 = time.time()
+    inp, des_np, R_np = datagen.make_unpaired(S, T, H, V, "bf16", seed=20290)
+    log(f"unpaired batch {S} x {T} tokens drawn in {time.time() - t0:.1f}s")
+    N = S * T
+    X = torch.from_numpy(inp.X.view(np.int16)).to(dev).view(torch.bfloat16)
+    W = torch.from_numpy(inp.W.view(np.int16)).to(dev).view(torch.bfloat16)
+    y = torch.from_numpy(inp.labels).to(dev)
+    des = torch.from_numpy(des_np).to(dev)
+    R = torch.from_numpy(R_np).to(dev)
+    dX = torch.empty_like(X)
+    dW = torch.empty((V, H), dtype=torch.float32, device=dev)
+    nbytes = fl.flce_kto_workspace_bytes(S, T, H, V, fl.FLCE_BF16, chunk_seqs)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    if args.copy_reference_mib:
+        copy_reference(args.copy_reference_mib, dev)
+
+    def step():
+        return fl.flce_kto_fwd_bwd(X, W, y, S, -100, des, R, pp["beta"], pp["z0"],
+                                   pp["lambda_d"], pp["lambda_u"], chunk_seqs, dX, dW, ws,
+                                   stream=stream)
+
+    for _ in range(args.warmup):
+        loss = step()
+    torch.cuda.synchronize()
+    fl.flce_profile_enable(True)
+    fl.flce_profile_read()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for _ in range(args.steps):
+        loss = step()
+    torch.cuda.synchronize()
+    ms = 1e3 * (time.perf_counter() - t1) / args.steps
+    prof = fl.flce_profile_read()
+    fl.flce_profile_enable(False)
+    tflops = 6.0 * N * H * V / (ms * 1e-3) / 1e12
+    chunks = [chunk_seqs * T] * (S // chunk_seqs)
+    kernels, roof = kernel_summary(prof, args.steps, chunks, H, V, "llama3-8b-head-kto")
+    out = {
+        "metric": "KTO fused-linear preference loss fwd+bwd tokens/s, Llama-3-8B head",
+        "value": round(N / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded; X ~ N(0,1), W ~ N(0,0.02^2); per sequence T/8..T/2 prompt "
+                "and 0..T/4 padding tokens unscored, uniform response labels, half desirable, "
+                "reference sums around the head's expected log-probability)",
+        "config": {"workload": "llama3-8b-head-kto", "sequences": S, "T": T, "N": N, "H": H,
+                   "V": V, "chunk_seqs": chunk_seqs, **pp, "workspace_bytes": nbytes},
+        "tflops": round(tflops, 2), "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        "loss": loss, "kernels": kernels, "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        n_s = 8                                      # the first 8 sequences: 4096 rows
+        rows = np.arange(n_s * T)
+        t2 = time.perf_counter()
+        oracle.kto(inp.X_f64()[rows], inp.W_f64(), inp.labels[rows], n_s,
+                   des_np[:n_s].astype(bool), R_np[:n_s].astype(np.float64), -100, **pp)
+        dt = time.perf_counter() - t2
+        out["cpu_baseline"] = {"value": rows.size / dt, "unit": "tokens/s",
+                               "cores": _blas_threads(), "kind": "oracle",
+                               "seconds": round(dt, 3),
+                               "sample": f"the first {n_s} sequences ({rows.size} rows), fp64 "
+                                         "loss + dX + dW on the host"}
+    else:
+        out["cpu_baseline"] = None
+    log(f"kto: {ms:.3f} ms/step  {tflops:.1f} TFLOP/s  loss={loss:.6f}")
+    for name, k in kernels.items():
+        log(f"  {name:12s} {k}")
+    print(json.dumps(out), flush=True)
+
+
 def _blas_threads():
     try:
         from threadpoolctl import threadpool_info
@@ -351,12 +440,12 @@ def main():
     ap.add_argument("--chunk", type=int, default=None, help="chunk tokens (default: the workload's)")
     ap.add_argument("--cpu-sample-tokens", type=int, default=4096)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--op", choices=("flce", "ce", "orpo", "simpo", "cpo", "dpo"),
+    ap.add_argument("--op", choices=("flce", "ce", "orpo", "simpo", "cpo", "dpo", "kto"),
                     default="flce",
                     help="flce: the fused linear cross-entropy step (default); ce: cross-entropy "
                          "on given logits of the Llama-3-8B head's size; orpo, simpo, cpo, dpo: "
                          "a fused-linear preference loss on 8 pairs of 512-token sequences on "
-                         "the same head")
+                         "the same head; kto: the unpaired one on 16 such sequences")
     ap.add_argument("--copy-reference-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (a known-size "
                          "reference for hardware byte counters)")
@@ -372,6 +461,9 @@ def main():
         return
     if args.op in PAIR_PARAMS:
         bench_orpo(args)
+        return
+    if args.op == "kto":
+        bench_kto(args)
         return
 
     import numpy as np
