@@ -527,24 +527,24 @@ FLCE_API int flce_ce_fwd(const void *logits, const int64_t *labels, int64_t N, i
 namespace flce {
 namespace {
 
-constexpr int64_t kOrpoAutoRows = 4096;
+constexpr int64_t kPrefAutoRows = 4096;
 
-struct OrpoLayout {
+struct PairLayout {
   Plan p;                 // the fused pipeline for chunks of C = 2 k T rows
   int64_t k = 0;          // pairs per chunk
   size_t off_x = 0, off_lab = 0, off_lp = 0, off_w = 0, off_dx = 0, off_nll = 0, off_or = 0,
          off_clp = 0, off_rlp = 0, off_lor = 0, total = 0;
 };
 
-int orpo_check(int64_t B, int64_t T, int64_t H, int64_t V, int dtype) {
+int pair_check(int64_t B, int64_t T, int64_t H, int64_t V, int dtype) {
   if (B <= 0 || T <= 0) return FLCE_EINVAL;
   if (T > ((int64_t)1 << 29) || B > kMaxN / (2 * T)) return FLCE_EUNSUPPORTED;
   return check_sizes(2 * B * T, H, V, dtype);
 }
 
-void orpo_layout(int64_t B, int64_t T, int64_t H, int64_t V, int dtype, int64_t chunk_pairs,
-                 OrpoLayout *L) {
-  int64_t k = chunk_pairs > 0 ? chunk_pairs : kOrpoAutoRows / (2 * T);
+void pair_layout(int64_t B, int64_t T, int64_t H, int64_t V, int dtype, int64_t chunk_pairs,
+                 PairLayout *L) {
+  int64_t k = chunk_pairs > 0 ? chunk_pairs : kPrefAutoRows / (2 * T);
   k = std::max<int64_t>(1, std::min(k, B));
   const int64_t C = 2 * k * T;
   const size_t esz = dtype == FLCE_BF16 ? 2 : 4;
@@ -574,7 +574,7 @@ int run_pairs(bool bwd, int kind, const void *X, const void *W, const int64_t *l
               int64_t chunk_pairs, float *loss, float *nll, void *dX, float *dW,
               float *chosen_logp, float *rejected_logp, float *log_odds_ratio, void *workspace,
               size_t workspace_bytes, void *stream) {
-  int st = orpo_check(B, T, H, V, dtype);
+  int st = pair_check(B, T, H, V, dtype);
   if (st != FLCE_OK) return st;
   if (kind != kPairOrpo && kind != kPairSimpo && kind != kPairCpo && kind != kPairDpo)
     return FLCE_EINVAL;
@@ -590,8 +590,8 @@ int run_pairs(bool bwd, int kind, const void *X, const void *W, const int64_t *l
   if (dtype == FLCE_F32 && (misaligned(X, 4) || misaligned(W, 4) || (bwd && misaligned(dX, 4))))
     return FLCE_EINVAL;
   if (bwd && misaligned(dW, 4)) return FLCE_EINVAL;
-  OrpoLayout L;
-  orpo_layout(B, T, H, V, dtype, chunk_pairs, &L);
+  PairLayout L;
+  pair_layout(B, T, H, V, dtype, chunk_pairs, &L);
   if (workspace_bytes < L.total) return FLCE_EWORKSPACE;
 
   const Plan &p = L.p;
@@ -685,9 +685,9 @@ PairParams pair_params(int kind, float beta, float gamma, float alpha, const flo
 
 FLCE_API size_t flce_pair_workspace_bytes(int64_t n_pairs, int64_t T, int64_t H, int64_t V,
                                           int dtype, int64_t chunk_pairs) {
-  if (flce::orpo_check(n_pairs, T, H, V, dtype) != FLCE_OK) return 0;
-  flce::OrpoLayout L;
-  flce::orpo_layout(n_pairs, T, H, V, dtype, chunk_pairs, &L);
+  if (flce::pair_check(n_pairs, T, H, V, dtype) != FLCE_OK) return 0;
+  flce::PairLayout L;
+  flce::pair_layout(n_pairs, T, H, V, dtype, chunk_pairs, &L);
   return L.total;
 }
 
@@ -768,7 +768,7 @@ int kto_check(int64_t S, int64_t T, int64_t H, int64_t V, int dtype) {
 
 void kto_layout(int64_t S, int64_t T, int64_t H, int64_t V, int dtype, int64_t chunk_seqs,
                 KtoLayout *L) {
-  int64_t k = chunk_seqs > 0 ? chunk_seqs : kOrpoAutoRows / T;
+  int64_t k = chunk_seqs > 0 ? chunk_seqs : kPrefAutoRows / T;
   k = std::max<int64_t>(1, std::min(k, S));
   const int64_t C = k * T;
   make_plan(C, H, V, dtype, C, &L->p);
