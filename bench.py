@@ -525,6 +525,16 @@ def main():
     torch.cuda.synchronize()
     elapsed_noev = time.perf_counter() - t1
 
+    # the forward-only call (loss, no gradients) on the same workload
+    for _ in range(2):
+        fl.flce_fwd(X, W, y, -100, chunk, ws, stream=stream)
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    for _ in range(args.steps):
+        fl.flce_fwd(X, W, y, -100, chunk, ws, stream=stream)
+    torch.cuda.synchronize()
+    fwd_ms = 1e3 * (time.perf_counter() - t2) / args.steps
+
     ms = 1e3 * elapsed / args.steps
     flops = 6.0 * N * H * V
     tflops = flops / (ms * 1e-3) / 1e12
@@ -551,6 +561,7 @@ def main():
         "tflops": round(tflops, 2),
         "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
         "ms_per_step_without_events": round(1e3 * elapsed_noev / args.steps, 4),
+        "fwd_only_ms_per_step": round(fwd_ms, 4),
         "loss": loss,
         "kernels": kernels,
         "roofline": roof,

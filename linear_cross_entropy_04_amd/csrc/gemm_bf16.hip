@@ -683,49 +683,56 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_tile_kernel(
 }
 
 // ---------------------------------------------------------------- dlogits
-// One thread per 16-byte slot of Zp (one token, 8 consecutive vocabulary
-// columns), in memory order, so a wave reads and writes 1 KB contiguous and
-// its 64 lanes cover 32 consecutive tokens.  In place:
+// One workgroup per 16 KB block of Zp (256 tokens x 32 vocabulary columns),
+// four 16-byte slots per thread (one token, 8 consecutive vocabulary columns
+// each), in memory order: pass k of a wave covers 1 KB contiguous, and all
+// four loads are in flight before any arithmetic.  In place:
 // G = w_r (exp(Z - lse) - onehot(y)) on valid tokens, 0 on ignored tokens and
 // outside [0, c) x [0, V); w_r = wrow_c[r] if given, else sc->scale
 // (1 / N_valid for the mean loss).
+constexpr int kDlSlots = 4;
+
 __global__ __launch_bounds__(256) void dlogits_kernel(
-    uint16_t *__restrict__ Zp, int64_t nks_z, int c, int V, int64_t nslot,
+    uint16_t *__restrict__ Zp, int64_t nks_z, int c, int V,
     const float *__restrict__ lse_c, const int64_t *__restrict__ labels_c, int64_t ii,
     const float *__restrict__ wrow_c, const Scalars *__restrict__ sc) {
-  const int64_t u = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-  if (u >= nslot) return;
-  // u = ((rt * nks_z + ks) * 16 + f) * 64 + slot, slot = 32 h + (r % 32 ^ 4 h ^ 8 (f % 2))
-  const int sl = (int)(u & 63), f = (int)((u >> 6) & 15);
-  const int64_t blk = u >> 10;
+  // slot u = (blk * 16 + f) * 64 + sl of block blk = (rt, ks); thread t of the
+  // block takes f = t / 64 + 4 k, sl = t % 64: slot sl = 32 h + (r % 32 ^ 4 h ^ 8 (f % 2))
+  const int64_t blk = blockIdx.x;
   const int64_t rt = blk / nks_z, ks = blk - rt * nks_z;
-  const int h = sl >> 5;
-  const int r = (int)(rt * 256) + (f >> 1) * 32 + ((sl & 31) ^ (h << 2) ^ ((f & 1) << 3));
-  const int v0 = (int)(ks * 32) + (f & 1) * 16 + h * 8;
-  int64_t y = ii;
-  float l2 = 0.f, inv = 0.f;
-  if (r < c) {
-    y = labels_c[r];
-    l2 = lse_c[r] * kLog2e;
-    inv = wrow_c ? wrow_c[r] : sc->scale;
-  }
-  const bool valid = r < c && y != ii;
-  uint16_t *zu = Zp + (u << 3);
-  const u32x4 z = *(const u32x4 *)zu;
-  u32x4 g;
+  const int w = threadIdx.x >> 6, sl = threadIdx.x & 63, h = sl >> 5;
+  const int v0 = (int)(ks * 32) + (w & 1) * 16 + h * 8;
+  const int rr = ((sl & 31) ^ (h << 2) ^ ((w & 1) << 3));
+  uint16_t *zb = Zp + (blk << 13) + ((int64_t)threadIdx.x << 3);
+  u32x4 z[kDlSlots];
 #pragma unroll
-  for (int d = 0; d < 4; ++d) {
-    float fv[2];
+  for (int k = 0; k < kDlSlots; ++k) z[k] = *(const u32x4 *)(zb + (k << 11));
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      const int v = v0 + 2 * d + hh;
-      const float zz = hh ? bf16_hi(z[d]) : bf16_lo(z[d]);
-      const float e = __builtin_amdgcn_exp2f(zz * kLog2e - l2) - ((int64_t)v == y ? 1.f : 0.f);
-      fv[hh] = (valid && v < V) ? e * inv : 0.f;
+  for (int k = 0; k < kDlSlots; ++k) {
+    const int r = (int)(rt * 256) + ((w >> 1) + 2 * k) * 32 + rr;
+    int64_t y = ii;
+    float l2 = 0.f, inv = 0.f;
+    if (r < c) {
+      y = labels_c[r];
+      l2 = lse_c[r] * kLog2e;
+      inv = wrow_c ? wrow_c[r] : sc->scale;
     }
-    g[d] = pack_bf16x2(fv[0], fv[1]);
+    const bool valid = r < c && y != ii;
+    u32x4 g;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      float fv[2];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int v = v0 + 2 * d + hh;
+        const float zz = hh ? bf16_hi(z[k][d]) : bf16_lo(z[k][d]);
+        const float e = __builtin_amdgcn_exp2f(zz * kLog2e - l2) - ((int64_t)v == y ? 1.f : 0.f);
+        fv[hh] = (valid && v < V) ? e * inv : 0.f;
+      }
+      g[d] = pack_bf16x2(fv[0], fv[1]);
+    }
+    *(u32x4 *)(zb + (k << 11)) = g;
   }
-  *(u32x4 *)zu = g;
 }
 
 // ---------------------------------------------------------------- dX (split-K)
@@ -908,10 +915,11 @@ hipError_t launch_fwd_tile_bf16(const uint16_t *Wp, const uint16_t *Xp, int64_t 
 hipError_t launch_dlogits_bf16(uint16_t *Zp, int64_t nks_z, int c, int V, const float *lse_c,
                                const int64_t *labels_c, int64_t ii, const float *wrow_c,
                                const Scalars *sc, hipStream_t s) {
-  // 16-byte slots over the row tiles that cover [0, c), every slice of Zp
-  const int64_t nslot = (int64_t)((c + 255) / 256) * nks_z * 1024;
-  hipLaunchKernelGGL(dlogits_kernel, dim3((unsigned)((nslot + 255) / 256)), dim3(256), 0, s, Zp,
-                     nks_z, c, V, nslot, lse_c, labels_c, ii, wrow_c, sc);
+  // one workgroup per 16 KB block of the row tiles that cover [0, c), every slice of Zp
+  const int64_t nblk = (int64_t)((c + 255) / 256) * nks_z;
+  static_assert(kDlSlots * 256 * 16 == 16384, "a workgroup covers one block");
+  hipLaunchKernelGGL(dlogits_kernel, dim3((unsigned)nblk), dim3(256), 0, s, Zp, nks_z, c, V,
+                     lse_c, labels_c, ii, wrow_c, sc);
   return hipGetLastError();
 }
 
