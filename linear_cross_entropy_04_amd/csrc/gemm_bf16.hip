@@ -529,13 +529,14 @@ __device__ __forceinline__ void transpose8x8(const u32x4 (&in)[8], u32x4 (&out)[
 // With PLAIN the same loads also fill the untransposed packed matrix P (rows
 // R, nks_p column slices): the 64 source rows x 256 columns are the same two
 // 32-row groups of 8 consecutive P blocks, i.e. 8 pieces of 4 KB, so the
-// source is read once for both.
+// source is read once for both.  The two outputs take turns in one 32 KB LDS
+// buffer, which keeps several workgroups (and their loads) per CU.
 template <bool PLAIN>
 __global__ __launch_bounds__(256) void pack_t_kernel(const uint16_t *__restrict__ src, int R,
                                                     int K, uint16_t *__restrict__ PT,
                                                     int64_t nks_t, uint16_t *__restrict__ P,
                                                     int64_t nks_p) {
-  __shared__ __attribute__((aligned(1024))) char lds[PLAIN ? 65536 : 32768];
+  __shared__ __attribute__((aligned(1024))) char lds[32768];
   const int npair = (int)(nks_t >> 1);
   const int rt = blockIdx.x / npair;                  // row tile of PT = 256 source columns
   const int kp = blockIdx.x - rt * npair;             // pair of PT column slices = 64 source rows
@@ -547,18 +548,6 @@ __global__ __launch_bounds__(256) void pack_t_kernel(const uint16_t *__restrict_
   for (int i = 0; i < 8; ++i)
     in[i] = (r0 + i < R && c0 < K) ? *(const u32x4 *)(src + (int64_t)(r0 + i) * K + c0)
                                    : u32x4{0u, 0u, 0u, 0u};
-  if constexpr (PLAIN) {
-    // P piece (t % 32) / 4 (column slice), fragment (row group, column half)
-    const int kk = (c0 & 31);
-    char *lp = lds + 32768 + (((t & 31) >> 2) << 12);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = (t >> 5) * 8 + i;                 // source row within the 64
-      const int off = ((((r >> 5) << 1) + (kk >> 4)) << 10) +
-                      (pk_slot(r & 31, (kk >> 3) & 1, kk >> 4) << 4);
-      *(u32x4 *)(lp + off) = in[i];
-    }
-  }
   transpose8x8(in, out);
   const int k = (t >> 5) * 8;                         // PT column within the pair, 0..56
   const int kk = k & 31;
@@ -577,12 +566,24 @@ __global__ __launch_bounds__(256) void pack_t_kernel(const uint16_t *__restrict_
     *(u32x4 *)(dst + q * 8) = *(const u32x4 *)(lds + q * 16);
   }
   if constexpr (PLAIN) {
+    __syncthreads();                                  // every wave has copied PT out of LDS
+    // P piece (t % 32) / 4 (column slice), fragment (row group, column half)
+    const int kk = (c0 & 31);
+    char *lp = lds + (((t & 31) >> 2) << 12);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = (t >> 5) * 8 + i;                 // source row within the 64
+      const int off = ((((r >> 5) << 1) + (kk >> 4)) << 10) +
+                      (pk_slot(r & 31, (kk >> 3) & 1, kk >> 4) << 4);
+      *(u32x4 *)(lp + off) = in[i];
+    }
+    __syncthreads();
     // 64 source rows = row groups 2 (kp % 4), +1 of P's row tile kp / 4
     const int64_t rtp = kp >> 2;
     uint16_t *dp = P + ((rtp * nks_p + 8 * (int64_t)rt) << 13) + ((kp & 3) << 11);
 #pragma unroll
     for (int i = 0; i < 8; ++i)       // piece i: P block (rtp, 8 rt + i), 4 KB
-      *(u32x4 *)(dp + ((int64_t)i << 13) + t * 8) = *(const u32x4 *)(lds + 32768 + (i << 12) + t * 16);
+      *(u32x4 *)(dp + ((int64_t)i << 13) + t * 8) = *(const u32x4 *)(lds + (i << 12) + t * 16);
   }
 }
 
