@@ -446,6 +446,11 @@ def main():
                          "on given logits of the Llama-3-8B head's size; orpo, simpo, cpo, dpo: "
                          "a fused-linear preference loss on 8 pairs of 512-token sequences on "
                          "the same head; kto: the unpaired one on 16 such sequences")
+    ap.add_argument("--share", choices=("dp8", "tp8"), default=None,
+                    help="measure one GPU's share of the workload sharded over 8 GPUs: dp8 = "
+                         "its N/8 tokens with the whole head, tp8 = all tokens against its V/8 "
+                         "vocabulary rows (labels reduced modulo V/8, so the call is a valid "
+                         "loss on the shard; the work is the shard's)")
     ap.add_argument("--copy-reference-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (a known-size "
                          "reference for hardware byte counters)")
@@ -474,6 +479,8 @@ def main():
     dev = torch.device("cuda:0")
     t0 = time.time()
     inp = datagen.make(args.workload)
+    if args.share:
+        inp = datagen.share_of(inp, args.share)
     wl = inp.wl
     log(f"workload {wl.name}: N={wl.N} H={wl.H} V={wl.V} drawn in {time.time() - t0:.1f}s")
     N, H, V = wl.N, wl.H, wl.V
@@ -556,6 +563,7 @@ def main():
         "dtype": wl.dtype,
         "data": "synthetic (seeded; X ~ N(0,1), W ~ N(0,0.02^2), uniform labels, 5% ignored)",
         "config": {"workload": wl.name, "N": N, "H": H, "V": V, "chunk_tokens": C,
+                   "share_of_8_gpus": args.share,
                    "ignored_tokens": int((inp.labels == -100).sum()),
                    "peak_scratch_bytes": peak_scratch},
         "tflops": round(tflops, 2),

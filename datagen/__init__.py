@@ -278,6 +278,26 @@ def make_unpaired(n_seq: int, T: int, H: int, V: int, dtype: str = "bf16", seed:
     return Inputs(wl, X, W, y.reshape(-1), seed), des, R
 
 
+def share_of(inp: Inputs, share: str) -> Inputs:
+    """One GPU's share of a workload sharded over 8 GPUs: "dp8" keeps the
+    first N/8 tokens with the whole head; "tp8" keeps every token against the
+    first ceil(V/8) vocabulary rows, with labels reduced modulo that count so
+    that the call is a valid loss on the shard (its work is the shard's)."""
+    wl = inp.wl
+    if share == "dp8":
+        n = wl.N // 8
+        return dataclasses.replace(inp, wl=dataclasses.replace(wl, name=f"{wl.name}-dp8-share",
+                                                               N=n),
+                                   X=inp.X[:n], labels=inp.labels[:n].copy())
+    if share != "tp8":
+        raise ValueError(f"unknown share {share!r}")
+    v = (wl.V + 7) // 8
+    y = inp.labels.copy()
+    y[y != IGNORE_INDEX] %= v
+    return dataclasses.replace(inp, wl=dataclasses.replace(wl, name=f"{wl.name}-tp8-share", V=v),
+                               W=np.ascontiguousarray(inp.W[:v]), labels=y)
+
+
 def sample_rows(n_total: int, k: int, seed: int, must: tuple = ()) -> np.ndarray:
     """Seeded sorted sample of k distinct row indices, always holding ``must``."""
     rng = np.random.default_rng(seed)
