@@ -18,6 +18,11 @@
  * "Operações In-Place").  The result is exact up to floating-point rounding
  * (overview page, "Implementação Técnica").
  *
+ * Built on the same chunk pipeline: other reductions and per-token outputs
+ * (flce_fwd_bwd_ex), cross-entropy on given logits (flce_ce_*), and the
+ * fused-linear post-training losses of the overview page's list: ORPO, SimPO,
+ * CPO, DPO (flce_orpo_*, flce_pair_*) and KTO (flce_kto_*).
+ *
  * Conventions for every entry point:
  *   - All arrays are row-major and contiguous: X [N, H], W [V, H], dX [N, H],
  *     dW [V, H], labels [N].

@@ -8,7 +8,10 @@ The operation is the one the Liger Kernel pages call as
 ``loss_fn(weight, input, target)`` (project overview page, "Método de API de
 Baixo Nível"): the LM-head projection fused with cross-entropy over tokens
 whose target is not ``ignore_index`` -- their mean, their sum, or the
-per-token losses with an upstream gradient per token.
+per-token losses with an upstream gradient per token.  On the same kernels:
+cross-entropy on given logits (``cross_entropy``) and the fused-linear
+post-training losses the pages list (``orpo_loss``, ``preference_loss`` for
+ORPO / SimPO / CPO / DPO, ``kto_loss``, and their module forms).
 """
 from __future__ import annotations
 

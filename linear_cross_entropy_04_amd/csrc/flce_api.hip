@@ -14,6 +14,12 @@
 // Before the chunks a label pass counts N_valid and checks label ranges; after
 // them one kernel forms the mean loss, which returns to the host with the
 // label flag in the call's single stream synchronisation.
+//
+// The other entry points reuse the chunk forward and backward below: the
+// reductions and per-token outputs change only the weights of step 3;
+// cross-entropy on given logits runs its own row kernel; the preference
+// losses insert a per-pair (or per-sequence) step between steps 2 and 3 that
+// turns the chunk's log-probabilities into loss terms and per-token weights.
 #include <algorithm>
 #include <atomic>
 #include <cstring>
