@@ -451,6 +451,9 @@ def main():
                          "its N/8 tokens with the whole head, tp8 = all tokens against its V/8 "
                          "vocabulary rows (labels reduced modulo V/8, so the call is a valid "
                          "loss on the shard; the work is the shard's)")
+    ap.add_argument("--no-fwd-only", action="store_true",
+                    help="skip timing the forward-only call (keeps profiler traces to the "
+                         "fwd+bwd steps)")
     ap.add_argument("--copy-reference-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (a known-size "
                          "reference for hardware byte counters)")
@@ -533,14 +536,16 @@ def main():
     elapsed_noev = time.perf_counter() - t1
 
     # the forward-only call (loss, no gradients) on the same workload
-    for _ in range(2):
-        fl.flce_fwd(X, W, y, -100, chunk, ws, stream=stream)
-    torch.cuda.synchronize()
-    t2 = time.perf_counter()
-    for _ in range(args.steps):
-        fl.flce_fwd(X, W, y, -100, chunk, ws, stream=stream)
-    torch.cuda.synchronize()
-    fwd_ms = 1e3 * (time.perf_counter() - t2) / args.steps
+    fwd_ms = None
+    if not args.no_fwd_only:
+        for _ in range(2):
+            fl.flce_fwd(X, W, y, -100, chunk, ws, stream=stream)
+        torch.cuda.synchronize()
+        t2 = time.perf_counter()
+        for _ in range(args.steps):
+            fl.flce_fwd(X, W, y, -100, chunk, ws, stream=stream)
+        torch.cuda.synchronize()
+        fwd_ms = 1e3 * (time.perf_counter() - t2) / args.steps
 
     ms = 1e3 * elapsed / args.steps
     flops = 6.0 * N * H * V
@@ -569,7 +574,7 @@ def main():
         "tflops": round(tflops, 2),
         "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
         "ms_per_step_without_events": round(1e3 * elapsed_noev / args.steps, 4),
-        "fwd_only_ms_per_step": round(fwd_ms, 4),
+        "fwd_only_ms_per_step": round(fwd_ms, 4) if fwd_ms is not None else None,
         "loss": loss,
         "kernels": kernels,
         "roofline": roof,
