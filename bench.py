@@ -88,22 +88,34 @@ def counter_traffic(kernel, workload):
     return float(v) if v else None
 
 
-def cpu_baseline(inp, n_tok):
-    import numpy as np
-    import oracle
+def host_info():
+    """Threads the host BLAS uses, the process's CPU affinity count and the
+    BLAS library, for the oracle baselines."""
+    info = {"cores": os.cpu_count() or 1, "affinity_cores": None, "blas": None}
+    try:
+        info["affinity_cores"] = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):    # pragma: no cover - informational only
+        pass
     try:
         from threadpoolctl import threadpool_info
-        threads = max((i.get("num_threads", 1) for i in threadpool_info()
-                       if i.get("user_api") == "blas"), default=1)
+        blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if blas:
+            info["cores"] = max(int(i.get("num_threads", 1)) for i in blas)
+            info["blas"] = blas[0].get("internal_api")
     except Exception:       # pragma: no cover - informational only
-        threads = os.cpu_count() or 1
+        pass
+    return info
+
+
+def cpu_baseline(inp, n_tok):
+    import oracle
     X = inp.X_f64()[:n_tok]
     W = inp.W_f64()
     y = inp.labels[:n_tok]
     t0 = time.perf_counter()
     oracle.flce(X, W, y)
     dt = time.perf_counter() - t0
-    return {"value": n_tok / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+    return {"value": n_tok / dt, "unit": "tokens/s", "kind": "oracle", **host_info(),
             "seconds": round(dt, 3),
             "sample": f"first {n_tok} tokens of the {inp.wl.name} workload (H={inp.wl.H}, "
                       f"V={inp.wl.V}), fp64 loss + dX + dW on the host"}
@@ -219,7 +231,7 @@ def bench_ce(args):
         oracle.cross_entropy(Z64, y_np[:n_tok])
         dt = time.perf_counter() - t2
         out["cpu_baseline"] = {"value": n_tok / dt, "unit": "tokens/s",
-                               "cores": _blas_threads(), "kind": "oracle",
+                               "kind": "oracle", **host_info(),
                                "seconds": round(dt, 3),
                                "sample": f"first {n_tok} rows of the logits, fp64 loss + gradient"}
     else:
@@ -321,7 +333,7 @@ def bench_orpo(args):
                           **pp)
         dt = time.perf_counter() - t2
         out["cpu_baseline"] = {"value": rows.size / dt, "unit": "tokens/s",
-                               "cores": _blas_threads(), "kind": "oracle",
+                               "kind": "oracle", **host_info(),
                                "seconds": round(dt, 3),
                                "sample": f"the first {n_pairs} pairs ({rows.size} rows), fp64 "
                                          "loss + dX + dW on the host"}
@@ -410,7 +422,7 @@ def bench_kto(args):
                    des_np[:n_s].astype(bool), R_np[:n_s].astype(np.float64), -100, **pp)
         dt = time.perf_counter() - t2
         out["cpu_baseline"] = {"value": rows.size / dt, "unit": "tokens/s",
-                               "cores": _blas_threads(), "kind": "oracle",
+                               "kind": "oracle", **host_info(),
                                "seconds": round(dt, 3),
                                "sample": f"the first {n_s} sequences ({rows.size} rows), fp64 "
                                          "loss + dX + dW on the host"}
@@ -420,15 +432,6 @@ def bench_kto(args):
     for name, k in kernels.items():
         log(f"  {name:12s} {k}")
     print(json.dumps(out), flush=True)
-
-
-def _blas_threads():
-    try:
-        from threadpoolctl import threadpool_info
-        return max((i.get("num_threads", 1) for i in threadpool_info()
-                    if i.get("user_api") == "blas"), default=1)
-    except Exception:       # pragma: no cover - informational only
-        return os.cpu_count() or 1
 
 
 def main():
