@@ -220,6 +220,14 @@ def make_logits(N: int, V: int, dtype: str = "bf16", seed: int = 1, std: float =
     return (f32_to_bf16_bits(Z) if dtype == "bf16" else Z), y
 
 
+def _prompt_lengths(rng: np.random.Generator, T: int, n: int) -> np.ndarray:
+    """U{ceil(T/8) .. floor(T/2)} unscored prompt tokens; none when T < 2."""
+    lo, hi = -(-T // 8), T // 2
+    if hi < lo:
+        return np.zeros(n, dtype=np.int64)
+    return rng.integers(lo, hi + 1, size=n)
+
+
 def make_pairs(n_pairs: int, T: int, H: int, V: int, dtype: str = "bf16", seed: int = 1,
                w_std: float = 0.02) -> Inputs:
     """Preference batch: 2 n_pairs sequences of T tokens as rows of X (the
@@ -238,7 +246,7 @@ def make_pairs(n_pairs: int, T: int, H: int, V: int, dtype: str = "bf16", seed: 
     X = _draw_X(np.random.default_rng(s_x), N, H, "normal", dtype)
     W = _draw_W(s_w, V, H, w_std, dtype)
     y = _draw_labels(np.random.default_rng(s_y), N, V, "uniform", 0.0).reshape(2 * n_pairs, T)
-    P = np.random.default_rng(s_p).integers(-(-T // 8), T // 2 + 1, size=n_pairs)
+    P = _prompt_lengths(np.random.default_rng(s_p), T, n_pairs)
     D = np.random.default_rng(s_d).integers(0, T // 4 + 1, size=2 * n_pairs)
     for s_ in range(2 * n_pairs):
         y[s_, :P[s_ % n_pairs]] = IGNORE_INDEX
@@ -264,7 +272,7 @@ def make_unpaired(n_seq: int, T: int, H: int, V: int, dtype: str = "bf16", seed:
     X = _draw_X(np.random.default_rng(s_x), N, H, "normal", dtype)
     W = _draw_W(s_w, V, H, w_std, dtype)
     y = _draw_labels(np.random.default_rng(s_y), N, V, "uniform", 0.0).reshape(n_seq, T)
-    P = np.random.default_rng(s_p).integers(-(-T // 8), T // 2 + 1, size=n_seq)
+    P = _prompt_lengths(np.random.default_rng(s_p), T, n_seq)
     D = np.random.default_rng(s_d).integers(0, T // 4 + 1, size=n_seq)
     for s_ in range(n_seq):
         y[s_, :P[s_]] = IGNORE_INDEX

@@ -135,3 +135,25 @@ def test_kto_saturated_sigmoid():
     assert r.loss > 0.0
     check_loss(out["loss"], r.loss, "f32")
     check_grad(out["dW_t"].double().cpu().numpy(), r.dW, "f32", "dW")
+
+
+def test_kto_degenerate_shapes():
+    """One sequence, one token per sequence, more sequences per chunk than
+    sequences, and a sequence with no scored token (its reward is -R)."""
+    S, T, H, V = 3, 1, 64, 300
+    inp, des, R = datagen.make_unpaired(S, T, H, V, "f32", seed=91)
+    inp.labels[:] = np.random.default_rng(2).integers(0, V, S * T)
+    inp.labels[1] = II
+    out = _run(inp, des, R, S, 7)
+    r = oracle.kto(inp.X_f64(), inp.W_f64(), inp.labels, S, des.astype(bool), R.astype(np.float64),
+                   II, **P)
+    check_loss(out["loss"], r.loss, "f32")
+    _check_seq(out, r, "f32")
+    check_grad(out["dW_t"].double().cpu().numpy(), r.dW, "f32", "dW")
+    assert np.all(out["dX_t"][1].cpu().numpy() == 0.0)
+    one, d1, R1 = datagen.make_unpaired(1, 40, H, V, "bf16", seed=92)
+    o1 = _run(one, d1, R1, 1, 0)
+    r1 = oracle.kto(one.X_f64(), one.W_f64(), one.labels, 1, d1.astype(bool), R1.astype(np.float64),
+                    II, **P)
+    check_loss(o1["loss"], r1.loss, "bf16")
+    check_grad(o1["dW_t"].double().cpu().numpy(), r1.dW, "bf16", "dW")

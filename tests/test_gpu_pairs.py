@@ -140,3 +140,19 @@ def test_pair_modules(kind):
     check_loss(float(loss), r.loss, "f32")
     check_grad(Xg.grad.reshape(-1, H).double().cpu().numpy(), 0.5 * r.dX, "f32", "dX")
     check_grad(Wg.grad.double().cpu().numpy(), 0.5 * r.dW, "f32", "dW")
+
+
+def test_pair_degenerate_shapes():
+    """T = 1 (one token per sequence), more pairs per chunk than pairs, and a
+    batch with no scored token (every pair empty: loss 0, gradients 0)."""
+    inp = datagen.make_pairs(5, 1, 64, 300, "f32", seed=81)
+    inp.labels[:] = np.random.default_rng(1).integers(0, 300, inp.labels.size)
+    for kind in ("orpo", "simpo", "cpo"):
+        out = _run(kind, inp, 5, 9)
+        _check(out, _oracle(kind, inp, 5), kind, "f32")
+    empty = datagen.make_pairs(3, 16, 64, 300, "bf16", seed=82)
+    empty.labels[:] = II
+    out = _run("orpo", empty, 3, 2)
+    r = _oracle("orpo", empty, 3)
+    assert out["loss"] == 0.0 and r.loss == 0.0
+    assert np.all(out["dX"] == 0.0) and np.all(out["dW"] == 0.0)
