@@ -78,8 +78,8 @@ typedef enum {
  * logits/dlogits [C, V], per-vocab-tile log-sum-exp partials, per-token
  * statistics, and the split-K partial sums of dX).  chunk_tokens <= 0 means
  * "auto" (as chosen by flce_plan with the default budget); chunk_tokens > N is
- * clamped to N.  Returns 0 for invalid sizes or dtype.  Host only; no device
- * call.
+ * clamped to N, and any chunk to at most 2^30 tokens.  Returns 0 for invalid
+ * sizes or dtype.  Host only; no device call.
  */
 size_t flce_workspace_bytes(int64_t N, int64_t H, int64_t V, int dtype, int64_t chunk_tokens);
 
@@ -218,7 +218,7 @@ int flce_ce_fwd(const void *logits, const int64_t *labels, int64_t N, int64_t V,
  *   beta       weight of the odds-ratio term
  *   chunk_pairs  pairs per chunk (a chunk holds both sequences of each of its
  *              pairs: 2 chunk_pairs T rows); <= 0: the largest count with at
- *              most 4096 rows (at least 1)
+ *              most 4096 rows (at least 1); at most n_pairs and 2^30 rows
  *   loss, nll  host float (nll may be NULL)
  *   dX         device [2 n_pairs T, H] (dtype), overwritten; dW device [V, H] fp32, overwritten
  *   chosen_logp, rejected_logp, log_odds_ratio   device [n_pairs] fp32 or NULL
@@ -287,6 +287,7 @@ int flce_pair_fwd(int kind, const void *X, const void *W, const int64_t *labels,
  *   desirable  device [n_seq] int32, nonzero marks a desirable sequence
  *   ref_logp   device [n_seq] fp32, R (required)
  *   chunk_seqs sequences per chunk; <= 0: the largest count with at most 4096 rows
+ *              (at least 1); at most n_seq and 2^30 rows
  *   logp, reward  device [n_seq] fp32 or NULL: S and r
  * Other arguments, alignment and errors as for flce_orpo_fwd_bwd.
  */

@@ -45,6 +45,8 @@ inline int64_t round_up(int64_t a, int64_t b) { return cdiv(a, b) * b; }
 constexpr int64_t kMaxV = 8000000;
 constexpr int64_t kMaxH = 1 << 20;
 constexpr int64_t kMaxN = (int64_t)1 << 40;
+// Kernels index a chunk's tokens with 32-bit integers.
+constexpr int64_t kMaxChunk = (int64_t)1 << 30;
 
 int check_sizes(int64_t N, int64_t H, int64_t V, int dtype) {
   if (dtype != FLCE_F32 && dtype != FLCE_BF16) return FLCE_EINVAL;
@@ -61,7 +63,7 @@ int check_sizes(int64_t N, int64_t H, int64_t V, int dtype) {
 int64_t auto_chunk(int64_t N, int64_t H, int64_t V, int dtype, size_t budget) {
   if (N <= 0) return 0;
   int64_t best = -1;
-  for (int64_t C = 256;; C *= 2) {
+  for (int64_t C = 256; C <= kMaxChunk; C *= 2) {
     const int64_t Cc = std::min(C, N);
     Plan p;
     make_plan(N, H, V, dtype, Cc, &p);
@@ -76,7 +78,7 @@ int64_t resolve_chunk(int64_t N, int64_t H, int64_t V, int dtype, int64_t req, s
                       bool *fits) {
   *fits = true;
   if (N <= 0) return 0;
-  if (req > 0) return std::min(req, N);
+  if (req > 0) return std::min(std::min(req, N), kMaxChunk);
   const int64_t c = auto_chunk(N, H, V, dtype, budget ? budget : FLCE_DEFAULT_SCRATCH_BUDGET);
   if (c > 0) return c;
   *fits = false;
@@ -551,7 +553,7 @@ int pair_check(int64_t B, int64_t T, int64_t H, int64_t V, int dtype) {
 void pair_layout(int64_t B, int64_t T, int64_t H, int64_t V, int dtype, int64_t chunk_pairs,
                  PairLayout *L) {
   int64_t k = chunk_pairs > 0 ? chunk_pairs : kPrefAutoRows / (2 * T);
-  k = std::max<int64_t>(1, std::min(k, B));
+  k = std::max<int64_t>(1, std::min({k, B, kMaxChunk / (2 * T)}));
   const int64_t C = 2 * k * T;
   const size_t esz = dtype == FLCE_BF16 ? 2 : 4;
   make_plan(C, H, V, dtype, C, &L->p);       // its per-token loss array holds one chunk
@@ -775,7 +777,7 @@ int kto_check(int64_t S, int64_t T, int64_t H, int64_t V, int dtype) {
 void kto_layout(int64_t S, int64_t T, int64_t H, int64_t V, int dtype, int64_t chunk_seqs,
                 KtoLayout *L) {
   int64_t k = chunk_seqs > 0 ? chunk_seqs : kPrefAutoRows / T;
-  k = std::max<int64_t>(1, std::min(k, S));
+  k = std::max<int64_t>(1, std::min({k, S, kMaxChunk / T}));
   const int64_t C = k * T;
   make_plan(C, H, V, dtype, C, &L->p);
   L->k = k;

@@ -210,6 +210,11 @@ def test_plan_auto_and_explicit():
             assert nxt - _wp_bytes(4096, 128256) > budget
     st, c, peak = fl.flce_plan(0, 64, 100, fl.FLCE_BF16)
     assert st == fl.FLCE_OK and c == 0 and peak > 0
+    # kernels index a chunk's tokens with 32-bit integers: chunks stop at 2^30
+    st, c, _ = fl.flce_plan(1 << 33, 8, 1, fl.FLCE_BF16, chunk_tokens=1 << 32)
+    assert st == fl.FLCE_OK and c == 1 << 30
+    st, c, _ = fl.flce_plan(1 << 33, 8, 1, fl.FLCE_BF16, scratch_budget_bytes=1 << 50)
+    assert st == fl.FLCE_OK and c == 1 << 30
 
 
 def test_binding_has_no_cpu_fallback():
