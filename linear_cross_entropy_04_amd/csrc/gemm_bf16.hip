@@ -805,7 +805,10 @@ __global__ void dx_reduce_kernel(const float *__restrict__ dxp, int splitk, int 
 // The epilogue goes through LDS in two halves of 128 rows (BN fp32 per row)
 // so that dW is read and written in row-contiguous 16-byte pieces: the waves
 // holding a half write their accumulators, then every thread moves its
-// pieces, with all of its loads of the current dW in flight before the adds.
+// pieces.  A thread's loads of the current dW for a half are issued before
+// the accumulators of that half reach LDS (for the second half, right after
+// the first half's stores), so their latency overlaps the staging; the
+// barriers wait for LDS only, not for these loads.
 // 128-byte column blocks of an LDS row are XOR-swizzled by row bit 2 so the
 // two rows a write instruction covers use both halves of the banks.
 template <int BN>
@@ -834,6 +837,23 @@ __global__ __launch_bounds__(NTHREADS, OCC) void dw_kernel(
   constexpr int RPP = NTHREADS / TPR;       // rows per pass of the workgroup
   constexpr int NQ = 128 / RPP;             // pieces per thread per half
   static_assert(T::BM == 256 && T::LDS >= 128 * T::BN * 4, "epilogue half tile must fit in LDS");
+  // thread t takes piece t % TPR of rows t / TPR + RPP q of each half
+  const int col = (threadIdx.x % TPR) * 4;
+  const int h = n0 + col;
+  const int rb = threadIdx.x / TPR;
+  // dW is touched once per chunk: non-temporal accesses keep it from
+  // evicting the G and X strips that the next tiles reuse from L2
+  f32x4 old[NQ];
+  auto load_old = [&](int half) {
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const int v = m0 + half * 128 + rb + RPP * q;
+      const bool ok = v < V && h < H;            // H % 8 == 0: a started piece fits
+      old[q] = (accumulate && ok) ? __builtin_nontemporal_load((const f32x4 *)(dW + (int64_t)v * H + h))
+                                  : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  load_old(0);
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
     if (wm == half) {
@@ -844,25 +864,13 @@ __global__ __launch_bounds__(NTHREADS, OCC) void dw_kernel(
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
             const int r = 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-            const int col = wn * T::WN + 32 * j + (lane & 31);
-            *(float *)(smem + dwst_off<T::BN>(r, col)) = acc[i][j][e];
+            const int cc = wn * T::WN + 32 * j + (lane & 31);
+            *(float *)(smem + dwst_off<T::BN>(r, cc)) = acc[i][j][e];
           }
     }
-    __syncthreads();
-    // thread t takes piece t % TPR of rows t / TPR + RPP q
-    const int col = (threadIdx.x % TPR) * 4;
-    const int h = n0 + col;
-    const int rb = threadIdx.x / TPR;
-    // dW is touched once per chunk: non-temporal accesses keep it from
-    // evicting the G and X strips that the next tiles reuse from L2
-    f32x4 old[NQ];
-#pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-      const int v = m0 + half * 128 + rb + RPP * q;
-      const bool ok = v < V && h < H;            // H % 8 == 0: a started piece fits
-      old[q] = (accumulate && ok) ? __builtin_nontemporal_load((const f32x4 *)(dW + (int64_t)v * H + h))
-                                  : f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+    // the half is in LDS (a fence-free barrier: the loads stay in flight)
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    bar();
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
       const int r = rb + RPP * q;
@@ -872,7 +880,10 @@ __global__ __launch_bounds__(NTHREADS, OCC) void dw_kernel(
         __builtin_nontemporal_store(old[q] + add, (f32x4 *)(dW + (int64_t)v * H + h));
       }
     }
-    __syncthreads();
+    if (half == 0) load_old(1);
+    // every thread has read its pieces before the next half overwrites LDS
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    bar();
   }
 }
 
