@@ -62,9 +62,14 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 enum Kind { PACKED = 0, PACKED_T = 1 };
 
-// 1 KB of zeros: the source of the copies a pipeline issues past its last
-// slice, so that every iteration issues the same copies.
-__device__ const uint4 g_zero_kb[64] = {};
+typedef __attribute__((address_space(3))) void lds_void;
+
+// LDS byte address of a pointer into __shared__ memory, made wave-uniform so
+// that the copies' destinations are computed in scalar registers.
+__device__ __forceinline__ uint32_t lds_addr(const char *p) {
+  return __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)p);
+}
 
 // ---------------------------------------------------------------- packed layout
 // 16-byte slot of row r32 = r % 32, column half h = (k / 8) % 2 and fragment
@@ -128,12 +133,13 @@ struct Op {
 };
 
 // Copy k-slice [k0, k0 + 32) (relative to the range) of an operand tile of
-// ROWS rows into LDS: ROWS / 16 pieces of 1 KB, piece b at tile + 1 KB b.
-// PACKED_T pieces 2q, 2q+1 are the two fragments of operand rows 32q..32q+31.
+// ROWS rows into LDS: ROWS / 16 pieces of 1 KB, piece b at LDS byte address
+// tile + 1 KB b.  PACKED_T pieces 2q, 2q+1 are the two fragments of operand
+// rows 32q..32q+31.  Only the source's lane offset is per lane.
 template <int KIND, int ROWS>
-__device__ __forceinline__ void issue_tile(const Op &op, int k0, char *tile, bool live) {
+__device__ __forceinline__ void issue_tile(const Op &op, int k0, uint32_t tile) {
   constexpr int N = ROWS * BK * 2 / 4096;
-  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), l = threadIdx.x & 63;
   const uint16_t *base;
   if constexpr (KIND == PACKED) {
     base = op.p + (int64_t)(k0 >> 5) * 8192;
@@ -149,8 +155,7 @@ __device__ __forceinline__ void issue_tile(const Op &op, int k0, char *tile, boo
       src = base + blk * 512 + l * 8;
     else
       src = base + (blk >> 1) * 8192 + (blk & 1) * 512 + l * 8;
-    if (!live) src = (const uint16_t *)g_zero_kb + l * 8;
-    __builtin_amdgcn_global_load_lds(src, tile + blk * 1024, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(src, (lds_void *)(uintptr_t)(tile + blk * 1024), 16, 0, 0);
   }
 }
 
@@ -223,15 +228,16 @@ __device__ __forceinline__ void mfma_block(const bf16x8 (&fa)[T::MI], const bf16
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
 }
 
-// Copies of slice `step`; past the last slice (step >= nk) they read zeros
-// into a ring slot that is not read again.
+// Copies of slice `step` into the ring slot at LDS byte address lds0 +
+// (step % STAGES) slots; past the last slice (step >= nk) they copy the last
+// slice again (still in cache) into a slot that is not read again.
 template <class T>
 __device__ __forceinline__ void issue_stage(const Op &a, const Op &b, int step, int nk,
-                                            char *smem) {
-  char *st = smem + (step % T::STAGES) * T::STAGE_BYTES;
-  const bool live = step < nk;
-  issue_tile<T::KA, T::BM>(a, live ? step * BK : 0, st, live);
-  issue_tile<T::KB, T::BN>(b, live ? step * BK : 0, st + T::A_BYTES, live);
+                                            uint32_t lds0) {
+  const uint32_t st = lds0 + (uint32_t)((step % T::STAGES) * T::STAGE_BYTES);
+  const int k0 = (step < nk ? step : nk - 1) * BK;
+  issue_tile<T::KA, T::BM>(a, k0, st);
+  issue_tile<T::KB, T::BN>(b, k0, st + T::A_BYTES);
 }
 
 // Instruction-group order for the scheduler (sched_group_barrier masks:
@@ -271,7 +277,7 @@ __device__ __forceinline__ void order_second_half() {
 // MFMAs of slice t's second half-step run, and the barrier itself waits with
 // MFMAs in flight.  Slice t+STAGES-1 is copied into the buffer of slice t-1,
 // whose reads every wave finished before that barrier.  Every iteration
-// issues one slice of copies (zeros past the end), so the wait is always for
+// issues one slice of copies (the last slice again past the end), so the wait is always for
 // all but the newest STAGES-3 slices, and the last slice is peeled: the loop
 // body is one straight path.  Packed operands carry zero padding up to whole
 // slices, so no copy needs a bounds check.
@@ -280,8 +286,9 @@ __device__ __forceinline__ void mainloop(const Op &a, const Op &b, int klen, cha
                                          f32x16 (&acc)[T::MI][T::NI]) {
   const int nk = (klen + BK - 1) / BK;
   if (nk > 0) {
+    const uint32_t lds0 = lds_addr(smem);
 #pragma unroll
-    for (int s = 0; s < T::STAGES - 1; ++s) issue_stage<T>(a, b, s, nk, smem);
+    for (int s = 0; s < T::STAGES - 1; ++s) issue_stage<T>(a, b, s, nk, lds0);
     wait_vm<(T::STAGES - 2) * T::NPER>();
     bar();
     bf16x8 fa0[T::MI], fb0[T::NI], fa1[T::MI], fb1[T::NI];
@@ -295,7 +302,7 @@ __device__ __forceinline__ void mainloop(const Op &a, const Op &b, int klen, cha
       wait_vm<(T::STAGES - 3) * T::NPER>();
       bar();
       load_frags<T>(smem + ((t + 1) % T::STAGES) * T::STAGE_BYTES, 0, fa0, fb0);
-      issue_stage<T>(a, b, t + T::STAGES - 1, nk, smem);
+      issue_stage<T>(a, b, t + T::STAGES - 1, nk, lds0);
       mfma_block<T>(fa1, fb1, acc);
       order_second_half<T>();
     }
@@ -323,42 +330,64 @@ struct TrFrag {
   i16x4 lo, hi;
 };
 
-__device__ __forceinline__ void tr_read(i16x4 &dst, const char *p) {
-  const uint32_t a = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)p;
-  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(dst) : "v"(a));
+// Compile-time loop: f(ic<B>{}), ..., f(ic<E - 1>{}), so that loop indices
+// can select immediates.
+template <int V>
+struct ic {
+  static constexpr int value = V;
+};
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F &&f) {
+  if constexpr (B < E) {
+    f(ic<B>{});
+    static_for<B + 1, E>(f);
+  }
 }
 
-// LDS addresses of the two transposing reads of this lane for the fragment
-// of operand rows r0..r0+31, half-step kk (see frag<PACKED_T>).
-__device__ __forceinline__ void tr_addrs(const char *tile, int r0, int kk, const char *&lo,
-                                         const char *&hi) {
+// ds_read_b64_tr_b16 from LDS byte address a + IMM.
+template <int IMM>
+__device__ __forceinline__ void tr_read(i16x4 &dst, uint32_t a) {
+  static_assert(IMM >= 0 && IMM < 65536, "LDS instruction offset range");
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(dst) : "v"(a), "i"(IMM));
+}
+
+// Byte offsets, within a slice, of this lane's two transposing reads for the
+// fragment of operand rows r0..r0+31, half-step kk (see frag<PACKED_T>).
+// For the fragments r0 + 32 i of one wave and the two half-steps they differ
+// from those of (r0, 0) by exactly 2048 i + 256 kk in every lane (fragment
+// r/32 moves by two 1 KB pieces; k + 16 flips bit 4 of the slot, which no XOR
+// term touches), so a wave keeps one address per read half and operand and
+// reaches every read through the instruction's immediate offset.
+__device__ __forceinline__ void tr_offsets(int r0, int kk, uint32_t &lo, uint32_t &hi) {
   const int l = threadIdx.x & 63;
   const int g = l >> 4, j = l & 15;
   const int r = r0 + ((g & 1) << 4) + ((j & 3) << 2);
   const int k = kk * 16 + ((g >> 1) << 3) + (j >> 2);
   const int h = (r >> 3) & 1, f = (r >> 4) & 1;
-  const char *p = tile + ((((r >> 5) << 1) + f) << 10) + ((r & 7) << 1);
-  lo = p + (pk_slot(k, h, f) << 4);
-  hi = p + (pk_slot(k + 4, h, f) << 4);
+  const int p = ((((r >> 5) << 1) + f) << 10) + ((r & 7) << 1);
+  lo = (uint32_t)(p + (pk_slot(k, h, f) << 4));
+  hi = (uint32_t)(p + (pk_slot(k + 4, h, f) << 4));
 }
 
-// Read q (0 .. 2 (MI + NI) - 1) of a half-step: fragment q/2 (A fragments
+// LDS addresses of this lane's reads of fragment 0, half-step 0, in one stage.
+struct TrBase {
+  uint32_t alo, ahi, blo, bhi;
+};
+
+// Read Q (0 .. 2 (MI + NI) - 1) of half-step KK: fragment Q/2 (A fragments
 // first), low or high half.
-template <class T>
-__device__ __forceinline__ void tr_issue(const char *sa, const char *sb, int kk, int q,
-                                         TrFrag (&fa)[T::MI], TrFrag (&fb)[T::NI]) {
-  const int w = threadIdx.x >> 6;
-  const int wm = w >> 1, wn = w & 1;
-  const int fi = q >> 1;
-  const char *lo, *hi;
-  if (fi < T::MI) {
-    tr_addrs(sa, wm * T::WM + 32 * fi, kk, lo, hi);
-    if (q & 1) tr_read(fa[fi].hi, hi);
-    else tr_read(fa[fi].lo, lo);
+template <class T, int KK, int Q>
+__device__ __forceinline__ void tr_issue(const TrBase &b, TrFrag (&fa)[T::MI],
+                                         TrFrag (&fb)[T::NI]) {
+  constexpr int fi = Q >> 1;
+  if constexpr (fi < T::MI) {
+    constexpr int imm = 2048 * fi + 256 * KK;
+    if constexpr (Q & 1) tr_read<imm>(fa[fi].hi, b.ahi);
+    else tr_read<imm>(fa[fi].lo, b.alo);
   } else {
-    tr_addrs(sb, wn * T::WN + 32 * (fi - T::MI), kk, lo, hi);
-    if (q & 1) tr_read(fb[fi - T::MI].hi, hi);
-    else tr_read(fb[fi - T::MI].lo, lo);
+    constexpr int imm = 2048 * (fi - T::MI) + 256 * KK;
+    if constexpr (Q & 1) tr_read<imm>(fb[fi - T::MI].hi, b.bhi);
+    else tr_read<imm>(fb[fi - T::MI].lo, b.blo);
   }
 }
 
@@ -396,26 +425,40 @@ __device__ __forceinline__ void mainloop_tt(const Op &a, const Op &b, int klen, 
   constexpr int R = 2 * (T::MI + T::NI);       // transposing reads per half-step
   const int nk = (klen + BK - 1) / BK;
   if (nk > 0) {
+    const int w = threadIdx.x >> 6;
+    const int wm = w >> 1, wn = w & 1;
+    const uint32_t lds0 = lds_addr(smem);
+    TrBase b0;
+    tr_offsets(wm * T::WM, 0, b0.alo, b0.ahi);
+    tr_offsets(wn * T::WN, 0, b0.blo, b0.bhi);
+    b0.alo += lds0;
+    b0.ahi += lds0;
+    b0.blo += lds0 + T::A_BYTES;
+    b0.bhi += lds0 + T::A_BYTES;
+    auto stage_base = [&](int stage) {
+      const uint32_t o = (uint32_t)(stage * T::STAGE_BYTES);
+      return TrBase{b0.alo + o, b0.ahi + o, b0.blo + o, b0.bhi + o};
+    };
 #pragma unroll
-    for (int s = 0; s < T::STAGES - 1; ++s) issue_stage<T>(a, b, s, nk, smem);
+    for (int s = 0; s < T::STAGES - 1; ++s) issue_stage<T>(a, b, s, nk, lds0);
     wait_vm<(T::STAGES - 2) * T::NPER>();
     bar();
     TrFrag fa0[T::MI], fb0[T::NI], fa1[T::MI], fb1[T::NI];
-#pragma unroll
-    for (int q = 0; q < R; ++q) tr_issue<T>(smem, smem + T::A_BYTES, 0, q, fa0, fb0);
+    TrBase cur = b0;                             // the stage of slice t
+    int st = 0;
+    static_for<0, R>([&](auto q) { tr_issue<T, 0, decltype(q)::value>(cur, fa0, fb0); });
     // the last slice is peeled so that the loop body is one straight path
     for (int t = 0; t < nk - 1; ++t) {
-      const char *st = smem + (t % T::STAGES) * T::STAGE_BYTES;
-      const char *sn = smem + ((t + 1) % T::STAGES) * T::STAGE_BYTES;
+      const int sn = st + 1 == T::STAGES ? 0 : st + 1;
+      const TrBase nxt = stage_base(sn);
       tr_wait<T>(fa0, fb0);
       // first half-step; the reads of the second go out between its MFMAs
-#pragma unroll
-      for (int i = 0; i < M; ++i) {
+      static_for<0, M>([&](auto ii) {
+        constexpr int i = decltype(ii)::value;
         tr_mfma<T>(i, fa0, fb0, acc);
-#pragma unroll
-        for (int q = i * R / M; q < (i + 1) * R / M; ++q)
-          tr_issue<T>(st, st + T::A_BYTES, 1, q, fa1, fb1);
-      }
+        static_for<i * R / M, (i + 1) * R / M>(
+            [&](auto q) { tr_issue<T, 1, decltype(q)::value>(cur, fa1, fb1); });
+      });
       // slice t+1 must have landed; slices t+2 .. t+STAGES-2 may stay in flight
       wait_vm<(T::STAGES - 3) * T::NPER>();
       bar();
@@ -423,27 +466,25 @@ __device__ __forceinline__ void mainloop_tt(const Op &a, const Op &b, int klen, 
       // second half-step: the next copies after its first MFMA, then the
       // next slice's first reads between the rest
       tr_mfma<T>(0, fa1, fb1, acc);
-      issue_stage<T>(a, b, t + T::STAGES - 1, nk, smem);
-#pragma unroll
-      for (int i = 1; i < M; ++i) {
+      issue_stage<T>(a, b, t + T::STAGES - 1, nk, lds0);
+      static_for<1, M>([&](auto ii) {
+        constexpr int i = decltype(ii)::value;
         tr_mfma<T>(i, fa1, fb1, acc);
-#pragma unroll
-        for (int q = (i - 1) * R / (M - 1); q < i * R / (M - 1); ++q)
-          tr_issue<T>(sn, sn + T::A_BYTES, 0, q, fa0, fb0);
-      }
+        static_for<(i - 1) * R / (M - 1), i * R / (M - 1)>(
+            [&](auto q) { tr_issue<T, 0, decltype(q)::value>(nxt, fa0, fb0); });
+      });
+      cur = nxt;
+      st = sn;
     }
-    const char *st = smem + ((nk - 1) % T::STAGES) * T::STAGE_BYTES;
     tr_wait<T>(fa0, fb0);
-#pragma unroll
-    for (int i = 0; i < M; ++i) {
+    static_for<0, M>([&](auto ii) {
+      constexpr int i = decltype(ii)::value;
       tr_mfma<T>(i, fa0, fb0, acc);
-#pragma unroll
-      for (int q = i * R / M; q < (i + 1) * R / M; ++q)
-        tr_issue<T>(st, st + T::A_BYTES, 1, q, fa1, fb1);
-    }
+      static_for<i * R / M, (i + 1) * R / M>(
+          [&](auto q) { tr_issue<T, 1, decltype(q)::value>(cur, fa1, fb1); });
+    });
     tr_wait<T>(fa1, fb1);
-#pragma unroll
-    for (int i = 0; i < M; ++i) tr_mfma<T>(i, fa1, fb1, acc);
+    static_for<0, M>([&](auto ii) { tr_mfma<T>(decltype(ii)::value, fa1, fb1, acc); });
   }
   // every wave is done with the LDS slices and no copy is still writing them;
   // the caller may reuse LDS
