@@ -312,8 +312,10 @@ int run(bool bwd, const void *X, const void *W, const int64_t *labels, int64_t N
 
 int choose_splitk(int64_t C, int64_t H, int64_t V) {
   // Spread the dX GEMM's few output tiles over the 256 CUs: pick the split
-  // count that fills whole waves of 256 workgroups, at least two of them,
-  // with every split at least 1024 vocabulary rows deep.
+  // count that fills whole waves of 256 workgroups, with every split at least
+  // 1024 vocabulary rows deep.  One full wave beats two (fewer fp32 partials
+  // to write and reduce: dX 0.797 against 0.802 ms, the reduction 0.014
+  // against 0.024 ms on the Llama-3-8B head at chunk 1024).
   const int64_t tiles = cdiv(C, 256) * cdiv(H, 256);
   double best = -1.0;
   int bestS = 1;
@@ -322,7 +324,7 @@ int choose_splitk(int64_t C, int64_t H, int64_t V) {
     const int64_t units = tiles * S;
     const int64_t waves = cdiv(units, 256);
     const double eff = (double)units / (double)(waves * 256);
-    const double fill = std::min(1.0, (double)units / 512.0);
+    const double fill = std::min(1.0, (double)units / 256.0);
     const double score = eff * fill - 0.001 * S;
     if (score > best + 1e-12) {
       best = score;
