@@ -178,6 +178,7 @@ int chunk_forward(const Plan &p, char *ws, const void *W, int64_t ii, bool keep_
   const int Hi = (int)p.H, Vi = (int)p.V;
   float *pm = (float *)(ws + p.off_pm);
   float *ps = (float *)(ws + p.off_ps);
+  float *pmt = (float *)(ws + p.off_pmt);
   float *zy = (float *)(ws + p.off_zy);
   float *lse = (float *)(ws + p.off_lse);
   if (p.dtype == FLCE_BF16) {
@@ -186,7 +187,7 @@ int chunk_forward(const Plan &p, char *ws, const void *W, int64_t ii, bool keep_
     uint16_t *Xp = (uint16_t *)(ws + p.off_xp);
     LAUNCH(FLCE_K_PACK, launch_pack_bf16((const uint16_t *)io.Xc, io.c, Hi, Xp, p.nks_h, s));
     LAUNCH(FLCE_K_FWD_TILE, launch_fwd_tile_bf16(Wp, Xp, p.nks_h, io.lab, ii, io.c, Hi, Vi, Zp,
-                                                 p.nks_z, pm, ps, zy, p.nvt, keep_z, s));
+                                                 p.nks_z, pm, ps, pmt, zy, p.nvt, keep_z, s));
   } else {
     float *z = (float *)(ws + p.off_z);
     LAUNCH(FLCE_K_FWD_TILE, launch_fwd_tile_f32((const float *)W, (const float *)io.Xc, io.lab,
@@ -207,8 +208,9 @@ int chunk_backward(const Plan &p, char *ws, const void *W, int64_t ii, const Chu
     uint16_t *Zp = (uint16_t *)(ws + p.off_z);
     const uint16_t *Xp = (const uint16_t *)(ws + p.off_xp);
     float *dxp = (float *)(ws + p.off_dxp);
-    LAUNCH(FLCE_K_DLOGITS, launch_dlogits_bf16(Zp, p.nks_z, io.c, Vi, lse, io.lab, ii, io.wr, sc,
-                                               s));
+    LAUNCH(FLCE_K_DLOGITS, launch_dlogits_bf16(Zp, p.nks_z, io.c, Vi,
+                                               (const float *)(ws + p.off_pmt), lse, io.lab, ii,
+                                               io.wr, sc, s));
     LAUNCH(FLCE_K_DX_GEMM, launch_dx_bf16(Zp, p.nks_z, (const uint16_t *)(ws + p.off_wtp), io.c,
                                           Hi, Vi, p.splitk, p.ksplit, dxp, s));
     LAUNCH(FLCE_K_DX_REDUCE, launch_dx_reduce_bf16(dxp, p.splitk, io.c, Hi, (uint16_t *)io.dXc, s));
@@ -377,6 +379,10 @@ void make_plan(int64_t N, int64_t H, int64_t V, int dtype, int64_t C, Plan *p) {
   o += align256((size_t)C * p->nvt * 4);
   p->off_ps = o;
   o += align256((size_t)C * p->nvt * 4);
+  if (bf) {
+    p->off_pmt = o;
+    o += align256((size_t)C * p->nvt * 4);
+  }
   p->off_zy = o;
   o += align256((size_t)C * 4);
   p->off_lse = o;

@@ -41,6 +41,7 @@ struct Plan {
   int64_t ksplit = 0;   // vocabulary rows per split (multiple of 64)
   size_t off_wp = 0, off_wtp = 0, off_z = 0, off_xp = 0, off_pm = 0, off_ps = 0, off_zy = 0, off_lse = 0,
          off_rowloss = 0, off_dxp = 0, off_scal = 0, total = 0;
+  size_t off_pmt = 0;   // bf16 path: the partial maxima again, [partial][token]
 };
 
 // Fill *p for the given sizes and chunk (C >= 1, C <= N or N == 0).
@@ -68,15 +69,20 @@ hipError_t launch_scale(void *buf, int64_t n, int dtype, const float *scale, hip
 // Pack a row-major [R][K] matrix into P (rows R padded to 256, nks_p slices).
 hipError_t launch_pack_bf16(const uint16_t *src, int R, int K, uint16_t *P, int64_t nks_p,
                             hipStream_t s);
+// Logits tile GEMM with the log-sum-exp epilogue.  pm, ps: [token][partial]
+// maximum and sum of exp per 128 vocabulary ids; with store_z, Zp receives
+// bf16(z - m) for the partial's maximum m, and pmt[partial * c + token] the m
+// that was subtracted.
 hipError_t launch_fwd_tile_bf16(const uint16_t *Wp, const uint16_t *Xp, int64_t nks_h,
                                 const int64_t *labels_c, int64_t ii, int c, int H, int V,
-                                uint16_t *Zp, int64_t nks_z, float *pm, float *ps, float *zy,
-                                int64_t nvt, bool store_z, hipStream_t s);
+                                uint16_t *Zp, int64_t nks_z, float *pm, float *ps, float *pmt,
+                                float *zy, int64_t nvt, bool store_z, hipStream_t s);
+// G in place over the stored bf16(z - m), with m from pmt.
 // wrow_c (may be null): per-token weight of the loss (the upstream gradient
 // of a per-token loss vector); null: sc->scale for every valid token.
-hipError_t launch_dlogits_bf16(uint16_t *Zp, int64_t nks_z, int c, int V, const float *lse_c,
-                               const int64_t *labels_c, int64_t ii, const float *wrow_c,
-                               const Scalars *sc, hipStream_t s);
+hipError_t launch_dlogits_bf16(uint16_t *Zp, int64_t nks_z, int c, int V, const float *pmt,
+                               const float *lse_c, const int64_t *labels_c, int64_t ii,
+                               const float *wrow_c, const Scalars *sc, hipStream_t s);
 // Pack the transpose of a row-major [R][K] matrix into PT (rows K padded to
 // 256, nks_t column slices covering R) and, if P is not null, the matrix
 // itself into P (rows R padded to 256, nks_p slices), reading it once.

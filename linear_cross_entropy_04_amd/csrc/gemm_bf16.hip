@@ -6,9 +6,9 @@
 // Z = X W^T that the Liger Kernel pages fuse with the cross-entropy loss):
 //   pack      X_c -> Xp (rows = tokens, k = hidden);
 //   forward   Z_c^T = W X_c^T      M = V (vocab), N = c (tokens), K = H
-//             + epilogue: per (token, 128-vocab half tile) max and sum of exp,
-//               the target logit, and the bf16 logits into Zp (rows = tokens,
-//               k = vocabulary);
+//             + epilogue: per (token, 128-vocab half tile) max m and sum of
+//               exp, the target logit, and bf16(z - m) into Zp (rows =
+//               tokens, k = vocabulary);
 //   dlogits   Zp rewritten in place into G = (softmax - onehot) / N_valid;
 //   dX        dX_c  = G_c W        M = c, N = H, K = V (split-K, fp32 partials),
 //             W from WTp, a second packed copy of W made once per call (rows =
@@ -636,14 +636,19 @@ __global__ __launch_bounds__(256) void pack_t_kernel(const uint16_t *__restrict_
 // Epilogue, wave by wave: each wave reduces its own 128 vocabulary rows, so a
 // token gets one (max, sum of exp) partial per 128 vocabulary ids, at index
 // 2 vt + wm.  The target logit is taken from the fp32 accumulators by the
-// lane that holds it.  The bf16 logits tile (8 consecutive blocks of Zp) is
-// stored straight from the accumulators in 512-byte half-fragments.
+// lane that holds it.  The logits tile (8 consecutive blocks of Zp) is
+// stored straight from the accumulators in 512-byte half-fragments, as
+// bf16(z - m) with m the token's maximum over the wave's 128 vocabulary ids
+// (written to pmt for dlogits).  Rounding then costs a relative 2^-9 of
+// m - z, not of z: exp(z - lse) keeps its accuracy however large the
+// logits or a common shift of a token's logits, and the entries that carry
+// the probability (z near m) are stored almost exactly.
 template <bool VTAIL>
 __global__ __launch_bounds__(NTHREADS, 1) void fwd_tile_kernel(
     const uint16_t *__restrict__ Wp, const uint16_t *__restrict__ Xp, int64_t nks_h,
     const int64_t *__restrict__ labels_c, int64_t ii, int c, int H, int V,
     uint16_t *__restrict__ Zp, int64_t nks_z, float *__restrict__ pm, float *__restrict__ ps,
-    float *__restrict__ zy, int64_t nvt, int vt0, int nct, int store_z) {
+    float *__restrict__ pmt, float *__restrict__ zy, int64_t nvt, int vt0, int nct, int store_z) {
   using T = FwdTile;
   __shared__ __attribute__((aligned(1024))) char smem[T::LDS];
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
@@ -661,6 +666,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_tile_kernel(
   const int vrow0 = m0 + wm * 128 + 4 * (lane >> 5);   // row r = 32 i + 8 (e/4) + e%4
   const int vlim = V - vrow0;                          // rows r < vlim exist
   const int64_t part = 2 * (int64_t)vt + wm;
+  float msub[4];                                       // the maximum each token's stored logits are taken from
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int tok = n0 + wn * 128 + j * 32 + (lane & 31);
@@ -678,7 +684,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_tile_kernel(
       }
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     // a wave whose rows all lie past V has mx = -inf: its sum must be 0, not NaN
-    const float ml = (VTAIL && mx == -INFINITY) ? 0.f : mx * kLog2e;
+    const float ms = (VTAIL && mx == -INFINITY) ? 0.f : mx;
+    const float ml = ms * kLog2e;
+    msub[j] = ms;
     float sum = 0.f, zsel = 0.f;
     bool found = false;
 #pragma unroll
@@ -696,6 +704,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_tile_kernel(
     if (lane < 32 && tok_ok) {
       pm[(int64_t)tok * nvt + part] = mx;
       ps[(int64_t)tok * nvt + part] = sum;
+      if (store_z) pmt[part * c + tok] = ms;
     }
   }
 
@@ -716,8 +725,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_tile_kernel(
         for (int i = 0; i < 4; ++i) {
           // vocabulary slice wm 4 + i of the tile, token row group wn 4 + j
           uint2 pk;
-          pk.x = pack_bf16x2(acc[i][j][4 * g], acc[i][j][4 * g + 1]);
-          pk.y = pack_bf16x2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
+          pk.x = pack_bf16x2(acc[i][j][4 * g] - msub[j], acc[i][j][4 * g + 1] - msub[j]);
+          pk.y = pack_bf16x2(acc[i][j][4 * g + 2] - msub[j], acc[i][j][4 * g + 3] - msub[j]);
           *(uint2 *)(zg + ((wm * 4 + i) << 13) + ((wn * 4 + j) << 10)) = pk;
         }
     }
@@ -728,14 +737,15 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_tile_kernel(
 // One workgroup per 16 KB block of Zp (256 tokens x 32 vocabulary columns),
 // four 16-byte slots per thread (one token, 8 consecutive vocabulary columns
 // each), in memory order: pass k of a wave covers 1 KB contiguous, and all
-// four loads are in flight before any arithmetic.  In place:
+// four loads are in flight before any arithmetic.  In place, from the stored
+// Z - m (m the token's maximum over the block's 128-wide partial, from pmt):
 // G = w_r (exp(Z - lse) - onehot(y)) on valid tokens, 0 on ignored tokens and
 // outside [0, c) x [0, V); w_r = wrow_c[r] if given, else sc->scale
 // (1 / N_valid for the mean loss).
 constexpr int kDlSlots = 4;
 
 __global__ __launch_bounds__(256) void dlogits_kernel(
-    uint16_t *__restrict__ Zp, int64_t nks_z, int c, int V,
+    uint16_t *__restrict__ Zp, int64_t nks_z, int c, int V, const float *__restrict__ pmt,
     const float *__restrict__ lse_c, const int64_t *__restrict__ labels_c, int64_t ii,
     const float *__restrict__ wrow_c, const Scalars *__restrict__ sc) {
   // slot u = (blk * 16 + f) * 64 + sl of block blk = (rt, ks); thread t of the
@@ -746,6 +756,8 @@ __global__ __launch_bounds__(256) void dlogits_kernel(
   const int v0 = (int)(ks * 32) + (w & 1) * 16 + h * 8;
   const int rr = ((sl & 31) ^ (h << 2) ^ ((w & 1) << 3));
   uint16_t *zb = Zp + (blk << 13) + ((int64_t)threadIdx.x << 3);
+  // the block's 32 vocabulary columns lie in one 128-wide partial
+  const float *mrow = pmt + (ks >> 2) * c;
   u32x4 z[kDlSlots];
 #pragma unroll
   for (int k = 0; k < kDlSlots; ++k) z[k] = *(const u32x4 *)(zb + (k << 11));
@@ -756,7 +768,7 @@ __global__ __launch_bounds__(256) void dlogits_kernel(
     float l2 = 0.f, inv = 0.f;
     if (r < c) {
       y = labels_c[r];
-      l2 = lse_c[r] * kLog2e;
+      l2 = (lse_c[r] - mrow[r]) * kLog2e;     // stored values are z - m
       inv = wrow_c ? wrow_c[r] : sc->scale;
     }
     const bool valid = r < c && y != ii;
@@ -946,32 +958,32 @@ hipError_t launch_pack_bf16(const uint16_t *src, int R, int K, uint16_t *P, int6
 
 hipError_t launch_fwd_tile_bf16(const uint16_t *Wp, const uint16_t *Xp, int64_t nks_h,
                                 const int64_t *labels_c, int64_t ii, int c, int H, int V,
-                                uint16_t *Zp, int64_t nks_z, float *pm, float *ps, float *zy,
-                                int64_t nvt, bool store_z, hipStream_t s) {
+                                uint16_t *Zp, int64_t nks_z, float *pm, float *ps, float *pmt,
+                                float *zy, int64_t nvt, bool store_z, hipStream_t s) {
   const int nct = (c + FwdTile::BN - 1) / FwdTile::BN;
   const int nfull = V / FwdTile::BM;                 // vocabulary tiles inside V
   if (nfull > 0) {
     hipLaunchKernelGGL(fwd_tile_kernel<false>, dim3(nfull * nct), dim3(NTHREADS), 0, s, Wp, Xp,
-                       nks_h, labels_c, ii, c, H, V, Zp, nks_z, pm, ps, zy, nvt, 0, nct,
+                       nks_h, labels_c, ii, c, H, V, Zp, nks_z, pm, ps, pmt, zy, nvt, 0, nct,
                        store_z ? 1 : 0);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (V % FwdTile::BM != 0) {
     hipLaunchKernelGGL(fwd_tile_kernel<true>, dim3(nct), dim3(NTHREADS), 0, s, Wp, Xp, nks_h,
-                       labels_c, ii, c, H, V, Zp, nks_z, pm, ps, zy, nvt, nfull, nct,
+                       labels_c, ii, c, H, V, Zp, nks_z, pm, ps, pmt, zy, nvt, nfull, nct,
                        store_z ? 1 : 0);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_dlogits_bf16(uint16_t *Zp, int64_t nks_z, int c, int V, const float *lse_c,
-                               const int64_t *labels_c, int64_t ii, const float *wrow_c,
-                               const Scalars *sc, hipStream_t s) {
+hipError_t launch_dlogits_bf16(uint16_t *Zp, int64_t nks_z, int c, int V, const float *pmt,
+                               const float *lse_c, const int64_t *labels_c, int64_t ii,
+                               const float *wrow_c, const Scalars *sc, hipStream_t s) {
   // one workgroup per 16 KB block of the row tiles that cover [0, c), every slice of Zp
   const int64_t nblk = (int64_t)((c + 255) / 256) * nks_z;
   static_assert(kDlSlots * 256 * 16 == 16384, "a workgroup covers one block");
-  hipLaunchKernelGGL(dlogits_kernel, dim3((unsigned)nblk), dim3(256), 0, s, Zp, nks_z, c, V,
+  hipLaunchKernelGGL(dlogits_kernel, dim3((unsigned)nblk), dim3(256), 0, s, Zp, nks_z, c, V, pmt,
                      lse_c, labels_c, ii, wrow_c, sc);
   return hipGetLastError();
 }
