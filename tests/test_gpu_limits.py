@@ -1,0 +1,58 @@
+"""GPU parity at the largest shapes the library accepts (V = 8,000,000 and
+H = 2^20), with few tokens so that the fp64 oracle's full logits stay a few GB.
+
+- V at its limit: 62,500 log-sum-exp partials per token, 31,250 vocabulary
+  tiles per chunk, a dX split over millions of vocabulary rows, and about
+  12 GB of workspace (the packed copies of W pad H = 8 to 256 columns).
+- H at its limit: one forward tile whose K loop runs 32,768 slices, dX over
+  4,096 output tiles, dW over 8,192 column tiles of one vocabulary strip.
+Both run two chunks, the second ragged.
+"""
+import numpy as np
+import pytest
+import torch
+
+import datagen
+import linear_cross_entropy_04_amd as fl
+import oracle
+from _gpu_common import check_grad, check_loss, run_gpu, say
+
+II = -100
+MAX_V = 8_000_000
+MAX_H = 1 << 20
+
+
+def _check(inp, chunk):
+    say(f"case {inp.wl.name} N={inp.wl.N} H={inp.wl.H} V={inp.wl.V} seed={inp.seed} chunk={chunk}")
+    need = fl.flce_workspace_bytes(inp.wl.N, inp.wl.H, inp.wl.V, fl.FLCE_BF16, chunk)
+    say(f"    workspace {need / 2**30:.2f} GiB")
+    g = run_gpu(inp, chunk, II)
+    r = oracle.flce(inp.X_f64(), inp.W_f64(), inp.labels, II)
+    check_loss(g["loss"], r.loss, "bf16")
+    check_grad(g["dX"], r.dX, "bf16", "dX")
+    check_grad(g["dW"], r.dW, "bf16", "dW")
+    assert np.max(np.abs(g["row_lse"] - r.lse) / np.abs(r.lse)) <= 1e-3
+    valid = inp.labels != II
+    assert np.all(g["dX"][~valid] == 0.0)
+    del g
+    torch.cuda.empty_cache()
+
+
+def test_limits_are_the_checked_ones():
+    """One past each limit is refused before anything runs."""
+    assert fl.flce_workspace_bytes(40, 8, MAX_V, fl.FLCE_BF16, 32) > 0
+    assert fl.flce_workspace_bytes(40, 8, MAX_V + 1, fl.FLCE_BF16, 32) == 0
+    assert fl.flce_workspace_bytes(40, MAX_H, 16, fl.FLCE_BF16, 32) > 0
+    assert fl.flce_workspace_bytes(40, MAX_H + 8, 16, fl.FLCE_BF16, 32) == 0
+
+
+@pytest.mark.gpu
+def test_maximum_vocabulary():
+    inp = datagen.make_custom(40, 8, MAX_V, "bf16", seed=41, ignore_frac=0.1, w_std=0.5)
+    _check(inp, 32)
+
+
+@pytest.mark.gpu
+def test_maximum_hidden():
+    inp = datagen.make_custom(40, MAX_H, 16, "bf16", seed=43, ignore_frac=0.1, w_std=0.002)
+    _check(inp, 32)
