@@ -580,6 +580,16 @@ def flce_scale_inplace(buf: torch.Tensor, scale: torch.Tensor, stream=None) -> N
         raise FLCEError(st, "flce_scale_inplace")
 
 
+def _consume_once(ctx):
+    """The backward functions below scale the gradients saved by the forward
+    in place by the upstream gradient, so a second backward through the same
+    graph (retain_graph=True) would see them already scaled: refuse it."""
+    if getattr(ctx, "consumed", False):
+        raise RuntimeError("the fused loss's saved gradients were already used by a backward "
+                           "pass; recompute the loss to differentiate it again")
+    ctx.consumed = True
+
+
 # ------------------------------------------------------------------ autograd
 
 class _FLCEFunction(torch.autograd.Function):
@@ -607,6 +617,7 @@ class _FLCEFunction(torch.autograd.Function):
 
     @staticmethod
     def backward(ctx, grad_out):
+        _consume_once(ctx)
         dX, dW = ctx.saved_tensors
         g = grad_out.detach().to(torch.float32).reshape(1).contiguous()
         flce_scale_inplace(dX, g)
@@ -695,6 +706,7 @@ class _CEFunction(torch.autograd.Function):
 
     @staticmethod
     def backward(ctx, grad_out):
+        _consume_once(ctx)
         (buf,) = ctx.saved_tensors
         g = grad_out.detach().to(torch.float32).reshape(1).contiguous()
         flce_scale_inplace(buf, g)
@@ -740,6 +752,7 @@ class _ORPOFunction(torch.autograd.Function):
 
     @staticmethod
     def backward(ctx, grad_out):
+        _consume_once(ctx)
         dX, dW = ctx.saved_tensors
         g = grad_out.detach().to(torch.float32).reshape(1).contiguous()
         flce_scale_inplace(dX, g)
@@ -805,6 +818,7 @@ class _PairFunction(torch.autograd.Function):
 
     @staticmethod
     def backward(ctx, grad_out):
+        _consume_once(ctx)
         dX, dW = ctx.saved_tensors
         g = grad_out.detach().to(torch.float32).reshape(1).contiguous()
         flce_scale_inplace(dX, g)
@@ -940,6 +954,7 @@ class _KTOFunction(torch.autograd.Function):
 
     @staticmethod
     def backward(ctx, grad_out):
+        _consume_once(ctx)
         dX, dW = ctx.saved_tensors
         g = grad_out.detach().to(torch.float32).reshape(1).contiguous()
         flce_scale_inplace(dX, g)

@@ -173,3 +173,24 @@ def test_autograd_binding():
     mod = fl.FusedLinearCrossEntropyLoss()
     with torch.no_grad():
         assert abs(mod(W, X, y).item() - r.loss) <= 1e-3 * r.loss
+
+
+def test_autograd_second_backward_refused():
+    """The backward scales the gradients saved with the loss in place, so a
+    second backward through a retained graph must fail loudly rather than
+    return gradients scaled twice; a fresh loss differentiates again."""
+    inp = datagen.make_custom(256, 128, 1000, "bf16", seed=14)
+    X, W, y = to_device(inp)
+    r = oracle.flce(inp.X_f64(), inp.W_f64(), inp.labels)
+    Xg = X.clone().requires_grad_(True)
+    Wg = W.clone().requires_grad_(True)
+    out = fl.loss(Wg, Xg, y)
+    (2.0 * out).backward(retain_graph=True)
+    check_grad(Xg.grad.double().cpu().numpy(), 2.0 * r.dX, "bf16", "first backward dX")
+    with pytest.raises(RuntimeError, match="already used"):
+        out.backward()
+    Xg.grad = None
+    Wg.grad = None
+    fl.loss(Wg, Xg, y).backward()
+    check_grad(Xg.grad.double().cpu().numpy(), r.dX, "bf16", "fresh loss dX")
+    check_grad(Wg.grad.double().cpu().numpy(), r.dW, "bf16", "fresh loss dW")
