@@ -60,7 +60,8 @@ typedef enum {
 
 typedef enum {
   FLCE_F32 = 0,          /* X, W, dX in fp32; scratch in fp32 */
-  FLCE_BF16 = 1          /* X, W, dX in bf16; fp32 accumulation; logits/dlogits scratch in bf16 */
+  FLCE_BF16 = 1          /* X, W, dX in bf16; fp32 accumulation; logits (less each token's partial
+                            maximum, kept in fp32) and dlogits scratch in bf16 */
 } flce_dtype;
 
 /* How the per-token losses l_i = lse_i - z_{i,y_i} of valid tokens are reduced. */
