@@ -30,7 +30,7 @@ __all__ = [
     "FusedLinearORPOLoss", "PAIR_KINDS", "flce_pair_workspace_bytes", "flce_pair_fwd_bwd",
     "flce_pair_fwd", "preference_loss", "sequence_logps", "FusedLinearSimPOLoss",
     "FusedLinearCPOLoss", "FusedLinearDPOLoss", "flce_kto_workspace_bytes", "flce_kto_fwd_bwd",
-    "flce_kto_fwd", "kto_loss", "FusedLinearKTOLoss",
+    "flce_kto_fwd", "kto_loss", "kto_reference_point", "FusedLinearKTOLoss",
 ]
 
 FLCE_F32 = 0
@@ -983,6 +983,31 @@ def kto_loss(weight: torch.Tensor, input: torch.Tensor, target: torch.Tensor,
     x, y, n_seq, des = _kto_rows(input, target, desirable)
     return _KTOFunction.apply(weight, x, y, n_seq, des, ref_logp.float().contiguous(),
                               ignore_index, beta, z0, lambda_d, lambda_u, chunk_seqs)
+
+
+@torch.no_grad()
+def kto_reference_point(weight: torch.Tensor, input: torch.Tensor, target: torch.Tensor,
+                        ref_logp: torch.Tensor, ignore_index: int = -100,
+                        chunk_seqs: int = 0) -> float:
+    """KTO's reference point from a batch of mismatched completions: input
+    [n_seq, T, H] (or [n_seq * T, H]) holds the hidden states of n_seq
+    completions each under a prompt that is not its own, target [n_seq, T]
+    their tokens, ref_logp [n_seq] the reference model's summed
+    log-probabilities of the same completions.  Returns z0 = max(0, mean of
+    S - ref_logp) with S the policy's sums (forward only, through
+    flce_kto_fwd), as a host float for kto_loss."""
+    if target.dim() != 2:
+        raise ValueError("target must be [n_seq, T]")
+    if ref_logp.numel() != target.shape[0]:
+        raise ValueError(f"ref_logp has {ref_logp.numel()} values for {target.shape[0]} sequences")
+    ones = torch.ones(target.shape[0], dtype=torch.int32, device=input.device)
+    x, y, n_seq, des = _kto_rows(input, target, ones)    # the flags do not enter S
+    S = torch.empty(n_seq, dtype=torch.float32, device=x.device)
+    zeros = torch.zeros(n_seq, dtype=torch.float32, device=x.device)
+    flce_kto_fwd(x.contiguous(), weight.detach().contiguous(), y, n_seq, ignore_index, des, zeros,
+                 0.1, 0.0, 1.0, 1.0, chunk_seqs, _kto_ws(x, weight, n_seq, chunk_seqs), logp=S)
+    d = S.double().cpu().numpy() - ref_logp.detach().double().cpu().numpy().reshape(-1)
+    return max(0.0, float(d.mean()))
 
 
 class FusedLinearKTOLoss(torch.nn.Module):

@@ -600,6 +600,26 @@ def kto_token_weights(dl_dr, valid, n_seq: int) -> np.ndarray:
     return np.where(v, (-dl_dr / n_seq)[:, None], 0.0).reshape(-1)
 
 
+def kto_reference_point(X, W, labels, n_seq: int, ref_logp,
+                        ignore_index: int = IGNORE_INDEX) -> float:
+    """KTO's reference point estimated from a batch (Ethayarajh et al., 2024):
+    the rows of X are n_seq completions each scored under a prompt that is
+    not its own (mismatched pairs), ref_logp the reference model's sums of
+    log p over the same completions; z0 = max(0, mean over sequences of
+    S - R), the policy-to-reference KL estimate clamped at zero.  No gradient
+    flows through it."""
+    X = np.asarray(X, dtype=np.float64)
+    W = np.asarray(W, dtype=np.float64)
+    labels = np.asarray(labels, dtype=np.int64)
+    if n_seq <= 0 or X.shape[0] % n_seq != 0:
+        raise ValueError("X must hold n_seq sequences of equal length")
+    valid = valid_mask(labels, W.shape[0], ignore_index)
+    Z = logits(X, W)
+    lp = log_probs(row_logsumexp(Z), target_logit(Z, labels, valid), valid)
+    S, _ = sequence_sums(lp, valid, n_seq)
+    return max(0.0, float(np.mean(S - np.asarray(ref_logp, dtype=np.float64))))
+
+
 def kto(X, W, labels, n_seq: int, desirable, ref_logp, ignore_index: int = IGNORE_INDEX,
         beta: float = 0.1, z0: float = 0.0, lambda_d: float = 1.0, lambda_u: float = 1.0,
         grads: bool = True) -> KTOResult:

@@ -157,3 +157,23 @@ def test_kto_degenerate_shapes():
                     II, **P)
     check_loss(o1["loss"], r1.loss, "bf16")
     check_grad(o1["dW_t"].double().cpu().numpy(), r1.dW, "bf16", "dW")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_kto_reference_point(dtype):
+    """z0 from a batch of completions (here the drawn sequences stand for
+    mismatched ones): the reference sums sit a known gap below or above the
+    oracle's policy sums, so z0 is the mean gap or, clamped, 0."""
+    S, T, H, V = 6, 64, 128, 1000
+    inp, _, _ = datagen.make_unpaired(S, T, H, V, dtype, seed=71)
+    X, W, y = to_device(inp)
+    Sp = oracle.kto(inp.X_f64(), inp.W_f64(), inp.labels, S, np.ones(S, bool), np.zeros(S),
+                    II, grads=False).logp
+    gap = np.array([0.5, 1.5, -0.25, 0.75, 0.0, 1.0])
+    tol = (2e-4 if dtype == "bf16" else 1e-5) * max(np.max(np.abs(Sp)), 1.0)
+    for R, want in ((Sp - gap, gap.mean()), (Sp + gap + 1.0, 0.0)):
+        z = fl.kto_reference_point(W, X.view(S, T, H), y.view(S, T),
+                                   torch.from_numpy(R.astype(np.float32)).to(DEV))
+        say(f"    z0 = {z:.6f} (want {want:.6f})")
+        assert abs(z - want) <= tol + 1e-6 * abs(want)
+        assert z == max(0.0, z)

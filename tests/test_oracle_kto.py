@@ -189,3 +189,35 @@ def test_planted_mistakes_kto(monkeypatch, step, mistake):
         except (AssertionError, ValueError, IndexError, FloatingPointError):
             caught.append(pin.__name__)
     assert caught, f"no pin catches the planted mistake {mistake.__name__}"
+
+
+# ------------------------------------------------------------------ reference point from a batch
+
+def test_kto_reference_point_closed_form():
+    """W = 0: every scored token has log p = -ln V, so S = -n ln V for a
+    sequence of n scored tokens and z0 = max(0, mean(S - R)) is a closed form;
+    a reference below the policy gives its mean gap, one above it gives 0."""
+    S, T, H, V = 4, 6, 5, 9
+    X, W, y, _, _ = _batch(S, T, H, V, seed=31, prompt=2)
+    W = np.zeros_like(W)
+    n = (y.reshape(S, T) != II).sum(axis=1)
+    gap = np.array([1.0, 3.0, -0.5, 0.5])
+    R = -n * np.log(V) - gap
+    assert abs(oracle.kto_reference_point(X, W, y, S, R) - gap.mean()) <= 1e-12
+    assert oracle.kto_reference_point(X, W, y, S, -n * np.log(V) + gap) == 0.0
+
+
+def test_kto_reference_point_against_torch():
+    """Random head: the mean policy-minus-reference gap with torch's
+    log_softmax for the policy sums, clamped at 0; invariant to the order of
+    the sequences."""
+    S, T, H, V = 5, 7, 6, 11
+    X, W, y, _, _ = _batch(S, T, H, V, seed=32)
+    Sp = _torch_logp_sums(X, W, y, S)
+    R = Sp - np.array([0.3, -0.1, 0.8, 0.2, 0.05])
+    z = oracle.kto_reference_point(X, W, y, S, R)
+    assert abs(z - 0.25) <= 1e-12
+    perm = np.array([3, 0, 4, 1, 2])
+    Xp = X.reshape(S, T, H)[perm].reshape(-1, H)
+    yp = y.reshape(S, T)[perm].reshape(-1)
+    assert abs(oracle.kto_reference_point(Xp, W, yp, S, R[perm]) - z) <= 1e-12
