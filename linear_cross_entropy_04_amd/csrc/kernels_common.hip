@@ -51,28 +51,56 @@ __global__ __launch_bounds__(1024) void label_check_kernel(const int64_t *__rest
   }
 }
 
-// One wave per token: lse = M + ln sum_t s_t exp(m_t - M) over the token's
-// vocabulary-tile partials (m_t = tile max, s_t = sum of exp(z - m_t)); the
-// token's loss lse - z_y and, if asked, its log-probability z_y - lse (both
-// 0 on ignored tokens).
-__global__ __launch_bounds__(256) void lse_combine_kernel(
+// Merge two (max, sum) pairs; a side whose max is -inf holds a sum of 0 and
+// must not contribute exp(nan).
+__device__ __forceinline__ void lse_merge(float &M, float &S, float Mo, float So) {
+  const float Mn = fmaxf(M, Mo);
+  const float a = M > -INFINITY ? __builtin_amdgcn_exp2f((M - Mn) * kLog2e) : 0.f;
+  const float b = Mo > -INFINITY ? __builtin_amdgcn_exp2f((Mo - Mn) * kLog2e) : 0.f;
+  S = S * a + So * b;
+  M = Mn;
+}
+
+// One workgroup of 256 threads per token: lse = M + ln sum_t s_t exp(m_t - M)
+// over the token's vocabulary-tile partials (m_t = tile max, s_t = sum of
+// exp(z - m_t)); the token's loss lse - z_y and, if asked, its
+// log-probability z_y - lse (both 0 on ignored tokens).  One pass: each
+// thread keeps a running (max, sum) over its partials, rescaling the sum when
+// the max grows; threads then merge within the wave, and the four waves
+// through LDS.  A partial with m = -inf (vocabulary ids past V) has s = 0 and
+// adds nothing; a NaN partial still reaches the sum.
+constexpr int kLseThreads = 256;
+
+__global__ __launch_bounds__(kLseThreads) void lse_combine_kernel(
     const float *__restrict__ pm, const float *__restrict__ ps, const float *__restrict__ zy,
     const int64_t *__restrict__ labels_c, int64_t ii, int c, int64_t nvt, float *__restrict__ lse_c,
     float *__restrict__ rowloss_c, float *__restrict__ rowlse_c, float *__restrict__ logprob_c) {
-  const int tok = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (tok >= c) return;
+  __shared__ float wm[kLseThreads / 64], wsum[kLseThreads / 64];
+  const int tok = blockIdx.x;
   const float *m = pm + (int64_t)tok * nvt;
   const float *s = ps + (int64_t)tok * nvt;
-  float M = -INFINITY;
-  for (int64_t t = lane; t < nvt; t += 64) M = fmaxf(M, m[t]);
+  float M = -INFINITY, S = 0.f;
+#pragma unroll 4
+  for (int64_t t = threadIdx.x; t < nvt; t += kLseThreads) {
+    const float mt = m[t], st = s[t];
+    if (mt > M) {
+      S = S * __builtin_amdgcn_exp2f((M - mt) * kLog2e) + st;
+      M = mt;
+    } else if (!(mt == -INFINITY)) {
+      S += st * __builtin_amdgcn_exp2f((mt - M) * kLog2e);
+    }
+  }
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-  float S = 0.f;
-  for (int64_t t = lane; t < nvt; t += 64) S += s[t] * __builtin_amdgcn_exp2f((m[t] - M) * kLog2e);
+  for (int o = 32; o > 0; o >>= 1) lse_merge(M, S, __shfl_xor(M, o), __shfl_xor(S, o));
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    wm[w] = M;
+    wsum[w] = S;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) S += __shfl_xor(S, o);
-  if (lane == 0) {
+    for (int k = 1; k < kLseThreads / 64; ++k) lse_merge(M, S, wm[k], wsum[k]);
     const float lse = M + __builtin_amdgcn_logf(S) * kLn2;
     const int64_t y = labels_c[tok];
     lse_c[tok] = lse;
@@ -144,8 +172,9 @@ hipError_t launch_lse_combine(const float *pm, const float *ps, const float *zy,
                               const int64_t *labels_c, int64_t ii, int c, int64_t nvt,
                               float *lse_c, float *rowloss_c, float *rowlse_c,
                               float *logprob_c, hipStream_t s) {
-  hipLaunchKernelGGL(lse_combine_kernel, dim3((c + 3) / 4), dim3(256), 0, s, pm, ps, zy, labels_c,
-                     ii, c, nvt, lse_c, rowloss_c, rowlse_c, logprob_c);
+  if (c <= 0) return hipSuccess;
+  hipLaunchKernelGGL(lse_combine_kernel, dim3((unsigned)c), dim3(kLseThreads), 0, s, pm, ps, zy,
+                     labels_c, ii, c, nvt, lse_c, rowloss_c, rowlse_c, logprob_c);
   return hipGetLastError();
 }
 
