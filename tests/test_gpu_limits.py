@@ -56,3 +56,28 @@ def test_maximum_vocabulary():
 def test_maximum_hidden():
     inp = datagen.make_custom(40, MAX_H, 16, "bf16", seed=43, ignore_frac=0.1, w_std=0.002)
     _check(inp, 32)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("N,H,V,chunk", [(1, 8, 1, 0), (37, 8, 1, 16), (1, 8, 2, 1), (5, 8, 3, 2)])
+def test_smallest_shapes(N, H, V, chunk):
+    """The degenerate end: one class (softmax 1 everywhere, so loss, dX and
+    dW are 0 up to fp32 rounding), the narrowest bf16 hidden size, a single
+    token, and chunks of one or two tokens."""
+    inp = datagen.make_custom(N, H, V, "bf16", seed=N * 10 + V, ignore_frac=0.0, w_std=0.5)
+    say(f"case N={N} H={H} V={V} chunk={chunk}")
+    g = run_gpu(inp, chunk, II)
+    r = oracle.flce(inp.X_f64(), inp.W_f64(), inp.labels, II)
+    if V == 1:
+        # exact arithmetic gives 0; the log-sum-exp of one fp32 logit comes
+        # out as z (1 + O(2^-24)) (exp2 of a fused z log2(e) - m log2(e)), so
+        # the outputs are 0 up to a few fp32 roundings of the operands
+        eps = 2.0 ** -20
+        assert abs(g["loss"]) <= eps * max(np.max(np.abs(r.lse)), 1.0)
+        assert np.max(np.abs(g["dX"])) <= eps * np.max(np.abs(inp.W_f64()))
+        assert np.max(np.abs(g["dW"])) <= eps * np.max(np.abs(inp.X_f64()))
+        assert np.allclose(g["row_lse"], r.lse, rtol=1e-3, atol=1e-3)
+    else:
+        check_loss(g["loss"], r.loss, "bf16")
+        check_grad(g["dX"], r.dX, "bf16", "dX")
+        check_grad(g["dW"], r.dW, "bf16", "dW")
