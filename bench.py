@@ -58,8 +58,8 @@ def kernel_work(name, chunks, H, V):
         return "hbm", sum(4.0 * c * V for c in chunks), "byte"
     if name == "pack_x":                       # bf16 X chunk read and written packed
         return "hbm", sum(4.0 * c * H for c in chunks), "byte"
-    if name == "pack_w":                       # W read once, written packed twice
-        return "hbm", 6.0 * V * H, "byte"
+    if name == "pack_w":                       # W read once, written packed once
+        return "hbm", 4.0 * V * H, "byte"
     if name == "pair_rows":                    # X rows gathered, dX rows scattered (bf16)
         return "hbm", sum(8.0 * c * H for c in chunks), "byte"
     return "hbm", None, "byte"
@@ -573,7 +573,8 @@ def main():
         "config": {"workload": wl.name, "N": N, "H": H, "V": V, "chunk_tokens": C,
                    "share_of_8_gpus": args.share,
                    "ignored_tokens": int((inp.labels == -100).sum()),
-                   "peak_scratch_bytes": peak_scratch},
+                   "peak_scratch_bytes": peak_scratch,
+                   "nxv_logits_bytes": N * V * (2 if wl.dtype == "bf16" else 4)},
         "tflops": round(tflops, 2),
         "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
         "ms_per_step_without_events": round(1e3 * elapsed_noev / args.steps, 4),

@@ -55,7 +55,9 @@ typedef enum {
   FLCE_ELABEL = 2,       /* a label is neither ignore_index nor in [0, V); outputs unspecified */
   FLCE_EWORKSPACE = 3,   /* workspace_bytes < flce_workspace_bytes(...) */
   FLCE_EHIP = 4,         /* a HIP call failed; see flce_last_error() */
-  FLCE_EUNSUPPORTED = 5  /* valid but unsupported shape (bf16 needs H % 8 == 0 and 16-byte aligned X, W, dX) */
+  FLCE_EUNSUPPORTED = 5  /* valid but unsupported shape: bf16 needs H % 8 == 0 and 16-byte aligned
+                            X, W, dX; N < 2^31, H <= 2^20, V <= 8,000,000, chunks <= 2^23
+                            tokens, and no launch of the call above 2^32 work-items */
 } flce_status;
 
 typedef enum {
@@ -71,32 +73,54 @@ typedef enum {
   FLCE_REDUCE_NONE = 2   /* the output is the vector l (row_loss); loss = sum_i l_i */
 } flce_reduction;
 
-/* Default scratch budget used when chunk_tokens <= 0 (auto): 3 GiB. */
-#define FLCE_DEFAULT_SCRATCH_BUDGET ((size_t)3 << 30)
+/*
+ * Chunk planning.  The pages split memory-heavy work into chunks to cut peak
+ * memory (project overview page, "Princípios Técnicos", Computação em
+ * Chunk); these calls choose the chunk and report what it costs.
+ *
+ * The workspace of a call holds, on the bf16 path, one packed copy of W (V x H
+ * bf16, rows and columns rounded up to 256), which the forward reads along
+ * its rows and dX transposed; and for one chunk of C tokens: its logits, then
+ * dlogits, in place ([C, V] bf16, or fp32 on the fp32 path), its packed X, the
+ * per-vocabulary-tile log-sum-exp partials, per-token statistics and the
+ * split-K partial sums of dX; plus one fp32 per-token loss for all N tokens.
+ * Only that last array grows with N.
+ *
+ * Budget used when a call plans its own chunk (chunk_tokens <= 0) and none is
+ * given: twice the bytes of W in its dtype (room for the packed copy of W and
+ * a chunk scratch as large as W again), but at least this floor.
+ */
+#define FLCE_DEFAULT_SCRATCH_FLOOR ((size_t)256 << 20)
 
 /*
- * Bytes of workspace a call with these sizes needs (scratch for one chunk:
- * logits/dlogits [C, V], per-vocab-tile log-sum-exp partials, per-token
- * statistics, and the split-K partial sums of dX).  chunk_tokens <= 0 means
- * "auto" (as chosen by flce_plan with the default budget); chunk_tokens > N is
- * clamped to N, and any chunk to at most 2^30 tokens.  Returns 0 for invalid
- * sizes or dtype.  Host only; no device call.
+ * Bytes of workspace a call with these sizes and this chunk needs (the whole
+ * workspace described above).  chunk_tokens <= 0 means "auto", as chosen by
+ * flce_plan with the default budget; chunk_tokens > N is clamped to N, and any
+ * chunk to at most 2^23 tokens.  Returns 0 for invalid sizes or dtype.  Host
+ * only; no device call.
  */
 size_t flce_workspace_bytes(int64_t N, int64_t H, int64_t V, int dtype, int64_t chunk_tokens);
 
 /*
- * Choose the chunk size.  On entry *chunk_tokens is the requested chunk
- * (<= 0: choose the largest power-of-two multiple of 256 tokens, at most N,
- * whose chunk scratch fits scratch_budget_bytes; 0 budget = the default).
- * The budget bounds the scratch that grows with the chunk; on the bf16 path a
- * pair of packed copies of W (as is and transposed, each V x H bf16 with both
- * rounded up to 256) comes on top of it.
- * On return *chunk_tokens holds the chunk that will be used and
- * *peak_scratch_bytes (may be NULL) the whole workspace it needs, which is the
- * peak device scratch of a call.  Host only; no device call.
+ * Choose the chunk and report the peak scratch of a call.
+ *   chunk_tokens  in/out.  On entry the requested chunk: > 0 is used as
+ *                 given (clamped to N and 2^23); <= 0 asks for the largest
+ *                 power-of-two multiple of 256 tokens, at most N, whose whole
+ *                 workspace fits scratch_budget_bytes.  On return the chunk a
+ *                 call will use.
+ *   scratch_budget_bytes  bound on the whole workspace, packed W included;
+ *                 0 = the default budget above.
+ *   peak_scratch_bytes  out (may be NULL): the workspace the returned chunk
+ *                 needs, which is the peak device scratch of a call.
+ * Returns FLCE_OK; FLCE_EWORKSPACE when even the smallest chunk (256 tokens,
+ * or N if fewer) does not fit the budget, or an explicit chunk exceeds an
+ * explicit budget (*chunk_tokens and *peak_scratch_bytes still report that
+ * chunk); FLCE_EUNSUPPORTED when a launch of the call would exceed 2^32
+ * work-items; FLCE_EINVAL / FLCE_EUNSUPPORTED for invalid sizes, as the
+ * calls below.  Host only; no device call.
  */
-int flce_plan(int64_t N, int64_t H, int64_t V, int dtype, size_t scratch_budget_bytes,
-              int64_t *chunk_tokens, size_t *peak_scratch_bytes);
+int flce_plan(int64_t N, int64_t H, int64_t V, int dtype, int64_t *chunk_tokens,
+              size_t scratch_budget_bytes, size_t *peak_scratch_bytes);
 
 /*
  * Forward and backward in one call.
@@ -307,6 +331,27 @@ int flce_kto_fwd(const void *X, const void *W, const int64_t *labels, int64_t n_
                  size_t workspace_bytes, void *stream);
 
 /*
+ * KTO's reference point z0, estimated from a batch the way its published
+ * definition does: the rows of X are n_seq completions, each scored under a
+ * prompt that is not its own (mismatched pairs), ref_logp their reference
+ * sums R; with S the policy's sum of log p(y_t) over a sequence's scored
+ * tokens,
+ *     z0 = max(0, (1 / n_seq) sum_s (S_s - R_s))
+ * computed on the device (forward only, fp64 mean), with no gradient.  The
+ * result is the host float *z0 that flce_kto_fwd_bwd takes.
+ *   X, W, labels, n_seq, T, H, V, dtype, ignore_index, chunk_seqs, workspace
+ *              as for flce_kto_fwd_bwd (workspace >= flce_kto_workspace_bytes(...))
+ *   ref_logp   device [n_seq] fp32, R (required)
+ *   z0         host float, out
+ *   logp, reward  device [n_seq] fp32 or NULL: S and S - R
+ * Same alignment rules and errors as flce_kto_fwd_bwd.
+ */
+int flce_kto_reference_point(const void *X, const void *W, const int64_t *labels, int64_t n_seq,
+                             int64_t T, int64_t H, int64_t V, int dtype, int64_t ignore_index,
+                             const float *ref_logp, int64_t chunk_seqs, float *z0, float *logp,
+                             float *reward, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * buf[i] *= *scale for i < n, in place, on the stream (no sync).  buf is a
  * device array of dtype (FLCE_F32 or FLCE_BF16); scale is a device fp32
  * scalar.  Used to apply an upstream gradient d(out)/d(loss) != 1 to dX, dW.
@@ -331,7 +376,7 @@ enum {
   FLCE_K_DW_GEMM = 6,     /* dW GEMM */
   FLCE_K_FINAL = 7,       /* final mean loss, fills */
   FLCE_K_PACK = 8,        /* per-chunk packing of X into the GEMM operand layout */
-  FLCE_K_PACK_W = 9,      /* per-call packing of W (as is and transposed) */
+  FLCE_K_PACK_W = 9,      /* per-call packing of W into the GEMM operand layout */
   FLCE_K_CE_ROWS = 10,    /* cross-entropy on given logits, one workgroup per row */
   FLCE_K_PAIRS = 11,      /* preference losses: label pass, per-pair step, final loss */
   FLCE_K_PAIR_ROWS = 12,  /* preference losses: gathering a chunk's rows, scattering dX */

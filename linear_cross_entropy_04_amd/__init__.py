@@ -30,7 +30,8 @@ __all__ = [
     "FusedLinearORPOLoss", "PAIR_KINDS", "flce_pair_workspace_bytes", "flce_pair_fwd_bwd",
     "flce_pair_fwd", "preference_loss", "sequence_logps", "FusedLinearSimPOLoss",
     "FusedLinearCPOLoss", "FusedLinearDPOLoss", "flce_kto_workspace_bytes", "flce_kto_fwd_bwd",
-    "flce_kto_fwd", "kto_loss", "kto_reference_point", "FusedLinearKTOLoss",
+    "flce_kto_fwd", "flce_kto_reference_point", "kto_loss", "kto_reference_point",
+    "FusedLinearKTOLoss",
 ]
 
 FLCE_F32 = 0
@@ -67,7 +68,7 @@ def _load():
     l = ctypes.CDLL(_LIB_PATH)
     l.flce_workspace_bytes.argtypes = [_i64, _i64, _i64, _i32, _i64]
     l.flce_workspace_bytes.restype = _sz
-    l.flce_plan.argtypes = [_i64, _i64, _i64, _i32, _sz, ctypes.POINTER(_i64),
+    l.flce_plan.argtypes = [_i64, _i64, _i64, _i32, ctypes.POINTER(_i64), _sz,
                             ctypes.POINTER(_sz)]
     l.flce_plan.restype = _i32
     l.flce_fwd_bwd.argtypes = [_p, _p, _p, _i64, _i64, _i64, _i32, _i64, _i64,
@@ -121,6 +122,9 @@ def _load():
     l.flce_kto_fwd.argtypes = [_p, _p, _p, _i64, _i64, _i64, _i64, _i32, _i64, _p, _p, _f, _f, _f,
                                _f, _i64, ctypes.POINTER(_f), _p, _p, _p, _sz, _p]
     l.flce_kto_fwd.restype = _i32
+    l.flce_kto_reference_point.argtypes = [_p, _p, _p, _i64, _i64, _i64, _i64, _i32, _i64, _p,
+                                           _i64, ctypes.POINTER(_f), _p, _p, _p, _sz, _p]
+    l.flce_kto_reference_point.restype = _i32
     l.flce_scale_inplace.argtypes = [_p, _i64, _i32, _p, _p]
     l.flce_scale_inplace.restype = _i32
     l.flce_status_string.argtypes = [_i32]
@@ -173,7 +177,7 @@ def flce_plan(N: int, H: int, V: int, dtype: int, scratch_budget_bytes: int = 0,
     """Returns (status, chunk_tokens, peak_scratch_bytes)."""
     c = _i64(chunk_tokens)
     peak = _sz(0)
-    st = _load().flce_plan(N, H, V, dtype, scratch_budget_bytes, ctypes.byref(c), ctypes.byref(peak))
+    st = _load().flce_plan(N, H, V, dtype, ctypes.byref(c), scratch_budget_bytes, ctypes.byref(peak))
     return int(st), int(c.value), int(peak.value)
 
 
@@ -566,6 +570,33 @@ def flce_kto_fwd(X: torch.Tensor, W: torch.Tensor, labels: torch.Tensor, n_seq: 
     if st != FLCE_OK:
         raise FLCEError(st, "flce_kto_fwd")
     return float(loss.value)
+
+
+def flce_kto_reference_point(X: torch.Tensor, W: torch.Tensor, labels: torch.Tensor, n_seq: int,
+                             ignore_index: int, ref_logp: torch.Tensor, chunk_seqs: int,
+                             workspace: torch.Tensor, logp: torch.Tensor | None = None,
+                             reward: torch.Tensor | None = None, stream=None) -> float:
+    """Call libflce's flce_kto_reference_point; returns z0."""
+    N, H = X.shape
+    V = W.shape[0]
+    if n_seq <= 0 or N % n_seq != 0:
+        raise ValueError(f"X has {N} rows: not n_seq = {n_seq} equal sequences")
+    _dev(X, "X")
+    _dev(W, "W", X.dtype, (V, H))
+    _dev(labels, "labels", torch.int64, (N,))
+    _dev(ref_logp, "ref_logp", torch.float32, (n_seq,))
+    _dev(workspace, "workspace")
+    for t, name in ((logp, "logp"), (reward, "reward")):
+        _dev(t, name, torch.float32, (n_seq,))
+    z0 = ctypes.c_float(0.0)
+    st = _load().flce_kto_reference_point(_ptr(X), _ptr(W), _ptr(labels), n_seq, N // n_seq, H, V,
+                                          _dtype_code(X), ignore_index, _ptr(ref_logp), chunk_seqs,
+                                          ctypes.byref(z0), _ptr(logp), _ptr(reward),
+                                          _ptr(workspace), workspace.numel(),
+                                          _stream(stream, X.device))
+    if st != FLCE_OK:
+        raise FLCEError(st, "flce_kto_reference_point")
+    return float(z0.value)
 
 
 def flce_scale_inplace(buf: torch.Tensor, scale: torch.Tensor, stream=None) -> None:
@@ -994,20 +1025,20 @@ def kto_reference_point(weight: torch.Tensor, input: torch.Tensor, target: torch
     completions each under a prompt that is not its own, target [n_seq, T]
     their tokens, ref_logp [n_seq] the reference model's summed
     log-probabilities of the same completions.  Returns z0 = max(0, mean of
-    S - ref_logp) with S the policy's sums (forward only, through
-    flce_kto_fwd), as a host float for kto_loss."""
+    S - ref_logp) with S the policy's sums, computed on the device by
+    flce_kto_reference_point, as a host float for kto_loss."""
     if target.dim() != 2:
         raise ValueError("target must be [n_seq, T]")
     if ref_logp.numel() != target.shape[0]:
         raise ValueError(f"ref_logp has {ref_logp.numel()} values for {target.shape[0]} sequences")
-    ones = torch.ones(target.shape[0], dtype=torch.int32, device=input.device)
-    x, y, n_seq, des = _kto_rows(input, target, ones)    # the flags do not enter S
-    S = torch.empty(n_seq, dtype=torch.float32, device=x.device)
-    zeros = torch.zeros(n_seq, dtype=torch.float32, device=x.device)
-    flce_kto_fwd(x.contiguous(), weight.detach().contiguous(), y, n_seq, ignore_index, des, zeros,
-                 0.1, 0.0, 1.0, 1.0, chunk_seqs, _kto_ws(x, weight, n_seq, chunk_seqs), logp=S)
-    d = S.double().cpu().numpy() - ref_logp.detach().double().cpu().numpy().reshape(-1)
-    return max(0.0, float(d.mean()))
+    x = input.reshape(-1, input.shape[-1]).contiguous()
+    if x.shape[0] != target.numel():
+        raise ValueError(f"input has {x.shape[0]} rows, target {target.numel()} tokens")
+    n_seq = target.shape[0]
+    w = weight.detach().contiguous()
+    return flce_kto_reference_point(x.detach(), w, target.reshape(-1).contiguous(), n_seq,
+                                    ignore_index, ref_logp.detach().reshape(-1).float().contiguous(),
+                                    chunk_seqs, _kto_ws(x, w, n_seq, chunk_seqs))
 
 
 class FusedLinearKTOLoss(torch.nn.Module):

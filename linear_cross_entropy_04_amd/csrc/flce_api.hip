@@ -21,6 +21,7 @@
 // losses insert a per-pair (or per-sequence) step between steps 2 and 3 that
 // turns the chunk's log-probabilities into loss terms and per-token weights.
 #include <algorithm>
+#include <cmath>
 #include <atomic>
 #include <cstring>
 #include <mutex>
@@ -41,12 +42,17 @@ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline int64_t round_up(int64_t a, int64_t b) { return cdiv(a, b) * b; }
 
-// Shape limits that keep every in-kernel offset within 32-bit ranges.
+// Shape limits.  N_valid is counted in 32 bits; a chunk's tokens are indexed
+// with 32-bit integers; V and H keep every offset inside a tile, a slice or a
+// packed block within 32 bits.  On top of these, every launch of a plan must
+// stay below 2^32 work-items (grid_fits).
 constexpr int64_t kMaxV = 8000000;
 constexpr int64_t kMaxH = 1 << 20;
-constexpr int64_t kMaxN = (int64_t)1 << 40;
-// Kernels index a chunk's tokens with 32-bit integers.
-constexpr int64_t kMaxChunk = (int64_t)1 << 30;
+constexpr int64_t kMaxN = ((int64_t)1 << 31) - 1;
+constexpr int64_t kMaxChunk = (int64_t)1 << 23;
+constexpr int64_t kMaxGridItems = ((int64_t)1 << 32) - 1;
+// Rows of cross-entropy on given logits: one workgroup of 1024 work-items per row.
+constexpr int64_t kMaxCeRows = kMaxGridItems / 1024;
 
 int check_sizes(int64_t N, int64_t H, int64_t V, int dtype) {
   if (dtype != FLCE_F32 && dtype != FLCE_BF16) return FLCE_EINVAL;
@@ -56,10 +62,45 @@ int check_sizes(int64_t N, int64_t H, int64_t V, int dtype) {
   return FLCE_OK;
 }
 
-// Largest power-of-two multiple of 256 tokens (capped at N) whose chunk
-// scratch fits the budget; -1 if even the smallest does not fit.  The budget
-// bounds what grows with the chunk; the packed copy of W (bf16 path) comes on
-// top of it.
+// Largest work-item count of any launch of a call with plan p (chunks of at
+// most p.C tokens).
+int64_t max_grid_items(const Plan &p) {
+  const int64_t C = std::max<int64_t>(p.C, 1), H = p.H, V = p.V;
+  int64_t m = C * 256;                                            // lse_combine
+  if (p.dtype == FLCE_BF16) {
+    const int64_t ct = cdiv(C, 256), vt = cdiv(V, 256);
+    m = std::max(m, vt * (p.nks_h / 2) * 256);                    // pack W
+    m = std::max(m, ct * (p.nks_h / 2) * 256);                    // pack X_c
+    m = std::max(m, vt * ct * 256);                               // forward tiles
+    m = std::max(m, ct * p.nks_z * 256);                          // dlogits
+    m = std::max(m, (int64_t)p.splitk * ct * cdiv(H, 256) * 256); // dX
+    m = std::max(m, vt * cdiv(H, 128) * 256);                     // dW
+  } else {
+    const int64_t T = kTileVF32;
+    m = std::max(m, cdiv(V, T) * cdiv(C, T) * 256);               // forward tiles
+    m = std::max(m, cdiv(C, T) * cdiv(H, T) * 256);               // dX
+    m = std::max(m, cdiv(V, T) * cdiv(H, T) * 256);               // dW
+  }
+  return m;
+}
+
+bool grid_fits(const Plan &p) { return max_grid_items(p) <= kMaxGridItems; }
+
+// Bytes of one row of W in the input dtype.
+inline size_t elem_bytes(int dtype) { return dtype == FLCE_BF16 ? 2 : 4; }
+
+// The budget used when the caller gives none: twice W's own size (room for
+// the packed copy of W and a chunk scratch as large as W again), at least
+// FLCE_DEFAULT_SCRATCH_FLOOR.  On the Llama-3-8B head this gives chunks of
+// 2048 tokens and 1.7 GB of scratch, against 2.1 GB for the whole bf16 logits.
+size_t default_budget(int64_t H, int64_t V, int dtype) {
+  const size_t w = (size_t)H * (size_t)V * elem_bytes(dtype);
+  return std::max<size_t>(2 * w, FLCE_DEFAULT_SCRATCH_FLOOR);
+}
+
+// Largest power-of-two multiple of 256 tokens (capped at N) whose whole
+// workspace fits the budget and whose launches fit their grids; -1 if even the
+// smallest does not.
 int64_t auto_chunk(int64_t N, int64_t H, int64_t V, int dtype, size_t budget) {
   if (N <= 0) return 0;
   int64_t best = -1;
@@ -67,19 +108,23 @@ int64_t auto_chunk(int64_t N, int64_t H, int64_t V, int dtype, size_t budget) {
     const int64_t Cc = std::min(C, N);
     Plan p;
     make_plan(N, H, V, dtype, Cc, &p);
-    if (p.total - p.off_z > budget) break;     // the chunk-dependent part (not the packed W)
+    if (p.total > budget || !grid_fits(p)) break;
     best = Cc;
     if (C >= N) break;
   }
   return best;
 }
 
+// The chunk of a call: the requested one (clamped to N and kMaxChunk) or, for
+// req <= 0, the largest that fits the budget (0: the default budget).  *fits
+// says whether the workspace of the returned chunk fits the budget; when
+// nothing fits, the smallest chunk is returned.
 int64_t resolve_chunk(int64_t N, int64_t H, int64_t V, int dtype, int64_t req, size_t budget,
                       bool *fits) {
   *fits = true;
   if (N <= 0) return 0;
   if (req > 0) return std::min(std::min(req, N), kMaxChunk);
-  const int64_t c = auto_chunk(N, H, V, dtype, budget ? budget : FLCE_DEFAULT_SCRATCH_BUDGET);
+  const int64_t c = auto_chunk(N, H, V, dtype, budget ? budget : default_budget(H, V, dtype));
   if (c > 0) return c;
   *fits = false;
   return std::min<int64_t>(256, N);
@@ -211,8 +256,8 @@ int chunk_backward(const Plan &p, char *ws, const void *W, int64_t ii, const Chu
     LAUNCH(FLCE_K_DLOGITS, launch_dlogits_bf16(Zp, p.nks_z, io.c, Vi,
                                                (const float *)(ws + p.off_pmt), lse, io.lab, ii,
                                                io.wr, sc, s));
-    LAUNCH(FLCE_K_DX_GEMM, launch_dx_bf16(Zp, p.nks_z, (const uint16_t *)(ws + p.off_wtp), io.c,
-                                          Hi, Vi, p.splitk, p.ksplit, dxp, s));
+    LAUNCH(FLCE_K_DX_GEMM, launch_dx_bf16(Zp, p.nks_z, (const uint16_t *)(ws + p.off_wp), p.nks_h,
+                                          io.c, Hi, Vi, p.splitk, p.ksplit, dxp, s));
     LAUNCH(FLCE_K_DX_REDUCE, launch_dx_reduce_bf16(dxp, p.splitk, io.c, Hi, (uint16_t *)io.dXc, s));
     LAUNCH(FLCE_K_DW_GEMM, launch_dw_bf16(Zp, p.nks_z, Xp, p.nks_h, io.c, Hi, Vi, dW, io.acc_dw, s));
   } else {
@@ -226,17 +271,13 @@ int chunk_backward(const Plan &p, char *ws, const void *W, int64_t ii, const Chu
   return FLCE_OK;
 }
 
-// Pack W once per call (bf16 path): Wp, and WTp too when a backward follows.
-int pack_weight(const Plan &p, char *ws, const void *W, bool bwd, hipStream_t s) {
+// Pack W once per call (bf16 path) into Wp, which the forward reads along
+// its rows and dX transposed.
+int pack_weight(const Plan &p, char *ws, const void *W, hipStream_t s) {
   if (p.dtype != FLCE_BF16) return FLCE_OK;
   const int Hi = (int)p.H, Vi = (int)p.V;
-  if (bwd)      // Wp and WTp from one read of W
-    LAUNCH(FLCE_K_PACK_W, launch_pack_t_bf16((const uint16_t *)W, Vi, Hi,
-                                             (uint16_t *)(ws + p.off_wtp), p.nks_z,
-                                             (uint16_t *)(ws + p.off_wp), p.nks_h, s));
-  else
-    LAUNCH(FLCE_K_PACK_W, launch_pack_bf16((const uint16_t *)W, Vi, Hi,
-                                           (uint16_t *)(ws + p.off_wp), p.nks_h, s));
+  LAUNCH(FLCE_K_PACK_W, launch_pack_bf16((const uint16_t *)W, Vi, Hi,
+                                         (uint16_t *)(ws + p.off_wp), p.nks_h, s));
   return FLCE_OK;
 }
 
@@ -267,6 +308,7 @@ int run(bool bwd, const void *X, const void *W, const int64_t *labels, int64_t N
   const int64_t C = resolve_chunk(N, H, V, dtype, chunk_tokens, 0, &fits);
   Plan p;
   make_plan(N, H, V, dtype, C, &p);
+  if (!grid_fits(p)) return FLCE_EUNSUPPORTED;
   if (workspace_bytes < p.total) return FLCE_EWORKSPACE;
 
   hipStream_t s = (hipStream_t)stream;
@@ -278,7 +320,7 @@ int run(bool bwd, const void *X, const void *W, const int64_t *labels, int64_t N
   if (bwd && N == 0 && !o.accumulate_dw) LAUNCH(FLCE_K_FINAL, launch_fill_f32(dW, V * H, 0.f, s));
 
   if (N > 0) {
-    st = pack_weight(p, ws, W, bwd, s);
+    st = pack_weight(p, ws, W, s);
     if (st != FLCE_OK) return st;
   }
   for (int64_t c0 = 0; c0 < N; c0 += C) {
@@ -313,23 +355,25 @@ int run(bool bwd, const void *X, const void *W, const int64_t *labels, int64_t N
 }  // namespace
 
 int choose_splitk(int64_t C, int64_t H, int64_t V) {
-  // Spread the dX GEMM's few output tiles over the 256 CUs: pick the split
-  // count that fills whole waves of 256 workgroups, with every split at least
-  // 1024 vocabulary rows deep.  One full wave beats two (fewer fp32 partials
-  // to write and reduce: dX 0.797 against 0.802 ms, the reduction 0.014
-  // against 0.024 ms on the Llama-3-8B head at chunk 1024).
-  const int64_t tiles = cdiv(C, 256) * cdiv(H, 256);
-  double best = -1.0;
+  // Spread the dX GEMM's few output tiles over the 256 CUs by splitting the
+  // vocabulary (its k) S ways, every split at least 1024 rows deep.  Time
+  // model: the main loop takes ceil(units / 256) waves of units = tiles S
+  // workgroups, each wave the time of 256 units' share of the GEMM; the S
+  // fp32 partial sums are written and read back once.  On the Llama-3-8B head
+  // at chunk 1024 it picks one full wave (S = 4); measured, one wave beats two
+  // (dX 0.797 against 0.802 ms, the reduction 0.014 against 0.024 ms).
+  const double tiles = (double)(cdiv(C, 256) * cdiv(H, 256));
+  const double gemm = 2.0 * (double)C * (double)H * (double)V / 1.3e15;   // s at one full wave
+  const double part = 8.0 * (double)C * (double)H / 6.0e12;              // s per split
+  double best = 1e300;
   int bestS = 1;
   for (int S = 1; S <= kMaxSplitK; ++S) {
     if (S > 1 && V / S < 1024) break;
-    const int64_t units = tiles * S;
-    const int64_t waves = cdiv(units, 256);
-    const double eff = (double)units / (double)(waves * 256);
-    const double fill = std::min(1.0, (double)units / 256.0);
-    const double score = eff * fill - 0.001 * S;
-    if (score > best + 1e-12) {
-      best = score;
+    const double units = tiles * S;
+    const double waves = std::ceil(units / 256.0);
+    const double t = gemm * waves * 256.0 / units + (S > 1 ? part * S : 0.0);
+    if (t < best * (1.0 - 1e-9)) {
+      best = t;
       bestS = S;
     }
   }
@@ -361,12 +405,9 @@ void make_plan(int64_t N, int64_t H, int64_t V, int dtype, int64_t C, Plan *p) {
     // packed layouts: rows and columns padded to 256 (see flce_internal.h)
     p->nks_z = cdiv(V, 256) * 8;
     p->nks_h = cdiv(H, 256) * 8;
-    const size_t cpad = (size_t)round_up(C, 256), vpad = (size_t)round_up(V, 256),
-                 hpad = (size_t)round_up(H, 256);
+    const size_t cpad = (size_t)round_up(C, 256), vpad = (size_t)round_up(V, 256);
     p->off_wp = o;                       // W packed once per call (rows = vocabulary)
     o += align256(vpad * p->nks_h * 64);
-    p->off_wtp = o;                      // and transposed (rows = hidden), for dX
-    o += align256(hpad * p->nks_z * 64);
     p->off_z = o;                        // logits, then G, of the chunk (rows = tokens)
     o += align256(cpad * p->nks_z * 64);
     p->off_xp = o;                       // the chunk's X (rows = tokens)
@@ -408,8 +449,8 @@ FLCE_API size_t flce_workspace_bytes(int64_t N, int64_t H, int64_t V, int dtype,
   return p.total;
 }
 
-FLCE_API int flce_plan(int64_t N, int64_t H, int64_t V, int dtype, size_t scratch_budget_bytes,
-                       int64_t *chunk_tokens, size_t *peak_scratch_bytes) {
+FLCE_API int flce_plan(int64_t N, int64_t H, int64_t V, int dtype, int64_t *chunk_tokens,
+                       size_t scratch_budget_bytes, size_t *peak_scratch_bytes) {
   const int st = check_sizes(N, H, V, dtype);
   if (st != FLCE_OK) return st;
   if (!chunk_tokens) return FLCE_EINVAL;
@@ -419,6 +460,9 @@ FLCE_API int flce_plan(int64_t N, int64_t H, int64_t V, int dtype, size_t scratc
   make_plan(N, H, V, dtype, C, &p);
   *chunk_tokens = C;
   if (peak_scratch_bytes) *peak_scratch_bytes = p.total;
+  if (!grid_fits(p)) return FLCE_EUNSUPPORTED;
+  // an explicit chunk is checked against an explicit budget too
+  if (scratch_budget_bytes && p.total > scratch_budget_bytes) fits = false;
   return fits ? FLCE_OK : FLCE_EWORKSPACE;
 }
 
@@ -478,7 +522,7 @@ int run_ce(bool grad, void *logits, const int64_t *labels, int64_t N, int64_t V,
            void *stream) {
   if (dtype != FLCE_F32 && dtype != FLCE_BF16) return FLCE_EINVAL;
   if (N < 0 || V <= 0 || !loss || !workspace) return FLCE_EINVAL;
-  if (N > kMaxN || V > ((int64_t)1 << 31)) return FLCE_EUNSUPPORTED;
+  if (N > kMaxCeRows || V > ((int64_t)1 << 31)) return FLCE_EUNSUPPORTED;
   if (N > 0 && (!logits || !labels)) return FLCE_EINVAL;
   if (reduction != kReduceMean && reduction != kReduceSum && reduction != kReduceNone)
     return FLCE_EINVAL;
@@ -608,6 +652,7 @@ int run_pairs(bool bwd, int kind, const void *X, const void *W, const int64_t *l
   if (bwd && misaligned(dW, 4)) return FLCE_EINVAL;
   PairLayout L;
   pair_layout(B, T, H, V, dtype, chunk_pairs, &L);
+  if (!grid_fits(L.p)) return FLCE_EUNSUPPORTED;
   if (workspace_bytes < L.total) return FLCE_EWORKSPACE;
 
   const Plan &p = L.p;
@@ -626,7 +671,7 @@ int run_pairs(bool bwd, int kind, const void *X, const void *W, const int64_t *l
   float *lor = log_odds_ratio ? log_odds_ratio : (float *)(ws + L.off_lor);
 
   LAUNCH(FLCE_K_PAIRS, launch_pairs_labels(labels, 2 * half, half, V, ii, sc, s));
-  st = pack_weight(p, ws, W, bwd, s);
+  st = pack_weight(p, ws, W, s);
   if (st != FLCE_OK) return st;
   for (int64_t p0 = 0; p0 < B; p0 += L.k) {
     const int64_t kk = std::min(L.k, B - p0);
@@ -802,13 +847,16 @@ void kto_layout(int64_t S, int64_t T, int64_t H, int64_t V, int dtype, int64_t c
   L->total = o;
 }
 
+// refpoint: forward only, and the call's scalar result is the reference point
+// z0 = max(0, mean of r) instead of the loss (the flags do not enter r).
 int run_kto(bool bwd, const void *X, const void *W, const int64_t *labels, int64_t S, int64_t T,
             int64_t H, int64_t V, int dtype, int64_t ii, const KtoParams &kp, int64_t chunk_seqs,
             float *loss, void *dX, float *dW, float *logp, float *reward, void *workspace,
-            size_t workspace_bytes, void *stream) {
+            size_t workspace_bytes, void *stream, bool refpoint = false) {
   int st = kto_check(S, T, H, V, dtype);
   if (st != FLCE_OK) return st;
-  if (!loss || !X || !W || !labels || !workspace || !kp.desirable || !kp.ref) return FLCE_EINVAL;
+  if (!loss || !X || !W || !labels || !workspace || !kp.ref) return FLCE_EINVAL;
+  if (!kp.desirable && !refpoint) return FLCE_EINVAL;
   if (bwd && (!dX || !dW)) return FLCE_EINVAL;
   if (misaligned(workspace, 256) || misaligned(labels, 8) || misaligned(kp.desirable, 4) ||
       misaligned(kp.ref, 4) || misaligned(logp, 4) || misaligned(reward, 4))
@@ -820,6 +868,7 @@ int run_kto(bool bwd, const void *X, const void *W, const int64_t *labels, int64
   if (bwd && misaligned(dW, 4)) return FLCE_EINVAL;
   KtoLayout L;
   kto_layout(S, T, H, V, dtype, chunk_seqs, &L);
+  if (!grid_fits(L.p)) return FLCE_EUNSUPPORTED;
   if (workspace_bytes < L.total) return FLCE_EWORKSPACE;
 
   const Plan &p = L.p;
@@ -833,7 +882,7 @@ int run_kto(bool bwd, const void *X, const void *W, const int64_t *labels, int64
   float *rwo = reward ? reward : (float *)(ws + L.off_rew);
 
   LAUNCH(FLCE_K_PAIRS, launch_pairs_labels(labels, S * T, 0, V, ii, sc, s));
-  st = pack_weight(p, ws, W, bwd, s);
+  st = pack_weight(p, ws, W, s);
   if (st != FLCE_OK) return st;
   for (int64_t s0 = 0; s0 < S; s0 += L.k) {
     const int64_t kk = std::min(L.k, S - s0);
@@ -855,8 +904,10 @@ int run_kto(bool bwd, const void *X, const void *W, const int64_t *labels, int64
       if (st != FLCE_OK) return st;
     }
   }
-  // loss = mean of the terms (no NLL term)
-  LAUNCH(FLCE_K_PAIRS, launch_pairs_final(term, term, S, 0.f, 1.f, sc, s));
+  if (refpoint)     // z0 = max(0, mean over sequences of r = S - R)
+    LAUNCH(FLCE_K_PAIRS, launch_kto_refpoint(rwo, S, sc, s));
+  else              // loss = mean of the terms (no NLL term)
+    LAUNCH(FLCE_K_PAIRS, launch_pairs_final(term, term, S, 0.f, 1.f, sc, s));
   Scalars host;
   CK(hipMemcpyAsync(&host, sc, sizeof(host), hipMemcpyDeviceToHost, s));
   CK(hipStreamSynchronize(s));
@@ -909,6 +960,16 @@ FLCE_API int flce_kto_fwd(const void *X, const void *W, const int64_t *labels, i
                        flce::kto_params(desirable, ref_logp, beta, z0, lambda_d, lambda_u),
                        chunk_seqs, loss, nullptr, nullptr, logp, reward, workspace,
                        workspace_bytes, stream);
+}
+
+FLCE_API int flce_kto_reference_point(const void *X, const void *W, const int64_t *labels,
+                                      int64_t n_seq, int64_t T, int64_t H, int64_t V, int dtype,
+                                      int64_t ignore_index, const float *ref_logp,
+                                      int64_t chunk_seqs, float *z0, float *logp, float *reward,
+                                      void *workspace, size_t workspace_bytes, void *stream) {
+  return flce::run_kto(false, X, W, labels, n_seq, T, H, V, dtype, ignore_index,
+                       flce::kto_params(nullptr, ref_logp, 0.f, 0.f, 1.f, 1.f), chunk_seqs, z0,
+                       nullptr, nullptr, logp, reward, workspace, workspace_bytes, stream, true);
 }
 
 FLCE_API int flce_scale_inplace(void *buf, int64_t n, int dtype, const float *scale,

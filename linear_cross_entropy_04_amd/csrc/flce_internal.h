@@ -39,7 +39,7 @@ struct Plan {
   int64_t nvt = 0;      // vocabulary tiles = log-sum-exp partials per token
   int splitk = 0;       // K-splits of the dX GEMM (0: the fp32 path writes dX directly)
   int64_t ksplit = 0;   // vocabulary rows per split (multiple of 64)
-  size_t off_wp = 0, off_wtp = 0, off_z = 0, off_xp = 0, off_pm = 0, off_ps = 0, off_zy = 0, off_lse = 0,
+  size_t off_wp = 0, off_z = 0, off_xp = 0, off_pm = 0, off_ps = 0, off_zy = 0, off_lse = 0,
          off_rowloss = 0, off_dxp = 0, off_scal = 0, total = 0;
   size_t off_pmt = 0;   // bf16 path: the partial maxima again, [partial][token]
 };
@@ -83,13 +83,10 @@ hipError_t launch_fwd_tile_bf16(const uint16_t *Wp, const uint16_t *Xp, int64_t 
 hipError_t launch_dlogits_bf16(uint16_t *Zp, int64_t nks_z, int c, int V, const float *pmt,
                                const float *lse_c, const int64_t *labels_c, int64_t ii,
                                const float *wrow_c, const Scalars *sc, hipStream_t s);
-// Pack the transpose of a row-major [R][K] matrix into PT (rows K padded to
-// 256, nks_t column slices covering R) and, if P is not null, the matrix
-// itself into P (rows R padded to 256, nks_p slices), reading it once.
-hipError_t launch_pack_t_bf16(const uint16_t *src, int R, int K, uint16_t *PT, int64_t nks_t,
-                              uint16_t *P, int64_t nks_p, hipStream_t s);
-hipError_t launch_dx_bf16(const uint16_t *Gp, int64_t nks_z, const uint16_t *WTp, int c, int H,
-                          int V, int splitk, int64_t ksplit, float *dxp, hipStream_t s);
+// dX partials from G (Zp) and W read transposed from Wp (nks_h slices).
+hipError_t launch_dx_bf16(const uint16_t *Gp, int64_t nks_z, const uint16_t *Wp, int64_t nks_h,
+                          int c, int H, int V, int splitk, int64_t ksplit, float *dxp,
+                          hipStream_t s);
 hipError_t launch_dx_reduce_bf16(const float *dxp, int splitk, int c, int H, uint16_t *dXc,
                                  hipStream_t s);
 hipError_t launch_dw_bf16(const uint16_t *Gp, int64_t nks_z, const uint16_t *Xp, int64_t nks_h,
@@ -133,12 +130,14 @@ hipError_t launch_pairs(int kind, const float *lp, const float *rl, const int64_
 // loss term at s0 + j and (wrow not null) the per-row backward weights.
 struct KtoParams {
   float beta, z0, lambda_d, lambda_u;
-  const int32_t *desirable;   // [n_seq], nonzero: desirable
+  const int32_t *desirable;   // [n_seq], nonzero: desirable (null: all desirable)
   const float *ref;           // [n_seq] the reference model's S
 };
 hipError_t launch_kto_seqs(const float *lp, const int64_t *labels_c, int64_t ii, int64_t T,
                           int k, int64_t s0, int64_t n_seq, const KtoParams &kp, float *wrow,
                           float *term, float *logp, float *reward, hipStream_t s);
+// sc->loss = max(0, mean of the n_seq rewards): KTO's reference point.
+hipError_t launch_kto_refpoint(const float *reward, int64_t n_seq, Scalars *sc, hipStream_t s);
 // sc->loss = alpha NLL + lambda mean pair term, sc->aux = NLL.
 hipError_t launch_pairs_final(const float *nll_sum, const float *pair_term, int64_t n_pairs,
                               float alpha, float lambda, Scalars *sc, hipStream_t s);

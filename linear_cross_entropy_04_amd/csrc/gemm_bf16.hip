@@ -11,16 +11,17 @@
 //               tokens, k = vocabulary);
 //   dlogits   Zp rewritten in place into G = (softmax - onehot) / N_valid;
 //   dX        dX_c  = G_c W        M = c, N = H, K = V (split-K, fp32 partials),
-//             W from WTp, a second packed copy of W made once per call (rows =
-//             hidden, k = vocabulary);
+//             W read transposed from Wp;
 //   dW        dW   (+)= G_c^T X_c  M = V, N = H, K = c (fp32)
 //
 // GEMM tiles: a workgroup of 4 waves (2 x 2) computes a BM x BN fp32 tile with
 // v_mfma_f32_32x32x16_bf16, each wave a (BM/2) x (BN/2) quarter of 32 x 32
-// blocks.  Operands flow global -> LDS through direct-to-LDS copies
-// (global_load_lds_dwordx4: lane l of a wave writes 16 bytes at LDS base +
-// 16 l) in k-slices of 32, STAGES slices in flight, each admitted by an
-// explicit vmcnt wait and one s_barrier.
+// blocks.  Operands flow global -> LDS through direct-to-LDS buffer loads
+// (buffer_load_dwordx4 ... lds: lane l of a wave writes 16 bytes at the LDS
+// address in M0 + 16 l; the source is a buffer descriptor for the slice, a
+// scalar offset for the 1 KB piece and the lane's constant 16-byte offset) in
+// k-slices of 32, STAGES slices in flight, each admitted by an explicit vmcnt
+// wait and one s_barrier.
 //
 // The packed layout (Wp, Xp, Zp): a matrix of R rows and K columns is stored
 // as 16 KB blocks of 256 rows x 32 columns; block (rt, ks) at element
@@ -54,7 +55,6 @@ typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr int BK = 32;             // k per pipeline slice
 constexpr int NTHREADS = 256;
@@ -76,14 +76,6 @@ __device__ __forceinline__ uint32_t lds_addr(const char *p) {
 // half f = (k / 16) % 2 inside a 1 KB fragment.
 __device__ __forceinline__ int pk_slot(int r32, int h, int f) {
   return (h << 5) + (r32 ^ (h << 2) ^ (f << 3));
-}
-
-// Element offset of (r, k) in a packed matrix with nks 32-column slices.
-__device__ __forceinline__ int64_t pk_off(int64_t r, int64_t k, int64_t nks) {
-  const int64_t blk = (r >> 8) * nks + (k >> 5);
-  const int rr = (int)(r & 255), kk = (int)(k & 31);
-  const int frag = ((rr >> 5) << 1) + (kk >> 4);
-  return (blk << 13) + (frag << 9) + (pk_slot(rr & 31, (kk >> 3) & 1, kk >> 4) << 3) + (kk & 7);
 }
 
 // Map the hardware's round-robin placement of workgroups over the 8 XCDs to
@@ -116,70 +108,58 @@ struct Tile {
   static constexpr int WM = BM / 2, WN = BN / 2, MI = WM / 32, NI = WN / 32;
   static constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2;
   static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
-  static constexpr int NPER = (A_BYTES + B_BYTES) / 4096;   // copies per thread per slice
+  static constexpr int NA = A_BYTES / 4096, NB = B_BYTES / 4096;   // copies per thread per slice
+  static constexpr int NPER = NA + NB;
   static constexpr int LDS = STAGES * STAGE_BYTES;
 };
 
-// One GEMM operand tile in a packed matrix P.
-//   PACKED:   p = the block of the tile's first row and of the range's first
-//             k; slice s at p + s * 8192.
-//   PACKED_T: p = the block of row tile 0 and of the column slice of the
-//             tile's first operand row; ld = nks_P * 8192 (one row tile of P);
-//             kb = the range's first k, a row of P (a multiple of 32).
+// One GEMM operand tile in a packed matrix (byte addresses).
+//   PACKED:   base = the block of the tile's first row and of the range's
+//             first k; slice s at base + 16 KB s.
+//   PACKED_T: base = the block of row tile 0 and of the column slice of the
+//             tile's first operand row; ld = bytes of one row tile of the
+//             matrix; kb = the range's first k, a row of the matrix (a
+//             multiple of 32).
 struct Op {
-  const uint16_t *p;
+  const char *base;
   int64_t ld;
   int64_t kb;
 };
 
-// Copy k-slice [k0, k0 + 32) (relative to the range) of an operand tile of
-// ROWS rows into LDS: ROWS / 16 pieces of 1 KB, piece b at LDS byte address
-// tile + 1 KB b.  PACKED_T pieces 2q, 2q+1 are the two fragments of operand
-// rows 32q..32q+31.  Only the source's lane offset is per lane.
-template <int KIND, int ROWS>
-__device__ __forceinline__ void issue_tile(const Op &op, int k0, uint32_t tile) {
-  constexpr int N = ROWS * BK * 2 / 4096;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), l = threadIdx.x & 63;
-  const uint16_t *base;
-  if constexpr (KIND == PACKED) {
-    base = op.p + (int64_t)(k0 >> 5) * 8192;
-  } else {
-    const int64_t kr = op.kb + k0;                 // row of P
-    base = op.p + (kr >> 8) * op.ld + (((kr & 255) >> 5) << 10);
-  }
-#pragma unroll
-  for (int i = 0; i < N; ++i) {
-    const int blk = i * 4 + w;                   // 1 KB piece written by this wave
-    const uint16_t *src;
-    if constexpr (KIND == PACKED)
-      src = base + blk * 512 + l * 8;
-    else
-      src = base + (blk >> 1) * 8192 + (blk & 1) * 512 + l * 8;
-    __builtin_amdgcn_global_load_lds(src, (lds_void *)(uintptr_t)(tile + blk * 1024), 16, 0, 0);
-  }
+// Buffer descriptor of a slice: raw (stride 0) 32-bit words, no range check
+// that a packed slice could reach.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t slice_rsrc(const char *p) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(p), (short)0, 0x7fffffff, 0x00020000);
 }
 
-// MFMA fragment of operand rows r0..r0+31 (r0 % 32 == 0), k = 16 kk .. 16 kk
-// + 15 of an LDS slice: lane l holds row r0 + l%32, k = 16 kk + 8 (l/32) + 0..7.
+// Copy i (0 .. ROWS/64 - 1) of this thread for k-slice [k0, k0 + 32) (relative
+// to the range) of an operand tile of ROWS rows: 1 KB piece blk = 4 i + wave,
+// written at LDS byte address tile + 1 KB blk.  PACKED_T pieces 2q, 2q+1 are
+// the two fragments of operand rows 32q..32q+31.  Only the lane's 16-byte
+// offset is per lane; the slice's descriptor and the piece offset are scalar.
 template <int KIND>
-__device__ __forceinline__ bf16x8 frag(const char *tile, int r0, int kk) {
-  const int l = threadIdx.x & 63;
+__device__ __forceinline__ void copy_piece(const Op &op, int k0, uint32_t tile, int i) {
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), l = threadIdx.x & 63;
+  const int blk = i * 4 + w;
+  const char *slice;
+  int off;
   if constexpr (KIND == PACKED) {
-    const char *f = tile + ((((r0 >> 5) << 1) + kk) << 10);
-    return *(const bf16x8 *)(f + (pk_slot(l & 31, l >> 5, kk) << 4));
+    slice = op.base + (int64_t)(k0 >> 5) * 16384;
+    off = blk * 1024;
   } else {
-    // operand row r is column r of the slice's P rows, operand k its row;
-    // lane j of a 16-lane group names the 4 operand rows r..r+3 at one k
-    const int g = l >> 4, j = l & 15;
-    const int r = r0 + ((g & 1) << 4) + ((j & 3) << 2);
-    const int k = kk * 16 + ((g >> 1) << 3) + (j >> 2);
-    const int h = (r >> 3) & 1, f = (r >> 4) & 1;
-    const char *p = tile + ((((r >> 5) << 1) + f) << 10) + ((r & 7) << 1);
-    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p + (pk_slot(k, h, f) << 4)));
-    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p + (pk_slot(k + 4, h, f) << 4)));
-    const i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-    return __builtin_bit_cast(bf16x8, v);
+    const int64_t kr = op.kb + k0;                 // row of the matrix
+    slice = op.base + (kr >> 8) * op.ld + (((kr & 255) >> 5) << 11);
+    off = (blk >> 1) * 16384 + (blk & 1) * 1024;
   }
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(slice_rsrc(slice), (lds_void *)(uintptr_t)(tile + blk * 1024),
+                                           16, l * 16, __builtin_amdgcn_readfirstlane(off), 0, 0);
+}
+
+// Copy g (0 .. NPER - 1) of a stage: the A operand's pieces, then B's.
+template <class T>
+__device__ __forceinline__ void stage_copy(const Op &a, const Op &b, int k0, uint32_t st, int g) {
+  if (g < T::NA) copy_piece<T::KA>(a, k0, st, g);
+  else copy_piece<T::KB>(b, k0, st + T::A_BYTES, g - T::NA);
 }
 
 // s_waitcnt vmcnt(N) leaving the other counters unconstrained.
@@ -187,15 +167,6 @@ template <int N>
 __device__ __forceinline__ void wait_vm() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-
-// s_waitcnt vmcnt(groups * PER) for a runtime number of groups in 0..3.
-template <int PER>
-__device__ __forceinline__ void wait_groups(int groups) {
-  if (groups >= 3) wait_vm<3 * PER>();
-  else if (groups == 2) wait_vm<2 * PER>();
-  else if (groups == 1) wait_vm<PER>();
-  else wait_vm<0>();
 }
 
 // Workgroup barrier without the memory fence of __syncthreads (which would
@@ -206,129 +177,6 @@ __device__ __forceinline__ void bar() {
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
-
-template <class T>
-__device__ __forceinline__ void load_frags(const char *st, int kk, bf16x8 (&fa)[T::MI],
-                                           bf16x8 (&fb)[T::NI]) {
-  const int w = threadIdx.x >> 6;
-  const int wm = w >> 1, wn = w & 1;
-#pragma unroll
-  for (int i = 0; i < T::MI; ++i) fa[i] = frag<T::KA>(st, wm * T::WM + 32 * i, kk);
-#pragma unroll
-  for (int j = 0; j < T::NI; ++j) fb[j] = frag<T::KB>(st + T::A_BYTES, wn * T::WN + 32 * j, kk);
-}
-
-template <class T>
-__device__ __forceinline__ void mfma_block(const bf16x8 (&fa)[T::MI], const bf16x8 (&fb)[T::NI],
-                                           f32x16 (&acc)[T::MI][T::NI]) {
-#pragma unroll
-  for (int i = 0; i < T::MI; ++i)
-#pragma unroll
-    for (int j = 0; j < T::NI; ++j)
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
-}
-
-// Copies of slice `step` into the ring slot at LDS byte address lds0 +
-// (step % STAGES) slots; past the last slice (step >= nk) they copy the last
-// slice again (still in cache) into a slot that is not read again.
-template <class T>
-__device__ __forceinline__ void issue_stage(const Op &a, const Op &b, int step, int nk,
-                                            uint32_t lds0) {
-  const uint32_t st = lds0 + (uint32_t)((step % T::STAGES) * T::STAGE_BYTES);
-  const int k0 = (step < nk ? step : nk - 1) * BK;
-  issue_tile<T::KA, T::BM>(a, k0, st);
-  issue_tile<T::KB, T::BN>(b, k0, st + T::A_BYTES);
-}
-
-// Instruction-group order for the scheduler (sched_group_barrier masks:
-// 0x008 MFMA, 0x010 VMEM, 0x100 DS read).  Before the barrier: each of the
-// half-step's MFMAs is followed by one fragment read of the next half-step.
-// After it: each MFMA is followed by one fragment read, then by one slice
-// copy, so the reads start first and the MFMA pipe never waits on issue.
-template <class T>
-__device__ __forceinline__ void order_first_half() {
-  constexpr int M = T::MI * T::NI, R = T::MI + T::NI;
-#pragma unroll
-  for (int i = 0; i < M; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    if (i < R) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-  }
-}
-
-template <class T>
-__device__ __forceinline__ void order_second_half() {
-  constexpr int M = T::MI * T::NI, R = T::MI + T::NI, G = T::NPER;
-#pragma unroll
-  for (int i = 0; i < M; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    if (i < R) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    else if (i < R + G) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
-  }
-  if (R + G > M) __builtin_amdgcn_sched_group_barrier(0x010, R + G - M, 0);
-}
-
-// acc[i][j] is the 32 x 32 block (i, j) of the wave's quarter.  Lane l of
-// block (i, j), register e, holds row 32 i + 8 (e/4) + 4 (l/32) + e%4 and
-// column 32 j + l%32 of the quarter.  acc enters initialised by the caller.
-//
-// Each 32-deep slice is two MFMA half-steps (k 0..15, 16..31).  The wait and
-// barrier that admit slice t+1 sit between the two half-steps of slice t, so
-// the fragments of slice t+1's first half-step are read from LDS while the
-// MFMAs of slice t's second half-step run, and the barrier itself waits with
-// MFMAs in flight.  Slice t+STAGES-1 is copied into the buffer of slice t-1,
-// whose reads every wave finished before that barrier.  Every iteration
-// issues one slice of copies (the last slice again past the end), so the wait is always for
-// all but the newest STAGES-3 slices, and the last slice is peeled: the loop
-// body is one straight path.  Packed operands carry zero padding up to whole
-// slices, so no copy needs a bounds check.
-template <class T>
-__device__ __forceinline__ void mainloop(const Op &a, const Op &b, int klen, char *smem,
-                                         f32x16 (&acc)[T::MI][T::NI]) {
-  const int nk = (klen + BK - 1) / BK;
-  if (nk > 0) {
-    const uint32_t lds0 = lds_addr(smem);
-#pragma unroll
-    for (int s = 0; s < T::STAGES - 1; ++s) issue_stage<T>(a, b, s, nk, lds0);
-    wait_vm<(T::STAGES - 2) * T::NPER>();
-    bar();
-    bf16x8 fa0[T::MI], fb0[T::NI], fa1[T::MI], fb1[T::NI];
-    load_frags<T>(smem, 0, fa0, fb0);
-    for (int t = 0; t < nk - 1; ++t) {
-      const char *st = smem + (t % T::STAGES) * T::STAGE_BYTES;
-      load_frags<T>(st, 1, fa1, fb1);
-      mfma_block<T>(fa0, fb0, acc);
-      order_first_half<T>();
-      // slice t+1 must have landed; slices t+2 .. t+STAGES-2 may stay in flight
-      wait_vm<(T::STAGES - 3) * T::NPER>();
-      bar();
-      load_frags<T>(smem + ((t + 1) % T::STAGES) * T::STAGE_BYTES, 0, fa0, fb0);
-      issue_stage<T>(a, b, t + T::STAGES - 1, nk, lds0);
-      mfma_block<T>(fa1, fb1, acc);
-      order_second_half<T>();
-    }
-    load_frags<T>(smem + ((nk - 1) % T::STAGES) * T::STAGE_BYTES, 1, fa1, fb1);
-    mfma_block<T>(fa0, fb0, acc);
-    mfma_block<T>(fa1, fb1, acc);
-  }
-  // every wave is done with the LDS slices and no copy is still writing them;
-  // the caller may reuse LDS
-  wait_vm<0>();
-  bar();
-}
-
-// ---------------------------------------------------------------- transposed main loop
-// Main loop of a tile whose operands are both read transposed (dW).  The
-// compiler guards every ds_read_b64_tr_b16 it emits with a wait for all
-// direct-to-LDS copies in flight, which would drain the copy pipeline once
-// per slice; so here the transposing reads are issued as inline asm, their
-// completion is awaited explicitly (s_waitcnt lgkmcnt(0), tied to the
-// fragment registers so no MFMA can move above it), and the source order of
-// reads, copies and MFMAs is the issue order (volatile asm statements keep
-// their order).  Same pipeline as mainloop: the wait and barrier admitting
-// slice t+1 sit between the half-steps of slice t.
-struct TrFrag {
-  i16x4 lo, hi;
-};
 
 // Compile-time loop: f(ic<B>{}), ..., f(ic<E - 1>{}), so that loop indices
 // can select immediates.
@@ -344,147 +192,221 @@ __device__ __forceinline__ void static_for(F &&f) {
   }
 }
 
-// ds_read_b64_tr_b16 from LDS byte address a + IMM.
+// ---------------------------------------------------------------- fragment reads
+// The fragment reads are issued as inline asm and awaited explicitly
+// (s_waitcnt lgkmcnt(0), tied to the fragment registers so that no MFMA
+// moves above it): the compiler would otherwise guard each LDS read with a
+// wait for every direct-to-LDS copy in flight, draining the copy pipeline
+// once per slice.  Volatile asm statements keep their source order, which is
+// the issue order.
+template <int KIND>
+struct Frag;
+template <>
+struct Frag<PACKED> {        // one 16-byte read
+  bf16x8 v;
+};
+template <>
+struct Frag<PACKED_T> {      // two transposing 8-byte reads
+  i16x4 lo, hi;
+};
+template <int KIND>
+constexpr int reads_per_frag() { return KIND == PACKED ? 1 : 2; }
+
 template <int IMM>
-__device__ __forceinline__ void tr_read(i16x4 &dst, uint32_t a) {
+__device__ __forceinline__ void rd_b128(bf16x8 &dst, uint32_t a) {
+  static_assert(IMM >= 0 && IMM < 65536, "LDS instruction offset range");
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(dst) : "v"(a), "i"(IMM));
+}
+template <int IMM>
+__device__ __forceinline__ void rd_tr(i16x4 &dst, uint32_t a) {
   static_assert(IMM >= 0 && IMM < 65536, "LDS instruction offset range");
   asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(dst) : "v"(a), "i"(IMM));
 }
 
-// Byte offsets, within a slice, of this lane's two transposing reads for the
-// fragment of operand rows r0..r0+31, half-step kk (see frag<PACKED_T>).
-// For the fragments r0 + 32 i of one wave and the two half-steps they differ
-// from those of (r0, 0) by exactly 2048 i + 256 kk in every lane (fragment
-// r/32 moves by two 1 KB pieces; k + 16 flips bit 4 of the slot, which no XOR
-// term touches), so a wave keeps one address per read half and operand and
-// reaches every read through the instruction's immediate offset.
-__device__ __forceinline__ void tr_offsets(int r0, int kk, uint32_t &lo, uint32_t &hi) {
+// This lane's two read addresses (bytes, within a stage) for fragment 0 of an
+// operand block of rows r0..: PACKED: the reads of half-steps kk = 0 and 1;
+// PACKED_T: the low and high reads of half-step 0.  Across a wave's
+// fragments (rows r0 + 32 i) the addresses move by exactly 2048 i bytes, and
+// a PACKED_T read of half-step kk by 256 kk more (k + 16 flips bit 4 of the
+// slot, which no XOR term touches; this was checked for every lane), so every
+// read is reached through the instruction's immediate offset.
+template <int KIND>
+__device__ __forceinline__ void rd_bases(int r0, uint32_t &b0, uint32_t &b1) {
   const int l = threadIdx.x & 63;
-  const int g = l >> 4, j = l & 15;
-  const int r = r0 + ((g & 1) << 4) + ((j & 3) << 2);
-  const int k = kk * 16 + ((g >> 1) << 3) + (j >> 2);
-  const int h = (r >> 3) & 1, f = (r >> 4) & 1;
-  const int p = ((((r >> 5) << 1) + f) << 10) + ((r & 7) << 1);
-  lo = (uint32_t)(p + (pk_slot(k, h, f) << 4));
-  hi = (uint32_t)(p + (pk_slot(k + 4, h, f) << 4));
-}
-
-// LDS addresses of this lane's reads of fragment 0, half-step 0, in one stage.
-struct TrBase {
-  uint32_t alo, ahi, blo, bhi;
-};
-
-// Read Q (0 .. 2 (MI + NI) - 1) of half-step KK: fragment Q/2 (A fragments
-// first), low or high half.
-template <class T, int KK, int Q>
-__device__ __forceinline__ void tr_issue(const TrBase &b, TrFrag (&fa)[T::MI],
-                                         TrFrag (&fb)[T::NI]) {
-  constexpr int fi = Q >> 1;
-  if constexpr (fi < T::MI) {
-    constexpr int imm = 2048 * fi + 256 * KK;
-    if constexpr (Q & 1) tr_read<imm>(fa[fi].hi, b.ahi);
-    else tr_read<imm>(fa[fi].lo, b.alo);
+  if constexpr (KIND == PACKED) {
+    b0 = (uint32_t)((((r0 >> 5) << 1) << 10) + (pk_slot(l & 31, l >> 5, 0) << 4));
+    b1 = (uint32_t)(((((r0 >> 5) << 1) + 1) << 10) + (pk_slot(l & 31, l >> 5, 1) << 4));
   } else {
-    constexpr int imm = 2048 * (fi - T::MI) + 256 * KK;
-    if constexpr (Q & 1) tr_read<imm>(fb[fi - T::MI].hi, b.bhi);
-    else tr_read<imm>(fb[fi - T::MI].lo, b.blo);
+    // lane j of a 16-lane group names the 4 operand rows r..r+3 at one k
+    const int g = l >> 4, j = l & 15;
+    const int r = r0 + ((g & 1) << 4) + ((j & 3) << 2);
+    const int k = ((g >> 1) << 3) + (j >> 2);
+    const int h = (r >> 3) & 1, f = (r >> 4) & 1;
+    const int p = ((((r >> 5) << 1) + f) << 10) + ((r & 7) << 1);
+    b0 = (uint32_t)(p + (pk_slot(k, h, f) << 4));
+    b1 = (uint32_t)(p + (pk_slot(k + 4, h, f) << 4));
   }
 }
 
+// Read Q of half-step KK of an operand with NF fragments.
+template <int KIND, int KK, int Q, int NF>
+__device__ __forceinline__ void rd_issue(uint32_t b0, uint32_t b1, Frag<KIND> (&f)[NF]) {
+  if constexpr (KIND == PACKED) {
+    rd_b128<2048 * Q>(f[Q].v, KK ? b1 : b0);
+  } else {
+    constexpr int fi = Q >> 1;
+    constexpr int imm = 2048 * fi + 256 * KK;
+    if constexpr (Q & 1) rd_tr<imm>(f[fi].hi, b1);
+    else rd_tr<imm>(f[fi].lo, b0);
+  }
+}
+
+template <int KIND, int NF>
+__device__ __forceinline__ void frag_tie(Frag<KIND> (&f)[NF]) {
+#pragma unroll
+  for (int i = 0; i < NF; ++i) {
+    if constexpr (KIND == PACKED) asm volatile("" : "+v"(f[i].v));
+    else asm volatile("" : "+v"(f[i].lo), "+v"(f[i].hi));
+  }
+}
+
+template <int KIND>
+__device__ __forceinline__ bf16x8 frag_val(const Frag<KIND> &f) {
+  if constexpr (KIND == PACKED) return f.v;
+  else return __builtin_bit_cast(bf16x8, __builtin_shufflevector(f.lo, f.hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// A wave's fragments of one half-step.
+template <class T>
+struct Frags {
+  Frag<T::KA> a[T::MI];
+  Frag<T::KB> b[T::NI];
+};
+
 // Wait for every LDS read of this wave and tie the fragments to the wait.
 template <class T>
-__device__ __forceinline__ void tr_wait(TrFrag (&fa)[T::MI], TrFrag (&fb)[T::NI]) {
+__device__ __forceinline__ void frags_wait(Frags<T> &f) {
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-#pragma unroll
-  for (int i = 0; i < T::MI; ++i) asm volatile("" : "+v"(fa[i].lo), "+v"(fa[i].hi));
-#pragma unroll
-  for (int j = 0; j < T::NI; ++j) asm volatile("" : "+v"(fb[j].lo), "+v"(fb[j].hi));
+  frag_tie<T::KA>(f.a);
+  frag_tie<T::KB>(f.b);
 }
 
-__device__ __forceinline__ bf16x8 tr_join(const TrFrag &f) {
-  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(f.lo, f.hi, 0, 1, 2, 3, 4, 5, 6, 7));
+// Read addresses of one stage: A's two, B's two.
+struct Bases {
+  uint32_t a0, a1, b0, b1;
+};
+
+// Read Q of half-step KK (A's reads first, then B's).
+template <class T, int KK, int Q>
+__device__ __forceinline__ void frag_read(const Bases &s, Frags<T> &f) {
+  constexpr int RA = T::MI * reads_per_frag<T::KA>();
+  if constexpr (Q < RA) rd_issue<T::KA, KK, Q>(s.a0, s.a1, f.a);
+  else rd_issue<T::KB, KK, Q - RA>(s.b0, s.b1, f.b);
 }
 
-// One MFMA of a half-step, fenced so that the scheduler keeps the source
-// order of MFMAs, reads and copies.
+// MFMA i of a half-step (block row i / NI, block column i % NI), fenced so
+// that the scheduler keeps the source order of MFMAs, reads and copies.
 template <class T>
-__device__ __forceinline__ void tr_mfma(int i, const TrFrag (&fa)[T::MI], const TrFrag (&fb)[T::NI],
-                                        f32x16 (&acc)[T::MI][T::NI]) {
+__device__ __forceinline__ void mfma_at(int i, const Frags<T> &f, f32x16 (&acc)[T::MI][T::NI]) {
   const int a = i / T::NI, b = i % T::NI;
   __builtin_amdgcn_sched_barrier(0);
-  acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_join(fa[a]), tr_join(fb[b]), acc[a][b], 0,
-                                                      0, 0);
+  acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_val<T::KA>(f.a[a]), frag_val<T::KB>(f.b[b]),
+                                                      acc[a][b], 0, 0, 0);
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <class T>
-__device__ __forceinline__ void mainloop_tt(const Op &a, const Op &b, int klen, char *smem,
-                                            f32x16 (&acc)[T::MI][T::NI]) {
-  static_assert(T::KA == PACKED_T && T::KB == PACKED_T, "transposed operands only");
-  constexpr int M = T::MI * T::NI;             // MFMAs per half-step
-  constexpr int R = 2 * (T::MI + T::NI);       // transposing reads per half-step
+// acc[i][j] is the 32 x 32 block (i, j) of the wave's quarter.  Lane l of
+// block (i, j), register e, holds row 32 i + 8 (e/4) + 4 (l/32) + e%4 and
+// column 32 j + l%32 of the quarter.  acc enters initialised by the caller.
+//
+// Each 32-deep slice is two MFMA half-steps (k 0..15, 16..31).  The wait and
+// barrier that admit slice t+1 sit between the two half-steps of slice t, so
+// the barrier waits with MFMAs in flight.  The reads of a half-step's
+// fragments go out during the previous half-step, RPM after each MFMA from
+// its first one, so they have most of a half-step to land.  Slice
+// t+STAGES-1 is copied into the buffer of slice t-1, whose reads every wave
+// finished before that barrier; its copies go out one after every CSP-th
+// MFMA of the second half-step rather than in one burst, which would hold up
+// the MFMA issue.  Every iteration issues one slice of copies (the last slice
+// again past the end, into a slot that is not read again), so the wait is
+// always for all but the newest STAGES-3 slices, and the last slice is
+// peeled: the loop body is one straight path.  Packed operands carry zero
+// padding up to whole slices, so no copy needs a bounds check.
+template <class T, int RPM, int CSP>
+__device__ __forceinline__ void mainloop(const Op &a, const Op &b, int klen, char *smem,
+                                         f32x16 (&acc)[T::MI][T::NI]) {
+  constexpr int M = T::MI * T::NI;                 // MFMAs per half-step
+  constexpr int R = T::MI * reads_per_frag<T::KA>() + T::NI * reads_per_frag<T::KB>();
+  constexpr int G = T::NPER;
+  static_assert(T::STAGES >= 3, "the wait below admits one slice of STAGES - 1 in flight");
   const int nk = (klen + BK - 1) / BK;
   if (nk > 0) {
     const int w = threadIdx.x >> 6;
     const int wm = w >> 1, wn = w & 1;
     const uint32_t lds0 = lds_addr(smem);
-    TrBase b0;
-    tr_offsets(wm * T::WM, 0, b0.alo, b0.ahi);
-    tr_offsets(wn * T::WN, 0, b0.blo, b0.bhi);
-    b0.alo += lds0;
-    b0.ahi += lds0;
-    b0.blo += lds0 + T::A_BYTES;
-    b0.bhi += lds0 + T::A_BYTES;
-    auto stage_base = [&](int stage) {
-      const uint32_t o = (uint32_t)(stage * T::STAGE_BYTES);
-      return TrBase{b0.alo + o, b0.ahi + o, b0.blo + o, b0.bhi + o};
+    Bases z;
+    rd_bases<T::KA>(wm * T::WM, z.a0, z.a1);
+    rd_bases<T::KB>(wn * T::WN, z.b0, z.b1);
+    z.a0 += lds0;
+    z.a1 += lds0;
+    z.b0 += lds0 + T::A_BYTES;
+    z.b1 += lds0 + T::A_BYTES;
+    auto stage_bases = [&](int s) {
+      const uint32_t o = (uint32_t)(s * T::STAGE_BYTES);
+      return Bases{z.a0 + o, z.a1 + o, z.b0 + o, z.b1 + o};
     };
 #pragma unroll
-    for (int s = 0; s < T::STAGES - 1; ++s) issue_stage<T>(a, b, s, nk, lds0);
-    wait_vm<(T::STAGES - 2) * T::NPER>();
+    for (int s = 0; s < T::STAGES - 1; ++s) {
+      const int k0 = (s < nk ? s : nk - 1) * BK;
+#pragma unroll
+      for (int g = 0; g < G; ++g) stage_copy<T>(a, b, k0, lds0 + (uint32_t)(s * T::STAGE_BYTES), g);
+    }
+    wait_vm<(T::STAGES - 2) * G>();
     bar();
-    TrFrag fa0[T::MI], fb0[T::NI], fa1[T::MI], fb1[T::NI];
-    TrBase cur = b0;                             // the stage of slice t
+    Frags<T> f0, f1;
+    Bases cur = z;                                 // the stage of slice t
     int st = 0;
-    static_for<0, R>([&](auto q) { tr_issue<T, 0, decltype(q)::value>(cur, fa0, fb0); });
-    // the last slice is peeled so that the loop body is one straight path
+    static_for<0, R>([&](auto q) { frag_read<T, 0, decltype(q)::value>(cur, f0); });
     for (int t = 0; t < nk - 1; ++t) {
       const int sn = st + 1 == T::STAGES ? 0 : st + 1;
-      const TrBase nxt = stage_base(sn);
-      tr_wait<T>(fa0, fb0);
+      const Bases nxt = stage_bases(sn);
+      const int ck = t + T::STAGES - 1;            // slice copied in this iteration
+      const int k0 = (ck < nk ? ck : nk - 1) * BK;
+      const uint32_t cst = lds0 + (uint32_t)((ck % T::STAGES) * T::STAGE_BYTES);
+      frags_wait<T>(f0);
       // first half-step; the reads of the second go out between its MFMAs
       static_for<0, M>([&](auto ii) {
         constexpr int i = decltype(ii)::value;
-        tr_mfma<T>(i, fa0, fb0, acc);
-        static_for<i * R / M, (i + 1) * R / M>(
-            [&](auto q) { tr_issue<T, 1, decltype(q)::value>(cur, fa1, fb1); });
+        mfma_at<T>(i, f0, acc);
+        constexpr int q0 = i * RPM < R ? i * RPM : R, q1 = (i + 1) * RPM < R ? (i + 1) * RPM : R;
+        static_for<q0, q1>([&](auto q) { frag_read<T, 1, decltype(q)::value>(cur, f1); });
       });
       // slice t+1 must have landed; slices t+2 .. t+STAGES-2 may stay in flight
-      wait_vm<(T::STAGES - 3) * T::NPER>();
+      wait_vm<(T::STAGES - 3) * G>();
       bar();
-      tr_wait<T>(fa1, fb1);
-      // second half-step: the next copies after its first MFMA, then the
-      // next slice's first reads between the rest
-      tr_mfma<T>(0, fa1, fb1, acc);
-      issue_stage<T>(a, b, t + T::STAGES - 1, nk, lds0);
-      static_for<1, M>([&](auto ii) {
+      frags_wait<T>(f1);
+      // second half-step: the next slice's copies and first reads between its MFMAs
+      static_for<0, M>([&](auto ii) {
         constexpr int i = decltype(ii)::value;
-        tr_mfma<T>(i, fa1, fb1, acc);
-        static_for<(i - 1) * R / (M - 1), i * R / (M - 1)>(
-            [&](auto q) { tr_issue<T, 0, decltype(q)::value>(nxt, fa0, fb0); });
+        mfma_at<T>(i, f1, acc);
+        if constexpr (i % CSP == 0 && i / CSP < G) stage_copy<T>(a, b, k0, cst, i / CSP);
+        constexpr int q0 = i * RPM < R ? i * RPM : R, q1 = (i + 1) * RPM < R ? (i + 1) * RPM : R;
+        static_for<q0, q1>([&](auto q) { frag_read<T, 0, decltype(q)::value>(nxt, f0); });
       });
+      if constexpr (G > (M + CSP - 1) / CSP)
+        static_for<(M + CSP - 1) / CSP, G>([&](auto g) { stage_copy<T>(a, b, k0, cst, decltype(g)::value); });
       cur = nxt;
       st = sn;
     }
-    tr_wait<T>(fa0, fb0);
+    frags_wait<T>(f0);
     static_for<0, M>([&](auto ii) {
       constexpr int i = decltype(ii)::value;
-      tr_mfma<T>(i, fa0, fb0, acc);
-      static_for<i * R / M, (i + 1) * R / M>(
-          [&](auto q) { tr_issue<T, 1, decltype(q)::value>(cur, fa1, fb1); });
+      mfma_at<T>(i, f0, acc);
+      constexpr int q0 = i * RPM < R ? i * RPM : R, q1 = (i + 1) * RPM < R ? (i + 1) * RPM : R;
+      static_for<q0, q1>([&](auto q) { frag_read<T, 1, decltype(q)::value>(cur, f1); });
     });
-    tr_wait<T>(fa1, fb1);
-    static_for<0, M>([&](auto ii) { tr_mfma<T>(decltype(ii)::value, fa1, fb1, acc); });
+    frags_wait<T>(f1);
+    static_for<0, M>([&](auto ii) { mfma_at<T>(decltype(ii)::value, f1, acc); });
   }
   // every wave is done with the LDS slices and no copy is still writing them;
   // the caller may reuse LDS
@@ -511,9 +433,14 @@ __device__ __forceinline__ float bf16_lo(uint32_t u) { return __builtin_bit_cast
 __device__ __forceinline__ float bf16_hi(uint32_t u) { return __builtin_bit_cast(float, u & 0xFFFF0000u); }
 
 using FwdTile = Tile<256, 256, 4, PACKED, PACKED>;     // A = Wp, B = Xp
-using DxTile = Tile<256, 256, 4, PACKED, PACKED>;      // A = G (Zp), B = WTp
+using DxTile = Tile<256, 256, 4, PACKED, PACKED_T>;    // A = G (Zp), B = Wp read transposed
 using DwTile = Tile<256, 128, 3, PACKED_T, PACKED_T>;  // A = G (Zp), B = Xp, both transposed
 constexpr int kDwOcc = 2;                              // dW workgroups per CU
+// Main-loop schedules (reads per MFMA, MFMAs per copy), the fastest of those
+// measured per kernel on the Llama-3-8B head at chunk 1024.
+constexpr int kFwdRpm = 2, kFwdCsp = 2;
+constexpr int kDxRpm = 2, kDxCsp = 2;
+constexpr int kDwRpm = 2, kDwCsp = 1;
 
 // ---------------------------------------------------------------- packing
 // One workgroup per 256 rows x 64 columns (two packed blocks, 32 KB) of a
@@ -548,86 +475,6 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint16_t *__restrict__ 
   }
 }
 
-// Transpose an 8 x 8 block of 16-bit values held as 8 rows of 16 bytes:
-// out[j] holds element j of rows 0..7, two per dword, low half first.
-__device__ __forceinline__ void transpose8x8(const u32x4 (&in)[8], u32x4 (&out)[8]) {
-#pragma unroll
-  for (int j = 0; j < 8; ++j)
-#pragma unroll
-    for (int pp = 0; pp < 4; ++pp) {
-      const uint32_t lo = in[2 * pp][j >> 1], hi = in[2 * pp + 1][j >> 1];
-      out[j][pp] = (j & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
-    }
-}
-
-// Transposed packing: the packed matrix PT has the columns of a row-major
-// bf16 [R][K] source as rows (rows = K, columns = R, nks_t column slices).
-// One workgroup per 256 rows x 64 columns of PT (two blocks, 32 KB): thread t
-// loads the 8 x 8 source block at source rows 64 p + 8 (t / 32) and columns
-// 256 rt + 8 (t % 32) (a wave reads 2 source rows x 512 contiguous bytes per
-// instruction), transposes it in registers, places its 8 row pieces in LDS in
-// packed order and the workgroup writes both blocks as one 32 KB copy.
-// With PLAIN the same loads also fill the untransposed packed matrix P (rows
-// R, nks_p column slices): the 64 source rows x 256 columns are the same two
-// 32-row groups of 8 consecutive P blocks, i.e. 8 pieces of 4 KB, so the
-// source is read once for both.  The two outputs take turns in one 32 KB LDS
-// buffer, which keeps several workgroups (and their loads) per CU.
-template <bool PLAIN>
-__global__ __launch_bounds__(256) void pack_t_kernel(const uint16_t *__restrict__ src, int R,
-                                                    int K, uint16_t *__restrict__ PT,
-                                                    int64_t nks_t, uint16_t *__restrict__ P,
-                                                    int64_t nks_p) {
-  __shared__ __attribute__((aligned(1024))) char lds[32768];
-  const int npair = (int)(nks_t >> 1);
-  const int rt = blockIdx.x / npair;                  // row tile of PT = 256 source columns
-  const int kp = blockIdx.x - rt * npair;             // pair of PT column slices = 64 source rows
-  const int t = threadIdx.x;
-  const int r0 = kp * 64 + (t >> 5) * 8;              // source rows r0..r0+7 = PT columns
-  const int c0 = rt * 256 + (t & 31) * 8;             // source columns c0..c0+7 = PT rows
-  u32x4 in[8], out[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-    in[i] = (r0 + i < R && c0 < K) ? *(const u32x4 *)(src + (int64_t)(r0 + i) * K + c0)
-                                   : u32x4{0u, 0u, 0u, 0u};
-  transpose8x8(in, out);
-  const int k = (t >> 5) * 8;                         // PT column within the pair, 0..56
-  const int kk = k & 31;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int r = (t & 31) * 8 + j;                   // PT row within the tile
-    const int off = ((k >> 5) << 14) + ((((r >> 5) << 1) + (kk >> 4)) << 10) +
-                    (pk_slot(r & 31, (kk >> 3) & 1, kk >> 4) << 4);
-    *(u32x4 *)(lds + off) = out[j];
-  }
-  __syncthreads();
-  uint16_t *dst = PT + (((int64_t)rt * nks_t + 2 * kp) << 13);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int q = i * 256 + t;
-    *(u32x4 *)(dst + q * 8) = *(const u32x4 *)(lds + q * 16);
-  }
-  if constexpr (PLAIN) {
-    __syncthreads();                                  // every wave has copied PT out of LDS
-    // P piece (t % 32) / 4 (column slice), fragment (row group, column half)
-    const int kk = (c0 & 31);
-    char *lp = lds + (((t & 31) >> 2) << 12);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = (t >> 5) * 8 + i;                 // source row within the 64
-      const int off = ((((r >> 5) << 1) + (kk >> 4)) << 10) +
-                      (pk_slot(r & 31, (kk >> 3) & 1, kk >> 4) << 4);
-      *(u32x4 *)(lp + off) = in[i];
-    }
-    __syncthreads();
-    // 64 source rows = row groups 2 (kp % 4), +1 of P's row tile kp / 4
-    const int64_t rtp = kp >> 2;
-    uint16_t *dp = P + ((rtp * nks_p + 8 * (int64_t)rt) << 13) + ((kp & 3) << 11);
-#pragma unroll
-    for (int i = 0; i < 8; ++i)       // piece i: P block (rtp, 8 rt + i), 4 KB
-      *(u32x4 *)(dp + ((int64_t)i << 13) + t * 8) = *(const u32x4 *)(lds + (i << 12) + t * 16);
-  }
-}
-
 // ---------------------------------------------------------------- forward tile
 // Z^T tile: rows = 256 vocabulary ids from m0, columns = 256 tokens from n0;
 // both operands packed (Wp rows = vocabulary, Xp rows = tokens, k = hidden).
@@ -655,11 +502,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_tile_kernel(
   const int vt = vt0 + tile / nct, ct = tile % nct;
   const int m0 = vt * T::BM, n0 = ct * T::BN;
 
-  const Op a{Wp + (int64_t)vt * nks_h * 8192, 0, 0};
-  const Op b{Xp + (int64_t)ct * nks_h * 8192, 0, 0};
+  const Op a{(const char *)(Wp + (int64_t)vt * nks_h * 8192), 0, 0};
+  const Op b{(const char *)(Xp + (int64_t)ct * nks_h * 8192), 0, 0};
   f32x16 acc[4][4];
   zero_acc<T>(acc);
-  mainloop<T>(a, b, H, smem, acc);
+  mainloop<T, kFwdRpm, kFwdCsp>(a, b, H, smem, acc);
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int wm = w >> 1, wn = w & 1;
@@ -791,11 +638,12 @@ __global__ __launch_bounds__(256) void dlogits_kernel(
 
 // ---------------------------------------------------------------- dX (split-K)
 // Unit (s, mt, nt): dxp[s][tok][h] = sum over vocabulary in split s of
-// G[tok][v] W[v][h].  G from Zp (rows = tokens), W from WTp (rows = hidden),
-// both with the vocabulary along k.
+// G[tok][v] W[v][h].  G from Zp (rows = tokens, k = vocabulary), W read
+// transposed from Wp (its columns, the hidden ids, are the operand rows; its
+// rows, the vocabulary, are k), so no transposed copy of W is made.
 __global__ __launch_bounds__(NTHREADS, 1) void dx_kernel(
-    const uint16_t *__restrict__ Gp, int64_t nks_z, const uint16_t *__restrict__ WTp,
-    int c, int H, int V, int64_t ksplit, int nmt, int nnt, float *__restrict__ dxp) {
+    const uint16_t *__restrict__ Gp, int64_t nks_z, const uint16_t *__restrict__ Wp,
+    int64_t nks_h, int c, int H, int V, int64_t ksplit, int nmt, int nnt, float *__restrict__ dxp) {
   using T = DxTile;
   __shared__ __attribute__((aligned(1024))) char smem[T::LDS];
   const int unit = xcd_remap(blockIdx.x, gridDim.x);
@@ -808,11 +656,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void dx_kernel(
   const int64_t ke = kb + ksplit < V ? kb + ksplit : V;
   const int klen = (int)(ke - kb);
 
-  const Op a{Gp + ((int64_t)mt * nks_z + (kb >> 5)) * 8192, 0, 0};
-  const Op b{WTp + ((int64_t)nt * nks_z + (kb >> 5)) * 8192, 0, 0};
+  const Op a{(const char *)(Gp + ((int64_t)mt * nks_z + (kb >> 5)) * 8192), 0, 0};
+  const Op b{(const char *)(Wp + (int64_t)(n0 >> 5) * 8192), nks_h * 16384, kb};
   f32x16 acc[4][4];
   zero_acc<T>(acc);
-  mainloop<T>(a, b, klen, smem, acc);
+  mainloop<T, kDxRpm, kDxCsp>(a, b, klen, smem, acc);
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int wm = w >> 1, wn = w & 1;
@@ -875,16 +723,16 @@ __global__ __launch_bounds__(NTHREADS, OCC) void dw_kernel(
     int64_t nks_h, int c, int H, int V, int nvt, int nht, float *__restrict__ dW, int accumulate) {
   __shared__ __attribute__((aligned(1024))) char smem[T::LDS];
   int vt, ht;
-  grouped<8>(xcd_remap(blockIdx.x, gridDim.x), nvt, nht, vt, ht);
+  grouped<4>(xcd_remap(blockIdx.x, gridDim.x), nvt, nht, vt, ht);
   const int m0 = vt * T::BM, n0 = ht * T::BN;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int wm = w >> 1, wn = w & 1;
 
   f32x16 acc[T::MI][T::NI];
   zero_acc<T>(acc);
-  const Op a{Gp + (int64_t)(m0 >> 5) * 8192, nks_z * 8192, 0};
-  const Op b{Xp + (int64_t)(n0 >> 5) * 8192, nks_h * 8192, 0};
-  mainloop_tt<T>(a, b, c, smem, acc);
+  const Op a{(const char *)(Gp + (int64_t)(m0 >> 5) * 8192), nks_z * 16384, 0};
+  const Op b{(const char *)(Xp + (int64_t)(n0 >> 5) * 8192), nks_h * 16384, 0};
+  mainloop<T, kDwRpm, kDwCsp>(a, b, c, smem, acc);
 
   constexpr int TPR = T::BN / 4;            // threads per row: one 16-byte piece each
   constexpr int RPP = NTHREADS / TPR;       // rows per pass of the workgroup
@@ -988,24 +836,12 @@ hipError_t launch_dlogits_bf16(uint16_t *Zp, int64_t nks_z, int c, int V, const 
   return hipGetLastError();
 }
 
-hipError_t launch_pack_t_bf16(const uint16_t *src, int R, int K, uint16_t *PT, int64_t nks_t,
-                              uint16_t *P, int64_t nks_p, hipStream_t s) {
-  // nks_t is a multiple of 8, so column pairs of slices tile it exactly
-  const int64_t nwg = (int64_t)(K + 255) / 256 * (nks_t / 2);
-  if (P)
-    hipLaunchKernelGGL(pack_t_kernel<true>, dim3((unsigned)nwg), dim3(256), 0, s, src, R, K, PT,
-                       nks_t, P, nks_p);
-  else
-    hipLaunchKernelGGL(pack_t_kernel<false>, dim3((unsigned)nwg), dim3(256), 0, s, src, R, K, PT,
-                       nks_t, P, nks_p);
-  return hipGetLastError();
-}
-
-hipError_t launch_dx_bf16(const uint16_t *Gp, int64_t nks_z, const uint16_t *WTp, int c, int H,
-                          int V, int splitk, int64_t ksplit, float *dxp, hipStream_t s) {
+hipError_t launch_dx_bf16(const uint16_t *Gp, int64_t nks_z, const uint16_t *Wp, int64_t nks_h,
+                          int c, int H, int V, int splitk, int64_t ksplit, float *dxp,
+                          hipStream_t s) {
   const int nmt = (c + DxTile::BM - 1) / DxTile::BM, nnt = (H + DxTile::BN - 1) / DxTile::BN;
-  hipLaunchKernelGGL(dx_kernel, dim3(splitk * nmt * nnt), dim3(NTHREADS), 0, s, Gp, nks_z, WTp,
-                     c, H, V, ksplit, nmt, nnt, dxp);
+  hipLaunchKernelGGL(dx_kernel, dim3(splitk * nmt * nnt), dim3(NTHREADS), 0, s, Gp, nks_z, Wp,
+                     nks_h, c, H, V, ksplit, nmt, nnt, dxp);
   return hipGetLastError();
 }
 

@@ -199,7 +199,7 @@ __global__ __launch_bounds__(kPairThreads) void kto_seq_kernel(
     if (labels_c[r0 + t] != ii) sum += lp[r0 + t];
   const float S = block_sum(sum, red);
   const float r = S - kp.ref[s0 + j];
-  const bool des = kp.desirable[s0 + j] != 0;
+  const bool des = kp.desirable ? kp.desirable[s0 + j] != 0 : true;
   const float u = des ? kp.beta * (r - kp.z0) : kp.beta * (kp.z0 - r);
   // sigmoid(u) and 1 - sigmoid(u) = sigmoid(-u), each from its own exp so
   // that neither loses its digits when the other rounds to 1
@@ -247,6 +247,26 @@ __global__ __launch_bounds__(256) void pairs_final_kernel(const float *__restric
     const float orl = (red2[0] + red2[1] + red2[2] + red2[3]) / (float)n_pairs;
     sc->aux = nll;
     sc->loss = alpha * nll + lambda * orl;
+  }
+}
+
+// KTO's reference point from the per-sequence rewards r = S - R of a batch of
+// mismatched completions: z0 = max(0, mean r), summed in fp64 in a fixed
+// order; the result goes to sc->loss, the call's scalar output.
+__global__ __launch_bounds__(256) void kto_refpoint_kernel(const float *__restrict__ r,
+                                                           int64_t n, Scalars *__restrict__ sc) {
+  __shared__ double part[256];
+  double a = 0.0;
+  for (int64_t i = threadIdx.x; i < n; i += 256) a += (double)r[i];
+  part[threadIdx.x] = a;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if ((int)threadIdx.x < o) part[threadIdx.x] += part[threadIdx.x + o];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const double m = part[0] / (double)(n > 0 ? n : 1);
+    sc->loss = (float)(m > 0.0 ? m : 0.0);
   }
 }
 
@@ -303,6 +323,11 @@ hipError_t launch_pairs_final(const float *nll_sum, const float *pair_term, int6
                               float alpha, float lambda, Scalars *sc, hipStream_t s) {
   hipLaunchKernelGGL(pairs_final_kernel, dim3(1), dim3(256), 0, s, nll_sum, pair_term, n_pairs,
                      alpha, lambda, sc);
+  return hipGetLastError();
+}
+
+hipError_t launch_kto_refpoint(const float *reward, int64_t n_seq, Scalars *sc, hipStream_t s) {
+  hipLaunchKernelGGL(kto_refpoint_kernel, dim3(1), dim3(256), 0, s, reward, n_seq, sc);
   return hipGetLastError();
 }
 

@@ -151,6 +151,11 @@ def test_status_strings(lib):
     assert fl.flce_last_error() == ""
 
 
+def _wp_bytes(H, V):
+    """The packed copy of W: rows and columns padded to 256, bf16."""
+    return ((V + 255) // 256 * 256) * ((H + 255) // 256 * 256) * 2
+
+
 def test_workspace_bounded_by_chunk_not_N():
     # Llama-3-8B head, long context: scratch grows with the chunk, not with N.
     H, V = 4096, 128256
@@ -160,26 +165,20 @@ def test_workspace_bounded_by_chunk_not_N():
     sizes = [fl.flce_workspace_bytes(16384, H, V, fl.FLCE_BF16, c) for c in (512, 1024, 4096)]
     assert sizes[0] < sizes[1] < sizes[2]
     for c, s in zip((512, 1024, 4096), sizes):
-        assert s >= c * V * 2 + V * H * 4          # the bf16 logits chunk and W packed twice
+        assert s >= c * V * 2 + _wp_bytes(H, V)     # the bf16 logits chunk and W packed once
         # plus the packed X chunk, log-sum-exp partials and split-K sums
-        assert s < c * V * 2 * 2 + V * H * 4.4
-    full_logits = 16384 * V * 2
-    assert sizes[1] - V * H * 4 < full_logits / 5
-
-
-def _wp_bytes(H, V):
-    """The two packed copies of W (as is and transposed): rows and columns
-    padded to 256, bf16."""
-    return 2 * ((V + 255) // 256 * 256) * ((H + 255) // 256 * 256) * 2
+        assert s < c * V * 2 * 1.5 + _wp_bytes(H, V) * 1.1
+    # at chunk 1024 the whole workspace is below the bf16 logits of the batch
+    assert fl.flce_workspace_bytes(8192, H, V, fl.FLCE_BF16, 1024) < 8192 * V * 2
 
 
 def _largest_fitting_chunk(N, H, V, budget):
-    """The rule flce_plan states: the largest power-of-two multiple of 256 tokens
-    (at most N) whose chunk-dependent scratch (workspace minus packed W) fits."""
+    """The rule flce_plan states: the largest power-of-two multiple of 256
+    tokens (at most N) whose whole workspace fits the budget."""
     best, c = None, 256
     while True:
         cc = min(c, N)
-        if fl.flce_workspace_bytes(N, H, V, fl.FLCE_BF16, cc) - _wp_bytes(H, V) > budget:
+        if fl.flce_workspace_bytes(N, H, V, fl.FLCE_BF16, cc) > budget:
             return best
         best = cc
         if c >= N:
@@ -187,12 +186,24 @@ def _largest_fitting_chunk(N, H, V, budget):
         c *= 2
 
 
+def test_plan_default_budget_keeps_scratch_below_the_logits():
+    # chunk 0 on the Llama-3-8B head: several chunks, and less scratch than N x V bf16 logits
+    N, H, V = 8192, 4096, 128256
+    st, c, peak = fl.flce_plan(N, H, V, fl.FLCE_BF16)
+    assert st == fl.FLCE_OK and c < N and peak < N * V * 2
+    # the default budget is twice W's bytes (at least 256 MiB); the plan is its largest fit
+    assert c == _largest_fitting_chunk(N, H, V, 2 * H * V * 2)
+    assert peak == fl.flce_workspace_bytes(N, H, V, fl.FLCE_BF16, 0) <= 2 * H * V * 2
+    # a tiny head gets the floor
+    st, c, peak = fl.flce_plan(100000, 64, 1000, fl.FLCE_BF16)
+    assert st == fl.FLCE_OK and peak <= 256 << 20
+    assert c == _largest_fitting_chunk(100000, 64, 1000, 256 << 20)
+
+
 def test_plan_auto_and_explicit():
     st, c, peak = fl.flce_plan(8192, 2304, 256000, fl.FLCE_BF16)      # large-vocabulary head
-    assert st == fl.FLCE_OK and c == _largest_fitting_chunk(8192, 2304, 256000, 3 << 30)
-    assert c in (2048, 4096)
+    assert st == fl.FLCE_OK and c == _largest_fitting_chunk(8192, 2304, 256000, 2 * 2304 * 256000 * 2)
     assert peak == fl.flce_workspace_bytes(8192, 2304, 256000, fl.FLCE_BF16, 0)
-    assert peak - _wp_bytes(2304, 256000) <= 3 << 30
     st, c, peak = fl.flce_plan(8192, 4096, 128256, fl.FLCE_BF16, chunk_tokens=1024)
     assert st == fl.FLCE_OK and c == 1024
     assert peak == fl.flce_workspace_bytes(8192, 4096, 128256, fl.FLCE_BF16, 1024)
@@ -200,21 +211,67 @@ def test_plan_auto_and_explicit():
     assert st == fl.FLCE_OK and c == 100                                  # clamped to N
     st, c, _ = fl.flce_plan(100, 64, 1000, fl.FLCE_BF16)
     assert st == fl.FLCE_OK and c == 100
-    st, c, _ = fl.flce_plan(8192, 4096, 128256, fl.FLCE_BF16, scratch_budget_bytes=1 << 20)
-    assert st == fl.FLCE_EWORKSPACE and c == 256                          # smallest chunk reported
-    for budget in (300 << 20, 800 << 20, 1500 << 20):
-        st, c, _ = fl.flce_plan(8192, 4096, 128256, fl.FLCE_BF16, scratch_budget_bytes=budget)
+    # the budget bounds the whole workspace: the packed W alone exceeds 1 GiB here
+    st, c, peak = fl.flce_plan(8192, 4096, 128256, fl.FLCE_BF16, scratch_budget_bytes=1 << 30)
+    assert st == fl.FLCE_EWORKSPACE and c == 256 and peak > 1 << 30    # smallest chunk reported
+    for budget in (1200 << 20, 1500 << 20, 2000 << 20, 3000 << 20):
+        st, c, peak = fl.flce_plan(8192, 4096, 128256, fl.FLCE_BF16, scratch_budget_bytes=budget)
         assert st == fl.FLCE_OK and c == _largest_fitting_chunk(8192, 4096, 128256, budget)
+        assert peak <= budget
         if c < 8192:       # the next chunk up does not fit
-            nxt = fl.flce_workspace_bytes(8192, 4096, 128256, fl.FLCE_BF16, 2 * c)
-            assert nxt - _wp_bytes(4096, 128256) > budget
+            assert fl.flce_workspace_bytes(8192, 4096, 128256, fl.FLCE_BF16, 2 * c) > budget
+    # an explicit chunk beyond an explicit budget is reported, not changed
+    st, c, peak = fl.flce_plan(8192, 4096, 128256, fl.FLCE_BF16, chunk_tokens=4096,
+                               scratch_budget_bytes=1500 << 20)
+    assert st == fl.FLCE_EWORKSPACE and c == 4096 and peak > 1500 << 20
     st, c, peak = fl.flce_plan(0, 64, 100, fl.FLCE_BF16)
     assert st == fl.FLCE_OK and c == 0 and peak > 0
-    # kernels index a chunk's tokens with 32-bit integers: chunks stop at 2^30
-    st, c, _ = fl.flce_plan(1 << 33, 8, 1, fl.FLCE_BF16, chunk_tokens=1 << 32)
-    assert st == fl.FLCE_OK and c == 1 << 30
-    st, c, _ = fl.flce_plan(1 << 33, 8, 1, fl.FLCE_BF16, scratch_budget_bytes=1 << 50)
-    assert st == fl.FLCE_OK and c == 1 << 30
+    # chunks stop at 2^23 tokens
+    st, c, _ = fl.flce_plan((1 << 31) - 1, 8, 1, fl.FLCE_BF16, chunk_tokens=1 << 30)
+    assert st == fl.FLCE_OK and c == 1 << 23
+    st, c, _ = fl.flce_plan((1 << 31) - 1, 8, 1, fl.FLCE_BF16, scratch_budget_bytes=1 << 50)
+    assert st == fl.FLCE_OK and c == 1 << 23
+
+
+def test_limits_refused_one_past():
+    # N_valid is counted in 32 bits
+    assert fl.flce_plan((1 << 31) - 1, 8, 1, fl.FLCE_BF16, chunk_tokens=1024)[0] == fl.FLCE_OK
+    assert fl.flce_plan(1 << 31, 8, 1, fl.FLCE_BF16, chunk_tokens=1024)[0] == fl.FLCE_EUNSUPPORTED
+    assert fl.flce_workspace_bytes(1 << 31, 8, 1, fl.FLCE_BF16, 1024) == 0
+    # V and H each within their limits, but dW's grid (V/256 x H/128 workgroups of 256)
+    # would pass 2^32 work-items: refused by the planner and by the call
+    st, c, _ = fl.flce_plan(1024, 1 << 20, 8000000, fl.FLCE_BF16, chunk_tokens=1024)
+    assert st == fl.FLCE_EUNSUPPORTED
+    assert fl.flce_plan(1024, 1 << 20, 4096, fl.FLCE_BF16, chunk_tokens=1024)[0] == fl.FLCE_OK
+    assert fl.flce_plan(1024, 4096, 8000000, fl.FLCE_BF16, chunk_tokens=1024)[0] == fl.FLCE_OK
+
+
+def test_fwd_bwd_refuses_oversized_grids(lib):
+    assert _fwd_bwd(lib, N=1024, H=1 << 20, V=8000000, chunk=1024) == fl.FLCE_EUNSUPPORTED
+
+
+def test_ce_row_limit(lib):
+    lv = ctypes.c_float(0)
+    max_rows = ((1 << 32) - 1) // 1024          # one workgroup of 1024 work-items per row
+    for n, want in ((max_rows, fl.FLCE_EWORKSPACE), (max_rows + 1, fl.FLCE_EUNSUPPORTED)):
+        st = lib.flce_ce_fwd_bwd(FAKE, FAKE, n, 8, fl.FLCE_BF16, -100, 0, None,
+                                 ctypes.byref(lv), None, None, None, FAKE, 10, None)
+        assert st == want
+
+
+def test_kto_reference_point_validation(lib):
+    z = ctypes.c_float(-1.0)
+
+    def call(ref=FAKE, ws_bytes=10, n_seq=2, T=8):
+        return lib.flce_kto_reference_point(FAKE, FAKE, FAKE, n_seq, T, 64, 100, fl.FLCE_BF16, -100,
+                                            ref, 1, ctypes.byref(z), None, None, FAKE, ws_bytes,
+                                            None)
+    assert call(ref=None) == fl.FLCE_EINVAL              # the reference sums are required
+    assert call(n_seq=0) == fl.FLCE_EINVAL
+    assert call() == fl.FLCE_EWORKSPACE                   # valid: stops at the small workspace
+    assert z.value == -1.0                                # untouched
+    ws = fl.flce_kto_workspace_bytes(2, 8, 64, 100, fl.FLCE_BF16, 1)
+    assert ws > 0 and call(ws_bytes=ws - 1) == fl.FLCE_EWORKSPACE
 
 
 def test_binding_has_no_cpu_fallback():

@@ -21,9 +21,13 @@ int main(void) {
   size_t ws = flce_workspace_bytes(8192, 4096, 128256, FLCE_BF16, 1024);
   int64_t c = 1024;
   size_t peak = 0;
-  int st = flce_plan(8192, 4096, 128256, FLCE_BF16, 0, &c, &peak);
+  int st = flce_plan(8192, 4096, 128256, FLCE_BF16, &c, 0, &peak);
   printf("workspace %zu plan %d chunk %lld peak %zu\n", ws, st, (long long)c, peak);
   if (ws == 0 || st != FLCE_OK || c != 1024 || peak != ws) return 1;
+  /* with no chunk asked for, the default budget keeps scratch below the N x V bf16 logits */
+  c = 0;
+  st = flce_plan(8192, 4096, 128256, FLCE_BF16, &c, 0, &peak);
+  if (st != FLCE_OK || c <= 0 || c >= 8192 || peak >= (size_t)8192 * 128256 * 2) return 10;
   /* scratch follows the chunk, not N */
   if (flce_workspace_bytes(4 * 8192, 4096, 128256, FLCE_BF16, 1024) - ws != 3 * 8192 * 4) return 2;
   /* invalid sizes: 0 bytes; H % 8 != 0 is unsupported on the bf16 path */

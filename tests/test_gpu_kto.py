@@ -177,3 +177,16 @@ def test_kto_reference_point(dtype):
         say(f"    z0 = {z:.6f} (want {want:.6f})")
         assert abs(z - want) <= tol + 1e-6 * abs(want)
         assert z == max(0.0, z)
+        # the C entry itself, with its per-sequence outputs S and S - R
+        Rt = torch.from_numpy(R.astype(np.float32)).to(DEV)
+        ws = torch.empty(fl.flce_kto_workspace_bytes(S, T, H, V, 1 if dtype == "bf16" else 0, 2),
+                         dtype=torch.uint8, device=DEV)
+        lp = torch.full((S,), float("nan"), dtype=torch.float32, device=DEV)
+        rw = torch.full((S,), float("nan"), dtype=torch.float32, device=DEV)
+        z2 = fl.flce_kto_reference_point(X, W, y, S, II, Rt, 2, ws, logp=lp, reward=rw)
+        assert abs(z2 - want) <= tol + 1e-6 * abs(want)
+        assert np.max(np.abs(lp.double().cpu().numpy() - Sp)) <= tol
+        assert np.max(np.abs(rw.double().cpu().numpy() - (Sp - R))) <= tol
+        # and against the oracle's own reference point
+        zo = oracle.kto_reference_point(inp.X_f64(), inp.W_f64(), inp.labels, S, R, II)
+        assert abs(z2 - zo) <= tol + 1e-6 * abs(zo)
