@@ -143,6 +143,29 @@ int flce_fwd_bwd(const void *X, const void *W, const int64_t *labels,
                  void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * flce_fwd_bwd with the workspace taken from a device array inside the
+ * library, FLCE_NOALLOC_SCRATCH_BYTES bytes on each GPU the library runs on,
+ * held until the process ends.  The call allocates nothing.
+ *   Arguments and results as for flce_fwd_bwd, without the workspace.
+ *   chunk_tokens <= 0 plans the largest chunk whose workspace fits the array.
+ *   A call whose workspace (flce_workspace_bytes with its chunk) exceeds the
+ *   array returns FLCE_EWORKSPACE before any device work
+ *   (flce_last_error() gives the sizes).
+ *   The current device must be the stream's device.
+ *   Every call on one GPU uses the same array: calls that overlap in time on
+ *   one GPU race.  The first call on a GPU looks up the array's address there.
+ */
+#define FLCE_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+size_t flce_noalloc_scratch_bytes(void);
+int flce_fwd_bwd_noalloc(const void *X, const void *W, const int64_t *labels,
+                         int64_t N, int64_t H, int64_t V, int dtype,
+                         int64_t ignore_index, int64_t chunk_tokens,
+                         float *loss, void *dX, float *dW,
+                         float *row_loss, float *row_lse, void *stream);
+
+/*
  * Forward only: the loss (and optional per-token outputs) without gradients.
  * Arguments as for flce_fwd_bwd.  Needs no more workspace than flce_fwd_bwd.
  */

@@ -22,6 +22,7 @@ import torch
 
 __all__ = [
     "FLCE_F32", "FLCE_BF16", "FLCEError", "flce_workspace_bytes", "flce_plan", "flce_fwd_bwd",
+    "flce_fwd_bwd_noalloc", "flce_noalloc_scratch_bytes",
     "flce_fwd", "flce_fwd_bwd_ex", "flce_fwd_ex", "REDUCTIONS", "flce_scale_inplace", "flce_status_string", "flce_last_error", "lib_path",
     "flce_profile_enable", "flce_profile_read",
     "workspace", "loss", "FusedLinearCrossEntropyLoss",
@@ -122,6 +123,11 @@ def _load():
     l.flce_kto_fwd.argtypes = [_p, _p, _p, _i64, _i64, _i64, _i64, _i32, _i64, _p, _p, _f, _f, _f,
                                _f, _i64, ctypes.POINTER(_f), _p, _p, _p, _sz, _p]
     l.flce_kto_fwd.restype = _i32
+    l.flce_noalloc_scratch_bytes.argtypes = []
+    l.flce_noalloc_scratch_bytes.restype = _sz
+    l.flce_fwd_bwd_noalloc.argtypes = [_p, _p, _p, _i64, _i64, _i64, _i32, _i64, _i64,
+                                       ctypes.POINTER(_f), _p, _p, _p, _p, _p]
+    l.flce_fwd_bwd_noalloc.restype = _i32
     l.flce_kto_reference_point.argtypes = [_p, _p, _p, _i64, _i64, _i64, _i64, _i32, _i64, _p,
                                            _i64, ctypes.POINTER(_f), _p, _p, _p, _sz, _p]
     l.flce_kto_reference_point.restype = _i32
@@ -246,6 +252,35 @@ def flce_fwd_bwd(X: torch.Tensor, W: torch.Tensor, labels: torch.Tensor, ignore_
                               workspace.numel(), _stream(stream, X.device))
     if st != FLCE_OK:
         raise FLCEError(st, "flce_fwd_bwd")
+    return float(loss.value)
+
+
+def flce_noalloc_scratch_bytes() -> int:
+    return int(_load().flce_noalloc_scratch_bytes())
+
+
+def flce_fwd_bwd_noalloc(X: torch.Tensor, W: torch.Tensor, labels: torch.Tensor,
+                         ignore_index: int, chunk_tokens: int, dX: torch.Tensor, dW: torch.Tensor,
+                         stream=None, row_loss: torch.Tensor | None = None,
+                         row_lse: torch.Tensor | None = None) -> float:
+    """Call libflce's flce_fwd_bwd_noalloc (no workspace argument: the library's
+    own device scratch array); returns the loss."""
+    N, H = X.shape
+    V = W.shape[0]
+    dt = _dtype_code(X)
+    _dev(X, "X")
+    _dev(W, "W", X.dtype, (V, H))
+    _dev(labels, "labels", torch.int64, (N,))
+    _dev(dX, "dX", X.dtype, (N, H))
+    _dev(dW, "dW", torch.float32, (V, H))
+    _dev(row_loss, "row_loss", torch.float32, (N,))
+    _dev(row_lse, "row_lse", torch.float32, (N,))
+    loss = ctypes.c_float(0.0)
+    st = _load().flce_fwd_bwd_noalloc(_ptr(X), _ptr(W), _ptr(labels), N, H, V, dt, ignore_index,
+                                      chunk_tokens, ctypes.byref(loss), _ptr(dX), _ptr(dW),
+                                      _ptr(row_loss), _ptr(row_lse), _stream(stream, X.device))
+    if st != FLCE_OK:
+        raise FLCEError(st, "flce_fwd_bwd_noalloc")
     return float(loss.value)
 
 

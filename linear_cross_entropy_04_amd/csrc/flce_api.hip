@@ -474,6 +474,78 @@ FLCE_API int flce_fwd_bwd(const void *X, const void *W, const int64_t *labels, i
              row_loss, row_lse, Options{}, workspace, workspace_bytes, stream);
 }
 
+// ---------------------------------------------------------------- no device allocation
+// flce_fwd_bwd for callers that cannot allocate device memory (code under
+// HIP graph capture, tight serving loops): its workspace is a file-scope
+// device array of fixed size instead of a caller buffer.  In host code the
+// array's name is only a stand-in; its device address, one per GPU, comes
+// from hipGetSymbolAddress with that GPU current and is what the kernels
+// get.  Nothing in the workspace has to start at zero (every call writes its
+// scratch before reading it), so the array is never cleared.  Calls that
+// overlap in time on one GPU share the array and race.
+
+namespace flce {
+namespace {
+
+constexpr size_t kStaticScratchBytes = FLCE_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+
+static __device__ __align__(256) char scratch[kStaticScratchBytes];
+
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// The scratch array's address on the current device, looked up once per device.
+int static_scratch(void **out) {
+  int dev = -1;
+  CK(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) {
+    g_last_error = "flce_fwd_bwd_noalloc: device ordinal beyond the supported range";
+    return FLCE_EUNSUPPORTED;
+  }
+  std::lock_guard<std::mutex> g(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *ptr = nullptr;
+    CK(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)));
+    if (!ptr) {
+      g_last_error = "flce_fwd_bwd_noalloc: no device address for the scratch array";
+      return FLCE_EHIP;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return FLCE_OK;
+}
+
+}  // namespace
+}  // namespace flce
+
+FLCE_API size_t flce_noalloc_scratch_bytes(void) { return flce::kStaticScratchBytes; }
+
+FLCE_API int flce_fwd_bwd_noalloc(const void *X, const void *W, const int64_t *labels, int64_t N,
+                                  int64_t H, int64_t V, int dtype, int64_t ignore_index,
+                                  int64_t chunk_tokens, float *loss, void *dX, float *dW,
+                                  float *row_loss, float *row_lse, void *stream) {
+  // sizes first, on the host: a call that cannot fit the array touches no device
+  int st = check_sizes(N, H, V, dtype);
+  if (st != FLCE_OK) return st;
+  bool fits;
+  const int64_t C = resolve_chunk(N, H, V, dtype, chunk_tokens, kStaticScratchBytes, &fits);
+  Plan p;
+  make_plan(N, H, V, dtype, C, &p);
+  if (!fits || p.total > kStaticScratchBytes) {
+    g_last_error = "flce_fwd_bwd_noalloc: the workspace of this call (" + std::to_string(p.total) +
+                   " bytes) exceeds the static scratch of " + std::to_string(kStaticScratchBytes) +
+                   " bytes";
+    return FLCE_EWORKSPACE;
+  }
+  void *ws = nullptr;
+  st = static_scratch(&ws);
+  if (st != FLCE_OK) return st;
+  return run(true, X, W, labels, N, H, V, dtype, ignore_index, C, loss, dX, dW, row_loss,
+             row_lse, Options{}, ws, kStaticScratchBytes, stream);
+}
+
 FLCE_API int flce_fwd(const void *X, const void *W, const int64_t *labels, int64_t N, int64_t H,
                       int64_t V, int dtype, int64_t ignore_index, int64_t chunk_tokens,
                       float *loss, float *row_loss, float *row_lse, void *workspace,
