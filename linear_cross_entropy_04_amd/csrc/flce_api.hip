@@ -230,7 +230,7 @@ int chunk_forward(const Plan &p, char *ws, const void *W, int64_t ii, bool keep_
     const uint16_t *Wp = (const uint16_t *)(ws + p.off_wp);
     uint16_t *Zp = (uint16_t *)(ws + p.off_z);
     uint16_t *Xp = (uint16_t *)(ws + p.off_xp);
-    LAUNCH(FLCE_K_PACK, launch_pack_bf16((const uint16_t *)io.Xc, io.c, Hi, Xp, p.nks_h, s));
+    LAUNCH(FLCE_K_PACK, launch_pack_bf16((const uint16_t *)io.Xc, io.c, Hi, Xp, p.nks_h, false, s));
     LAUNCH(FLCE_K_FWD_TILE, launch_fwd_tile_bf16(Wp, Xp, p.nks_h, io.lab, ii, io.c, Hi, Vi, Zp,
                                                  p.nks_z, pm, ps, pmt, zy, p.nvt, keep_z, s));
   } else {
@@ -277,7 +277,7 @@ int pack_weight(const Plan &p, char *ws, const void *W, hipStream_t s) {
   if (p.dtype != FLCE_BF16) return FLCE_OK;
   const int Hi = (int)p.H, Vi = (int)p.V;
   LAUNCH(FLCE_K_PACK_W, launch_pack_bf16((const uint16_t *)W, Vi, Hi,
-                                         (uint16_t *)(ws + p.off_wp), p.nks_h, s));
+                                         (uint16_t *)(ws + p.off_wp), p.nks_h, true, s));
   return FLCE_OK;
 }
 

@@ -68,7 +68,7 @@ hipError_t launch_scale(void *buf, int64_t n, int dtype, const float *scale, hip
 // along their rows or transposed, so no transposed copy is ever made.
 // Pack a row-major [R][K] matrix into P (rows R padded to 256, nks_p slices).
 hipError_t launch_pack_bf16(const uint16_t *src, int R, int K, uint16_t *P, int64_t nks_p,
-                            hipStream_t s);
+                            bool weight, hipStream_t s);
 // Logits tile GEMM with the log-sum-exp epilogue.  pm, ps: [token][partial]
 // maximum and sum of exp per 128 vocabulary ids; with store_z, Zp receives
 // bf16(z - m) for the partial's maximum m, and pmt[partial * c + token] the m

@@ -339,6 +339,7 @@ __device__ __forceinline__ void mainloop(const Op &a, const Op &b, int klen, cha
   constexpr int R = T::MI * reads_per_frag<T::KA>() + T::NI * reads_per_frag<T::KB>();
   constexpr int G = T::NPER;
   static_assert(T::STAGES >= 3, "the wait below admits one slice of STAGES - 1 in flight");
+  static_assert(RPM * M >= R, "every fragment read of a half-step must be issued during the previous one");
   const int nk = (klen + BK - 1) / BK;
   if (nk > 0) {
     const int w = threadIdx.x >> 6;
@@ -440,13 +441,16 @@ constexpr int kDwOcc = 2;                              // dW workgroups per CU
 // measured per kernel on the Llama-3-8B head at chunk 1024.
 constexpr int kFwdRpm = 2, kFwdCsp = 2;
 constexpr int kDxRpm = 2, kDxCsp = 2;
-constexpr int kDwRpm = 2, kDwCsp = 1;
+constexpr int kDwRpm = 4, kDwCsp = 1;
 
 // ---------------------------------------------------------------- packing
 // One workgroup per 256 rows x 64 columns (two packed blocks, 32 KB) of a
 // row-major bf16 matrix [R][K]: it reads the rows' 128-byte pieces (8 full
 // rows per wave instruction), places them in LDS in packed order, and writes
 // the two blocks as one contiguous 32 KB copy.  Zero outside [0, R) x [0, K).
+// WEIGHT only names the instance (W once per call, X once per chunk), so that
+// kernel traces tell the two apart.
+template <bool WEIGHT>
 __global__ __launch_bounds__(256) void pack_kernel(const uint16_t *__restrict__ src, int R, int K,
                                                   uint16_t *__restrict__ P, int64_t nks_p) {
   __shared__ __attribute__((aligned(1024))) char lds[32768];
@@ -490,13 +494,13 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint16_t *__restrict__ 
 // m - z, not of z: exp(z - lse) keeps its accuracy however large the
 // logits or a common shift of a token's logits, and the entries that carry
 // the probability (z near m) are stored almost exactly.
-template <bool VTAIL>
+template <bool VTAIL, class T = FwdTile, int RPM = kFwdRpm, int CSP = kFwdCsp>
 __global__ __launch_bounds__(NTHREADS, 1) void fwd_tile_kernel(
     const uint16_t *__restrict__ Wp, const uint16_t *__restrict__ Xp, int64_t nks_h,
     const int64_t *__restrict__ labels_c, int64_t ii, int c, int H, int V,
     uint16_t *__restrict__ Zp, int64_t nks_z, float *__restrict__ pm, float *__restrict__ ps,
     float *__restrict__ pmt, float *__restrict__ zy, int64_t nvt, int vt0, int nct, int store_z) {
-  using T = FwdTile;
+  static_assert(T::BM == 256 && T::BN == 256, "the epilogue reduces a 256 x 256 tile");
   __shared__ __attribute__((aligned(1024))) char smem[T::LDS];
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
   const int vt = vt0 + tile / nct, ct = tile % nct;
@@ -506,7 +510,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_tile_kernel(
   const Op b{(const char *)(Xp + (int64_t)ct * nks_h * 8192), 0, 0};
   f32x16 acc[4][4];
   zero_acc<T>(acc);
-  mainloop<T, kFwdRpm, kFwdCsp>(a, b, H, smem, acc);
+  mainloop<T, RPM, CSP>(a, b, H, smem, acc);
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int wm = w >> 1, wn = w & 1;
@@ -641,10 +645,11 @@ __global__ __launch_bounds__(256) void dlogits_kernel(
 // G[tok][v] W[v][h].  G from Zp (rows = tokens, k = vocabulary), W read
 // transposed from Wp (its columns, the hidden ids, are the operand rows; its
 // rows, the vocabulary, are k), so no transposed copy of W is made.
+template <class T = DxTile, int RPM = kDxRpm, int CSP = kDxCsp>
 __global__ __launch_bounds__(NTHREADS, 1) void dx_kernel(
     const uint16_t *__restrict__ Gp, int64_t nks_z, const uint16_t *__restrict__ Wp,
     int64_t nks_h, int c, int H, int V, int64_t ksplit, int nmt, int nnt, float *__restrict__ dxp) {
-  using T = DxTile;
+  static_assert(T::BM == 256 && T::BN == 256, "256 x 256 output tiles");
   __shared__ __attribute__((aligned(1024))) char smem[T::LDS];
   const int unit = xcd_remap(blockIdx.x, gridDim.x);
   const int per = nmt * nnt;
@@ -660,7 +665,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void dx_kernel(
   const Op b{(const char *)(Wp + (int64_t)(n0 >> 5) * 8192), nks_h * 16384, kb};
   f32x16 acc[4][4];
   zero_acc<T>(acc);
-  mainloop<T, kDxRpm, kDxCsp>(a, b, klen, smem, acc);
+  mainloop<T, RPM, CSP>(a, b, klen, smem, acc);
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int wm = w >> 1, wn = w & 1;
@@ -717,13 +722,13 @@ __device__ __forceinline__ int dwst_off(int r, int col) {   // bytes
   return r * (BN * 4) + (((col >> 5) ^ ((r >> 2) & 1)) << 7) + ((col & 31) << 2);
 }
 
-template <class T, int OCC>
+template <class T = DwTile, int OCC = kDwOcc, int RPM = kDwRpm, int CSP = kDwCsp, int GROUP = 4>
 __global__ __launch_bounds__(NTHREADS, OCC) void dw_kernel(
     const uint16_t *__restrict__ Gp, int64_t nks_z, const uint16_t *__restrict__ Xp,
     int64_t nks_h, int c, int H, int V, int nvt, int nht, float *__restrict__ dW, int accumulate) {
   __shared__ __attribute__((aligned(1024))) char smem[T::LDS];
   int vt, ht;
-  grouped<4>(xcd_remap(blockIdx.x, gridDim.x), nvt, nht, vt, ht);
+  grouped<GROUP>(xcd_remap(blockIdx.x, gridDim.x), nvt, nht, vt, ht);
   const int m0 = vt * T::BM, n0 = ht * T::BN;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int wm = w >> 1, wn = w & 1;
@@ -732,7 +737,7 @@ __global__ __launch_bounds__(NTHREADS, OCC) void dw_kernel(
   zero_acc<T>(acc);
   const Op a{(const char *)(Gp + (int64_t)(m0 >> 5) * 8192), nks_z * 16384, 0};
   const Op b{(const char *)(Xp + (int64_t)(n0 >> 5) * 8192), nks_h * 16384, 0};
-  mainloop<T, kDwRpm, kDwCsp>(a, b, c, smem, acc);
+  mainloop<T, RPM, CSP>(a, b, c, smem, acc);
 
   constexpr int TPR = T::BN / 4;            // threads per row: one 16-byte piece each
   constexpr int RPP = NTHREADS / TPR;       // rows per pass of the workgroup
@@ -797,10 +802,13 @@ inline int grid_for(int64_t n, int block, int cap) {
 }  // namespace
 
 hipError_t launch_pack_bf16(const uint16_t *src, int R, int K, uint16_t *P, int64_t nks_p,
-                            hipStream_t s) {
+                            bool weight, hipStream_t s) {
   // nks_p is a multiple of 8, so column pairs of slices tile it exactly
   const int64_t nwg = (int64_t)(R + 255) / 256 * (nks_p / 2);
-  hipLaunchKernelGGL(pack_kernel, dim3((unsigned)nwg), dim3(256), 0, s, src, R, K, P, nks_p);
+  if (weight)
+    hipLaunchKernelGGL(pack_kernel<true>, dim3((unsigned)nwg), dim3(256), 0, s, src, R, K, P, nks_p);
+  else
+    hipLaunchKernelGGL(pack_kernel<false>, dim3((unsigned)nwg), dim3(256), 0, s, src, R, K, P, nks_p);
   return hipGetLastError();
 }
 
@@ -811,14 +819,14 @@ hipError_t launch_fwd_tile_bf16(const uint16_t *Wp, const uint16_t *Xp, int64_t 
   const int nct = (c + FwdTile::BN - 1) / FwdTile::BN;
   const int nfull = V / FwdTile::BM;                 // vocabulary tiles inside V
   if (nfull > 0) {
-    hipLaunchKernelGGL(fwd_tile_kernel<false>, dim3(nfull * nct), dim3(NTHREADS), 0, s, Wp, Xp,
+    hipLaunchKernelGGL((fwd_tile_kernel<false>), dim3(nfull * nct), dim3(NTHREADS), 0, s, Wp, Xp,
                        nks_h, labels_c, ii, c, H, V, Zp, nks_z, pm, ps, pmt, zy, nvt, 0, nct,
                        store_z ? 1 : 0);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (V % FwdTile::BM != 0) {
-    hipLaunchKernelGGL(fwd_tile_kernel<true>, dim3(nct), dim3(NTHREADS), 0, s, Wp, Xp, nks_h,
+    hipLaunchKernelGGL((fwd_tile_kernel<true>), dim3(nct), dim3(NTHREADS), 0, s, Wp, Xp, nks_h,
                        labels_c, ii, c, H, V, Zp, nks_z, pm, ps, pmt, zy, nvt, nfull, nct,
                        store_z ? 1 : 0);
   }
@@ -840,7 +848,7 @@ hipError_t launch_dx_bf16(const uint16_t *Gp, int64_t nks_z, const uint16_t *Wp,
                           int c, int H, int V, int splitk, int64_t ksplit, float *dxp,
                           hipStream_t s) {
   const int nmt = (c + DxTile::BM - 1) / DxTile::BM, nnt = (H + DxTile::BN - 1) / DxTile::BN;
-  hipLaunchKernelGGL(dx_kernel, dim3(splitk * nmt * nnt), dim3(NTHREADS), 0, s, Gp, nks_z, Wp,
+  hipLaunchKernelGGL((dx_kernel<>), dim3(splitk * nmt * nnt), dim3(NTHREADS), 0, s, Gp, nks_z, Wp,
                      nks_h, c, H, V, ksplit, nmt, nnt, dxp);
   return hipGetLastError();
 }
@@ -856,7 +864,7 @@ hipError_t launch_dx_reduce_bf16(const float *dxp, int splitk, int c, int H, uin
 hipError_t launch_dw_bf16(const uint16_t *Gp, int64_t nks_z, const uint16_t *Xp, int64_t nks_h,
                           int c, int H, int V, float *dW, bool accumulate, hipStream_t s) {
   const int nvt = (V + DwTile::BM - 1) / DwTile::BM, nht = (H + DwTile::BN - 1) / DwTile::BN;
-  hipLaunchKernelGGL((dw_kernel<DwTile, kDwOcc>), dim3(nvt * nht), dim3(NTHREADS), 0, s, Gp, nks_z, Xp, nks_h, c, H,
+  hipLaunchKernelGGL((dw_kernel<>), dim3(nvt * nht), dim3(NTHREADS), 0, s, Gp, nks_z, Xp, nks_h, c, H,
                      V, nvt, nht, dW, accumulate ? 1 : 0);
   return hipGetLastError();
 }
