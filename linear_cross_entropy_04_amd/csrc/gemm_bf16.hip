@@ -46,6 +46,8 @@
 // 8-byte bank pairs.
 #include "flce_internal.h"
 
+#include <type_traits>
+
 namespace flce {
 namespace {
 
@@ -315,6 +317,50 @@ __device__ __forceinline__ void mfma_at(int i, const Frags<T> &f, f32x16 (&acc)[
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// A main-loop hook issues vector-memory loads of its own during the first NU
+// iterations (compile-time indices, so that the values can go to fixed
+// registers) and works on the accumulators during those iterations and after
+// the loop.  Its loads are issued in the first half-step of an iteration:
+// LP of them in the prologue, after the prologue's copies, and loads(u) in
+// iteration u.  NoHook issues none.
+struct NoHook {
+  static constexpr int NU = 0, LP = 0;
+  static constexpr int loads(int) { return 0; }
+  template <int U, int I>
+  __device__ __forceinline__ void load() {}
+  template <int U, int I, class A>
+  __device__ __forceinline__ void add(A &) {}
+  __device__ __forceinline__ void prologue() {}
+  template <class A>
+  __device__ __forceinline__ void drain(A &) {}
+};
+
+// vmcnt of the wait in iteration t (slice t+1 must have landed): the number
+// of vector-memory operations issued after slice t+1's last copy, for the
+// issue order prologue = copies of slices 0 .. S-2 (G each) then LP loads;
+// iteration u = loads(u) loads, then the G copies of slice u + S - 1.  t = -1
+// is the prologue's own wait (slice 0).  Vector-memory operations complete
+// in issue order, so waiting for this count admits slice t+1 and everything
+// issued before it.
+template <class H>
+constexpr int hook_loads_upto(int t) {
+  int n = 0;
+  for (int u = 0; u <= t; ++u) n += H::loads(u);
+  return n;
+}
+template <class H, int S, int G>
+constexpr int wait_count(int t) {
+  if (t < 0) return (S - 2) * G + H::LP;
+  if (t + 1 <= S - 2) return (S - 3) * G + H::LP + hook_loads_upto<H>(t);
+  return (S - 3) * G + hook_loads_upto<H>(t) - hook_loads_upto<H>(t - S + 2);
+}
+template <class H, int S, int G>
+constexpr int max_wait_count() {
+  int m = 0;
+  for (int t = -1; t <= H::NU + S; ++t) m = wait_count<H, S, G>(t) > m ? wait_count<H, S, G>(t) : m;
+  return m;
+}
+
 // acc[i][j] is the 32 x 32 block (i, j) of the wave's quarter.  Lane l of
 // block (i, j), register e, holds row 32 i + 8 (e/4) + 4 (l/32) + e%4 and
 // column 32 j + l%32 of the quarter.  acc enters initialised by the caller.
@@ -329,17 +375,22 @@ __device__ __forceinline__ void mfma_at(int i, const Frags<T> &f, f32x16 (&acc)[
 // MFMA of the second half-step rather than in one burst, which would hold up
 // the MFMA issue.  Every iteration issues one slice of copies (the last slice
 // again past the end, into a slot that is not read again), so the wait is
-// always for all but the newest STAGES-3 slices, and the last slice is
-// peeled: the loop body is one straight path.  Packed operands carry zero
-// padding up to whole slices, so no copy needs a bounds check.
-template <class T, int RPM, int CSP>
+// always for all but the newest STAGES-3 slices (plus the hook's loads), and
+// the last slice is peeled: the loop body is one straight path.  Packed
+// operands carry zero padding up to whole slices, so no copy needs a bounds
+// check.  The first Hook::NU iterations are unrolled; the caller guarantees
+// that the loop has at least that many (nk - 1 >= NU).
+template <class T, int RPM, int CSP, class Hook = NoHook>
 __device__ __forceinline__ void mainloop(const Op &a, const Op &b, int klen, char *smem,
-                                         f32x16 (&acc)[T::MI][T::NI]) {
+                                         f32x16 (&acc)[T::MI][T::NI], Hook &&hook = Hook{}) {
+  using HK = std::remove_reference_t<Hook>;
   constexpr int M = T::MI * T::NI;                 // MFMAs per half-step
   constexpr int R = T::MI * reads_per_frag<T::KA>() + T::NI * reads_per_frag<T::KB>();
   constexpr int G = T::NPER;
-  static_assert(T::STAGES >= 3, "the wait below admits one slice of STAGES - 1 in flight");
+  constexpr int S = T::STAGES;
+  static_assert(S >= 3, "the wait below admits one slice of STAGES - 1 in flight");
   static_assert(RPM * M >= R, "every fragment read of a half-step must be issued during the previous one");
+  static_assert(max_wait_count<HK, S, G>() < 64, "vmcnt range");
   const int nk = (klen + BK - 1) / BK;
   if (nk > 0) {
     const int w = threadIdx.x >> 6;
@@ -357,23 +408,27 @@ __device__ __forceinline__ void mainloop(const Op &a, const Op &b, int klen, cha
       return Bases{z.a0 + o, z.a1 + o, z.b0 + o, z.b1 + o};
     };
 #pragma unroll
-    for (int s = 0; s < T::STAGES - 1; ++s) {
+    for (int s = 0; s < S - 1; ++s) {
       const int k0 = (s < nk ? s : nk - 1) * BK;
 #pragma unroll
       for (int g = 0; g < G; ++g) stage_copy<T>(a, b, k0, lds0 + (uint32_t)(s * T::STAGE_BYTES), g);
     }
-    wait_vm<(T::STAGES - 2) * G>();
+    hook.prologue();
+    wait_vm<wait_count<HK, S, G>(-1)>();
     bar();
     Frags<T> f0, f1;
     Bases cur = z;                                 // the stage of slice t
     int st = 0;
     static_for<0, R>([&](auto q) { frag_read<T, 0, decltype(q)::value>(cur, f0); });
-    for (int t = 0; t < nk - 1; ++t) {
-      const int sn = st + 1 == T::STAGES ? 0 : st + 1;
+    // one iteration; U >= 0 is an unrolled iteration of the hook, U < 0 a
+    // runtime one
+    auto body = [&](int t, auto uu) {
+      constexpr int U = decltype(uu)::value;
+      const int sn = st + 1 == S ? 0 : st + 1;
       const Bases nxt = stage_bases(sn);
-      const int ck = t + T::STAGES - 1;            // slice copied in this iteration
+      const int ck = t + S - 1;                    // slice copied in this iteration
       const int k0 = (ck < nk ? ck : nk - 1) * BK;
-      const uint32_t cst = lds0 + (uint32_t)((ck % T::STAGES) * T::STAGE_BYTES);
+      const uint32_t cst = lds0 + (uint32_t)((ck % S) * T::STAGE_BYTES);
       frags_wait<T>(f0);
       // first half-step; the reads of the second go out between its MFMAs
       static_for<0, M>([&](auto ii) {
@@ -381,14 +436,17 @@ __device__ __forceinline__ void mainloop(const Op &a, const Op &b, int klen, cha
         mfma_at<T>(i, f0, acc);
         constexpr int q0 = i * RPM < R ? i * RPM : R, q1 = (i + 1) * RPM < R ? (i + 1) * RPM : R;
         static_for<q0, q1>([&](auto q) { frag_read<T, 1, decltype(q)::value>(cur, f1); });
+        if constexpr (U >= 0) hook.template load<U, i>();
       });
       // slice t+1 must have landed; slices t+2 .. t+STAGES-2 may stay in flight
-      wait_vm<(T::STAGES - 3) * G>();
+      if constexpr (U >= 0) wait_vm<wait_count<HK, S, G>(U)>();
+      else wait_vm<(S - 3) * G>();                 // at most the exact count: safe
       bar();
       frags_wait<T>(f1);
       // second half-step: the next slice's copies and first reads between its MFMAs
       static_for<0, M>([&](auto ii) {
         constexpr int i = decltype(ii)::value;
+        if constexpr (U >= 0) hook.template add<U, i>(acc);
         mfma_at<T>(i, f1, acc);
         if constexpr (i % CSP == 0 && i / CSP < G) stage_copy<T>(a, b, k0, cst, i / CSP);
         constexpr int q0 = i * RPM < R ? i * RPM : R, q1 = (i + 1) * RPM < R ? (i + 1) * RPM : R;
@@ -398,7 +456,9 @@ __device__ __forceinline__ void mainloop(const Op &a, const Op &b, int klen, cha
         static_for<(M + CSP - 1) / CSP, G>([&](auto g) { stage_copy<T>(a, b, k0, cst, decltype(g)::value); });
       cur = nxt;
       st = sn;
-    }
+    };
+    static_for<0, HK::NU>([&](auto uu) { body(decltype(uu)::value, uu); });
+    for (int t = HK::NU; t < nk - 1; ++t) body(t, ic<-1>{});
     frags_wait<T>(f0);
     static_for<0, M>([&](auto ii) {
       constexpr int i = decltype(ii)::value;
@@ -409,10 +469,11 @@ __device__ __forceinline__ void mainloop(const Op &a, const Op &b, int klen, cha
     frags_wait<T>(f1);
     static_for<0, M>([&](auto ii) { mfma_at<T>(decltype(ii)::value, f1, acc); });
   }
-  // every wave is done with the LDS slices and no copy is still writing them;
-  // the caller may reuse LDS
+  // every wave is done with the LDS slices and no copy or load is still in
+  // flight; the caller may reuse LDS
   wait_vm<0>();
   bar();
+  if (nk > 0) hook.drain(acc);
 }
 
 template <class T>
@@ -435,13 +496,13 @@ __device__ __forceinline__ float bf16_hi(uint32_t u) { return __builtin_bit_cast
 
 using FwdTile = Tile<256, 256, 4, PACKED, PACKED>;     // A = Wp, B = Xp
 using DxTile = Tile<256, 256, 4, PACKED, PACKED_T>;    // A = G (Zp), B = Wp read transposed
-using DwTile = Tile<256, 128, 3, PACKED_T, PACKED_T>;  // A = G (Zp), B = Xp, both transposed
-constexpr int kDwOcc = 2;                              // dW workgroups per CU
+using DwTile = Tile<256, 256, 4, PACKED_T, PACKED_T>;  // A = G (Zp), B = Xp, both transposed
+constexpr int kDwGroup = 4;                            // vocabulary strips per group of dW tiles
 // Main-loop schedules (reads per MFMA, MFMAs per copy), the fastest of those
 // measured per kernel on the Llama-3-8B head at chunk 1024.
 constexpr int kFwdRpm = 2, kFwdCsp = 2;
 constexpr int kDxRpm = 2, kDxCsp = 2;
-constexpr int kDwRpm = 4, kDwCsp = 1;
+constexpr int kDwRpm = 1, kDwCsp = 2;
 
 // ---------------------------------------------------------------- packing
 // One workgroup per 256 rows x 64 columns (two packed blocks, 32 KB) of a
@@ -704,92 +765,162 @@ __global__ void dx_reduce_kernel(const float *__restrict__ dxp, int splitk, int 
 
 // ---------------------------------------------------------------- dW
 // dW[v][h] (+)= sum over the chunk's tokens of G[tok][v] X[tok][h], in
-// BM x BN = 256 x 128 tiles, two workgroups per CU so that one's dW traffic
-// overlaps the other's MFMA work; G from Zp and X from Xp, both read
-// transposed.
+// 256 x 256 tiles, one workgroup per CU; G from Zp and X from Xp, both read
+// transposed.  Lane l of wave (wm, wn) holds, in acc[i][j][e], dW row
+// v0 + 128 wm + 32 i + 8 (e/4) + 4 (l/32) + e%4 and column
+// h0 + 128 wn + 32 j + l%32, so one dword access per (i, j, e) moves two
+// whole 128-byte row pieces per wave.
 //
-// The epilogue goes through LDS in two halves of 128 rows (BN fp32 per row)
-// so that dW is read and written in row-contiguous 16-byte pieces: the waves
-// holding a half write their accumulators, then every thread moves its
-// pieces.  A thread's loads of the current dW for a half are issued before
-// the accumulators of that half reach LDS (for the second half, right after
-// the first half's stores), so their latency overlaps the staging; the
-// barriers wait for LDS only, not for these loads.
-// 128-byte column blocks of an LDS row are XOR-swizzled by row bit 2 so the
-// two rows a write instruction covers use both halves of the banks.
-template <int BN>
-__device__ __forceinline__ int dwst_off(int r, int col) {   // bytes
-  return r * (BN * 4) + (((col >> 5) ^ ((r >> 2) & 1)) << 7) + ((col & 31) << 2);
+// Accumulating into dW (every chunk after the first) needs the tile's old
+// values.  Loaded in one burst after the main loop, they compete with the
+// operand copies of the workgroups still in their main loops for each CU's
+// vector-memory path; instead, the old values reach the accumulators during
+// the main loop (DwOld): the first 15 iterations are unrolled, and iteration
+// u loads block u + 1's 16 values per lane (block 0 in the prologue), one
+// after each MFMA of its first half-step.  Two iterations later, once the
+// loop's own wait has admitted a copy issued after them, the block is added
+// into its accumulators as a whole, right before the second half-step's MFMA
+// on it.  (Adding single registers of a block makes the compiler copy the
+// whole block out of and back into the accumulator registers around every
+// MFMA.)  After the loop only stores remain.  Tiles that reach past V or H,
+// chunks of fewer than 16 slices and the first chunk (nothing to add) take
+// the plain path: the main loop alone, then a predicated read-add-store (or
+// store) pass.
+constexpr int kDwAux = 2;          // non-temporal: dW is touched once per chunk
+
+template <int S>
+struct DwOld {
+  static constexpr int NB = 16;                    // blocks = MFMAs per half-step
+  static constexpr int NU = NB - 1;                // iteration u loads block u + 1
+  static constexpr int LP = 16;                    // the prologue loads block 0
+  static constexpr int loads(int u) { return u < NU ? 16 : 0; }
+  // the first iteration whose wait admits a copy issued after block b's loads
+  static constexpr int add_iter(int b) { return b == 0 ? S - 2 : b + S - 3; }
+
+  __amdgpu_buffer_rsrc_t rs;       // this wave's 128 x 128 quarter of dW
+  int voff;                        // the lane's byte offset in it
+  int ldb;                         // bytes per dW row
+  float v[NB][16];
+
+  template <int b, int e>
+  __device__ __forceinline__ void load_one() {
+    constexpr int i = b / 4, j = b % 4, row = 32 * i + 8 * (e / 4) + e % 4;
+    v[b][e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, voff + 128 * j, row * ldb,
+                                                                              kDwAux));
+  }
+  template <int b, class A>
+  __device__ __forceinline__ void add_block(A &acc) {
+    f32x16 o;
+    static_for<0, 16>([&](auto e) { o[decltype(e)::value] = v[b][decltype(e)::value]; });
+    acc[b / 4][b % 4] += o;
+  }
+  __device__ __forceinline__ void prologue() {
+    static_for<0, 16>([&](auto e) { load_one<0, decltype(e)::value>(); });
+  }
+  // iteration U: value I of block U + 1 after the first half-step's MFMA I
+  template <int U, int I>
+  __device__ __forceinline__ void load() {
+    if constexpr (U + 1 < NB) load_one<U + 1, I>();
+  }
+  // iteration U, before the second half-step's MFMA on block I
+  template <int U, int I, class A>
+  __device__ __forceinline__ void add(A &acc) {
+    if constexpr (add_iter(I) == U) add_block<I>(acc);
+  }
+  template <class A>
+  __device__ __forceinline__ void drain(A &acc) {
+    static_for<0, NB>([&](auto bb) {
+      constexpr int b = decltype(bb)::value;
+      if constexpr (add_iter(b) >= NU) add_block<b>(acc);
+    });
+  }
+};
+
+// Write a wave's 128 x 128 quarter: dW = acc, or dW + acc with OLD.  CHECK
+// masks rows >= vlim and columns >= hlim (relative to the quarter).
+template <bool OLD, bool CHECK, class A>
+__device__ __forceinline__ void dw_store(const A &acc, __amdgpu_buffer_rsrc_t rs, int voff, int ldb,
+                                         int vlim, int hlim) {
+  const int lane = threadIdx.x & 63;
+  static_for<0, 16>([&](auto bb) {
+    constexpr int b = decltype(bb)::value, i = b / 4, j = b % 4;
+    const bool col_ok = !CHECK || 32 * j + (lane & 31) < hlim;
+    float old[16];
+    static_for<0, 16>([&](auto ee) {
+      constexpr int e = decltype(ee)::value, row = 32 * i + 8 * (e / 4) + e % 4;
+      old[e] = 0.f;
+      if constexpr (OLD) {
+        if (col_ok && (!CHECK || row + 4 * (lane >> 5) < vlim))
+          old[e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, voff + 128 * j, row * ldb,
+                                                                                  kDwAux));
+      }
+    });
+    static_for<0, 16>([&](auto ee) {
+      constexpr int e = decltype(ee)::value, row = 32 * i + 8 * (e / 4) + e % 4;
+      // read the accumulator here, not all of them after the main loop
+      float x;
+      asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(x) : "a"(acc[i][j][e]));
+      if constexpr (OLD) x += old[e];
+      if (col_ok && (!CHECK || row + 4 * (lane >> 5) < vlim))
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, x), rs, voff + 128 * j, row * ldb,
+                                              kDwAux);
+    });
+    // one block's old values at a time in registers
+    asm volatile("" ::: "memory");
+  });
 }
 
-template <class T = DwTile, int OCC = kDwOcc, int RPM = kDwRpm, int CSP = kDwCsp, int GROUP = 4>
-__global__ __launch_bounds__(NTHREADS, OCC) void dw_kernel(
+// Tile (vt, ht) of launch index t.  SPREAD launches cover the nvt x nht
+// tiles inside V and H; the others cover all nvt x nht tiles (tails = 0), or
+// only those that reach past V or H (tails = 1): first the last vocabulary
+// row of tiles when V has a tail (vtail), then the last hidden column when H
+// has one (htail), without the corner twice.
+template <int GROUP>
+__device__ __forceinline__ void dw_tile(int t, int nvt, int nht, int tails, int vtail, int htail, int &vt,
+                                        int &ht) {
+  if (!tails) {
+    grouped<GROUP>(xcd_remap(t, nvt * nht), nvt, nht, vt, ht);
+  } else if (vtail && t < nht) {
+    vt = nvt - 1;
+    ht = t;
+  } else {
+    vt = t - (vtail ? nht : 0);
+    ht = nht - 1;
+  }
+}
+
+template <bool SPREAD, class T = DwTile, int RPM = kDwRpm, int CSP = kDwCsp, int GROUP = kDwGroup>
+__global__ __launch_bounds__(NTHREADS, 1) void dw_kernel(
     const uint16_t *__restrict__ Gp, int64_t nks_z, const uint16_t *__restrict__ Xp,
-    int64_t nks_h, int c, int H, int V, int nvt, int nht, float *__restrict__ dW, int accumulate) {
+    int64_t nks_h, int c, int H, int V, int nvt, int nht, int tails, int vtail, int htail,
+    float *__restrict__ dW, int accumulate) {
+  static_assert(T::BM == 256 && T::BN == 256, "a wave's quarter is 128 x 128");
   __shared__ __attribute__((aligned(1024))) char smem[T::LDS];
   int vt, ht;
-  grouped<GROUP>(xcd_remap(blockIdx.x, gridDim.x), nvt, nht, vt, ht);
+  dw_tile<GROUP>(blockIdx.x, nvt, nht, tails, vtail, htail, vt, ht);
   const int m0 = vt * T::BM, n0 = ht * T::BN;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = w >> 1, wn = w & 1;
 
   f32x16 acc[T::MI][T::NI];
   zero_acc<T>(acc);
   const Op a{(const char *)(Gp + (int64_t)(m0 >> 5) * 8192), nks_z * 16384, 0};
   const Op b{(const char *)(Xp + (int64_t)(n0 >> 5) * 8192), nks_h * 16384, 0};
-  mainloop<T, RPM, CSP>(a, b, c, smem, acc);
-
-  constexpr int TPR = T::BN / 4;            // threads per row: one 16-byte piece each
-  constexpr int RPP = NTHREADS / TPR;       // rows per pass of the workgroup
-  constexpr int NQ = 128 / RPP;             // pieces per thread per half
-  static_assert(T::BM == 256 && T::LDS >= 128 * T::BN * 4, "epilogue half tile must fit in LDS");
-  // thread t takes piece t % TPR of rows t / TPR + RPP q of each half
-  const int col = (threadIdx.x % TPR) * 4;
-  const int h = n0 + col;
-  const int rb = threadIdx.x / TPR;
-  // dW is touched once per chunk: non-temporal accesses keep it from
-  // evicting the G and X strips that the next tiles reuse from L2
-  f32x4 old[NQ];
-  auto load_old = [&](int half) {
-#pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-      const int v = m0 + half * 128 + rb + RPP * q;
-      const bool ok = v < V && h < H;            // H % 8 == 0: a started piece fits
-      old[q] = (accumulate && ok) ? __builtin_nontemporal_load((const f32x4 *)(dW + (int64_t)v * H + h))
-                                  : f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-  };
-  load_old(0);
-#pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    if (wm == half) {
-#pragma unroll
-      for (int i = 0; i < T::MI; ++i)
-#pragma unroll
-        for (int j = 0; j < T::NI; ++j)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int r = 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-            const int cc = wn * T::WN + 32 * j + (lane & 31);
-            *(float *)(smem + dwst_off<T::BN>(r, cc)) = acc[i][j][e];
-          }
-    }
-    // the half is in LDS (a fence-free barrier: the loads stay in flight)
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    bar();
-#pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-      const int r = rb + RPP * q;
-      const int v = m0 + half * 128 + r;
-      if (v < V && h < H) {
-        const f32x4 add = *(const f32x4 *)(smem + dwst_off<T::BN>(r, col));
-        __builtin_nontemporal_store(old[q] + add, (f32x4 *)(dW + (int64_t)v * H + h));
-      }
-    }
-    if (half == 0) load_old(1);
-    // every thread has read its pieces before the next half overwrites LDS
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    bar();
+  // the wave's quarter of dW; offsets stay below 2^31 for H <= 2^20
+  const int vq = m0 + wm * T::WM, hq = n0 + wn * T::WN;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      dW + (int64_t)vq * H + hq, (short)0, 0x7fffffff, 0x00020000);
+  const int voff = ((lane >> 5) * 4 * H + (lane & 31)) * 4, ldb = H * 4;
+  if constexpr (SPREAD) {
+    // the launch guarantees: accumulate, tile inside V and H, c >= 16 slices
+    DwOld<T::STAGES> hk{rs, voff, ldb};
+    mainloop<T, RPM, CSP>(a, b, c, smem, acc, hk);
+    dw_store<false, false>(acc, rs, voff, ldb, 0, 0);
+  } else {
+    mainloop<T, RPM, CSP>(a, b, c, smem, acc);
+    const int vlim = V - vq, hlim = H - hq;
+    if (accumulate) dw_store<true, true>(acc, rs, voff, ldb, vlim, hlim);
+    else dw_store<false, true>(acc, rs, voff, ldb, vlim, hlim);
   }
 }
 
@@ -864,8 +995,21 @@ hipError_t launch_dx_reduce_bf16(const float *dxp, int splitk, int c, int H, uin
 hipError_t launch_dw_bf16(const uint16_t *Gp, int64_t nks_z, const uint16_t *Xp, int64_t nks_h,
                           int c, int H, int V, float *dW, bool accumulate, hipStream_t s) {
   const int nvt = (V + DwTile::BM - 1) / DwTile::BM, nht = (H + DwTile::BN - 1) / DwTile::BN;
-  hipLaunchKernelGGL((dw_kernel<>), dim3(nvt * nht), dim3(NTHREADS), 0, s, Gp, nks_z, Xp, nks_h, c, H,
-                     V, nvt, nht, dW, accumulate ? 1 : 0);
+  const int nvi = V / DwTile::BM, nhi = H / DwTile::BN;        // tiles inside V, H
+  const int vtail = nvi < nvt, htail = nhi < nht;
+  const int nk = (c + BK - 1) / BK;
+  const dim3 block(NTHREADS);
+  if (accumulate && nk >= DwOld<DwTile::STAGES>::NB && nvi > 0 && nhi > 0) {
+    hipLaunchKernelGGL((dw_kernel<true>), dim3(nvi * nhi), block, 0, s, Gp, nks_z, Xp, nks_h, c, H, V, nvi,
+                       nhi, 0, 0, 0, dW, 1);
+    const int ntail = (vtail ? nht : 0) + (htail ? nvt - vtail : 0);
+    if (ntail > 0)
+      hipLaunchKernelGGL((dw_kernel<false>), dim3(ntail), block, 0, s, Gp, nks_z, Xp, nks_h, c, H, V, nvt,
+                         nht, 1, vtail, htail, dW, 1);
+  } else {
+    hipLaunchKernelGGL((dw_kernel<false>), dim3(nvt * nht), block, 0, s, Gp, nks_z, Xp, nks_h, c, H, V, nvt,
+                       nht, 0, 0, 0, dW, accumulate ? 1 : 0);
+  }
   return hipGetLastError();
 }
 

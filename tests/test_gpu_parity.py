@@ -51,6 +51,8 @@ def test_pages_api_example_shape():
     (513, 256, 257, 512),       # one token past a tile; one vocab id past a tile
     (64, 64, 40000, 64),        # many vocabulary tiles, one small chunk
     (300, 1024, 700, 1000),     # one chunk (chunk > N), deep K
+    (1500, 320, 1100, 512),     # dW old values added in the main loop (16 slices), V and H tails
+    (2100, 512, 600, 1024),     # the same at 32 slices, V tail; last chunk of 52 rows
 ])
 def test_bf16_ragged(N, H, V, chunk):
     inp = datagen.make_custom(N, H, V, "bf16", seed=N + V, ignore_frac=0.1)
