@@ -134,35 +134,63 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t slice_rsrc(const char *p) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(p), (short)0, 0x7fffffff, 0x00020000);
 }
 
-// Copy i (0 .. ROWS/64 - 1) of this thread for k-slice [k0, k0 + 32) (relative
-// to the range) of an operand tile of ROWS rows: 1 KB piece blk = 4 i + wave,
-// written at LDS byte address tile + 1 KB blk.  PACKED_T pieces 2q, 2q+1 are
-// the two fragments of operand rows 32q..32q+31.  Only the lane's 16-byte
-// offset is per lane; the slice's descriptor and the piece offset are scalar.
-template <int KIND>
-__device__ __forceinline__ void copy_piece(const Op &op, int k0, uint32_t tile, int i) {
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), l = threadIdx.x & 63;
-  const int blk = i * 4 + w;
-  const char *slice;
-  int off;
-  if constexpr (KIND == PACKED) {
-    slice = op.base + (int64_t)(k0 >> 5) * 16384;
-    off = blk * 1024;
-  } else {
-    const int64_t kr = op.kb + k0;                 // row of the matrix
-    slice = op.base + (kr >> 8) * op.ld + (((kr & 255) >> 5) << 11);
-    off = (blk >> 1) * 16384 + (blk & 1) * 1024;
-  }
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(slice_rsrc(slice), (lds_void *)(uintptr_t)(tile + blk * 1024),
-                                           16, l * 16, __builtin_amdgcn_readfirstlane(off), 0, 0);
-}
+// The copies of one operand tile: this wave's pieces of a k-slice, at
+// scalar offsets fixed for the whole loop, and the slice's address, advanced
+// once per slice (no per-copy address arithmetic in the loop).  Piece i of
+// the wave is 1 KB piece blk = 4 i + wave of the slice, written at LDS byte
+// address stage + 1 KB blk.  PACKED_T pieces 2q, 2q+1 are the two fragments
+// of operand rows 32q..32q+31.  Only the lane's 16-byte offset is per lane.
+template <int KIND, int NP>
+struct OpStream {
+  const char *ptr;         // the slice copied next
+  int64_t ld;              // PACKED_T: bytes of one row tile of the matrix
+  int kr;                  // PACKED_T: the matrix row of ptr's slice
+  int soff[NP];            // piece offsets within a slice (bytes)
+  uint32_t loff[NP];       // piece offsets within the operand's stage area
 
-// Copy g (0 .. NPER - 1) of a stage: the A operand's pieces, then B's.
+  __device__ __forceinline__ void init(const Op &op) {
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      const int blk = i * 4 + w;
+      soff[i] = KIND == PACKED ? blk * 1024 : (blk >> 1) * 16384 + (blk & 1) * 1024;
+      loff[i] = (uint32_t)(blk * 1024);
+    }
+    ld = op.ld;
+    kr = (int)op.kb;
+    if constexpr (KIND == PACKED) ptr = op.base;
+    else ptr = op.base + (int64_t)(kr >> 8) * ld + (((kr & 255) >> 5) << 11);
+  }
+  // on to the next k-slice if go (selects, not a branch, inside the loop)
+  __device__ __forceinline__ void advance(bool go = true) {
+    if constexpr (KIND == PACKED) {
+      ptr += go ? 16384 : 0;
+    } else {
+      const int64_t inc = (kr & 255) == 224 ? ld - 7 * 2048 : 2048;
+      ptr += go ? inc : 0;
+      kr += go ? 32 : 0;
+    }
+  }
+  __device__ __forceinline__ void copy(int i, uint32_t stage) const {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(slice_rsrc(ptr), (lds_void *)(uintptr_t)(stage + loff[i]), 16,
+                                             (threadIdx.x & 63) * 16, soff[i], 0, 0);
+  }
+};
+
 template <class T>
-__device__ __forceinline__ void stage_copy(const Op &a, const Op &b, int k0, uint32_t st, int g) {
-  if (g < T::NA) copy_piece<T::KA>(a, k0, st, g);
-  else copy_piece<T::KB>(b, k0, st + T::A_BYTES, g - T::NA);
-}
+struct Streams {
+  OpStream<T::KA, T::NA> a;
+  OpStream<T::KB, T::NB> b;
+  // copy g (0 .. NPER - 1) of a stage: the A operand's pieces, then B's
+  __device__ __forceinline__ void copy(int g, uint32_t st) const {
+    if (g < T::NA) a.copy(g, st);
+    else b.copy(g - T::NA, st + T::A_BYTES);
+  }
+  __device__ __forceinline__ void advance(bool go = true) {
+    a.advance(go);
+    b.advance(go);
+  }
+};
 
 // s_waitcnt vmcnt(N) leaving the other counters unconstrained.
 template <int N>
@@ -407,11 +435,15 @@ __device__ __forceinline__ void mainloop(const Op &a, const Op &b, int klen, cha
       const uint32_t o = (uint32_t)(s * T::STAGE_BYTES);
       return Bases{z.a0 + o, z.a1 + o, z.b0 + o, z.b1 + o};
     };
+    // the prologue's slices 0 .. S-2 (the last slice again past the end)
+    Streams<T> cs;
+    cs.a.init(a);
+    cs.b.init(b);
 #pragma unroll
     for (int s = 0; s < S - 1; ++s) {
-      const int k0 = (s < nk ? s : nk - 1) * BK;
+      if (s > 0 && s < nk) cs.advance();
 #pragma unroll
-      for (int g = 0; g < G; ++g) stage_copy<T>(a, b, k0, lds0 + (uint32_t)(s * T::STAGE_BYTES), g);
+      for (int g = 0; g < G; ++g) cs.copy(g, lds0 + (uint32_t)(s * T::STAGE_BYTES));
     }
     hook.prologue();
     wait_vm<wait_count<HK, S, G>(-1)>();
@@ -427,7 +459,6 @@ __device__ __forceinline__ void mainloop(const Op &a, const Op &b, int klen, cha
       const int sn = st + 1 == S ? 0 : st + 1;
       const Bases nxt = stage_bases(sn);
       const int ck = t + S - 1;                    // slice copied in this iteration
-      const int k0 = (ck < nk ? ck : nk - 1) * BK;
       const uint32_t cst = lds0 + (uint32_t)((ck % S) * T::STAGE_BYTES);
       frags_wait<T>(f0);
       // first half-step; the reads of the second go out between its MFMAs
@@ -442,18 +473,19 @@ __device__ __forceinline__ void mainloop(const Op &a, const Op &b, int klen, cha
       if constexpr (U >= 0) wait_vm<wait_count<HK, S, G>(U)>();
       else wait_vm<(S - 3) * G>();                 // at most the exact count: safe
       bar();
+      cs.advance(ck < nk);                         // else the last slice again
       frags_wait<T>(f1);
       // second half-step: the next slice's copies and first reads between its MFMAs
       static_for<0, M>([&](auto ii) {
         constexpr int i = decltype(ii)::value;
         if constexpr (U >= 0) hook.template add<U, i>(acc);
         mfma_at<T>(i, f1, acc);
-        if constexpr (i % CSP == 0 && i / CSP < G) stage_copy<T>(a, b, k0, cst, i / CSP);
+        if constexpr (i % CSP == 0 && i / CSP < G) cs.copy(i / CSP, cst);
         constexpr int q0 = i * RPM < R ? i * RPM : R, q1 = (i + 1) * RPM < R ? (i + 1) * RPM : R;
         static_for<q0, q1>([&](auto q) { frag_read<T, 0, decltype(q)::value>(nxt, f0); });
       });
       if constexpr (G > (M + CSP - 1) / CSP)
-        static_for<(M + CSP - 1) / CSP, G>([&](auto g) { stage_copy<T>(a, b, k0, cst, decltype(g)::value); });
+        static_for<(M + CSP - 1) / CSP, G>([&](auto g) { cs.copy(decltype(g)::value, cst); });
       cur = nxt;
       st = sn;
     };
