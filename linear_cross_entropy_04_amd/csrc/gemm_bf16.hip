@@ -530,6 +530,7 @@ using FwdTile = Tile<256, 256, 4, PACKED, PACKED>;     // A = Wp, B = Xp
 using DxTile = Tile<256, 256, 4, PACKED, PACKED_T>;    // A = G (Zp), B = Wp read transposed
 using DwTile = Tile<256, 256, 4, PACKED_T, PACKED_T>;  // A = G (Zp), B = Xp, both transposed
 constexpr int kDwGroup = 4;                            // vocabulary strips per group of dW tiles
+constexpr int kDwOcc = 1;                              // dW workgroups per CU
 // Main-loop schedules (reads per MFMA, MFMAs per copy), the fastest of those
 // measured per kernel on the Llama-3-8B head at chunk 1024.
 constexpr int kFwdRpm = 2, kFwdCsp = 2;
@@ -807,9 +808,10 @@ __global__ void dx_reduce_kernel(const float *__restrict__ dxp, int splitk, int 
 // values.  Loaded in one burst after the main loop, they compete with the
 // operand copies of the workgroups still in their main loops for each CU's
 // vector-memory path; instead, the old values reach the accumulators during
-// the main loop (DwOld): the first 15 iterations are unrolled, and iteration
-// u loads block u + 1's 16 values per lane (block 0 in the prologue), one
-// after each MFMA of its first half-step.  Two iterations later, once the
+// the main loop (DwOld): the first 15 iterations (one fewer than a wave's
+// 16 accumulator blocks) are unrolled, and iteration u loads block u + 1's
+// 16 values per lane (block 0 in the prologue), one after each MFMA of its
+// first half-step.  Two iterations later, once the
 // loop's own wait has admitted a copy issued after them, the block is added
 // into its accumulators as a whole, right before the second half-step's MFMA
 // on it.  (Adding single registers of a block makes the compiler copy the
@@ -820,11 +822,13 @@ __global__ void dx_reduce_kernel(const float *__restrict__ dxp, int splitk, int 
 // store) pass.
 constexpr int kDwAux = 2;          // non-temporal: dW is touched once per chunk
 
-template <int S>
+template <class T>
 struct DwOld {
-  static constexpr int NB = 16;                    // blocks = MFMAs per half-step
+  static constexpr int S = T::STAGES, NI = T::NI;
+  static constexpr int NB = T::MI * T::NI;         // blocks = MFMAs per half-step
   static constexpr int NU = NB - 1;                // iteration u loads block u + 1
   static constexpr int LP = 16;                    // the prologue loads block 0
+  static_assert(16 % NB == 0 || NB % 16 == 0, "a block's loads spread evenly over a half-step");
   static constexpr int loads(int u) { return u < NU ? 16 : 0; }
   // the first iteration whose wait admits a copy issued after block b's loads
   static constexpr int add_iter(int b) { return b == 0 ? S - 2 : b + S - 3; }
@@ -836,7 +840,7 @@ struct DwOld {
 
   template <int b, int e>
   __device__ __forceinline__ void load_one() {
-    constexpr int i = b / 4, j = b % 4, row = 32 * i + 8 * (e / 4) + e % 4;
+    constexpr int i = b / NI, j = b % NI, row = 32 * i + 8 * (e / 4) + e % 4;
     v[b][e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, voff + 128 * j, row * ldb,
                                                                               kDwAux));
   }
@@ -844,15 +848,19 @@ struct DwOld {
   __device__ __forceinline__ void add_block(A &acc) {
     f32x16 o;
     static_for<0, 16>([&](auto e) { o[decltype(e)::value] = v[b][decltype(e)::value]; });
-    acc[b / 4][b % 4] += o;
+    acc[b / NI][b % NI] += o;
   }
   __device__ __forceinline__ void prologue() {
     static_for<0, 16>([&](auto e) { load_one<0, decltype(e)::value>(); });
   }
-  // iteration U: value I of block U + 1 after the first half-step's MFMA I
+  // iteration U: block U + 1's 16 values spread over the first half-step's
+  // NB MFMAs, 16 / NB after each
   template <int U, int I>
   __device__ __forceinline__ void load() {
-    if constexpr (U + 1 < NB) load_one<U + 1, I>();
+    if constexpr (U + 1 < NB) {
+      constexpr int per = 16 / NB > 0 ? 16 / NB : 1, first = I * per;
+      if constexpr (first < 16) static_for<first, first + per>([&](auto e) { load_one<U + 1, decltype(e)::value>(); });
+    }
   }
   // iteration U, before the second half-step's MFMA on block I
   template <int U, int I, class A>
@@ -870,12 +878,12 @@ struct DwOld {
 
 // Write a wave's 128 x 128 quarter: dW = acc, or dW + acc with OLD.  CHECK
 // masks rows >= vlim and columns >= hlim (relative to the quarter).
-template <bool OLD, bool CHECK, class A>
+template <class T, bool OLD, bool CHECK, class A>
 __device__ __forceinline__ void dw_store(const A &acc, __amdgpu_buffer_rsrc_t rs, int voff, int ldb,
                                          int vlim, int hlim) {
   const int lane = threadIdx.x & 63;
-  static_for<0, 16>([&](auto bb) {
-    constexpr int b = decltype(bb)::value, i = b / 4, j = b % 4;
+  static_for<0, T::MI * T::NI>([&](auto bb) {
+    constexpr int b = decltype(bb)::value, i = b / T::NI, j = b % T::NI;
     const bool col_ok = !CHECK || 32 * j + (lane & 31) < hlim;
     float old[16];
     static_for<0, 16>([&](auto ee) {
@@ -921,12 +929,12 @@ __device__ __forceinline__ void dw_tile(int t, int nvt, int nht, int tails, int 
   }
 }
 
-template <bool SPREAD, class T = DwTile, int RPM = kDwRpm, int CSP = kDwCsp, int GROUP = kDwGroup>
-__global__ __launch_bounds__(NTHREADS, 1) void dw_kernel(
+template <bool SPREAD, class T = DwTile, int RPM = kDwRpm, int CSP = kDwCsp, int GROUP = kDwGroup,
+          int OCC = kDwOcc>
+__global__ __launch_bounds__(NTHREADS, OCC) void dw_kernel(
     const uint16_t *__restrict__ Gp, int64_t nks_z, const uint16_t *__restrict__ Xp,
     int64_t nks_h, int c, int H, int V, int nvt, int nht, int tails, int vtail, int htail,
     float *__restrict__ dW, int accumulate) {
-  static_assert(T::BM == 256 && T::BN == 256, "a wave's quarter is 128 x 128");
   __shared__ __attribute__((aligned(1024))) char smem[T::LDS];
   int vt, ht;
   dw_tile<GROUP>(blockIdx.x, nvt, nht, tails, vtail, htail, vt, ht);
@@ -945,14 +953,14 @@ __global__ __launch_bounds__(NTHREADS, 1) void dw_kernel(
   const int voff = ((lane >> 5) * 4 * H + (lane & 31)) * 4, ldb = H * 4;
   if constexpr (SPREAD) {
     // the launch guarantees: accumulate, tile inside V and H, c >= 16 slices
-    DwOld<T::STAGES> hk{rs, voff, ldb};
+    DwOld<T> hk{rs, voff, ldb};
     mainloop<T, RPM, CSP>(a, b, c, smem, acc, hk);
-    dw_store<false, false>(acc, rs, voff, ldb, 0, 0);
+    dw_store<T, false, false>(acc, rs, voff, ldb, 0, 0);
   } else {
     mainloop<T, RPM, CSP>(a, b, c, smem, acc);
     const int vlim = V - vq, hlim = H - hq;
-    if (accumulate) dw_store<true, true>(acc, rs, voff, ldb, vlim, hlim);
-    else dw_store<false, true>(acc, rs, voff, ldb, vlim, hlim);
+    if (accumulate) dw_store<T, true, true>(acc, rs, voff, ldb, vlim, hlim);
+    else dw_store<T, false, true>(acc, rs, voff, ldb, vlim, hlim);
   }
 }
 
@@ -1031,7 +1039,7 @@ hipError_t launch_dw_bf16(const uint16_t *Gp, int64_t nks_z, const uint16_t *Xp,
   const int vtail = nvi < nvt, htail = nhi < nht;
   const int nk = (c + BK - 1) / BK;
   const dim3 block(NTHREADS);
-  if (accumulate && nk >= DwOld<DwTile::STAGES>::NB && nvi > 0 && nhi > 0) {
+  if (accumulate && nk >= DwOld<DwTile>::NB && nvi > 0 && nhi > 0) {
     hipLaunchKernelGGL((dw_kernel<true>), dim3(nvi * nhi), block, 0, s, Gp, nks_z, Xp, nks_h, c, H, V, nvi,
                        nhi, 0, 0, 0, dW, 1);
     const int ntail = (vtail ? nht : 0) + (htail ? nvt - vtail : 0);
