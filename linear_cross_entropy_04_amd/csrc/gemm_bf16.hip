@@ -46,6 +46,7 @@
 // 8-byte bank pairs.
 #include "flce_internal.h"
 
+#include <atomic>
 #include <type_traits>
 
 namespace flce {
@@ -171,6 +172,17 @@ struct OpStream {
       kr += go ? 32 : 0;
     }
   }
+  // on to slice CK of a range that starts at a multiple of 256 rows (the
+  // wrap into the next row tile known at compile time)
+  template <int CK>
+  __device__ __forceinline__ void advance_to() {
+    if constexpr (KIND == PACKED) {
+      ptr += 16384;
+    } else {
+      ptr += (CK - 1) % 8 == 7 ? ld - 7 * 2048 : 2048;
+      kr += 32;
+    }
+  }
   __device__ __forceinline__ void copy(int i, uint32_t stage) const {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(slice_rsrc(ptr), (lds_void *)(uintptr_t)(stage + loff[i]), 16,
                                              (threadIdx.x & 63) * 16, soff[i], 0, 0);
@@ -189,6 +201,11 @@ struct Streams {
   __device__ __forceinline__ void advance(bool go = true) {
     a.advance(go);
     b.advance(go);
+  }
+  template <int CK>
+  __device__ __forceinline__ void advance_to() {
+    a.template advance_to<CK>();
+    b.template advance_to<CK>();
   }
 };
 
@@ -389,6 +406,27 @@ constexpr int max_wait_count() {
   return m;
 }
 
+// Tiles worked one after another by a resident workgroup: the main loop's
+// last iterations copy the next tile's first STAGES - 1 slices into the ring
+// instead of the last slice again, so that they arrive while the caller
+// stores the tile.  The next tile's loop then starts warm: it issues its
+// hook's prologue, and one full wait (which also covers the stores still in
+// flight, whose completion order against loads is not guaranteed) admits
+// them.  The caller guarantees
+// nk >= Hook::NU + STAGES slices (the unrolled iterations never reach the
+// tile's end) and ranges that start at row 0.  NoChain is the single-tile
+// loop.
+struct NoChain {
+  static constexpr bool on = false;
+};
+struct Chain {
+  static constexpr bool on = true;
+  bool warm;               // this tile's first slices were copied by the previous tile's loop
+  int rb;                  // ring slot of this tile's slice 0
+  bool has_next;           // a next tile follows
+  Op na, nb;               // its operands
+};
+
 // acc[i][j] is the 32 x 32 block (i, j) of the wave's quarter.  Lane l of
 // block (i, j), register e, holds row 32 i + 8 (e/4) + 4 (l/32) + e%4 and
 // column 32 j + l%32 of the quarter.  acc enters initialised by the caller.
@@ -401,16 +439,20 @@ constexpr int max_wait_count() {
 // t+STAGES-1 is copied into the buffer of slice t-1, whose reads every wave
 // finished before that barrier; its copies go out one after every CSP-th
 // MFMA of the second half-step rather than in one burst, which would hold up
-// the MFMA issue.  Every iteration issues one slice of copies (the last slice
-// again past the end, into a slot that is not read again), so the wait is
-// always for all but the newest STAGES-3 slices (plus the hook's loads), and
-// the last slice is peeled: the loop body is one straight path.  Packed
+// the MFMA issue.  Every iteration issues one slice of copies (past the end,
+// the last slice again into a slot that is not read again, or the next
+// tile's first slices), so the wait is always for all but the newest
+// STAGES-3 slices (plus the hook's loads), and every slice, the last one
+// included, runs the same loop body (its reads of the half-step after the
+// last fetch a slice that nothing uses; a peeled last slice made the
+// compiler move the accumulators to other registers after the loop).  Packed
 // operands carry zero padding up to whole slices, so no copy needs a bounds
 // check.  The first Hook::NU iterations are unrolled; the caller guarantees
-// that the loop has at least that many (nk - 1 >= NU).
-template <class T, int RPM, int CSP, class Hook = NoHook>
+// that the loop has at least that many (nk >= NU).
+template <class T, int RPM, int CSP, class Hook = NoHook, class Ch = NoChain>
 __device__ __forceinline__ void mainloop(const Op &a, const Op &b, int klen, char *smem,
-                                         f32x16 (&acc)[T::MI][T::NI], Hook &&hook = Hook{}) {
+                                         f32x16 (&acc)[T::MI][T::NI], Hook &&hook = Hook{},
+                                         const Ch &ch = Ch{}) {
   using HK = std::remove_reference_t<Hook>;
   constexpr int M = T::MI * T::NI;                 // MFMAs per half-step
   constexpr int R = T::MI * reads_per_frag<T::KA>() + T::NI * reads_per_frag<T::KB>();
@@ -420,7 +462,7 @@ __device__ __forceinline__ void mainloop(const Op &a, const Op &b, int klen, cha
   static_assert(RPM * M >= R, "every fragment read of a half-step must be issued during the previous one");
   static_assert(max_wait_count<HK, S, G>() < 64, "vmcnt range");
   const int nk = (klen + BK - 1) / BK;
-  if (nk > 0) {
+  if (Ch::on || nk > 0) {                          // chained tiles have nk >= NU + S
     const int w = threadIdx.x >> 6;
     const int wm = w >> 1, wn = w & 1;
     const uint32_t lds0 = lds_addr(smem);
@@ -435,22 +477,46 @@ __device__ __forceinline__ void mainloop(const Op &a, const Op &b, int klen, cha
       const uint32_t o = (uint32_t)(s * T::STAGE_BYTES);
       return Bases{z.a0 + o, z.a1 + o, z.b0 + o, z.b1 + o};
     };
+    int rb = 0;                                    // ring slot of slice 0
+    if constexpr (Ch::on) rb = ch.rb;
+    auto slot = [&](int s) { return (rb + s) % S; };
     // the prologue's slices 0 .. S-2 (the last slice again past the end)
     Streams<T> cs;
     cs.a.init(a);
     cs.b.init(b);
+    bool warm = false;
+    if constexpr (Ch::on) warm = ch.warm;
+    if constexpr (Ch::on) {
+      // ranges start at row 0 and have nk >= NU + S slices
+      if (warm) {
+        // slices 0 .. S-2 were copied by the previous tile's loop
+        static_for<1, S - 1>([&](auto ss) { cs.template advance_to<decltype(ss)::value>(); });
+        hook.prologue();
+        wait_vm<0>();
+      } else {
+        static_for<0, S - 1>([&](auto ss) {
+          constexpr int sl = decltype(ss)::value;
+          if constexpr (sl > 0) cs.template advance_to<sl>();
 #pragma unroll
-    for (int s = 0; s < S - 1; ++s) {
-      if (s > 0 && s < nk) cs.advance();
+          for (int g = 0; g < G; ++g) cs.copy(g, lds0 + (uint32_t)(slot(sl) * T::STAGE_BYTES));
+        });
+        hook.prologue();
+        wait_vm<wait_count<HK, S, G>(-1)>();
+      }
+    } else {
 #pragma unroll
-      for (int g = 0; g < G; ++g) cs.copy(g, lds0 + (uint32_t)(s * T::STAGE_BYTES));
+      for (int s = 0; s < S - 1; ++s) {
+        if (s > 0 && s < nk) cs.advance();
+#pragma unroll
+        for (int g = 0; g < G; ++g) cs.copy(g, lds0 + (uint32_t)(slot(s) * T::STAGE_BYTES));
+      }
+      hook.prologue();
+      wait_vm<wait_count<HK, S, G>(-1)>();
     }
-    hook.prologue();
-    wait_vm<wait_count<HK, S, G>(-1)>();
     bar();
     Frags<T> f0, f1;
-    Bases cur = z;                                 // the stage of slice t
-    int st = 0;
+    Bases cur = stage_bases(rb);                   // the stage of slice t
+    int st = rb;
     static_for<0, R>([&](auto q) { frag_read<T, 0, decltype(q)::value>(cur, f0); });
     // one iteration; U >= 0 is an unrolled iteration of the hook, U < 0 a
     // runtime one
@@ -459,7 +525,7 @@ __device__ __forceinline__ void mainloop(const Op &a, const Op &b, int klen, cha
       const int sn = st + 1 == S ? 0 : st + 1;
       const Bases nxt = stage_bases(sn);
       const int ck = t + S - 1;                    // slice copied in this iteration
-      const uint32_t cst = lds0 + (uint32_t)((ck % S) * T::STAGE_BYTES);
+      const uint32_t cst = lds0 + (uint32_t)(slot(ck) * T::STAGE_BYTES);
       frags_wait<T>(f0);
       // first half-step; the reads of the second go out between its MFMAs
       static_for<0, M>([&](auto ii) {
@@ -473,7 +539,25 @@ __device__ __forceinline__ void mainloop(const Op &a, const Op &b, int klen, cha
       if constexpr (U >= 0) wait_vm<wait_count<HK, S, G>(U)>();
       else wait_vm<(S - 3) * G>();                 // at most the exact count: safe
       bar();
-      cs.advance(ck < nk);                         // else the last slice again
+      if constexpr (Ch::on && U >= 0) {
+        cs.template advance_to<U + S - 1>();       // ck < nk: the caller has nk >= NU + S
+      } else if constexpr (Ch::on && U == -1) {
+        cs.advance();                              // ck < nk
+      } else if constexpr (Ch::on) {
+        // past the end (ck = nk + j): the next tile's slices, or the last
+        // slice again
+        constexpr int j = -2 - U;
+        if constexpr (j == 0) {
+          if (ch.has_next) {
+            cs.a.init(ch.na);
+            cs.b.init(ch.nb);
+          }
+        } else {
+          cs.advance(ch.has_next);
+        }
+      } else {
+        cs.advance(ck < nk);                       // else the last slice again
+      }
       frags_wait<T>(f1);
       // second half-step: the next slice's copies and first reads between its MFMAs
       static_for<0, M>([&](auto ii) {
@@ -490,22 +574,29 @@ __device__ __forceinline__ void mainloop(const Op &a, const Op &b, int klen, cha
       st = sn;
     };
     static_for<0, HK::NU>([&](auto uu) { body(decltype(uu)::value, uu); });
-    for (int t = HK::NU; t < nk - 1; ++t) body(t, ic<-1>{});
-    frags_wait<T>(f0);
-    static_for<0, M>([&](auto ii) {
-      constexpr int i = decltype(ii)::value;
-      mfma_at<T>(i, f0, acc);
-      constexpr int q0 = i * RPM < R ? i * RPM : R, q1 = (i + 1) * RPM < R ? (i + 1) * RPM : R;
-      static_for<q0, q1>([&](auto q) { frag_read<T, 1, decltype(q)::value>(cur, f1); });
-    });
-    frags_wait<T>(f1);
-    static_for<0, M>([&](auto ii) { mfma_at<T>(decltype(ii)::value, f1, acc); });
+    if constexpr (Ch::on) {
+      // the slices of this tile, then S - 1 iterations that copy past its end
+      for (int t = HK::NU; t < nk - S + 1; ++t) body(t, ic<-1>{});
+      static_for<0, S - 1>([&](auto jj) { body(nk - S + 1 + decltype(jj)::value, ic<-2 - decltype(jj)::value>{}); });
+    } else {
+      for (int t = HK::NU; t < nk; ++t) body(t, ic<-1>{});
+    }
+    // (the last iteration's reads of the next half-step fetch a slice past
+    // the end that nothing uses: one loop shape for every slice keeps the
+    // accumulators in the loop's registers)
   }
-  // every wave is done with the LDS slices and no copy or load is still in
-  // flight; the caller may reuse LDS
-  wait_vm<0>();
-  bar();
-  if (nk > 0) hook.drain(acc);
+  if constexpr (Ch::on) {
+    // the next tile's first slices stay in flight while the caller stores
+    if (!ch.has_next) wait_vm<0>();
+    bar();
+    hook.drain(acc);
+  } else {
+    // every wave is done with the LDS slices and no copy or load is still in
+    // flight; the caller may reuse LDS
+    wait_vm<0>();
+    bar();
+    if (nk > 0) hook.drain(acc);
+  }
 }
 
 template <class T>
@@ -822,6 +913,14 @@ __global__ void dx_reduce_kernel(const float *__restrict__ dxp, int splitk, int 
 // store) pass.
 constexpr int kDwAux = 2;          // non-temporal: dW is touched once per chunk
 
+// Scalar byte offset of row `row` of a dW quarter, computed where it is used:
+// the empty asm keeps the compiler from hoisting the row offsets of a whole
+// tile (up to 256 distinct values) into scalar registers.
+__device__ __forceinline__ int row_off(int row, int ldb) {
+  asm volatile("" : "+s"(ldb));
+  return row * ldb;
+}
+
 template <class T>
 struct DwOld {
   static constexpr int S = T::STAGES, NI = T::NI;
@@ -841,8 +940,8 @@ struct DwOld {
   template <int b, int e>
   __device__ __forceinline__ void load_one() {
     constexpr int i = b / NI, j = b % NI, row = 32 * i + 8 * (e / 4) + e % 4;
-    v[b][e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, voff + 128 * j, row * ldb,
-                                                                              kDwAux));
+    v[b][e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, voff + 128 * j,
+                                                                              row_off(row, ldb), kDwAux));
   }
   template <int b, class A>
   __device__ __forceinline__ void add_block(A &acc) {
@@ -891,8 +990,8 @@ __device__ __forceinline__ void dw_store(const A &acc, __amdgpu_buffer_rsrc_t rs
       old[e] = 0.f;
       if constexpr (OLD) {
         if (col_ok && (!CHECK || row + 4 * (lane >> 5) < vlim))
-          old[e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, voff + 128 * j, row * ldb,
-                                                                                  kDwAux));
+          old[e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, voff + 128 * j,
+                                                                                  row_off(row, ldb), kDwAux));
       }
     });
     static_for<0, 16>([&](auto ee) {
@@ -902,8 +1001,8 @@ __device__ __forceinline__ void dw_store(const A &acc, __amdgpu_buffer_rsrc_t rs
       asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(x) : "a"(acc[i][j][e]));
       if constexpr (OLD) x += old[e];
       if (col_ok && (!CHECK || row + 4 * (lane >> 5) < vlim))
-        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, x), rs, voff + 128 * j, row * ldb,
-                                              kDwAux);
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, x), rs, voff + 128 * j,
+                                              row_off(row, ldb), kDwAux);
     });
     // one block's old values at a time in registers
     asm volatile("" ::: "memory");
@@ -964,6 +1063,62 @@ __global__ __launch_bounds__(NTHREADS, OCC) void dw_kernel(
   }
 }
 
+// dW of the tiles inside V and H, one resident workgroup per CU working
+// through tiles t = blockIdx.x, + gridDim.x, ... (the order of the
+// one-tile-per-workgroup launch, since gridDim.x is a multiple of the 8
+// XCDs), each tile's loop fetching the next tile's first slices while the
+// tile's stores go out (Chain).  OLD: accumulate, with the old values added
+// in the main loop (DwOld; needs c >= NU + STAGES = 19 slices); else store
+// (c >= STAGES slices).
+template <bool OLD, class T = DwTile, int RPM = kDwRpm, int CSP = kDwCsp, int GROUP = kDwGroup>
+__global__ __launch_bounds__(NTHREADS, 1) void dw_chain_kernel(
+    const uint16_t *__restrict__ Gp, int64_t nks_z, const uint16_t *__restrict__ Xp,
+    int64_t nks_h, int c, int H, int V, int nvt, int nht, float *__restrict__ dW) {
+  __shared__ __attribute__((aligned(1024))) char smem[T::LDS];
+  const int ntiles = nvt * nht;
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = w >> 1, wn = w & 1;
+  const int voff = ((lane >> 5) * 4 * H + (lane & 31)) * 4, ldb = H * 4;
+  const int nk = (c + BK - 1) / BK;
+  // operands and this wave's quarter of dW for tile t
+  auto tile_ops = [&](int t, Op &a, Op &b, __amdgpu_buffer_rsrc_t &rs) {
+    int vt, ht;
+    dw_tile<GROUP>(t, nvt, nht, 0, 0, 0, vt, ht);
+    const int m0 = vt * T::BM, n0 = ht * T::BN;
+    a = Op{(const char *)(Gp + (int64_t)(m0 >> 5) * 8192), nks_z * 16384, 0};
+    b = Op{(const char *)(Xp + (int64_t)(n0 >> 5) * 8192), nks_h * 16384, 0};
+    rs = __builtin_amdgcn_make_buffer_rsrc(dW + (int64_t)(m0 + wm * T::WM) * H + n0 + wn * T::WN, (short)0,
+                                           0x7fffffff, 0x00020000);
+  };
+  int t = blockIdx.x;
+  Op a, b;
+  __amdgpu_buffer_rsrc_t rs;
+  tile_ops(t, a, b, rs);
+  bool warm = false;
+  int rb = 0;
+  while (true) {
+    const int tn = t + (int)gridDim.x;
+    Chain ch;
+    ch.warm = warm;
+    ch.rb = rb;
+    ch.has_next = tn < ntiles;
+    __amdgpu_buffer_rsrc_t rsn = rs;
+    if (ch.has_next) tile_ops(tn, ch.na, ch.nb, rsn);
+    f32x16 acc[T::MI][T::NI];
+    zero_acc<T>(acc);
+    if constexpr (OLD) mainloop<T, RPM, CSP>(a, b, c, smem, acc, DwOld<T>{rs, voff, ldb}, ch);
+    else mainloop<T, RPM, CSP>(a, b, c, smem, acc, NoHook{}, ch);
+    dw_store<T, false, false>(acc, rs, voff, ldb, 0, 0);
+    if (!ch.has_next) break;
+    t = tn;
+    a = ch.na;
+    b = ch.nb;
+    rs = rsn;
+    warm = true;
+    rb = (rb + nk) % T::STAGES;
+  }
+}
+
 inline int grid_for(int64_t n, int block, int cap) {
   int64_t g = (n + block - 1) / block;
   if (g < 1) g = 1;
@@ -971,6 +1126,21 @@ inline int grid_for(int64_t n, int block, int cap) {
 }
 
 }  // namespace
+
+// Compute units of the current device (looked up once per device).
+static int cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return -1;
+  if (dev < 64) {
+    const int v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
+  if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
 
 hipError_t launch_pack_bf16(const uint16_t *src, int R, int K, uint16_t *P, int64_t nks_p,
                             bool weight, hipStream_t s) {
@@ -1039,16 +1209,35 @@ hipError_t launch_dw_bf16(const uint16_t *Gp, int64_t nks_z, const uint16_t *Xp,
   const int vtail = nvi < nvt, htail = nhi < nht;
   const int nk = (c + BK - 1) / BK;
   const dim3 block(NTHREADS);
-  if (accumulate && nk >= DwOld<DwTile>::NB && nvi > 0 && nhi > 0) {
-    hipLaunchKernelGGL((dw_kernel<true>), dim3(nvi * nhi), block, 0, s, Gp, nks_z, Xp, nks_h, c, H, V, nvi,
-                       nhi, 0, 0, 0, dW, 1);
+  constexpr int S = DwTile::STAGES, NB = DwOld<DwTile>::NB, NU = DwOld<DwTile>::NU;
+  // the tiles inside V and H: chained through resident workgroups, or one
+  // workgroup per tile; the tail tiles then take the plain kernel
+  const bool chain = nk >= (accumulate ? NU + S : S);
+  const bool spread = accumulate && nk >= NB;
+  if (nvi > 0 && nhi > 0 && (chain || spread)) {
+    const int ntiles = nvi * nhi;
+    if (chain) {
+      // one resident workgroup per CU (a multiple of the 8 XCDs)
+      const int ncu = cu_count();
+      if (ncu <= 0) return hipErrorInvalidDevice;
+      const int nres = ncu >= 8 ? ncu / 8 * 8 : ncu;
+      const dim3 grid(ntiles < nres ? ntiles : nres);
+      if (accumulate)
+        hipLaunchKernelGGL((dw_chain_kernel<true>), grid, block, 0, s, Gp, nks_z, Xp, nks_h, c, H, V, nvi, nhi, dW);
+      else
+        hipLaunchKernelGGL((dw_chain_kernel<false>), grid, block, 0, s, Gp, nks_z, Xp, nks_h, c, H, V, nvi, nhi,
+                           dW);
+    } else {
+      hipLaunchKernelGGL((dw_kernel<true>), dim3(ntiles), block, 0, s, Gp, nks_z, Xp, nks_h, c, H, V, nvi, nhi, 0,
+                         0, 0, dW, 1);
+    }
     const int ntail = (vtail ? nht : 0) + (htail ? nvt - vtail : 0);
     if (ntail > 0)
-      hipLaunchKernelGGL((dw_kernel<false>), dim3(ntail), block, 0, s, Gp, nks_z, Xp, nks_h, c, H, V, nvt,
-                         nht, 1, vtail, htail, dW, 1);
+      hipLaunchKernelGGL((dw_kernel<false>), dim3(ntail), block, 0, s, Gp, nks_z, Xp, nks_h, c, H, V, nvt, nht, 1,
+                         vtail, htail, dW, accumulate ? 1 : 0);
   } else {
-    hipLaunchKernelGGL((dw_kernel<false>), dim3(nvt * nht), block, 0, s, Gp, nks_z, Xp, nks_h, c, H, V, nvt,
-                       nht, 0, 0, 0, dW, accumulate ? 1 : 0);
+    hipLaunchKernelGGL((dw_kernel<false>), dim3(nvt * nht), block, 0, s, Gp, nks_z, Xp, nks_h, c, H, V, nvt, nht,
+                       0, 0, 0, dW, accumulate ? 1 : 0);
   }
   return hipGetLastError();
 }
