@@ -679,23 +679,14 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint16_t *__restrict__ 
 // m - z, not of z: exp(z - lse) keeps its accuracy however large the
 // logits or a common shift of a token's logits, and the entries that carry
 // the probability (z near m) are stored almost exactly.
-template <bool VTAIL, class T = FwdTile, int RPM = kFwdRpm, int CSP = kFwdCsp>
-__global__ __launch_bounds__(NTHREADS, 1) void fwd_tile_kernel(
-    const uint16_t *__restrict__ Wp, const uint16_t *__restrict__ Xp, int64_t nks_h,
-    const int64_t *__restrict__ labels_c, int64_t ii, int c, int H, int V,
+// The forward tile's epilogue (see fwd_tile_kernel): per-token partials, the
+// target logit and the logits tile from the accumulators of tile (vt, ct).
+template <bool VTAIL, class T>
+__device__ __forceinline__ void fwd_epilogue(
+    f32x16 (&acc)[4][4], int vt, int ct, const int64_t *__restrict__ labels_c, int64_t ii, int c, int V,
     uint16_t *__restrict__ Zp, int64_t nks_z, float *__restrict__ pm, float *__restrict__ ps,
-    float *__restrict__ pmt, float *__restrict__ zy, int64_t nvt, int vt0, int nct, int store_z) {
-  static_assert(T::BM == 256 && T::BN == 256, "the epilogue reduces a 256 x 256 tile");
-  __shared__ __attribute__((aligned(1024))) char smem[T::LDS];
-  const int tile = xcd_remap(blockIdx.x, gridDim.x);
-  const int vt = vt0 + tile / nct, ct = tile % nct;
+    float *__restrict__ pmt, float *__restrict__ zy, int64_t nvt, int store_z) {
   const int m0 = vt * T::BM, n0 = ct * T::BN;
-
-  const Op a{(const char *)(Wp + (int64_t)vt * nks_h * 8192), 0, 0};
-  const Op b{(const char *)(Xp + (int64_t)ct * nks_h * 8192), 0, 0};
-  f32x16 acc[4][4];
-  zero_acc<T>(acc);
-  mainloop<T, RPM, CSP>(a, b, H, smem, acc);
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int wm = w >> 1, wn = w & 1;
@@ -767,6 +758,25 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_tile_kernel(
         }
     }
   }
+}
+
+template <bool VTAIL, class T = FwdTile, int RPM = kFwdRpm, int CSP = kFwdCsp>
+__global__ __launch_bounds__(NTHREADS, 1) void fwd_tile_kernel(
+    const uint16_t *__restrict__ Wp, const uint16_t *__restrict__ Xp, int64_t nks_h,
+    const int64_t *__restrict__ labels_c, int64_t ii, int c, int H, int V,
+    uint16_t *__restrict__ Zp, int64_t nks_z, float *__restrict__ pm, float *__restrict__ ps,
+    float *__restrict__ pmt, float *__restrict__ zy, int64_t nvt, int vt0, int nct, int store_z) {
+  static_assert(T::BM == 256 && T::BN == 256, "the epilogue reduces a 256 x 256 tile");
+  __shared__ __attribute__((aligned(1024))) char smem[T::LDS];
+  const int tile = xcd_remap(blockIdx.x, gridDim.x);
+  const int vt = vt0 + tile / nct, ct = tile % nct;
+
+  const Op a{(const char *)(Wp + (int64_t)vt * nks_h * 8192), 0, 0};
+  const Op b{(const char *)(Xp + (int64_t)ct * nks_h * 8192), 0, 0};
+  f32x16 acc[4][4];
+  zero_acc<T>(acc);
+  mainloop<T, RPM, CSP>(a, b, H, smem, acc);
+  fwd_epilogue<VTAIL, T>(acc, vt, ct, labels_c, ii, c, V, Zp, nks_z, pm, ps, pmt, zy, nvt, store_z);
 }
 
 // ---------------------------------------------------------------- dlogits
