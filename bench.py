@@ -58,8 +58,6 @@ def kernel_work(name, chunks, H, V):
         return "hbm", sum(4.0 * c * V for c in chunks), "byte"
     if name == "pack_x":                       # bf16 X chunk read and written packed
         return "hbm", sum(4.0 * c * H for c in chunks), "byte"
-    if name == "pack_w":                       # W read once, written packed once
-        return "hbm", 4.0 * V * H, "byte"
     if name == "pair_rows":                    # X rows gathered, dX rows scattered (bf16)
         return "hbm", sum(8.0 * c * H for c in chunks), "byte"
     return "hbm", None, "byte"

@@ -78,17 +78,15 @@ typedef enum {
  * memory (project overview page, "Princípios Técnicos", Computação em
  * Chunk); these calls choose the chunk and report what it costs.
  *
- * The workspace of a call holds, on the bf16 path, one packed copy of W (V x H
- * bf16, rows and columns rounded up to 256), which the forward reads along
- * its rows and dX transposed; and for one chunk of C tokens: its logits, then
- * dlogits, in place ([C, V] bf16, or fp32 on the fp32 path), its packed X, the
- * per-vocabulary-tile log-sum-exp partials, per-token statistics and the
- * split-K partial sums of dX; plus one fp32 per-token loss for all N tokens.
- * Only that last array grows with N.
+ * The workspace of a call holds, for one chunk of C tokens: its logits, then
+ * dlogits, in place ([C, V] bf16, or fp32 on the fp32 path), its X in the
+ * GEMM operand layout (bf16 path), the per-vocabulary-tile log-sum-exp
+ * partials, per-token statistics and the split-K partial sums of dX; plus
+ * one fp32 per-token loss for all N tokens.  Only that last array grows with
+ * N; nothing grows with W beyond the chunk's logits (W is read in place).
  *
  * Budget used when a call plans its own chunk (chunk_tokens <= 0) and none is
- * given: twice the bytes of W in its dtype (room for the packed copy of W and
- * a chunk scratch as large as W again), but at least this floor.
+ * given: the bytes of W in its dtype, but at least this floor.
  */
 #define FLCE_DEFAULT_SCRATCH_FLOOR ((size_t)256 << 20)
 
@@ -108,7 +106,7 @@ size_t flce_workspace_bytes(int64_t N, int64_t H, int64_t V, int dtype, int64_t 
  *                 power-of-two multiple of 256 tokens, at most N, whose whole
  *                 workspace fits scratch_budget_bytes.  On return the chunk a
  *                 call will use.
- *   scratch_budget_bytes  bound on the whole workspace, packed W included;
+ *   scratch_budget_bytes  bound on the whole workspace;
  *                 0 = the default budget above.
  *   peak_scratch_bytes  out (may be NULL): the workspace the returned chunk
  *                 needs, which is the peak device scratch of a call.
@@ -399,11 +397,10 @@ enum {
   FLCE_K_DW_GEMM = 6,     /* dW GEMM */
   FLCE_K_FINAL = 7,       /* final mean loss, fills */
   FLCE_K_PACK = 8,        /* per-chunk packing of X into the GEMM operand layout */
-  FLCE_K_PACK_W = 9,      /* per-call packing of W into the GEMM operand layout */
-  FLCE_K_CE_ROWS = 10,    /* cross-entropy on given logits, one workgroup per row */
-  FLCE_K_PAIRS = 11,      /* preference losses: label pass, per-pair step, final loss */
-  FLCE_K_PAIR_ROWS = 12,  /* preference losses: gathering a chunk's rows, scattering dX */
-  FLCE_K_COUNT = 13
+  FLCE_K_CE_ROWS = 9,     /* cross-entropy on given logits, one workgroup per row */
+  FLCE_K_PAIRS = 10,      /* preference losses: label pass, per-pair step, final loss */
+  FLCE_K_PAIR_ROWS = 11,  /* preference losses: gathering a chunk's rows, scattering dX */
+  FLCE_K_COUNT = 12
 };
 int flce_profile_enable(int enable);
 int flce_profile_read(double *ms, int64_t *launches, int n);

@@ -155,7 +155,7 @@ def flce_last_error() -> str:
     return _load().flce_last_error().decode()
 
 
-KERNEL_CLASSES = 13
+KERNEL_CLASSES = 12
 
 
 def flce_profile_enable(enable: bool = True) -> None:

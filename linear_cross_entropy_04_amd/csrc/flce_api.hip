@@ -69,7 +69,6 @@ int64_t max_grid_items(const Plan &p) {
   int64_t m = C * 256;                                            // lse_combine
   if (p.dtype == FLCE_BF16) {
     const int64_t ct = cdiv(C, 256), vt = cdiv(V, 256);
-    m = std::max(m, vt * (p.nks_h / 2) * 256);                    // pack W
     m = std::max(m, ct * (p.nks_h / 2) * 256);                    // pack X_c
     m = std::max(m, vt * ct * 256);                               // forward tiles
     m = std::max(m, ct * p.nks_z * 256);                          // dlogits
@@ -89,13 +88,11 @@ bool grid_fits(const Plan &p) { return max_grid_items(p) <= kMaxGridItems; }
 // Bytes of one row of W in the input dtype.
 inline size_t elem_bytes(int dtype) { return dtype == FLCE_BF16 ? 2 : 4; }
 
-// The budget used when the caller gives none: twice W's own size (room for
-// the packed copy of W and a chunk scratch as large as W again), at least
-// FLCE_DEFAULT_SCRATCH_FLOOR.  On the Llama-3-8B head this gives chunks of
-// 2048 tokens and 1.7 GB of scratch, against 2.1 GB for the whole bf16 logits.
+// The budget used when the caller gives none: W's own size, at least
+// FLCE_DEFAULT_SCRATCH_FLOOR.
 size_t default_budget(int64_t H, int64_t V, int dtype) {
   const size_t w = (size_t)H * (size_t)V * elem_bytes(dtype);
-  return std::max<size_t>(2 * w, FLCE_DEFAULT_SCRATCH_FLOOR);
+  return std::max<size_t>(w, FLCE_DEFAULT_SCRATCH_FLOOR);
 }
 
 // Largest power-of-two multiple of 256 tokens (capped at N) whose whole
@@ -227,12 +224,11 @@ int chunk_forward(const Plan &p, char *ws, const void *W, int64_t ii, bool keep_
   float *zy = (float *)(ws + p.off_zy);
   float *lse = (float *)(ws + p.off_lse);
   if (p.dtype == FLCE_BF16) {
-    const uint16_t *Wp = (const uint16_t *)(ws + p.off_wp);
     uint16_t *Zp = (uint16_t *)(ws + p.off_z);
     uint16_t *Xp = (uint16_t *)(ws + p.off_xp);
-    LAUNCH(FLCE_K_PACK, launch_pack_bf16((const uint16_t *)io.Xc, io.c, Hi, Xp, p.nks_h, false, s));
-    LAUNCH(FLCE_K_FWD_TILE, launch_fwd_tile_bf16(Wp, Xp, p.nks_h, io.lab, ii, io.c, Hi, Vi, Zp,
-                                                 p.nks_z, pm, ps, pmt, zy, p.nvt, keep_z, s));
+    LAUNCH(FLCE_K_PACK, launch_pack_bf16((const uint16_t *)io.Xc, io.c, Hi, Xp, p.nks_h, s));
+    LAUNCH(FLCE_K_FWD_TILE, launch_fwd_tile_bf16((const uint16_t *)W, Xp, io.lab, ii, io.c, Hi, Vi,
+                                                 Zp, p.nks_z, pm, ps, pmt, zy, p.nvt, keep_z, s));
   } else {
     float *z = (float *)(ws + p.off_z);
     LAUNCH(FLCE_K_FWD_TILE, launch_fwd_tile_f32((const float *)W, (const float *)io.Xc, io.lab,
@@ -256,8 +252,8 @@ int chunk_backward(const Plan &p, char *ws, const void *W, int64_t ii, const Chu
     LAUNCH(FLCE_K_DLOGITS, launch_dlogits_bf16(Zp, p.nks_z, io.c, Vi,
                                                (const float *)(ws + p.off_pmt), lse, io.lab, ii,
                                                io.wr, sc, s));
-    LAUNCH(FLCE_K_DX_GEMM, launch_dx_bf16(Zp, p.nks_z, (const uint16_t *)(ws + p.off_wp), p.nks_h,
-                                          io.c, Hi, Vi, p.splitk, p.ksplit, dxp, s));
+    LAUNCH(FLCE_K_DX_GEMM, launch_dx_bf16(Zp, p.nks_z, (const uint16_t *)W, io.c, Hi, Vi,
+                                          p.splitk, p.ksplit, dxp, s));
     LAUNCH(FLCE_K_DX_REDUCE, launch_dx_reduce_bf16(dxp, p.splitk, io.c, Hi, (uint16_t *)io.dXc, s));
     LAUNCH(FLCE_K_DW_GEMM, launch_dw_bf16(Zp, p.nks_z, Xp, p.nks_h, io.c, Hi, Vi, dW, io.acc_dw, s));
   } else {
@@ -268,16 +264,6 @@ int chunk_backward(const Plan &p, char *ws, const void *W, int64_t ii, const Chu
     LAUNCH(FLCE_K_DW_GEMM, launch_dw_f32(z, p.ldz, (const float *)io.Xc, io.c, Hi, Vi, dW,
                                          io.acc_dw, s));
   }
-  return FLCE_OK;
-}
-
-// Pack W once per call (bf16 path) into Wp, which the forward reads along
-// its rows and dX transposed.
-int pack_weight(const Plan &p, char *ws, const void *W, hipStream_t s) {
-  if (p.dtype != FLCE_BF16) return FLCE_OK;
-  const int Hi = (int)p.H, Vi = (int)p.V;
-  LAUNCH(FLCE_K_PACK_W, launch_pack_bf16((const uint16_t *)W, Vi, Hi,
-                                         (uint16_t *)(ws + p.off_wp), p.nks_h, true, s));
   return FLCE_OK;
 }
 
@@ -319,10 +305,6 @@ int run(bool bwd, const void *X, const void *W, const int64_t *labels, int64_t N
   LAUNCH(FLCE_K_LABELS, launch_label_check(labels, N, V, ii, o.reduction, sc, s));
   if (bwd && N == 0 && !o.accumulate_dw) LAUNCH(FLCE_K_FINAL, launch_fill_f32(dW, V * H, 0.f, s));
 
-  if (N > 0) {
-    st = pack_weight(p, ws, W, s);
-    if (st != FLCE_OK) return st;
-  }
   for (int64_t c0 = 0; c0 < N; c0 += C) {
     ChunkIO io;
     io.c = (int)std::min(C, N - c0);
@@ -405,9 +387,7 @@ void make_plan(int64_t N, int64_t H, int64_t V, int dtype, int64_t C, Plan *p) {
     // packed layouts: rows and columns padded to 256 (see flce_internal.h)
     p->nks_z = cdiv(V, 256) * 8;
     p->nks_h = cdiv(H, 256) * 8;
-    const size_t cpad = (size_t)round_up(C, 256), vpad = (size_t)round_up(V, 256);
-    p->off_wp = o;                       // W packed once per call (rows = vocabulary)
-    o += align256(vpad * p->nks_h * 64);
+    const size_t cpad = (size_t)round_up(C, 256);
     p->off_z = o;                        // logits, then G, of the chunk (rows = tokens)
     o += align256(cpad * p->nks_z * 64);
     p->off_xp = o;                       // the chunk's X (rows = tokens)
@@ -743,8 +723,6 @@ int run_pairs(bool bwd, int kind, const void *X, const void *W, const int64_t *l
   float *lor = log_odds_ratio ? log_odds_ratio : (float *)(ws + L.off_lor);
 
   LAUNCH(FLCE_K_PAIRS, launch_pairs_labels(labels, 2 * half, half, V, ii, sc, s));
-  st = pack_weight(p, ws, W, s);
-  if (st != FLCE_OK) return st;
   for (int64_t p0 = 0; p0 < B; p0 += L.k) {
     const int64_t kk = std::min(L.k, B - p0);
     const int64_t rows = kk * T;                     // rows of each half in this chunk
@@ -954,8 +932,6 @@ int run_kto(bool bwd, const void *X, const void *W, const int64_t *labels, int64
   float *rwo = reward ? reward : (float *)(ws + L.off_rew);
 
   LAUNCH(FLCE_K_PAIRS, launch_pairs_labels(labels, S * T, 0, V, ii, sc, s));
-  st = pack_weight(p, ws, W, s);
-  if (st != FLCE_OK) return st;
   for (int64_t s0 = 0; s0 < S; s0 += L.k) {
     const int64_t kk = std::min(L.k, S - s0);
     ChunkIO io;
@@ -1084,7 +1060,7 @@ FLCE_API int flce_profile_read(double *ms, int64_t *launches, int n) {
 FLCE_API const char *flce_kernel_name(int k) {
   static const char *names[FLCE_K_COUNT] = {"label_check", "fwd_tile", "lse_combine", "dlogits",
                                             "dx_gemm", "dx_reduce", "dw_gemm", "final",
-                                            "pack_x", "pack_w", "ce_rows", "pairs",
+                                            "pack_x", "ce_rows", "pairs",
                                             "pair_rows"};
   return (k >= 0 && k < FLCE_K_COUNT) ? names[k] : "";
 }

@@ -39,7 +39,7 @@ struct Plan {
   int64_t nvt = 0;      // vocabulary tiles = log-sum-exp partials per token
   int splitk = 0;       // K-splits of the dX GEMM (0: the fp32 path writes dX directly)
   int64_t ksplit = 0;   // vocabulary rows per split (multiple of 64)
-  size_t off_wp = 0, off_z = 0, off_xp = 0, off_pm = 0, off_ps = 0, off_zy = 0, off_lse = 0,
+  size_t off_z = 0, off_xp = 0, off_pm = 0, off_ps = 0, off_zy = 0, off_lse = 0,
          off_rowloss = 0, off_dxp = 0, off_scal = 0, total = 0;
   size_t off_pmt = 0;   // bf16 path: the partial maxima again, [partial][token]
 };
@@ -62,18 +62,20 @@ hipError_t launch_fill_f32(float *p, int64_t n, float v, hipStream_t s);
 hipError_t launch_scale(void *buf, int64_t n, int dtype, const float *scale, hipStream_t s);
 
 // ---------------------------------------------------------------- bf16 path (MFMA)
-// Packed matrices (Wp, Xp, Zp) are 16 KB blocks of 256 rows x 32 columns; a
+// Packed matrices (Xp, Zp) are 16 KB blocks of 256 rows x 32 columns; a
 // matrix with nks column slices (nks a multiple of 8) stores row tile rt,
 // slice ks at element (rt * nks + ks) * 8192.  Each GEMM reads them either
-// along their rows or transposed, so no transposed copy is ever made.
+// along their rows or transposed, so no transposed copy is ever made.  W is
+// read where it lies, row-major [V][H], along its rows by the forward and
+// transposed by dX.
 // Pack a row-major [R][K] matrix into P (rows R padded to 256, nks_p slices).
 hipError_t launch_pack_bf16(const uint16_t *src, int R, int K, uint16_t *P, int64_t nks_p,
-                            bool weight, hipStream_t s);
+                            hipStream_t s);
 // Logits tile GEMM with the log-sum-exp epilogue.  pm, ps: [token][partial]
 // maximum and sum of exp per 128 vocabulary ids; with store_z, Zp receives
 // bf16(z - m) for the partial's maximum m, and pmt[partial * c + token] the m
 // that was subtracted.
-hipError_t launch_fwd_tile_bf16(const uint16_t *Wp, const uint16_t *Xp, int64_t nks_h,
+hipError_t launch_fwd_tile_bf16(const uint16_t *W, const uint16_t *Xp,
                                 const int64_t *labels_c, int64_t ii, int c, int H, int V,
                                 uint16_t *Zp, int64_t nks_z, float *pm, float *ps, float *pmt,
                                 float *zy, int64_t nvt, bool store_z, hipStream_t s);
@@ -83,8 +85,8 @@ hipError_t launch_fwd_tile_bf16(const uint16_t *Wp, const uint16_t *Xp, int64_t 
 hipError_t launch_dlogits_bf16(uint16_t *Zp, int64_t nks_z, int c, int V, const float *pmt,
                                const float *lse_c, const int64_t *labels_c, int64_t ii,
                                const float *wrow_c, const Scalars *sc, hipStream_t s);
-// dX partials from G (Zp) and W read transposed from Wp (nks_h slices).
-hipError_t launch_dx_bf16(const uint16_t *Gp, int64_t nks_z, const uint16_t *Wp, int64_t nks_h,
+// dX partials from G (Zp) and W (row-major [V][H]) read transposed.
+hipError_t launch_dx_bf16(const uint16_t *Gp, int64_t nks_z, const uint16_t *W,
                           int c, int H, int V, int splitk, int64_t ksplit, float *dxp,
                           hipStream_t s);
 hipError_t launch_dx_reduce_bf16(const float *dxp, int splitk, int c, int H, uint16_t *dXc,

@@ -1,8 +1,8 @@
 // bf16 MFMA GEMMs of the chunked fused linear cross-entropy (gfx950), and
 // the data movement that feeds them.
 //
-// Per call, W is packed once into Wp (rows = vocabulary, k = hidden).  Per
-// chunk of c tokens (the chain rule through the LM-head projection
+// W is read where it lies (row-major [V][H], never copied).  Per chunk of c
+// tokens (the chain rule through the LM-head projection
 // Z = X W^T that the Liger Kernel pages fuse with the cross-entropy loss):
 //   pack      X_c -> Xp (rows = tokens, k = hidden);
 //   forward   Z_c^T = W X_c^T      M = V (vocab), N = c (tokens), K = H
@@ -11,7 +11,7 @@
 //               tokens, k = vocabulary);
 //   dlogits   Zp rewritten in place into G = (softmax - onehot) / N_valid;
 //   dX        dX_c  = G_c W        M = c, N = H, K = V (split-K, fp32 partials),
-//             W read transposed from Wp;
+//             W read transposed;
 //   dW        dW   (+)= G_c^T X_c  M = V, N = H, K = c (fp32)
 //
 // GEMM tiles: a workgroup of 4 waves (2 x 2) computes a BM x BN fp32 tile with
@@ -23,7 +23,7 @@
 // k-slices of 32, STAGES slices in flight, each admitted by an explicit vmcnt
 // wait and one s_barrier.
 //
-// The packed layout (Wp, Xp, Zp): a matrix of R rows and K columns is stored
+// The packed layout (Xp, Zp): a matrix of R rows and K columns is stored
 // as 16 KB blocks of 256 rows x 32 columns; block (rt, ks) at element
 // (rt * nks + ks) * 8192, nks = 8 ceil(K / 256) (columns padded to 256 so a
 // 256-wide tile of columns always exists).  A block is 16 fragments of 1 KB;
@@ -63,7 +63,7 @@ constexpr int BK = 32;             // k per pipeline slice
 constexpr int NTHREADS = 256;
 constexpr float kLog2e = 1.4426950408889634f;
 
-enum Kind { PACKED = 0, PACKED_T = 1 };
+enum Kind { PACKED = 0, PACKED_T = 1, ROW = 2, ROWT = 3 };
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -123,10 +123,17 @@ struct Tile {
 //             tile's first operand row; ld = bytes of one row tile of the
 //             matrix; kb = the range's first k, a row of the matrix (a
 //             multiple of 32).
+//   ROW:      base = the tile's first row; ld = bytes per matrix row; kb =
+//             the range's first k (a column of the matrix, a multiple of 32);
+//             end = the end of the matrix (rows past it read as zero).
+//   ROWT:     base = the matrix's first row at the tile's first column; ld =
+//             bytes per matrix row; kb = the range's first k (a row of the
+//             matrix, a multiple of 32); end as for ROW.
 struct Op {
   const char *base;
   int64_t ld;
   int64_t kb;
+  const char *end;
 };
 
 // Buffer descriptor of a slice: raw (stride 0) 32-bit words, no range check
@@ -141,51 +148,87 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t slice_rsrc(const char *p) {
 // the wave is 1 KB piece blk = 4 i + wave of the slice, written at LDS byte
 // address stage + 1 KB blk.  PACKED_T pieces 2q, 2q+1 are the two fragments
 // of operand rows 32q..32q+31.  Only the lane's 16-byte offset is per lane.
+//   ROW:      piece blk = 16 matrix rows x 64 bytes (rows 16 blk ..); lane l
+//             copies row 16 blk + l/4, 16-byte chunk (l%4) ^ (l/16 % 4), so
+//             that its LDS position holds the swizzled layout;
+//   ROWT:     piece blk = matrix rows 2 blk, 2 blk + 1 of the slice, 512
+//             bytes each; lane l copies row 2 blk + l/32, chunk
+//             (l%32) ^ 4 ((2 blk + l/32) % 4).
+// Row-major pieces take their offsets in the lane's offset, where the
+// descriptor's range check applies: rows past the matrix's end read as
+// zero.
 template <int KIND, int NP>
 struct OpStream {
+  static constexpr bool RM = KIND == ROW || KIND == ROWT;
   const char *ptr;         // the slice copied next
-  int64_t ld;              // PACKED_T: bytes of one row tile of the matrix
+  const char *end;         // row-major: the end of the matrix
+  int64_t ld;              // PACKED_T: bytes of one row tile; row-major: bytes per row
   int kr;                  // PACKED_T: the matrix row of ptr's slice
-  int soff[NP];            // piece offsets within a slice (bytes)
+  int soff[NP];            // packed: piece offsets within a slice (bytes)
+  int voff[RM ? NP : 1];   // row-major: the lane's offsets of the pieces
   uint32_t loff[NP];       // piece offsets within the operand's stage area
 
   __device__ __forceinline__ void init(const Op &op) {
-    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), l = threadIdx.x & 63;
+    ld = op.ld;
+    kr = (int)op.kb;
+    end = op.end;
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
       const int blk = i * 4 + w;
       soff[i] = KIND == PACKED ? blk * 1024 : (blk >> 1) * 16384 + (blk & 1) * 1024;
       loff[i] = (uint32_t)(blk * 1024);
+      if constexpr (KIND == ROW)
+        voff[i] = (int)((16 * blk + (l >> 2)) * ld) + 16 * ((l & 3) ^ ((l >> 4) & 3));
+      else if constexpr (KIND == ROWT)
+        voff[i] = (int)((2 * blk + (l >> 5)) * ld) + 16 * ((l & 31) ^ (4 * ((2 * blk + (l >> 5)) & 3)));
     }
-    ld = op.ld;
-    kr = (int)op.kb;
     if constexpr (KIND == PACKED) ptr = op.base;
-    else ptr = op.base + (int64_t)(kr >> 8) * ld + (((kr & 255) >> 5) << 11);
+    else if constexpr (KIND == PACKED_T) ptr = op.base + (int64_t)(kr >> 8) * ld + (((kr & 255) >> 5) << 11);
+    else if constexpr (KIND == ROW) ptr = op.base + 2 * op.kb;
+    else ptr = op.base + op.kb * ld;
   }
   // on to the next k-slice if go (selects, not a branch, inside the loop)
   __device__ __forceinline__ void advance(bool go = true) {
     if constexpr (KIND == PACKED) {
       ptr += go ? 16384 : 0;
-    } else {
+    } else if constexpr (KIND == PACKED_T) {
       const int64_t inc = (kr & 255) == 224 ? ld - 7 * 2048 : 2048;
       ptr += go ? inc : 0;
       kr += go ? 32 : 0;
+    } else if constexpr (KIND == ROW) {
+      ptr += go ? 64 : 0;
+    } else {
+      ptr += go ? 32 * ld : 0;
     }
   }
   // on to slice CK of a range that starts at a multiple of 256 rows (the
   // wrap into the next row tile known at compile time)
   template <int CK>
   __device__ __forceinline__ void advance_to() {
-    if constexpr (KIND == PACKED) {
-      ptr += 16384;
-    } else {
+    if constexpr (KIND == PACKED_T) {
       ptr += (CK - 1) % 8 == 7 ? ld - 7 * 2048 : 2048;
       kr += 32;
+    } else {
+      advance();
     }
   }
   __device__ __forceinline__ void copy(int i, uint32_t stage) const {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(slice_rsrc(ptr), (lds_void *)(uintptr_t)(stage + loff[i]), 16,
-                                             (threadIdx.x & 63) * 16, soff[i], 0, 0);
+    if constexpr (RM) {
+      // bytes from ptr to the matrix's end (ptr never passes it: every slice
+      // starts inside the matrix), clamped to the descriptor's range; 32-bit
+      // scalar arithmetic only
+      const uint64_t left = (uint64_t)(end - ptr);
+      uint32_t lo = (uint32_t)left, hi = (uint32_t)(left >> 32);
+      asm("" : "+s"(hi));               // keeps the test a 32-bit scalar compare
+      const int nrec = hi ? 0x7fffffff : (int)min(lo, 0x7fffffffu);
+      const __amdgpu_buffer_rsrc_t rs =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(ptr), (short)0, nrec, 0x00020000);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(uintptr_t)(stage + loff[i]), 16, voff[i], 0, 0, 0);
+    } else {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(slice_rsrc(ptr), (lds_void *)(uintptr_t)(stage + loff[i]), 16,
+                                               (threadIdx.x & 63) * 16, soff[i], 0, 0);
+    }
   }
 };
 
@@ -246,18 +289,36 @@ __device__ __forceinline__ void static_for(F &&f) {
 // wait for every direct-to-LDS copy in flight, draining the copy pipeline
 // once per slice.  Volatile asm statements keep their source order, which is
 // the issue order.
+//
+// Two more layouts read an operand straight from a row-major bf16 matrix
+// (the weight W), without a packed copy:
+//   ROW   rows of the matrix are rows of the GEMM operand (k runs along a
+//         row): a stage holds the tile's rows as 64-byte pieces (32 k), one
+//         after another, with the four 16-byte chunks of row r XOR-swizzled
+//         by (r/4) % 4; a fragment is one 16-byte read per lane;
+//   ROWT  columns of the matrix are rows of the GEMM operand (k runs down
+//         the matrix's rows): a stage holds 32 matrix rows of 512 bytes (the
+//         tile's 256 columns), the 16-byte chunks of matrix row k
+//         XOR-swizzled by 4 (k % 4); a fragment is two transposing reads.
+// Both swizzles keep every read conflict-free (an aligned group of 16 lanes
+// of a 16-byte read covers 256 distinct bytes; each half-wave of a
+// transposing read, 32 distinct 8-byte bank pairs).
+constexpr bool kind_tr(int kind) { return kind == PACKED_T || kind == ROWT; }
+
 template <int KIND>
-struct Frag;
-template <>
-struct Frag<PACKED> {        // one 16-byte read
+struct Frag {                // one 16-byte read
   bf16x8 v;
 };
 template <>
 struct Frag<PACKED_T> {      // two transposing 8-byte reads
   i16x4 lo, hi;
 };
+template <>
+struct Frag<ROWT> {
+  i16x4 lo, hi;
+};
 template <int KIND>
-constexpr int reads_per_frag() { return KIND == PACKED ? 1 : 2; }
+constexpr int reads_per_frag() { return kind_tr(KIND) ? 2 : 1; }
 
 template <int IMM>
 __device__ __forceinline__ void rd_b128(bf16x8 &dst, uint32_t a) {
@@ -270,41 +331,66 @@ __device__ __forceinline__ void rd_tr(i16x4 &dst, uint32_t a) {
   asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(dst) : "v"(a), "i"(IMM));
 }
 
-// This lane's two read addresses (bytes, within a stage) for fragment 0 of an
-// operand block of rows r0..: PACKED: the reads of half-steps kk = 0 and 1;
-// PACKED_T: the low and high reads of half-step 0.  Across a wave's
-// fragments (rows r0 + 32 i) the addresses move by exactly 2048 i bytes, and
-// a PACKED_T read of half-step kk by 256 kk more (k + 16 flips bit 4 of the
-// slot, which no XOR term touches; this was checked for every lane), so every
-// read is reached through the instruction's immediate offset.
-template <int KIND>
-__device__ __forceinline__ void rd_bases(int r0, uint32_t &b0, uint32_t &b1) {
+// A lane's read addresses (bytes, within a stage) for an operand block of NF
+// fragments, rows r0 ... (r0 a multiple of 32):
+//   PACKED, ROW  v[kk]: fragment 0's read of half-step kk;
+//   PACKED_T     v[0], v[1]: fragment 0's low and high reads of half-step 0;
+//   ROWT         v[i]: fragment i's low read of half-step 0.
+// Every other read is a fixed offset away, reached through the
+// instruction's immediate: fragment i of PACKED, ROW and PACKED_T at
+// 2048 i; PACKED_T's half-step kk at 256 kk more (k + 16 flips bit 4 of
+// the slot, which no XOR term touches; this was checked for every lane);
+// ROWT's high read at 2048 (k + 4, same swizzle) and half-step kk at
+// 8192 kk (k + 16).
+template <int KIND, int NF>
+struct OpBases {
+  uint32_t v[KIND == ROWT ? NF : 2];
+};
+
+template <int KIND, int NF>
+__device__ __forceinline__ void rd_bases(int r0, OpBases<KIND, NF> &b) {
   const int l = threadIdx.x & 63;
   if constexpr (KIND == PACKED) {
-    b0 = (uint32_t)((((r0 >> 5) << 1) << 10) + (pk_slot(l & 31, l >> 5, 0) << 4));
-    b1 = (uint32_t)(((((r0 >> 5) << 1) + 1) << 10) + (pk_slot(l & 31, l >> 5, 1) << 4));
+    b.v[0] = (uint32_t)((((r0 >> 5) << 1) << 10) + (pk_slot(l & 31, l >> 5, 0) << 4));
+    b.v[1] = (uint32_t)(((((r0 >> 5) << 1) + 1) << 10) + (pk_slot(l & 31, l >> 5, 1) << 4));
+  } else if constexpr (KIND == ROW) {
+    // lane l: row r0 + l%32, k-half l/32 of a 16-k half-step
+    const int r = l & 31, h = l >> 5, sw = (r >> 2) & 3;
+    b.v[0] = (uint32_t)((r0 + r) * 64 + 16 * ((0 + h) ^ sw));
+    b.v[1] = (uint32_t)((r0 + r) * 64 + 16 * ((2 + h) ^ sw));
   } else {
-    // lane j of a 16-lane group names the 4 operand rows r..r+3 at one k
+    // lane j of a 16-lane group names the 4 operand rows n..n+3 at one k
     const int g = l >> 4, j = l & 15;
-    const int r = r0 + ((g & 1) << 4) + ((j & 3) << 2);
+    const int n = r0 + ((g & 1) << 4) + ((j & 3) << 2);
     const int k = ((g >> 1) << 3) + (j >> 2);
-    const int h = (r >> 3) & 1, f = (r >> 4) & 1;
-    const int p = ((((r >> 5) << 1) + f) << 10) + ((r & 7) << 1);
-    b0 = (uint32_t)(p + (pk_slot(k, h, f) << 4));
-    b1 = (uint32_t)(p + (pk_slot(k + 4, h, f) << 4));
+    if constexpr (KIND == PACKED_T) {
+      const int h = (n >> 3) & 1, f = (n >> 4) & 1;
+      const int p = ((((n >> 5) << 1) + f) << 10) + ((n & 7) << 1);
+      b.v[0] = (uint32_t)(p + (pk_slot(k, h, f) << 4));
+      b.v[1] = (uint32_t)(p + (pk_slot(k + 4, h, f) << 4));
+    } else {
+#pragma unroll
+      for (int i = 0; i < NF; ++i)
+        b.v[i] = (uint32_t)(k * 512 + 16 * (((n >> 3) + 4 * i) ^ (4 * (k & 3))) + 2 * (n & 7));
+    }
   }
 }
 
 // Read Q of half-step KK of an operand with NF fragments.
 template <int KIND, int KK, int Q, int NF>
-__device__ __forceinline__ void rd_issue(uint32_t b0, uint32_t b1, Frag<KIND> (&f)[NF]) {
-  if constexpr (KIND == PACKED) {
-    rd_b128<2048 * Q>(f[Q].v, KK ? b1 : b0);
-  } else {
+__device__ __forceinline__ void rd_issue(const OpBases<KIND, NF> &b, Frag<KIND> (&f)[NF]) {
+  if constexpr (KIND == PACKED || KIND == ROW) {
+    rd_b128<2048 * Q>(f[Q].v, b.v[KK]);
+  } else if constexpr (KIND == PACKED_T) {
     constexpr int fi = Q >> 1;
     constexpr int imm = 2048 * fi + 256 * KK;
-    if constexpr (Q & 1) rd_tr<imm>(f[fi].hi, b1);
-    else rd_tr<imm>(f[fi].lo, b0);
+    if constexpr (Q & 1) rd_tr<imm>(f[fi].hi, b.v[1]);
+    else rd_tr<imm>(f[fi].lo, b.v[0]);
+  } else {
+    constexpr int fi = Q >> 1;
+    constexpr int imm = 8192 * KK + 2048 * (Q & 1);
+    if constexpr (Q & 1) rd_tr<imm>(f[fi].hi, b.v[fi]);
+    else rd_tr<imm>(f[fi].lo, b.v[fi]);
   }
 }
 
@@ -312,14 +398,14 @@ template <int KIND, int NF>
 __device__ __forceinline__ void frag_tie(Frag<KIND> (&f)[NF]) {
 #pragma unroll
   for (int i = 0; i < NF; ++i) {
-    if constexpr (KIND == PACKED) asm volatile("" : "+v"(f[i].v));
+    if constexpr (!kind_tr(KIND)) asm volatile("" : "+v"(f[i].v));
     else asm volatile("" : "+v"(f[i].lo), "+v"(f[i].hi));
   }
 }
 
 template <int KIND>
 __device__ __forceinline__ bf16x8 frag_val(const Frag<KIND> &f) {
-  if constexpr (KIND == PACKED) return f.v;
+  if constexpr (!kind_tr(KIND)) return f.v;
   else return __builtin_bit_cast(bf16x8, __builtin_shufflevector(f.lo, f.hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
@@ -338,17 +424,27 @@ __device__ __forceinline__ void frags_wait(Frags<T> &f) {
   frag_tie<T::KB>(f.b);
 }
 
-// Read addresses of one stage: A's two, B's two.
+// Read addresses of one stage, A's then B's.
+template <class T>
 struct Bases {
-  uint32_t a0, a1, b0, b1;
+  OpBases<T::KA, T::MI> a;
+  OpBases<T::KB, T::NI> b;
+  __device__ __forceinline__ Bases plus(uint32_t o) const {
+    Bases r = *this;
+#pragma unroll
+    for (auto &x : r.a.v) x += o;
+#pragma unroll
+    for (auto &x : r.b.v) x += o;
+    return r;
+  }
 };
 
 // Read Q of half-step KK (A's reads first, then B's).
 template <class T, int KK, int Q>
-__device__ __forceinline__ void frag_read(const Bases &s, Frags<T> &f) {
+__device__ __forceinline__ void frag_read(const Bases<T> &s, Frags<T> &f) {
   constexpr int RA = T::MI * reads_per_frag<T::KA>();
-  if constexpr (Q < RA) rd_issue<T::KA, KK, Q>(s.a0, s.a1, f.a);
-  else rd_issue<T::KB, KK, Q - RA>(s.b0, s.b1, f.b);
+  if constexpr (Q < RA) rd_issue<T::KA, KK, Q>(s.a, f.a);
+  else rd_issue<T::KB, KK, Q - RA>(s.b, f.b);
 }
 
 // MFMA i of a half-step (block row i / NI, block column i % NI), fenced so
@@ -466,17 +562,14 @@ __device__ __forceinline__ void mainloop(const Op &a, const Op &b, int klen, cha
     const int w = threadIdx.x >> 6;
     const int wm = w >> 1, wn = w & 1;
     const uint32_t lds0 = lds_addr(smem);
-    Bases z;
-    rd_bases<T::KA>(wm * T::WM, z.a0, z.a1);
-    rd_bases<T::KB>(wn * T::WN, z.b0, z.b1);
-    z.a0 += lds0;
-    z.a1 += lds0;
-    z.b0 += lds0 + T::A_BYTES;
-    z.b1 += lds0 + T::A_BYTES;
-    auto stage_bases = [&](int s) {
-      const uint32_t o = (uint32_t)(s * T::STAGE_BYTES);
-      return Bases{z.a0 + o, z.a1 + o, z.b0 + o, z.b1 + o};
-    };
+    Bases<T> z;
+    rd_bases<T::KA>(wm * T::WM, z.a);
+    rd_bases<T::KB>(wn * T::WN, z.b);
+#pragma unroll
+    for (auto &x : z.a.v) x += lds0;
+#pragma unroll
+    for (auto &x : z.b.v) x += lds0 + T::A_BYTES;
+    auto stage_bases = [&](int s) { return z.plus((uint32_t)(s * T::STAGE_BYTES)); };
     int rb = 0;                                    // ring slot of slice 0
     if constexpr (Ch::on) rb = ch.rb;
     auto slot = [&](int s) { return (rb + s) % S; };
@@ -515,7 +608,7 @@ __device__ __forceinline__ void mainloop(const Op &a, const Op &b, int klen, cha
     }
     bar();
     Frags<T> f0, f1;
-    Bases cur = stage_bases(rb);                   // the stage of slice t
+    Bases<T> cur = stage_bases(rb);                // the stage of slice t
     int st = rb;
     static_for<0, R>([&](auto q) { frag_read<T, 0, decltype(q)::value>(cur, f0); });
     // one iteration; U >= 0 is an unrolled iteration of the hook, U < 0 a
@@ -523,7 +616,7 @@ __device__ __forceinline__ void mainloop(const Op &a, const Op &b, int klen, cha
     auto body = [&](int t, auto uu) {
       constexpr int U = decltype(uu)::value;
       const int sn = st + 1 == S ? 0 : st + 1;
-      const Bases nxt = stage_bases(sn);
+      const Bases<T> nxt = stage_bases(sn);
       const int ck = t + S - 1;                    // slice copied in this iteration
       const uint32_t cst = lds0 + (uint32_t)(slot(ck) * T::STAGE_BYTES);
       frags_wait<T>(f0);
@@ -617,8 +710,8 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 __device__ __forceinline__ float bf16_lo(uint32_t u) { return __builtin_bit_cast(float, u << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t u) { return __builtin_bit_cast(float, u & 0xFFFF0000u); }
 
-using FwdTile = Tile<256, 256, 4, PACKED, PACKED>;     // A = Wp, B = Xp
-using DxTile = Tile<256, 256, 4, PACKED, PACKED_T>;    // A = G (Zp), B = Wp read transposed
+using FwdTile = Tile<256, 256, 4, ROW, PACKED>;        // A = W (row-major), B = Xp
+using DxTile = Tile<256, 256, 4, PACKED, ROWT>;        // A = G (Zp), B = W read transposed
 using DwTile = Tile<256, 256, 4, PACKED_T, PACKED_T>;  // A = G (Zp), B = Xp, both transposed
 constexpr int kDwGroup = 4;                            // vocabulary strips per group of dW tiles
 constexpr int kDwOcc = 1;                              // dW workgroups per CU
@@ -633,9 +726,6 @@ constexpr int kDwRpm = 1, kDwCsp = 2;
 // row-major bf16 matrix [R][K]: it reads the rows' 128-byte pieces (8 full
 // rows per wave instruction), places them in LDS in packed order, and writes
 // the two blocks as one contiguous 32 KB copy.  Zero outside [0, R) x [0, K).
-// WEIGHT only names the instance (W once per call, X once per chunk), so that
-// kernel traces tell the two apart.
-template <bool WEIGHT>
 __global__ __launch_bounds__(256) void pack_kernel(const uint16_t *__restrict__ src, int R, int K,
                                                   uint16_t *__restrict__ P, int64_t nks_p) {
   __shared__ __attribute__((aligned(1024))) char lds[32768];
@@ -666,7 +756,7 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint16_t *__restrict__ 
 
 // ---------------------------------------------------------------- forward tile
 // Z^T tile: rows = 256 vocabulary ids from m0, columns = 256 tokens from n0;
-// both operands packed (Wp rows = vocabulary, Xp rows = tokens, k = hidden).
+// A = W along its rows (vocabulary), B = Xp (rows = tokens), k = hidden.
 // VTAIL instantiates the tile that reaches past V (its rows >= V are masked).
 //
 // Epilogue, wave by wave: each wave reduces its own 128 vocabulary rows, so a
@@ -740,7 +830,8 @@ __device__ __forceinline__ void fwd_epilogue(
     // consecutive tokens x 4 consecutive vocabulary ids each (lanes 32..63
     // the next 4), i.e. the 32 slots of one half of a Zp fragment, so each
     // store instruction writes 512 contiguous bytes.  Rows past V hold
-    // products with Wp's zero padding; dlogits zeroes them.
+    // products with zero rows (copies past W's end read as zero); dlogits
+    // zeroes them.
     uint16_t *zt = Zp + ((int64_t)ct * nks_z + 8 * (int64_t)vt) * 8192 + 4 * (lane >> 5);
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
@@ -762,7 +853,7 @@ __device__ __forceinline__ void fwd_epilogue(
 
 template <bool VTAIL, class T = FwdTile, int RPM = kFwdRpm, int CSP = kFwdCsp>
 __global__ __launch_bounds__(NTHREADS, 1) void fwd_tile_kernel(
-    const uint16_t *__restrict__ Wp, const uint16_t *__restrict__ Xp, int64_t nks_h,
+    const uint16_t *__restrict__ W, const uint16_t *__restrict__ Xp,
     const int64_t *__restrict__ labels_c, int64_t ii, int c, int H, int V,
     uint16_t *__restrict__ Zp, int64_t nks_z, float *__restrict__ pm, float *__restrict__ ps,
     float *__restrict__ pmt, float *__restrict__ zy, int64_t nvt, int vt0, int nct, int store_z) {
@@ -771,8 +862,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_tile_kernel(
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
   const int vt = vt0 + tile / nct, ct = tile % nct;
 
-  const Op a{(const char *)(Wp + (int64_t)vt * nks_h * 8192), 0, 0};
-  const Op b{(const char *)(Xp + (int64_t)ct * nks_h * 8192), 0, 0};
+  const int64_t nks_h = (int64_t)((H + 255) >> 8) << 3;
+  const Op a{(const char *)(W + (int64_t)vt * T::BM * H), 2 * (int64_t)H, 0, (const char *)(W + (int64_t)V * H)};
+  const Op b{(const char *)(Xp + (int64_t)ct * nks_h * 8192), 0, 0, nullptr};
   f32x16 acc[4][4];
   zero_acc<T>(acc);
   mainloop<T, RPM, CSP>(a, b, H, smem, acc);
@@ -838,12 +930,12 @@ __global__ __launch_bounds__(256) void dlogits_kernel(
 // ---------------------------------------------------------------- dX (split-K)
 // Unit (s, mt, nt): dxp[s][tok][h] = sum over vocabulary in split s of
 // G[tok][v] W[v][h].  G from Zp (rows = tokens, k = vocabulary), W read
-// transposed from Wp (its columns, the hidden ids, are the operand rows; its
-// rows, the vocabulary, are k), so no transposed copy of W is made.
+// transposed in place (its columns, the hidden ids, are the operand rows;
+// its rows, the vocabulary, are k), so no copy of W is made.
 template <class T = DxTile, int RPM = kDxRpm, int CSP = kDxCsp>
 __global__ __launch_bounds__(NTHREADS, 1) void dx_kernel(
-    const uint16_t *__restrict__ Gp, int64_t nks_z, const uint16_t *__restrict__ Wp,
-    int64_t nks_h, int c, int H, int V, int64_t ksplit, int nmt, int nnt, float *__restrict__ dxp) {
+    const uint16_t *__restrict__ Gp, int64_t nks_z, const uint16_t *__restrict__ W,
+    int c, int H, int V, int64_t ksplit, int nmt, int nnt, float *__restrict__ dxp) {
   static_assert(T::BM == 256 && T::BN == 256, "256 x 256 output tiles");
   __shared__ __attribute__((aligned(1024))) char smem[T::LDS];
   const int unit = xcd_remap(blockIdx.x, gridDim.x);
@@ -856,8 +948,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void dx_kernel(
   const int64_t ke = kb + ksplit < V ? kb + ksplit : V;
   const int klen = (int)(ke - kb);
 
-  const Op a{(const char *)(Gp + ((int64_t)mt * nks_z + (kb >> 5)) * 8192), 0, 0};
-  const Op b{(const char *)(Wp + (int64_t)(n0 >> 5) * 8192), nks_h * 16384, kb};
+  const Op a{(const char *)(Gp + ((int64_t)mt * nks_z + (kb >> 5)) * 8192), 0, 0, nullptr};
+  const Op b{(const char *)(W + n0), 2 * (int64_t)H, kb, (const char *)(W + (int64_t)V * H)};
   f32x16 acc[4][4];
   zero_acc<T>(acc);
   mainloop<T, RPM, CSP>(a, b, klen, smem, acc);
@@ -1153,31 +1245,28 @@ static int cu_count() {
 }
 
 hipError_t launch_pack_bf16(const uint16_t *src, int R, int K, uint16_t *P, int64_t nks_p,
-                            bool weight, hipStream_t s) {
+                            hipStream_t s) {
   // nks_p is a multiple of 8, so column pairs of slices tile it exactly
   const int64_t nwg = (int64_t)(R + 255) / 256 * (nks_p / 2);
-  if (weight)
-    hipLaunchKernelGGL(pack_kernel<true>, dim3((unsigned)nwg), dim3(256), 0, s, src, R, K, P, nks_p);
-  else
-    hipLaunchKernelGGL(pack_kernel<false>, dim3((unsigned)nwg), dim3(256), 0, s, src, R, K, P, nks_p);
+  hipLaunchKernelGGL(pack_kernel, dim3((unsigned)nwg), dim3(256), 0, s, src, R, K, P, nks_p);
   return hipGetLastError();
 }
 
-hipError_t launch_fwd_tile_bf16(const uint16_t *Wp, const uint16_t *Xp, int64_t nks_h,
+hipError_t launch_fwd_tile_bf16(const uint16_t *W, const uint16_t *Xp,
                                 const int64_t *labels_c, int64_t ii, int c, int H, int V,
                                 uint16_t *Zp, int64_t nks_z, float *pm, float *ps, float *pmt,
                                 float *zy, int64_t nvt, bool store_z, hipStream_t s) {
   const int nct = (c + FwdTile::BN - 1) / FwdTile::BN;
   const int nfull = V / FwdTile::BM;                 // vocabulary tiles inside V
   if (nfull > 0) {
-    hipLaunchKernelGGL((fwd_tile_kernel<false>), dim3(nfull * nct), dim3(NTHREADS), 0, s, Wp, Xp,
-                       nks_h, labels_c, ii, c, H, V, Zp, nks_z, pm, ps, pmt, zy, nvt, 0, nct,
+    hipLaunchKernelGGL((fwd_tile_kernel<false>), dim3(nfull * nct), dim3(NTHREADS), 0, s, W, Xp,
+                       labels_c, ii, c, H, V, Zp, nks_z, pm, ps, pmt, zy, nvt, 0, nct,
                        store_z ? 1 : 0);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (V % FwdTile::BM != 0) {
-    hipLaunchKernelGGL((fwd_tile_kernel<true>), dim3(nct), dim3(NTHREADS), 0, s, Wp, Xp, nks_h,
+    hipLaunchKernelGGL((fwd_tile_kernel<true>), dim3(nct), dim3(NTHREADS), 0, s, W, Xp,
                        labels_c, ii, c, H, V, Zp, nks_z, pm, ps, pmt, zy, nvt, nfull, nct,
                        store_z ? 1 : 0);
   }
@@ -1195,12 +1284,12 @@ hipError_t launch_dlogits_bf16(uint16_t *Zp, int64_t nks_z, int c, int V, const 
   return hipGetLastError();
 }
 
-hipError_t launch_dx_bf16(const uint16_t *Gp, int64_t nks_z, const uint16_t *Wp, int64_t nks_h,
+hipError_t launch_dx_bf16(const uint16_t *Gp, int64_t nks_z, const uint16_t *W,
                           int c, int H, int V, int splitk, int64_t ksplit, float *dxp,
                           hipStream_t s) {
   const int nmt = (c + DxTile::BM - 1) / DxTile::BM, nnt = (H + DxTile::BN - 1) / DxTile::BN;
-  hipLaunchKernelGGL((dx_kernel<>), dim3(splitk * nmt * nnt), dim3(NTHREADS), 0, s, Gp, nks_z, Wp,
-                     nks_h, c, H, V, ksplit, nmt, nnt, dxp);
+  hipLaunchKernelGGL((dx_kernel<>), dim3(splitk * nmt * nnt), dim3(NTHREADS), 0, s, Gp, nks_z, W,
+                     c, H, V, ksplit, nmt, nnt, dxp);
   return hipGetLastError();
 }
 

@@ -60,17 +60,43 @@ def test_noalloc_matches_workspace_entry(dtype):
         check_grad(dW1.double().cpu().numpy(), r.dW, dtype, "dW")
 
 
-def test_noalloc_refuses_oversized_workspace():
-    # the Llama-3-8B head needs more than the static array at any chunk
+def test_noalloc_llama_head_and_refusal():
+    # The Llama-3-8B head: with the chunk left to the library it plans the
+    # largest chunk whose workspace fits the static array, and matches the
+    # workspace entry point at that chunk bitwise; an explicit chunk whose
+    # workspace exceeds the array is refused before any device work.
     N, H, V = 8192, 4096, 128256
-    assert fl.flce_workspace_bytes(N, H, V, fl.FLCE_BF16, 256) > fl.flce_noalloc_scratch_bytes()
-    X = torch.zeros(N, H, dtype=torch.bfloat16, device=DEV)
-    W = torch.zeros(V, H, dtype=torch.bfloat16, device=DEV)
-    y = torch.zeros(N, dtype=torch.int64, device=DEV)
+    cap = fl.flce_noalloc_scratch_bytes()
+    st, chunk, peak = fl.flce_plan(N, H, V, fl.FLCE_BF16, scratch_budget_bytes=cap)
+    assert st == fl.FLCE_OK and peak <= cap
+    assert fl.flce_workspace_bytes(N, H, V, fl.FLCE_BF16, 2 * chunk) > cap
+    say(f"  noalloc case: N={N} H={H} V={V} bf16 chunk={chunk} (auto)")
+    g = torch.Generator(device="cpu").manual_seed(7)
+    X = (torch.randn(N, H, generator=g) * 0.5).to(torch.bfloat16).to(DEV)
+    W = (torch.randn(V, H, generator=g) * 0.02).to(torch.bfloat16).to(DEV)
+    y = torch.randint(0, V, (N,), generator=g).to(DEV)
+    ws = fl.workspace(N, H, V, fl.FLCE_BF16, chunk, device=DEV)
+    dX0, dW0 = torch.empty_like(X), torch.empty((V, H), dtype=torch.float32, device=DEV)
+    rl0 = torch.empty(N, dtype=torch.float32, device=DEV)
+    loss0 = fl.flce_fwd_bwd(X, W, y, -100, chunk, dX0, dW0, ws, row_loss=rl0, row_lse=None)
+    del ws
+    dX1 = torch.full_like(X, float("nan"))
+    dW1 = torch.full((V, H), float("nan"), dtype=torch.float32, device=DEV)
+    rl1 = torch.full((N,), float("nan"), dtype=torch.float32, device=DEV)
+    rs1 = torch.empty(N, dtype=torch.float32, device=DEV)
+    st, loss1 = _noalloc(X, W, y, 0, dX1, dW1, rl1, rs1)
+    torch.cuda.synchronize()
+    assert st == fl.FLCE_OK, fl.flce_status_string(st)
+    assert loss1 == loss0
+    assert torch.equal(dX1, dX0) and torch.equal(dW1, dW0) and torch.equal(rl1, rl0)
+    del dX0, dW0, dX1
+
+    big = 2 * chunk
+    say(f"  noalloc refusal: chunk={big}")
     dX = torch.empty_like(X)
-    dW = torch.full((V, H), 7.0, dtype=torch.float32, device=DEV)
-    rl = torch.empty(N, dtype=torch.float32, device=DEV)
-    st, _ = _noalloc(X, W, y, 0, dX, dW, rl, rl)
+    dW1.fill_(7.0)
+    st, _ = _noalloc(X, W, y, big, dX, dW1, rl1, rs1)
     assert st == fl.FLCE_EWORKSPACE
     assert "exceeds the static scratch" in fl.flce_last_error()
-    assert bool((dW == 7.0).all())                     # untouched
+    torch.cuda.synchronize()
+    assert bool((dW1 == 7.0).all())                    # untouched
