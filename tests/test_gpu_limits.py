@@ -3,7 +3,8 @@ H = 2^20), with few tokens so that the fp64 oracle's full logits stay a few GB.
 
 - V at its limit: 62,500 log-sum-exp partials per token, 31,250 vocabulary
   tiles per chunk, a dX split over millions of vocabulary rows, and about
-  12 GB of workspace (the packed copies of W pad H = 8 to 256 columns).
+  3.8 GiB of workspace (nearly all of it the chunk's bf16 logits, packed in
+  row tiles of 256 tokens; W, 16 bytes per row, is read in place).
 - H at its limit: one forward tile whose K loop runs 32,768 slices, dX over
   4,096 output tiles, dW over 8,192 column tiles of one vocabulary strip.
 Both run two chunks, the second ragged.
