@@ -702,9 +702,13 @@ __device__ __forceinline__ void zero_acc(f32x16 (&acc)[T::MI][T::NI]) {
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// a in the low half, b in the high half, each rounded to nearest even (one
+// packed conversion)
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  __bf16 x = (__bf16)a, y = (__bf16)b;
-  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t u) { return __builtin_bit_cast(float, u << 16); }
@@ -805,7 +809,6 @@ __device__ __forceinline__ void fwd_epilogue(
     const float ml = ms * kLog2e;
     msub[j] = ms;
     float sum = 0.f, zsel = 0.f;
-    bool found = false;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -814,9 +817,11 @@ __device__ __forceinline__ void fwd_epilogue(
         const float z = (VTAIL && r >= vlim) ? -INFINITY : acc[i][j][e];
         sum += __builtin_amdgcn_exp2f(z * kLog2e - ml);
         zsel = (r == yr) ? acc[i][j][e] : zsel;
-        found = found || (r == yr);
       }
     sum += __shfl_xor(sum, 32);
+    // the lane's rows r have bit 2 clear (4 (lane / 32) is in vrow0), so it
+    // holds the target exactly when yr is such a row
+    const bool found = (unsigned)yr < 128u && (yr & 4) == 0;
     if (found && tok_ok) zy[tok] = zsel;             // one lane holds the target
     if (lane < 32 && tok_ok) {
       pm[(int64_t)tok * nvt + part] = mx;
