@@ -777,7 +777,7 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint16_t *__restrict__ 
 // target logit and the logits tile from the accumulators of tile (vt, ct).
 template <bool VTAIL, class T>
 __device__ __forceinline__ void fwd_epilogue(
-    f32x16 (&acc)[4][4], int vt, int ct, const int64_t *__restrict__ labels_c, int64_t ii, int c, int V,
+    f32x16 (&acc)[4][4], int vt, int ct, const int *lab_s, int c, int V,
     uint16_t *__restrict__ Zp, int64_t nks_z, float *__restrict__ pm, float *__restrict__ ps,
     float *__restrict__ pmt, float *__restrict__ zy, int64_t nvt, int store_z) {
   const int m0 = vt * T::BM, n0 = ct * T::BN;
@@ -790,10 +790,10 @@ __device__ __forceinline__ void fwd_epilogue(
   float msub[4];                                       // the maximum each token's stored logits are taken from
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int tok = n0 + wn * 128 + j * 32 + (lane & 31);
+    const int tl = wn * 128 + j * 32 + (lane & 31), tok = n0 + tl;
     const bool tok_ok = tok < c;
-    const int64_t y = tok_ok ? labels_c[tok] : ii;
-    const int yr = (y != ii && y >= 0 && y < V) ? (int)y - vrow0 : -1;
+    const int y = lab_s[tl];
+    const int yr = y >= 0 ? y - vrow0 : -1;
     float mx = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -808,20 +808,37 @@ __device__ __forceinline__ void fwd_epilogue(
     const float ms = (VTAIL && mx == -INFINITY) ? 0.f : mx;
     const float ml = ms * kLog2e;
     msub[j] = ms;
-    float sum = 0.f, zsel = 0.f;
+    // four independent partial sums, so that the exponentials do not wait
+    // on one another
+    float s4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int r = 32 * i + 8 * (e >> 2) + (e & 3);
         const float z = (VTAIL && r >= vlim) ? -INFINITY : acc[i][j][e];
-        sum += __builtin_amdgcn_exp2f(z * kLog2e - ml);
-        zsel = (r == yr) ? acc[i][j][e] : zsel;
+        s4[e & 3] += __builtin_amdgcn_exp2f(z * kLog2e - ml);
       }
+    float sum = (s4[0] + s4[1]) + (s4[2] + s4[3]);
     sum += __shfl_xor(sum, 32);
-    // the lane's rows r have bit 2 clear (4 (lane / 32) is in vrow0), so it
-    // holds the target exactly when yr is such a row
+    // The lane's rows r = 32 i + 8 (e/4) + e%4 have bit 2 clear (4 (lane/32)
+    // is in vrow0), so it holds the target exactly when yr is such a row,
+    // namely value 16 i + e with i = yr/32, e = 4 ((yr/8) % 4) + yr % 4.  A
+    // tree of selects on the six bits of that index picks it.
     const bool found = (unsigned)yr < 128u && (yr & 4) == 0;
+    const int ti = ((yr >> 5) << 4) | (((yr >> 3) & 3) << 2) | (yr & 3);
+    float zt[64];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) zt[16 * i + e] = acc[i][j][e];
+#pragma unroll
+    for (int bit = 0; bit < 6; ++bit) {
+      const bool hi = (ti >> bit) & 1;
+#pragma unroll
+      for (int x = 0; x < (32 >> bit); ++x) zt[x] = hi ? zt[2 * x + 1] : zt[2 * x];
+    }
+    const float zsel = zt[0];
     if (found && tok_ok) zy[tok] = zsel;             // one lane holds the target
     if (lane < 32 && tok_ok) {
       pm[(int64_t)tok * nvt + part] = mx;
@@ -856,24 +873,43 @@ __device__ __forceinline__ void fwd_epilogue(
   }
 }
 
+// The forward's main-loop hook: the tile's labels, loaded from global memory
+// before the prologue's copies, are written to LDS once those copies are
+// issued, so that their latency overlaps the pipeline fill instead of the
+// epilogue.  y is the label if it is a vocabulary id, else -1 (ignored, out
+// of range, or a token past the chunk).
+struct FwdLabels : NoHook {
+  int *lab_s;
+  int y;
+  __device__ __forceinline__ void prologue() { lab_s[threadIdx.x] = y; }
+};
+
 template <bool VTAIL, class T = FwdTile, int RPM = kFwdRpm, int CSP = kFwdCsp>
 __global__ __launch_bounds__(NTHREADS, 1) void fwd_tile_kernel(
     const uint16_t *__restrict__ W, const uint16_t *__restrict__ Xp,
     const int64_t *__restrict__ labels_c, int64_t ii, int c, int H, int V,
     uint16_t *__restrict__ Zp, int64_t nks_z, float *__restrict__ pm, float *__restrict__ ps,
     float *__restrict__ pmt, float *__restrict__ zy, int64_t nvt, int vt0, int nct, int store_z) {
-  static_assert(T::BM == 256 && T::BN == 256, "the epilogue reduces a 256 x 256 tile");
+  static_assert(T::BM == 256 && T::BN == 256 && NTHREADS == T::BN, "the epilogue reduces a 256 x 256 tile");
   __shared__ __attribute__((aligned(1024))) char smem[T::LDS];
+  __shared__ int lab_s[T::BN];
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
   const int vt = vt0 + tile / nct, ct = tile % nct;
+  FwdLabels hook;
+  hook.lab_s = lab_s;
+  {
+    const int tok = ct * T::BN + (int)threadIdx.x;
+    const int64_t y = tok < c ? labels_c[tok] : ii;
+    hook.y = (y != ii && y >= 0 && y < V) ? (int)y : -1;
+  }
 
   const int64_t nks_h = (int64_t)((H + 255) >> 8) << 3;
   const Op a{(const char *)(W + (int64_t)vt * T::BM * H), 2 * (int64_t)H, 0, (const char *)(W + (int64_t)V * H)};
   const Op b{(const char *)(Xp + (int64_t)ct * nks_h * 8192), 0, 0, nullptr};
   f32x16 acc[4][4];
   zero_acc<T>(acc);
-  mainloop<T, RPM, CSP>(a, b, H, smem, acc);
-  fwd_epilogue<VTAIL, T>(acc, vt, ct, labels_c, ii, c, V, Zp, nks_z, pm, ps, pmt, zy, nvt, store_z);
+  mainloop<T, RPM, CSP>(a, b, H, smem, acc, hook);
+  fwd_epilogue<VTAIL, T>(acc, vt, ct, lab_s, c, V, Zp, nks_z, pm, ps, pmt, zy, nvt, store_z);
 }
 
 // ---------------------------------------------------------------- dlogits
