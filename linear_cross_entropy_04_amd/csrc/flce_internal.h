@@ -73,13 +73,13 @@ hipError_t launch_pack_bf16(const uint16_t *src, int R, int K, uint16_t *P, int6
                             hipStream_t s);
 // Logits tile GEMM with the log-sum-exp epilogue.  pm, ps: [token][partial]
 // maximum and sum of exp per 128 vocabulary ids; with store_z, Zp receives
-// bf16(z - m) for the partial's maximum m, and pmt[partial * c + token] the m
-// that was subtracted.
+// bf16((z - m) log2 e) for the partial's maximum m, and pmt[partial * c +
+// token] the m that was subtracted.
 hipError_t launch_fwd_tile_bf16(const uint16_t *W, const uint16_t *Xp,
                                 const int64_t *labels_c, int64_t ii, int c, int H, int V,
                                 uint16_t *Zp, int64_t nks_z, float *pm, float *ps, float *pmt,
                                 float *zy, int64_t nvt, bool store_z, hipStream_t s);
-// G in place over the stored bf16(z - m), with m from pmt.
+// G in place over the stored bf16((z - m) log2 e), with m from pmt.
 // wrow_c (may be null): per-token weight of the loss (the upstream gradient
 // of a per-token loss vector); null: sc->scale for every valid token.
 hipError_t launch_dlogits_bf16(uint16_t *Zp, int64_t nks_z, int c, int V, const float *pmt,

@@ -7,7 +7,7 @@
 //   pack      X_c -> Xp (rows = tokens, k = hidden);
 //   forward   Z_c^T = W X_c^T      M = V (vocab), N = c (tokens), K = H
 //             + epilogue: per (token, 128-vocab half tile) max m and sum of
-//               exp, the target logit, and bf16(z - m) into Zp (rows =
+//               exp, the target logit, and bf16((z - m) log2 e) into Zp (rows =
 //               tokens, k = vocabulary);
 //   dlogits   Zp rewritten in place into G = (softmax - onehot) / N_valid;
 //   dX        dX_c  = G_c W        M = c, N = H, K = V (split-K, fp32 partials),
@@ -58,6 +58,7 @@ typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int BK = 32;             // k per pipeline slice
 constexpr int NTHREADS = 256;
@@ -273,6 +274,10 @@ __device__ __forceinline__ void bar() {
 template <int V>
 struct ic {
   static constexpr int value = V;
+};
+template <bool V>
+struct bc {
+  static constexpr bool value = V;
 };
 template <int B, int E, class F>
 __device__ __forceinline__ void static_for(F &&f) {
@@ -768,72 +773,104 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint16_t *__restrict__ 
 // 2 vt + wm.  The target logit is taken from the fp32 accumulators by the
 // lane that holds it.  The logits tile (8 consecutive blocks of Zp) is
 // stored straight from the accumulators in 512-byte half-fragments, as
-// bf16(z - m) with m the token's maximum over the wave's 128 vocabulary ids
-// (written to pmt for dlogits).  Rounding then costs a relative 2^-9 of
-// m - z, not of z: exp(z - lse) keeps its accuracy however large the
-// logits or a common shift of a token's logits, and the entries that carry
-// the probability (z near m) are stored almost exactly.
+// bf16((z - m) log2 e) with m the token's maximum over the wave's 128
+// vocabulary ids (written to pmt for dlogits): the argument of the
+// exponential the sum needs anyway, so one fma serves both.  Rounding then
+// costs a relative 2^-9 of m - z, not of z: exp(z - lse) keeps its accuracy
+// however large the logits or a common shift of a token's logits, and the
+// entries that carry the probability (z near m) are stored almost exactly.
+// Rows past V (VTAIL) are stored as -inf; dlogits zeroes them.
 // The forward tile's epilogue (see fwd_tile_kernel): per-token partials, the
-// target logit and the logits tile from the accumulators of tile (vt, ct).
-template <bool VTAIL, class T>
+// target logit and, with STORE, the logits tile from the accumulators of
+// tile (vt, ct).
+template <bool VTAIL, bool STORE, class T>
 __device__ __forceinline__ void fwd_epilogue(
     f32x16 (&acc)[4][4], int vt, int ct, const int *lab_s, int c, int V,
     uint16_t *__restrict__ Zp, int64_t nks_z, float *__restrict__ pm, float *__restrict__ ps,
-    float *__restrict__ pmt, float *__restrict__ zy, int64_t nvt, int store_z) {
+    float *__restrict__ pmt, float *__restrict__ zy, int64_t nvt) {
   const int m0 = vt * T::BM, n0 = ct * T::BN;
 
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = w >> 1, wn = w & 1;
   const int vrow0 = m0 + wm * 128 + 4 * (lane >> 5);   // row r = 32 i + 8 (e/4) + e%4
   const int vlim = V - vrow0;                          // rows r < vlim exist
   const int64_t part = 2 * (int64_t)vt + wm;
-  float msub[4];                                       // the maximum each token's stored logits are taken from
+  // The tile's logits are the 8 blocks of vocabulary slices 8 vt .. 8 vt + 7
+  // in token row tile ct of Zp, 128 KB from zbase.  For one (i, j, g) the
+  // lanes hold 32 consecutive tokens x 4 consecutive vocabulary ids each
+  // (lanes 32..63 the next 4), i.e. the 32 slots of one half of a Zp
+  // fragment, so each store instruction writes 512 contiguous bytes: the
+  // lane's part of the address depends on g only, the wave's on (i, j).
+  const __amdgpu_buffer_rsrc_t zrs = __builtin_amdgcn_make_buffer_rsrc(
+      Zp + ((int64_t)ct * nks_z + 8 * (int64_t)vt) * 8192, (short)0, 131072, 0x00020000);
+  int zvoff[4];
+#pragma unroll
+  for (int g = 0; g < 4; ++g)
+    zvoff[g] = 2 * (4 * (lane >> 5) + ((g >> 1) << 9) + (pk_slot(lane & 31, g & 1, g >> 1) << 3));
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int tl = wn * 128 + j * 32 + (lane & 31), tok = n0 + tl;
     const bool tok_ok = tok < c;
     const int y = lab_s[tl];
     const int yr = y >= 0 ? y - vrow0 : -1;
+    // this token group's accumulators, read here (volatile asm keeps the
+    // compiler from reading every group's at the start and spilling them)
+    float av[4][16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(av[i][e]) : "a"(acc[i][j][e]));
     float mx = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int r = 32 * i + 8 * (e >> 2) + (e & 3);
-        const float z = (VTAIL && r >= vlim) ? -INFINITY : acc[i][j][e];
+        const float z = (VTAIL && r >= vlim) ? -INFINITY : av[i][e];
         mx = fmaxf(mx, z);
       }
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     // a wave whose rows all lie past V has mx = -inf: its sum must be 0, not NaN
     const float ms = (VTAIL && mx == -INFINITY) ? 0.f : mx;
     const float ml = ms * kLog2e;
-    msub[j] = ms;
+    // The lane's rows r = 32 i + 8 (e/4) + e%4 have bit 2 clear (4 (lane/32)
+    // is in vrow0), so it holds the target exactly when yr is such a row,
+    // namely value 16 i + e with i = yr/32, e = 4 ((yr/8) % 4) + yr % 4.  A
+    // tree of selects on the six bits of that index picks it: its first two
+    // levels (e % 4) inside the loop below, the other four after it.
+    const bool found = (unsigned)yr < 128u && (yr & 4) == 0;
+    const int ti = ((yr >> 5) << 4) | (((yr >> 3) & 3) << 2) | (yr & 3);
+    const bool b0 = ti & 1, b1 = ti & 2;
+    float zt[16];
     // four independent partial sums, so that the exponentials do not wait
-    // on one another
+    // on one another; each group of four values goes out as it is formed
     float s4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int r = 32 * i + 8 * (e >> 2) + (e & 3);
-        const float z = (VTAIL && r >= vlim) ? -INFINITY : acc[i][j][e];
-        s4[e & 3] += __builtin_amdgcn_exp2f(z * kLog2e - ml);
+      for (int g = 0; g < 4; ++g) {
+        float t[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int e = 4 * g + q, r = 32 * i + 8 * g + q;
+          const float z = (VTAIL && r >= vlim) ? -INFINITY : av[i][e];
+          t[q] = __builtin_fmaf(z, kLog2e, -ml);
+          s4[q] += __builtin_amdgcn_exp2f(t[q]);
+        }
+        const float z01 = b0 ? av[i][4 * g + 1] : av[i][4 * g];
+        const float z23 = b0 ? av[i][4 * g + 3] : av[i][4 * g + 2];
+        zt[4 * i + g] = b1 ? z23 : z01;
+        if constexpr (STORE) {
+          // vocabulary slice wm 4 + i of the tile, token row group wn 4 + j
+          const u32x2 pk = {pack_bf16x2(t[0], t[1]), pack_bf16x2(t[2], t[3])};
+          __builtin_amdgcn_raw_buffer_store_b64(pk, zrs, zvoff[g],
+                                                2 * (((wm * 4 + i) << 13) + ((wn * 4 + j) << 10)), 0);
+        }
       }
     float sum = (s4[0] + s4[1]) + (s4[2] + s4[3]);
     sum += __shfl_xor(sum, 32);
-    // The lane's rows r = 32 i + 8 (e/4) + e%4 have bit 2 clear (4 (lane/32)
-    // is in vrow0), so it holds the target exactly when yr is such a row,
-    // namely value 16 i + e with i = yr/32, e = 4 ((yr/8) % 4) + yr % 4.  A
-    // tree of selects on the six bits of that index picks it.
-    const bool found = (unsigned)yr < 128u && (yr & 4) == 0;
-    const int ti = ((yr >> 5) << 4) | (((yr >> 3) & 3) << 2) | (yr & 3);
-    float zt[64];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) zt[16 * i + e] = acc[i][j][e];
-#pragma unroll
-    for (int bit = 0; bit < 6; ++bit) {
+    for (int bit = 2; bit < 6; ++bit) {
       const bool hi = (ti >> bit) & 1;
 #pragma unroll
       for (int x = 0; x < (32 >> bit); ++x) zt[x] = hi ? zt[2 * x + 1] : zt[2 * x];
@@ -843,32 +880,7 @@ __device__ __forceinline__ void fwd_epilogue(
     if (lane < 32 && tok_ok) {
       pm[(int64_t)tok * nvt + part] = mx;
       ps[(int64_t)tok * nvt + part] = sum;
-      if (store_z) pmt[part * c + tok] = ms;
-    }
-  }
-
-  if (store_z) {
-    // Straight from the accumulators: for one (i, j, g) the lanes hold 32
-    // consecutive tokens x 4 consecutive vocabulary ids each (lanes 32..63
-    // the next 4), i.e. the 32 slots of one half of a Zp fragment, so each
-    // store instruction writes 512 contiguous bytes.  Rows past V hold
-    // products with zero rows (copies past W's end read as zero); dlogits
-    // zeroes them.
-    uint16_t *zt = Zp + ((int64_t)ct * nks_z + 8 * (int64_t)vt) * 8192 + 4 * (lane >> 5);
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int h = g & 1, f = g >> 1;
-      uint16_t *zg = zt + (f << 9) + (pk_slot(lane & 31, h, f) << 3);
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          // vocabulary slice wm 4 + i of the tile, token row group wn 4 + j
-          uint2 pk;
-          pk.x = pack_bf16x2(acc[i][j][4 * g] - msub[j], acc[i][j][4 * g + 1] - msub[j]);
-          pk.y = pack_bf16x2(acc[i][j][4 * g + 2] - msub[j], acc[i][j][4 * g + 3] - msub[j]);
-          *(uint2 *)(zg + ((wm * 4 + i) << 13) + ((wn * 4 + j) << 10)) = pk;
-        }
+      if constexpr (STORE) pmt[part * c + tok] = ms;
     }
   }
 }
@@ -884,12 +896,12 @@ struct FwdLabels : NoHook {
   __device__ __forceinline__ void prologue() { lab_s[threadIdx.x] = y; }
 };
 
-template <bool VTAIL, class T = FwdTile, int RPM = kFwdRpm, int CSP = kFwdCsp>
+template <bool VTAIL, bool STORE, class T = FwdTile, int RPM = kFwdRpm, int CSP = kFwdCsp>
 __global__ __launch_bounds__(NTHREADS, 1) void fwd_tile_kernel(
     const uint16_t *__restrict__ W, const uint16_t *__restrict__ Xp,
     const int64_t *__restrict__ labels_c, int64_t ii, int c, int H, int V,
     uint16_t *__restrict__ Zp, int64_t nks_z, float *__restrict__ pm, float *__restrict__ ps,
-    float *__restrict__ pmt, float *__restrict__ zy, int64_t nvt, int vt0, int nct, int store_z) {
+    float *__restrict__ pmt, float *__restrict__ zy, int64_t nvt, int vt0, int nct) {
   static_assert(T::BM == 256 && T::BN == 256 && NTHREADS == T::BN, "the epilogue reduces a 256 x 256 tile");
   __shared__ __attribute__((aligned(1024))) char smem[T::LDS];
   __shared__ int lab_s[T::BN];
@@ -909,7 +921,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_tile_kernel(
   f32x16 acc[4][4];
   zero_acc<T>(acc);
   mainloop<T, RPM, CSP>(a, b, H, smem, acc, hook);
-  fwd_epilogue<VTAIL, T>(acc, vt, ct, lab_s, c, V, Zp, nks_z, pm, ps, pmt, zy, nvt, store_z);
+  fwd_epilogue<VTAIL, STORE, T>(acc, vt, ct, lab_s, c, V, Zp, nks_z, pm, ps, pmt, zy, nvt);
 }
 
 // ---------------------------------------------------------------- dlogits
@@ -917,7 +929,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_tile_kernel(
 // four 16-byte slots per thread (one token, 8 consecutive vocabulary columns
 // each), in memory order: pass k of a wave covers 1 KB contiguous, and all
 // four loads are in flight before any arithmetic.  In place, from the stored
-// Z - m (m the token's maximum over the block's 128-wide partial, from pmt):
+// (Z - m) log2 e (m the token's maximum over the block's 128-wide partial, from pmt):
 // G = w_r (exp(Z - lse) - onehot(y)) on valid tokens, 0 on ignored tokens and
 // outside [0, c) x [0, V); w_r = wrow_c[r] if given, else sc->scale
 // (1 / N_valid for the mean loss).
@@ -947,7 +959,7 @@ __global__ __launch_bounds__(256) void dlogits_kernel(
     float l2 = 0.f, inv = 0.f;
     if (r < c) {
       y = labels_c[r];
-      l2 = (lse_c[r] - mrow[r]) * kLog2e;     // stored values are z - m
+      l2 = (lse_c[r] - mrow[r]) * kLog2e;     // stored values are (z - m) log2 e
       inv = wrow_c ? wrow_c[r] : sc->scale;
     }
     const bool valid = r < c && y != ii;
@@ -959,7 +971,7 @@ __global__ __launch_bounds__(256) void dlogits_kernel(
       for (int hh = 0; hh < 2; ++hh) {
         const int v = v0 + 2 * d + hh;
         const float zz = hh ? bf16_hi(z[k][d]) : bf16_lo(z[k][d]);
-        const float e = __builtin_amdgcn_exp2f(zz * kLog2e - l2) - ((int64_t)v == y ? 1.f : 0.f);
+        const float e = __builtin_amdgcn_exp2f(zz - l2) - ((int64_t)v == y ? 1.f : 0.f);
         fv[hh] = (valid && v < V) ? e * inv : 0.f;
       }
       g[d] = pack_bf16x2(fv[0], fv[1]);
@@ -1299,19 +1311,18 @@ hipError_t launch_fwd_tile_bf16(const uint16_t *W, const uint16_t *Xp,
                                 float *zy, int64_t nvt, bool store_z, hipStream_t s) {
   const int nct = (c + FwdTile::BN - 1) / FwdTile::BN;
   const int nfull = V / FwdTile::BM;                 // vocabulary tiles inside V
-  if (nfull > 0) {
-    hipLaunchKernelGGL((fwd_tile_kernel<false>), dim3(nfull * nct), dim3(NTHREADS), 0, s, W, Xp,
-                       labels_c, ii, c, H, V, Zp, nks_z, pm, ps, pmt, zy, nvt, 0, nct,
-                       store_z ? 1 : 0);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  if (V % FwdTile::BM != 0) {
-    hipLaunchKernelGGL((fwd_tile_kernel<true>), dim3(nct), dim3(NTHREADS), 0, s, W, Xp,
-                       labels_c, ii, c, H, V, Zp, nks_z, pm, ps, pmt, zy, nvt, nfull, nct,
-                       store_z ? 1 : 0);
-  }
-  return hipGetLastError();
+  auto launch = [&](auto vtail, auto store, int ntiles, int vt0) {
+    hipLaunchKernelGGL((fwd_tile_kernel<decltype(vtail)::value, decltype(store)::value>), dim3(ntiles),
+                       dim3(NTHREADS), 0, s, W, Xp, labels_c, ii, c, H, V, Zp, nks_z, pm, ps, pmt, zy,
+                       nvt, vt0, nct);
+    return hipGetLastError();
+  };
+  hipError_t e = hipSuccess;
+  if (nfull > 0)
+    e = store_z ? launch(bc<false>{}, bc<true>{}, nfull * nct, 0) : launch(bc<false>{}, bc<false>{}, nfull * nct, 0);
+  if (e == hipSuccess && V % FwdTile::BM != 0)
+    e = store_z ? launch(bc<true>{}, bc<true>{}, nct, nfull) : launch(bc<true>{}, bc<false>{}, nct, nfull);
+  return e;
 }
 
 hipError_t launch_dlogits_bf16(uint16_t *Zp, int64_t nks_z, int c, int V, const float *pmt,
