@@ -54,6 +54,7 @@ def test_pages_api_example_shape():
     (1500, 320, 1100, 512),     # dW old values added in the main loop (16 slices), V and H tails
     (2100, 512, 600, 1024),     # the same at 32 slices, V tail; last chunk of 52 rows
     (2100, 4096, 4452, 1024),   # 272 dW tiles inside V: resident workgroups chain tiles; V tail
+    (1000, 256, 70000, 1000),   # 1092 forward tiles (more than one wave of 256 CUs); V and token tails
 ])
 def test_bf16_ragged(N, H, V, chunk):
     inp = datagen.make_custom(N, H, V, "bf16", seed=N + V, ignore_frac=0.1)
