@@ -980,68 +980,6 @@ __global__ __launch_bounds__(256) void dlogits_kernel(
   }
 }
 
-// ---------------------------------------------------------------- dX (split-K)
-// Unit (s, mt, nt): dxp[s][tok][h] = sum over vocabulary in split s of
-// G[tok][v] W[v][h].  G from Zp (rows = tokens, k = vocabulary), W read
-// transposed in place (its columns, the hidden ids, are the operand rows;
-// its rows, the vocabulary, are k), so no copy of W is made.
-template <class T = DxTile, int RPM = kDxRpm, int CSP = kDxCsp>
-__global__ __launch_bounds__(NTHREADS, 1) void dx_kernel(
-    const uint16_t *__restrict__ Gp, int64_t nks_z, const uint16_t *__restrict__ W,
-    int c, int H, int V, int64_t ksplit, int nmt, int nnt, float *__restrict__ dxp) {
-  static_assert(T::BM == 256 && T::BN == 256, "256 x 256 output tiles");
-  __shared__ __attribute__((aligned(1024))) char smem[T::LDS];
-  const int unit = xcd_remap(blockIdx.x, gridDim.x);
-  const int per = nmt * nnt;
-  // token tile fastest: the few token tiles of a split share each W block
-  const int s = unit / per, rem = unit - s * per;
-  const int nt = rem / nmt, mt = rem - nt * nmt;
-  const int m0 = mt * T::BM, n0 = nt * T::BN;
-  const int64_t kb = (int64_t)s * ksplit;
-  const int64_t ke = kb + ksplit < V ? kb + ksplit : V;
-  const int klen = (int)(ke - kb);
-
-  const Op a{(const char *)(Gp + ((int64_t)mt * nks_z + (kb >> 5)) * 8192), 0, 0, nullptr};
-  const Op b{(const char *)(W + n0), 2 * (int64_t)H, kb, (const char *)(W + (int64_t)V * H)};
-  f32x16 acc[4][4];
-  zero_acc<T>(acc);
-  mainloop<T, RPM, CSP>(a, b, klen, smem, acc);
-
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int wm = w >> 1, wn = w & 1;
-  float *out = dxp + (int64_t)s * c * H;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int h = n0 + wn * 128 + j * 32 + (lane & 31);
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int tok = m0 + wm * 128 + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-        if (tok < c && h < H) out[(int64_t)tok * H + h] = acc[i][j][e];
-      }
-    }
-}
-
-// dXc[tok][h] = bf16(sum_s dxp[s][tok][h]), 4 columns per thread (H % 8 == 0).
-__global__ void dx_reduce_kernel(const float *__restrict__ dxp, int splitk, int c, int H,
-                                 uint16_t *__restrict__ dXc) {
-  const int64_t n4 = (int64_t)c * H / 4;
-  const int64_t stride = (int64_t)c * H;
-  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n4;
-       i += (int64_t)gridDim.x * blockDim.x) {
-    float4 a = ((const float4 *)dxp)[i];
-    for (int s = 1; s < splitk; ++s) {
-      float4 b = ((const float4 *)(dxp + s * stride))[i];
-      a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
-    }
-    uint2 pk;
-    pk.x = pack_bf16x2(a.x, a.y);
-    pk.y = pack_bf16x2(a.z, a.w);
-    ((uint2 *)dXc)[i] = pk;
-  }
-}
-
 // ---------------------------------------------------------------- dW
 // dW[v][h] (+)= sum over the chunk's tokens of G[tok][v] X[tok][h], in
 // 256 x 256 tiles, one workgroup per CU; G from Zp and X from Xp, both read
@@ -1130,9 +1068,12 @@ struct DwOld {
   }
 };
 
-// Write a wave's 128 x 128 quarter: dW = acc, or dW + acc with OLD.  CHECK
-// masks rows >= vlim and columns >= hlim (relative to the quarter).
-template <class T, bool OLD, bool CHECK, class A>
+// Write a wave's 128 x 128 quarter of an fp32 tile with row stride ldb
+// bytes (rs: the quarter's first element; voff: the lane's byte offset,
+// column and row half): out = acc, or out + acc with OLD.  CHECK masks rows
+// >= vlim and columns >= hlim (relative to the quarter).  AUX: the accesses'
+// cache policy.
+template <class T, bool OLD, bool CHECK, int AUX = kDwAux, class A>
 __device__ __forceinline__ void dw_store(const A &acc, __amdgpu_buffer_rsrc_t rs, int voff, int ldb,
                                          int vlim, int hlim) {
   const int lane = threadIdx.x & 63;
@@ -1146,7 +1087,7 @@ __device__ __forceinline__ void dw_store(const A &acc, __amdgpu_buffer_rsrc_t rs
       if constexpr (OLD) {
         if (col_ok && (!CHECK || row + 4 * (lane >> 5) < vlim))
           old[e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, voff + 128 * j,
-                                                                                  row_off(row, ldb), kDwAux));
+                                                                                  row_off(row, ldb), AUX));
       }
     });
     static_for<0, 16>([&](auto ee) {
@@ -1157,7 +1098,7 @@ __device__ __forceinline__ void dw_store(const A &acc, __amdgpu_buffer_rsrc_t rs
       if constexpr (OLD) x += old[e];
       if (col_ok && (!CHECK || row + 4 * (lane >> 5) < vlim))
         __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, x), rs, voff + 128 * j,
-                                              row_off(row, ldb), kDwAux);
+                                              row_off(row, ldb), AUX);
     });
     // one block's old values at a time in registers
     asm volatile("" ::: "memory");
@@ -1271,6 +1212,65 @@ __global__ __launch_bounds__(NTHREADS, 1) void dw_chain_kernel(
     rs = rsn;
     warm = true;
     rb = (rb + nk) % T::STAGES;
+  }
+}
+
+// ---------------------------------------------------------------- dX (split-K)
+// Unit (s, mt, nt): dxp[s][tok][h] = sum over vocabulary in split s of
+// G[tok][v] W[v][h].  G from Zp (rows = tokens, k = vocabulary), W read
+// transposed in place (its columns, the hidden ids, are the operand rows;
+// its rows, the vocabulary, are k), so no copy of W is made.
+template <class T = DxTile, int RPM = kDxRpm, int CSP = kDxCsp>
+__global__ __launch_bounds__(NTHREADS, 1) void dx_kernel(
+    const uint16_t *__restrict__ Gp, int64_t nks_z, const uint16_t *__restrict__ W,
+    int c, int H, int V, int64_t ksplit, int nmt, int nnt, float *__restrict__ dxp) {
+  static_assert(T::BM == 256 && T::BN == 256, "256 x 256 output tiles");
+  __shared__ __attribute__((aligned(1024))) char smem[T::LDS];
+  const int unit = xcd_remap(blockIdx.x, gridDim.x);
+  const int per = nmt * nnt;
+  // token tile fastest: the few token tiles of a split share each W block
+  const int s = unit / per, rem = unit - s * per;
+  const int nt = rem / nmt, mt = rem - nt * nmt;
+  const int m0 = mt * T::BM, n0 = nt * T::BN;
+  const int64_t kb = (int64_t)s * ksplit;
+  const int64_t ke = kb + ksplit < V ? kb + ksplit : V;
+  const int klen = (int)(ke - kb);
+
+  const Op a{(const char *)(Gp + ((int64_t)mt * nks_z + (kb >> 5)) * 8192), 0, 0, nullptr};
+  const Op b{(const char *)(W + n0), 2 * (int64_t)H, kb, (const char *)(W + (int64_t)V * H)};
+  f32x16 acc[4][4];
+  zero_acc<T>(acc);
+  mainloop<T, RPM, CSP>(a, b, klen, smem, acc);
+
+  // the partials straight from the accumulators, as dW stores its tiles
+  // (plain stores: dx_reduce reads them right after); only tiles that reach
+  // past c tokens or H columns check their rows and columns
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = w >> 1, wn = w & 1;
+  const int r0 = m0 + wm * T::WM, c0 = n0 + wn * T::WN;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      dxp + (int64_t)s * c * H + (int64_t)r0 * H + c0, (short)0, 0x7fffffff, 0x00020000);
+  const int voff = ((lane >> 5) * 4 * H + (lane & 31)) * 4, ldb = H * 4;
+  if (m0 + T::BM <= c && n0 + T::BN <= H) dw_store<T, false, false, 0>(acc, rs, voff, ldb, 0, 0);
+  else dw_store<T, false, true, 0>(acc, rs, voff, ldb, c - r0, H - c0);
+}
+
+// dXc[tok][h] = bf16(sum_s dxp[s][tok][h]), 4 columns per thread (H % 8 == 0).
+__global__ void dx_reduce_kernel(const float *__restrict__ dxp, int splitk, int c, int H,
+                                 uint16_t *__restrict__ dXc) {
+  const int64_t n4 = (int64_t)c * H / 4;
+  const int64_t stride = (int64_t)c * H;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n4;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    float4 a = ((const float4 *)dxp)[i];
+    for (int s = 1; s < splitk; ++s) {
+      float4 b = ((const float4 *)(dxp + s * stride))[i];
+      a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
+    }
+    uint2 pk;
+    pk.x = pack_bf16x2(a.x, a.y);
+    pk.y = pack_bf16x2(a.z, a.w);
+    ((uint2 *)dXc)[i] = pk;
   }
 }
 
