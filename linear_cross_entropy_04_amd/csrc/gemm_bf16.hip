@@ -19,9 +19,10 @@
 // blocks.  Operands flow global -> LDS through direct-to-LDS buffer loads
 // (buffer_load_dwordx4 ... lds: lane l of a wave writes 16 bytes at the LDS
 // address in M0 + 16 l; the source is a buffer descriptor for the slice, a
-// scalar offset for the 1 KB piece and the lane's constant 16-byte offset) in
-// k-slices of 32, STAGES slices in flight, each admitted by an explicit vmcnt
-// wait and one s_barrier.
+// scalar offset for the 1 KB piece and the lane's constant 16-byte offset,
+// or for W read in place the lane's offset into the rows) in k-slices of 32,
+// STAGES slices in flight, each admitted by an explicit vmcnt wait and one
+// s_barrier.
 //
 // The packed layout (Xp, Zp): a matrix of R rows and K columns is stored
 // as 16 KB blocks of 256 rows x 32 columns; block (rt, ks) at element
@@ -547,8 +548,9 @@ struct Chain {
 // included, runs the same loop body (its reads of the half-step after the
 // last fetch a slice that nothing uses; a peeled last slice made the
 // compiler move the accumulators to other registers after the loop).  Packed
-// operands carry zero padding up to whole slices, so no copy needs a bounds
-// check.  The first Hook::NU iterations are unrolled; the caller guarantees
+// operands carry zero padding up to whole slices, so their copies need no
+// bounds check; row-major ones (W) end their descriptors at the matrix's
+// end.  The first Hook::NU iterations are unrolled; the caller guarantees
 // that the loop has at least that many (nk >= NU).
 template <class T, int RPM, int CSP, class Hook = NoHook, class Ch = NoChain>
 __device__ __forceinline__ void mainloop(const Op &a, const Op &b, int klen, char *smem,
