@@ -82,3 +82,41 @@ def test_smallest_shapes(N, H, V, chunk):
         check_loss(g["loss"], r.loss, "bf16")
         check_grad(g["dX"], r.dX, "bf16", "dX")
         check_grad(g["dW"], r.dW, "bf16", "dW")
+
+
+@pytest.mark.gpu
+@pytest.mark.timeout(600)
+def test_weight_over_4_gib():
+    """W of 4.4 GB (bf16, read in place by the forward and by dX) and dW of
+    8.8 GB: the copies' buffer descriptors start at their slice and clamp
+    their record counts, which differ for slices more than 4 GiB, between 2
+    and 4 GiB, and less than 2 GiB from W's end.  Two chunks of 100 tokens.
+    Checked against the fp64 oracle: the loss and every token's log-sum-exp
+    over the whole vocabulary, sampled rows of dX and of dW (the latter at
+    the vocabulary rows where the distance to W's end crosses 4 GiB and 2
+    GiB)."""
+    N, H, V, chunk = 200, 4096, 540_000, 100
+    assert V * H * 2 > 4 << 30
+    inp = datagen.make_custom(N, H, V, "bf16", seed=53, ignore_frac=0.1)
+    say(f"case N={N} H={H} V={V} chunk={chunk}: W {V * H * 2 / 2**30:.2f} GiB")
+    g = run_gpu(inp, chunk, II, poison=False, host_grads=False)
+    X64, W64 = inp.X_f64(), inp.W_f64()
+    loss, lse, rl, _ = oracle.loss_blocked(X64, W64, inp.labels, II, block=100)
+    check_loss(g["loss"], loss, "bf16")
+    assert np.max(np.abs(g["row_lse"] - lse) / np.abs(lse)) <= 1e-3
+    assert np.max(np.abs(g["row_loss"] - rl)) <= 1e-3 * np.max(np.abs(lse))
+    row_4g, row_2g = V - (4 << 30) // (2 * H), V - (2 << 30) // (2 * H)
+    lab = inp.labels[inp.labels != II]
+    vrows = datagen.sample_rows(V, 16, 59, must=(0, 1, row_4g - 1, row_4g, row_2g - 1, row_2g,
+                                                 V - 1, int(lab[0]), int(lab[-1])))
+    rows = datagen.sample_rows(N, 8, 61, must=(0, 99, 100, N - 1))
+    dX_ref = oracle.dX_rows(X64, W64, inp.labels, rows, II)
+    dW_ref = oracle.dW_rows(X64, W64, inp.labels, lse, vrows, II)
+    dX_t, dW_t = g["dX_t"], g["dW_t"]
+    check_grad(dX_t[torch.from_numpy(rows).to(dX_t.device)].double().cpu().numpy(), dX_ref, "bf16",
+               "dX sampled rows")
+    check_grad(dW_t[torch.from_numpy(vrows).to(dW_t.device)].double().cpu().numpy(), dW_ref, "bf16",
+               "dW sampled rows")
+    assert bool(torch.isfinite(dW_t).all()) and bool(torch.isfinite(dX_t.float()).all())
+    del g, dX_t, dW_t
+    torch.cuda.empty_cache()
