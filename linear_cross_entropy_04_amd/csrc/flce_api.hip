@@ -69,7 +69,7 @@ int64_t max_grid_items(const Plan &p) {
   int64_t m = C * 256;                                            // lse_combine
   if (p.dtype == FLCE_BF16) {
     const int64_t ct = cdiv(C, 256), vt = cdiv(V, 256);
-    m = std::max(m, ct * (p.nks_h / 2) * 256);                    // pack X_c
+    m = std::max(m, (ct * (p.nks_h / 2) + cdiv(H, 256) * (p.nks_c / 2)) * 256);  // pack X_c and X_c^T
     m = std::max(m, vt * ct * 256);                               // forward tiles
     m = std::max(m, ct * p.nks_z * 256);                          // dlogits
     m = std::max(m, (int64_t)p.splitk * ct * cdiv(H, 256) * 256); // dX
@@ -226,7 +226,9 @@ int chunk_forward(const Plan &p, char *ws, const void *W, int64_t ii, bool keep_
   if (p.dtype == FLCE_BF16) {
     uint16_t *Zp = (uint16_t *)(ws + p.off_z);
     uint16_t *Xp = (uint16_t *)(ws + p.off_xp);
-    LAUNCH(FLCE_K_PACK, launch_pack_bf16((const uint16_t *)io.Xc, io.c, Hi, Xp, p.nks_h, s));
+    // with the backward to follow, X_c transposed for dW too (same launch)
+    uint16_t *XpT = keep_z ? (uint16_t *)(ws + p.off_xpt) : nullptr;
+    LAUNCH(FLCE_K_PACK, launch_pack_bf16((const uint16_t *)io.Xc, io.c, Hi, Xp, p.nks_h, XpT, p.nks_c, s));
     LAUNCH(FLCE_K_FWD_TILE, launch_fwd_tile_bf16((const uint16_t *)W, Xp, io.lab, ii, io.c, Hi, Vi,
                                                  Zp, p.nks_z, pm, ps, pmt, zy, p.nvt, keep_z, s));
   } else {
@@ -247,7 +249,7 @@ int chunk_backward(const Plan &p, char *ws, const void *W, int64_t ii, const Chu
   const float *lse = (const float *)(ws + p.off_lse);
   if (p.dtype == FLCE_BF16) {
     uint16_t *Zp = (uint16_t *)(ws + p.off_z);
-    const uint16_t *Xp = (const uint16_t *)(ws + p.off_xp);
+    const uint16_t *XpT = (const uint16_t *)(ws + p.off_xpt);
     float *dxp = (float *)(ws + p.off_dxp);
     LAUNCH(FLCE_K_DLOGITS, launch_dlogits_bf16(Zp, p.nks_z, io.c, Vi,
                                                (const float *)(ws + p.off_pmt), lse, io.lab, ii,
@@ -255,7 +257,7 @@ int chunk_backward(const Plan &p, char *ws, const void *W, int64_t ii, const Chu
     LAUNCH(FLCE_K_DX_GEMM, launch_dx_bf16(Zp, p.nks_z, (const uint16_t *)W, io.c, Hi, Vi,
                                           p.splitk, p.ksplit, dxp, s));
     LAUNCH(FLCE_K_DX_REDUCE, launch_dx_reduce_bf16(dxp, p.splitk, io.c, Hi, (uint16_t *)io.dXc, s));
-    LAUNCH(FLCE_K_DW_GEMM, launch_dw_bf16(Zp, p.nks_z, Xp, p.nks_h, io.c, Hi, Vi, dW, io.acc_dw, s));
+    LAUNCH(FLCE_K_DW_GEMM, launch_dw_bf16(Zp, p.nks_z, XpT, p.nks_c, io.c, Hi, Vi, dW, io.acc_dw, s));
   } else {
     const float *Wf = (const float *)W;
     float *z = (float *)(ws + p.off_z);
@@ -392,6 +394,9 @@ void make_plan(int64_t N, int64_t H, int64_t V, int dtype, int64_t C, Plan *p) {
     o += align256(cpad * p->nks_z * 64);
     p->off_xp = o;                       // the chunk's X (rows = tokens)
     o += align256(cpad * p->nks_h * 64);
+    p->nks_c = cdiv(C, 256) * 8;
+    p->off_xpt = o;                      // the chunk's X transposed (rows = hidden), for dW
+    o += align256((size_t)round_up(H, 256) * p->nks_c * 64);
   } else {
     p->off_z = o;
     o += align256((size_t)C * p->ldz * esz);

@@ -36,12 +36,14 @@ struct Plan {
   int64_t C = 0;        // tokens per chunk (last chunk may be shorter)
   int64_t ldz = 0;      // fp32 path: leading dimension (elements) of the chunk logits scratch
   int64_t nks_z = 0, nks_h = 0;   // bf16 path: 32-column slices of V and H, padded to 256
+  int64_t nks_c = 0;    // bf16 path: 32-column slices of the chunk's tokens, padded to 256
   int64_t nvt = 0;      // vocabulary tiles = log-sum-exp partials per token
   int splitk = 0;       // K-splits of the dX GEMM (0: the fp32 path writes dX directly)
   int64_t ksplit = 0;   // vocabulary rows per split (multiple of 64)
   size_t off_z = 0, off_xp = 0, off_pm = 0, off_ps = 0, off_zy = 0, off_lse = 0,
          off_rowloss = 0, off_dxp = 0, off_scal = 0, total = 0;
   size_t off_pmt = 0;   // bf16 path: the partial maxima again, [partial][token]
+  size_t off_xpt = 0;   // bf16 path: the chunk's X transposed and packed (rows = hidden) for dW
 };
 
 // Fill *p for the given sizes and chunk (C >= 1, C <= N or N == 0).
@@ -68,9 +70,11 @@ hipError_t launch_scale(void *buf, int64_t n, int dtype, const float *scale, hip
 // along their rows or transposed, so no transposed copy is ever made.  W is
 // read where it lies, row-major [V][H], along its rows by the forward and
 // transposed by dX.
-// Pack a row-major [R][K] matrix into P (rows R padded to 256, nks_p slices).
+// Pack a row-major [R][K] matrix into P (rows R padded to 256, nks_p slices)
+// and, if PT is not null, its transpose into PT (K rows padded to 256, nks_t
+// slices of the R columns), in one launch.
 hipError_t launch_pack_bf16(const uint16_t *src, int R, int K, uint16_t *P, int64_t nks_p,
-                            hipStream_t s);
+                            uint16_t *PT, int64_t nks_t, hipStream_t s);
 // Logits tile GEMM with the log-sum-exp epilogue.  pm, ps: [token][partial]
 // maximum and sum of exp per 128 vocabulary ids; with store_z, Zp receives
 // bf16((z - m) log2 e) for the partial's maximum m, and pmt[partial * c +
@@ -91,7 +95,9 @@ hipError_t launch_dx_bf16(const uint16_t *Gp, int64_t nks_z, const uint16_t *W,
                           hipStream_t s);
 hipError_t launch_dx_reduce_bf16(const float *dxp, int splitk, int c, int H, uint16_t *dXc,
                                  hipStream_t s);
-hipError_t launch_dw_bf16(const uint16_t *Gp, int64_t nks_z, const uint16_t *Xp, int64_t nks_h,
+// dW (+)= G^T X_c with G from Zp (read transposed) and X_c^T packed (XpT,
+// rows = hidden, nks_c slices of the tokens).
+hipError_t launch_dw_bf16(const uint16_t *Gp, int64_t nks_z, const uint16_t *XpT, int64_t nks_c,
                           int c, int H, int V, float *dW, bool accumulate, hipStream_t s);
 
 // ---------------------------------------------------------------- cross-entropy on given logits

@@ -723,7 +723,7 @@ __device__ __forceinline__ float bf16_hi(uint32_t u) { return __builtin_bit_cast
 
 using FwdTile = Tile<256, 256, 4, ROW, PACKED>;        // A = W (row-major), B = Xp
 using DxTile = Tile<256, 256, 4, PACKED, ROWT>;        // A = G (Zp), B = W read transposed
-using DwTile = Tile<256, 256, 4, PACKED_T, PACKED_T>;  // A = G (Zp), B = Xp, both transposed
+using DwTile = Tile<256, 256, 4, PACKED_T, PACKED>;    // A = G (Zp) transposed, B = XpT
 constexpr int kDwGroup = 4;                            // vocabulary strips per group of dW tiles
 constexpr int kDwOcc = 1;                              // dW workgroups per CU
 // Main-loop schedules (reads per MFMA, MFMAs per copy), the fastest of those
@@ -733,13 +733,60 @@ constexpr int kDxRpm = 2, kDxCsp = 2;
 constexpr int kDwRpm = 1, kDwCsp = 2;
 
 // ---------------------------------------------------------------- packing
-// One workgroup per 256 rows x 64 columns (two packed blocks, 32 KB) of a
-// row-major bf16 matrix [R][K]: it reads the rows' 128-byte pieces (8 full
-// rows per wave instruction), places them in LDS in packed order, and writes
-// the two blocks as one contiguous 32 KB copy.  Zero outside [0, R) x [0, K).
+// Workgroups [0, ndirect): one per 256 rows x 64 columns (two packed blocks,
+// 32 KB) of a row-major bf16 matrix [R][K] (the chunk's X: rows = tokens,
+// k = hidden): it reads the rows' 128-byte pieces (8 full rows per wave
+// instruction), places them in LDS in packed order, and writes the two blocks
+// as one contiguous 32 KB copy.  Zero outside [0, R) x [0, K).
+// Workgroups from ndirect on: the transpose, a packed matrix of K rows and R
+// columns (rows = hidden, k = tokens), for dW's operand: one per 256 of its
+// rows x 64 of its columns.  Lane t loads an 8 x 8 group (8 consecutive
+// source rows, 16 bytes = 8 consecutive columns each; one wave instruction
+// reads two whole 512-byte row pieces), transposes it in registers, and
+// writes eight 16-byte slots (one transposed row, 8 consecutive k) to their
+// packed place in LDS; the two blocks then go out as one 32 KB copy.
+__device__ __forceinline__ void pack_transposed(const uint16_t *__restrict__ src, int R, int K,
+                                                uint16_t *__restrict__ PT, int64_t nks_t, int b,
+                                                char *lds) {
+  const int npair = (int)(nks_t >> 1);
+  const int rt = b / npair, kp = b - rt * npair;      // output rows 256 rt .., columns 64 kp ..
+  const int t = threadIdx.x, hg = t & 31, tg = t >> 5;
+  const int h0 = rt * 256 + 8 * hg, r0 = kp * 64 + 8 * tg;  // source columns h0 .., rows r0 ..
+  u32x4 in[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    in[j] = (r0 + j < R && h0 < K) ? *(const u32x4 *)(src + (int64_t)(r0 + j) * K + h0)
+                                    : u32x4{0u, 0u, 0u, 0u};
+  // out[q] = column h0 + q of source rows r0 .. r0 + 7: word w holds rows
+  // 2w (low half) and 2w + 1 (high half)
+  const int f = (tg >> 1) & 1, hh = tg & 1, blk = tg >> 2;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    u32x4 o;
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      o[w] = __builtin_amdgcn_perm(in[2 * w + 1][q >> 1], in[2 * w][q >> 1], (q & 1) ? 0x07060302u : 0x05040100u);
+    const int hr = 8 * hg + q;                          // row of the output block
+    const int off = (blk << 14) + ((((hr >> 5) << 1) + f) << 10) + (pk_slot(hr & 31, hh, f) << 4);
+    *(u32x4 *)(lds + off) = o;
+  }
+  __syncthreads();
+  uint16_t *dst = PT + (((int64_t)rt * nks_t + 2 * kp) << 13);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int q = i * 256 + t;
+    *(u32x4 *)(dst + q * 8) = *(const u32x4 *)(lds + q * 16);
+  }
+}
+
 __global__ __launch_bounds__(256) void pack_kernel(const uint16_t *__restrict__ src, int R, int K,
-                                                  uint16_t *__restrict__ P, int64_t nks_p) {
+                                                  uint16_t *__restrict__ P, int64_t nks_p, int ndirect,
+                                                  uint16_t *__restrict__ PT, int64_t nks_t) {
   __shared__ __attribute__((aligned(1024))) char lds[32768];
+  if ((int)blockIdx.x >= ndirect) {
+    pack_transposed(src, R, K, PT, nks_t, (int)blockIdx.x - ndirect, lds);
+    return;
+  }
   const int npair = (int)(nks_p >> 1);
   const int64_t rt = blockIdx.x / npair;
   const int kp = blockIdx.x - (int)(rt * npair);
@@ -1129,8 +1176,8 @@ __device__ __forceinline__ void dw_tile(int t, int nvt, int nht, int tails, int 
 template <bool SPREAD, class T = DwTile, int RPM = kDwRpm, int CSP = kDwCsp, int GROUP = kDwGroup,
           int OCC = kDwOcc>
 __global__ __launch_bounds__(NTHREADS, OCC) void dw_kernel(
-    const uint16_t *__restrict__ Gp, int64_t nks_z, const uint16_t *__restrict__ Xp,
-    int64_t nks_h, int c, int H, int V, int nvt, int nht, int tails, int vtail, int htail,
+    const uint16_t *__restrict__ Gp, int64_t nks_z, const uint16_t *__restrict__ XpT,
+    int64_t nks_c, int c, int H, int V, int nvt, int nht, int tails, int vtail, int htail,
     float *__restrict__ dW, int accumulate) {
   __shared__ __attribute__((aligned(1024))) char smem[T::LDS];
   int vt, ht;
@@ -1142,7 +1189,7 @@ __global__ __launch_bounds__(NTHREADS, OCC) void dw_kernel(
   f32x16 acc[T::MI][T::NI];
   zero_acc<T>(acc);
   const Op a{(const char *)(Gp + (int64_t)(m0 >> 5) * 8192), nks_z * 16384, 0};
-  const Op b{(const char *)(Xp + (int64_t)(n0 >> 5) * 8192), nks_h * 16384, 0};
+  const Op b{(const char *)(XpT + (int64_t)ht * nks_c * 8192), 0, 0, nullptr};
   // the wave's quarter of dW; offsets stay below 2^31 for H <= 2^20
   const int vq = m0 + wm * T::WM, hq = n0 + wn * T::WN;
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
@@ -1170,8 +1217,8 @@ __global__ __launch_bounds__(NTHREADS, OCC) void dw_kernel(
 // (c >= STAGES slices).
 template <bool OLD, class T = DwTile, int RPM = kDwRpm, int CSP = kDwCsp, int GROUP = kDwGroup>
 __global__ __launch_bounds__(NTHREADS, 1) void dw_chain_kernel(
-    const uint16_t *__restrict__ Gp, int64_t nks_z, const uint16_t *__restrict__ Xp,
-    int64_t nks_h, int c, int H, int V, int nvt, int nht, float *__restrict__ dW) {
+    const uint16_t *__restrict__ Gp, int64_t nks_z, const uint16_t *__restrict__ XpT,
+    int64_t nks_c, int c, int H, int V, int nvt, int nht, float *__restrict__ dW) {
   __shared__ __attribute__((aligned(1024))) char smem[T::LDS];
   const int ntiles = nvt * nht;
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1184,7 +1231,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void dw_chain_kernel(
     dw_tile<GROUP>(t, nvt, nht, 0, 0, 0, vt, ht);
     const int m0 = vt * T::BM, n0 = ht * T::BN;
     a = Op{(const char *)(Gp + (int64_t)(m0 >> 5) * 8192), nks_z * 16384, 0};
-    b = Op{(const char *)(Xp + (int64_t)(n0 >> 5) * 8192), nks_h * 16384, 0};
+    b = Op{(const char *)(XpT + (int64_t)ht * nks_c * 8192), 0, 0, nullptr};
     rs = __builtin_amdgcn_make_buffer_rsrc(dW + (int64_t)(m0 + wm * T::WM) * H + n0 + wn * T::WN, (short)0,
                                            0x7fffffff, 0x00020000);
   };
@@ -1300,10 +1347,12 @@ static int cu_count() {
 }
 
 hipError_t launch_pack_bf16(const uint16_t *src, int R, int K, uint16_t *P, int64_t nks_p,
-                            hipStream_t s) {
-  // nks_p is a multiple of 8, so column pairs of slices tile it exactly
-  const int64_t nwg = (int64_t)(R + 255) / 256 * (nks_p / 2);
-  hipLaunchKernelGGL(pack_kernel, dim3((unsigned)nwg), dim3(256), 0, s, src, R, K, P, nks_p);
+                            uint16_t *PT, int64_t nks_t, hipStream_t s) {
+  // nks_p and nks_t are multiples of 8, so column pairs of slices tile them exactly
+  const int64_t ndirect = (int64_t)(R + 255) / 256 * (nks_p / 2);
+  const int64_t ntrans = PT ? (int64_t)(K + 255) / 256 * (nks_t / 2) : 0;
+  hipLaunchKernelGGL(pack_kernel, dim3((unsigned)(ndirect + ntrans)), dim3(256), 0, s, src, R, K, P, nks_p,
+                     (int)ndirect, PT, nks_t);
   return hipGetLastError();
 }
 
@@ -1355,7 +1404,7 @@ hipError_t launch_dx_reduce_bf16(const float *dxp, int splitk, int c, int H, uin
   return hipGetLastError();
 }
 
-hipError_t launch_dw_bf16(const uint16_t *Gp, int64_t nks_z, const uint16_t *Xp, int64_t nks_h,
+hipError_t launch_dw_bf16(const uint16_t *Gp, int64_t nks_z, const uint16_t *XpT, int64_t nks_c,
                           int c, int H, int V, float *dW, bool accumulate, hipStream_t s) {
   const int nvt = (V + DwTile::BM - 1) / DwTile::BM, nht = (H + DwTile::BN - 1) / DwTile::BN;
   const int nvi = V / DwTile::BM, nhi = H / DwTile::BN;        // tiles inside V, H
@@ -1376,20 +1425,20 @@ hipError_t launch_dw_bf16(const uint16_t *Gp, int64_t nks_z, const uint16_t *Xp,
       const int nres = ncu >= 8 ? ncu / 8 * 8 : ncu;
       const dim3 grid(ntiles < nres ? ntiles : nres);
       if (accumulate)
-        hipLaunchKernelGGL((dw_chain_kernel<true>), grid, block, 0, s, Gp, nks_z, Xp, nks_h, c, H, V, nvi, nhi, dW);
+        hipLaunchKernelGGL((dw_chain_kernel<true>), grid, block, 0, s, Gp, nks_z, XpT, nks_c, c, H, V, nvi, nhi, dW);
       else
-        hipLaunchKernelGGL((dw_chain_kernel<false>), grid, block, 0, s, Gp, nks_z, Xp, nks_h, c, H, V, nvi, nhi,
+        hipLaunchKernelGGL((dw_chain_kernel<false>), grid, block, 0, s, Gp, nks_z, XpT, nks_c, c, H, V, nvi, nhi,
                            dW);
     } else {
-      hipLaunchKernelGGL((dw_kernel<true>), dim3(ntiles), block, 0, s, Gp, nks_z, Xp, nks_h, c, H, V, nvi, nhi, 0,
+      hipLaunchKernelGGL((dw_kernel<true>), dim3(ntiles), block, 0, s, Gp, nks_z, XpT, nks_c, c, H, V, nvi, nhi, 0,
                          0, 0, dW, 1);
     }
     const int ntail = (vtail ? nht : 0) + (htail ? nvt - vtail : 0);
     if (ntail > 0)
-      hipLaunchKernelGGL((dw_kernel<false>), dim3(ntail), block, 0, s, Gp, nks_z, Xp, nks_h, c, H, V, nvt, nht, 1,
+      hipLaunchKernelGGL((dw_kernel<false>), dim3(ntail), block, 0, s, Gp, nks_z, XpT, nks_c, c, H, V, nvt, nht, 1,
                          vtail, htail, dW, accumulate ? 1 : 0);
   } else {
-    hipLaunchKernelGGL((dw_kernel<false>), dim3(nvt * nht), block, 0, s, Gp, nks_z, Xp, nks_h, c, H, V, nvt, nht,
+    hipLaunchKernelGGL((dw_kernel<false>), dim3(nvt * nht), block, 0, s, Gp, nks_z, XpT, nks_c, c, H, V, nvt, nht,
                        0, 0, 0, dW, accumulate ? 1 : 0);
   }
   return hipGetLastError();
