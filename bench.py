@@ -56,8 +56,8 @@ def kernel_work(name, chunks, H, V):
         return "hbm", b, "byte"
     if name == "dlogits":                      # bf16 logits read, G written in place
         return "hbm", sum(4.0 * c * V for c in chunks), "byte"
-    if name == "pack_x":                       # bf16 X chunk read and written packed
-        return "hbm", sum(4.0 * c * H for c in chunks), "byte"
+    if name == "pack_x":                       # bf16 X chunk read, written packed and packed transposed
+        return "hbm", sum(6.0 * c * H for c in chunks), "byte"
     if name == "pair_rows":                    # X rows gathered, dX rows scattered (bf16)
         return "hbm", sum(8.0 * c * H for c in chunks), "byte"
     return "hbm", None, "byte"
