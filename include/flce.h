@@ -80,7 +80,8 @@ typedef enum {
  *
  * The workspace of a call holds, for one chunk of C tokens: its logits, then
  * dlogits, in place ([C, V] bf16, or fp32 on the fp32 path), its X in the
- * GEMM operand layout (bf16 path), the per-vocabulary-tile log-sum-exp
+ * GEMM operand layout and, for the backward, transposed in it too (bf16
+ * path), the per-vocabulary-tile log-sum-exp
  * partials, per-token statistics and the split-K partial sums of dX; plus
  * one fp32 per-token loss for all N tokens.  Only that last array grows with
  * N; nothing grows with W beyond the chunk's logits (W is read in place).
@@ -396,7 +397,7 @@ enum {
   FLCE_K_DX_REDUCE = 5,   /* dX split-K reduction */
   FLCE_K_DW_GEMM = 6,     /* dW GEMM */
   FLCE_K_FINAL = 7,       /* final mean loss, fills */
-  FLCE_K_PACK = 8,        /* per-chunk packing of X into the GEMM operand layout */
+  FLCE_K_PACK = 8,        /* per-chunk packing of X (and X transposed) into the GEMM operand layout */
   FLCE_K_CE_ROWS = 9,     /* cross-entropy on given logits, one workgroup per row */
   FLCE_K_PAIRS = 10,      /* preference losses: label pass, per-pair step, final loss */
   FLCE_K_PAIR_ROWS = 11,  /* preference losses: gathering a chunk's rows, scattering dX */
