@@ -405,6 +405,13 @@ enum {
 };
 int flce_profile_enable(int enable);
 int flce_profile_read(double *ms, int64_t *launches, int n);
+/*
+ * Which kernel classes get events while timing is enabled: bit k of
+ * class_mask for class k (process-wide; all classes until first called).
+ * Lets a caller time a run with events on a few launches only, since every
+ * event pair costs the stream a little.  Host only; returns FLCE_OK.
+ */
+int flce_profile_select(uint32_t class_mask);
 
 /* Static name of a kernel class (FLCE_K_*), "" if out of range. */
 const char *flce_kernel_name(int k);

@@ -24,7 +24,7 @@ __all__ = [
     "FLCE_F32", "FLCE_BF16", "FLCEError", "flce_workspace_bytes", "flce_plan", "flce_fwd_bwd",
     "flce_fwd_bwd_noalloc", "flce_noalloc_scratch_bytes",
     "flce_fwd", "flce_fwd_bwd_ex", "flce_fwd_ex", "REDUCTIONS", "flce_scale_inplace", "flce_status_string", "flce_last_error", "lib_path",
-    "flce_profile_enable", "flce_profile_read",
+    "flce_profile_enable", "flce_profile_read", "flce_profile_select",
     "workspace", "loss", "FusedLinearCrossEntropyLoss",
     "flce_ce_workspace_bytes", "flce_ce_fwd_bwd", "flce_ce_fwd", "cross_entropy",
     "flce_orpo_workspace_bytes", "flce_orpo_fwd_bwd", "flce_orpo_fwd", "orpo_loss",
@@ -141,6 +141,8 @@ def _load():
     l.flce_profile_enable.restype = _i32
     l.flce_profile_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i64), _i32]
     l.flce_profile_read.restype = _i32
+    l.flce_profile_select.argtypes = [ctypes.c_uint32]
+    l.flce_profile_select.restype = _i32
     l.flce_kernel_name.argtypes = [_i32]
     l.flce_kernel_name.restype = ctypes.c_char_p
     _lib = l
@@ -161,6 +163,23 @@ KERNEL_CLASSES = 12
 def flce_profile_enable(enable: bool = True) -> None:
     """Turn per-kernel event timing on or off (process-wide)."""
     _load().flce_profile_enable(1 if enable else 0)
+
+
+def flce_profile_select(classes=None) -> None:
+    """Time only these kernel classes (names as flce_profile_read reports
+    them, or FLCE_K_* ids) while timing is on; None: every class."""
+    if classes is None:
+        mask = 0xFFFFFFFF
+    else:
+        l = _load()
+        names = {l.flce_kernel_name(k).decode(): k for k in range(KERNEL_CLASSES)}
+        mask = 0
+        for c in classes:
+            k = names[c] if isinstance(c, str) else int(c)
+            if not 0 <= k < KERNEL_CLASSES:
+                raise ValueError(f"kernel class {c!r}")
+            mask |= 1 << k
+    _load().flce_profile_select(mask)
 
 
 def flce_profile_read() -> dict:

@@ -143,6 +143,7 @@ bool misaligned(const void *p, uintptr_t a) { return ((uintptr_t)p % a) != 0; }
 // ---------------------------------------------------------------- kernel timing
 struct Profiler {
   std::atomic<bool> on{false};
+  std::atomic<uint32_t> mask{0xffffffffu};   // kernel classes timed while on
   std::mutex mu;
   struct Rec {
     int cls;
@@ -170,7 +171,8 @@ Profiler &prof() {
 template <class F>
 hipError_t timed(int cls, hipStream_t s, F &&launch) {
   Profiler &P = prof();
-  if (!P.on.load(std::memory_order_relaxed)) return launch();
+  if (!P.on.load(std::memory_order_relaxed) || !((P.mask.load(std::memory_order_relaxed) >> cls) & 1u))
+    return launch();
   hipEvent_t a, b;
   {
     std::lock_guard<std::mutex> g(P.mu);
@@ -1035,6 +1037,11 @@ FLCE_API int flce_scale_inplace(void *buf, int64_t n, int dtype, const float *sc
 
 FLCE_API int flce_profile_enable(int enable) {
   prof().on.store(enable != 0);
+  return FLCE_OK;
+}
+
+FLCE_API int flce_profile_select(uint32_t class_mask) {
+  prof().mask.store(class_mask);
   return FLCE_OK;
 }
 

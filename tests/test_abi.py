@@ -151,6 +151,18 @@ def test_kernel_classes_match_the_header(lib):
     assert lib.flce_kernel_name(fl.KERNEL_CLASSES).decode() == ""
 
 
+def test_profile_select(lib):
+    # host only: the class mask is stored; the binding maps names to bits
+    assert lib.flce_profile_select(ctypes.c_uint32(1 << 6)) == fl.FLCE_OK
+    fl.flce_profile_select(["dw_gemm", "fwd_tile"])
+    fl.flce_profile_select([0, 11])
+    with pytest.raises(KeyError):
+        fl.flce_profile_select(["no such kernel"])
+    with pytest.raises(ValueError):
+        fl.flce_profile_select([fl.KERNEL_CLASSES])
+    fl.flce_profile_select(None)                      # every class again
+
+
 def test_status_strings(lib):
     for s in range(6):
         assert fl.flce_status_string(s) and fl.flce_status_string(s) != "unknown status"
