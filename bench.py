@@ -119,6 +119,8 @@ def cpu_baseline(inp, n_tok):
                       f"V={inp.wl.V}), fp64 loss + dX + dW on the host"}
 
 
+KERNELS_FROM = "an untimed pass of the same steps, events around every launch"
+ROOFLINE_FROM = "the timed steps, events around the dominant kernel's launches only"
 CE_N, CE_V = 8192, 128256     # the Llama-3-8B head's logits: 8 x 1024 tokens x vocabulary
 
 
@@ -163,6 +165,37 @@ def roofline(dom, tot_n, steps, chunks, H, V, workload):
             "traffic": counter_traffic(dom, workload), "avg_ms": round(avg, 5)}
 
 
+def timed_steps(step, steps, chunks, H, V, workload):
+    """Per-kernel times from an untimed pass of `steps` steps with events
+    around every launch, then `steps` timed steps with events around the
+    dominant kernel class's launches only (its live duration for the
+    roofline; about 50 event pairs per step would cost the stream a
+    fraction of a millisecond).  Returns (ms per timed step, the kernels
+    table, the roofline, the last step's result)."""
+    import torch
+    import linear_cross_entropy_04_amd as fl
+    fl.flce_profile_select(None)
+    fl.flce_profile_enable(True)
+    fl.flce_profile_read()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    kernels, _ = kernel_summary(fl.flce_profile_read(), steps, chunks, H, V, workload)
+    dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
+    fl.flce_profile_select([dom])
+    fl.flce_profile_read()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        res = step()
+    torch.cuda.synchronize()
+    ms = 1e3 * (time.perf_counter() - t0) / steps
+    prof = fl.flce_profile_read()
+    fl.flce_profile_enable(False)
+    fl.flce_profile_select(None)
+    return ms, kernels, roofline(dom, prof[dom], steps, chunks, H, V, workload), res
+
+
 def copy_reference(mib, dev):
     """One plain device copy of `mib` MiB: a transfer of known size that the
     hardware byte counters of the same run can be scaled by."""
@@ -202,6 +235,7 @@ def bench_ce(args):
     for _ in range(max(args.warmup - 1, 0)):
         fl.flce_ce_fwd_bwd(L, y, -100, ws, stream=stream)
     torch.cuda.synchronize()
+    fl.flce_profile_select(["ce_rows"])        # events around the row kernel only
     fl.flce_profile_enable(True)
     fl.flce_profile_read()
     torch.cuda.synchronize()
@@ -212,6 +246,7 @@ def bench_ce(args):
     ms = 1e3 * (time.perf_counter() - t1) / args.steps
     prof = fl.flce_profile_read()
     fl.flce_profile_enable(False)
+    fl.flce_profile_select(None)
     tot, n = prof["ce_rows"]
     k_ms = tot / n
     traffic = 3.0 * CE_N * CE_V * 2
@@ -298,19 +333,10 @@ def bench_orpo(args):
     for _ in range(args.warmup):
         loss, nll = step()
     torch.cuda.synchronize()
-    fl.flce_profile_enable(True)
-    fl.flce_profile_read()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    for _ in range(args.steps):
-        loss, nll = step()
-    torch.cuda.synchronize()
-    ms = 1e3 * (time.perf_counter() - t1) / args.steps
-    prof = fl.flce_profile_read()
-    fl.flce_profile_enable(False)
-    tflops = 6.0 * N * H * V / (ms * 1e-3) / 1e12
     chunks = [2 * chunk_pairs * T] * (B // chunk_pairs)
-    kernels, roof = kernel_summary(prof, args.steps, chunks, H, V, f"llama3-8b-head-{kind}")
+    ms, kernels, roof, (loss, nll) = timed_steps(step, args.steps, chunks, H, V,
+                                                 f"llama3-8b-head-{kind}")
+    tflops = 6.0 * N * H * V / (ms * 1e-3) / 1e12
     out = {
         "metric": f"{kind.upper()} fused-linear preference loss fwd+bwd tokens/s, Llama-3-8B head",
         "value": round(N / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
@@ -322,7 +348,8 @@ def bench_orpo(args):
         "config": {"workload": f"llama3-8b-head-{kind}", "pairs": B, "T": T, "N": N, "H": H,
                    "V": V, "chunk_pairs": chunk_pairs, **pp, "workspace_bytes": nbytes},
         "tflops": round(tflops, 2), "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
-        "loss": loss, "nll": nll, "kernels": kernels, "roofline": roof,
+        "loss": loss, "nll": nll, "kernels": kernels, "kernels_from": KERNELS_FROM,
+        "roofline": roof, "roofline_from": ROOFLINE_FROM,
     }
     if not args.no_cpu_baseline:
         import oracle
@@ -392,19 +419,9 @@ def bench_kto(args):
     for _ in range(args.warmup):
         loss = step()
     torch.cuda.synchronize()
-    fl.flce_profile_enable(True)
-    fl.flce_profile_read()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    for _ in range(args.steps):
-        loss = step()
-    torch.cuda.synchronize()
-    ms = 1e3 * (time.perf_counter() - t1) / args.steps
-    prof = fl.flce_profile_read()
-    fl.flce_profile_enable(False)
-    tflops = 6.0 * N * H * V / (ms * 1e-3) / 1e12
     chunks = [chunk_seqs * T] * (S // chunk_seqs)
-    kernels, roof = kernel_summary(prof, args.steps, chunks, H, V, "llama3-8b-head-kto")
+    ms, kernels, roof, loss = timed_steps(step, args.steps, chunks, H, V, "llama3-8b-head-kto")
+    tflops = 6.0 * N * H * V / (ms * 1e-3) / 1e12
     out = {
         "metric": "KTO fused-linear preference loss fwd+bwd tokens/s, Llama-3-8B head",
         "value": round(N / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
@@ -416,7 +433,8 @@ def bench_kto(args):
         "config": {"workload": "llama3-8b-head-kto", "sequences": S, "T": T, "N": N, "H": H,
                    "V": V, "chunk_seqs": chunk_seqs, **pp, "workspace_bytes": nbytes},
         "tflops": round(tflops, 2), "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
-        "loss": loss, "kernels": kernels, "roofline": roof,
+        "loss": loss, "kernels": kernels, "kernels_from": KERNELS_FROM,
+        "roofline": roof, "roofline_from": ROOFLINE_FROM,
     }
     if not args.no_cpu_baseline:
         import oracle
@@ -523,31 +541,7 @@ def main():
         loss = step()
     torch.cuda.synchronize()
     chunks = [min(C, N - c0) for c0 in range(0, N, C)]
-
-    # per-kernel times: the same number of steps, untimed, with events around
-    # every launch (on the launch stream)
-    fl.flce_profile_select(None)
-    fl.flce_profile_enable(True)
-    fl.flce_profile_read()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    kernels, _ = kernel_summary(fl.flce_profile_read(), args.steps, chunks, H, V, wl.name)
-    dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
-
-    # timed steps, with events around the dominant kernel's launches only:
-    # its live duration for the roofline, at a fraction of the event cost
-    fl.flce_profile_select([dom])
-    fl.flce_profile_read()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        loss = step()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    prof = fl.flce_profile_read()
-    fl.flce_profile_enable(False)
-    fl.flce_profile_select(None)
+    ms, kernels, roof, loss = timed_steps(step, args.steps, chunks, H, V, wl.name)
 
     # the same steps without events, to show what the event records cost
     torch.cuda.synchronize()
@@ -569,10 +563,8 @@ def main():
         torch.cuda.synchronize()
         fwd_ms = 1e3 * (time.perf_counter() - t2) / args.steps
 
-    ms = 1e3 * elapsed / args.steps
     flops = 6.0 * N * H * V
     tflops = flops / (ms * 1e-3) / 1e12
-    roof = roofline(dom, prof[dom], args.steps, chunks, H, V, wl.name)
 
     out = {
         "metric": METRIC,
@@ -598,9 +590,9 @@ def main():
         "fwd_only_ms_per_step": round(fwd_ms, 4) if fwd_ms is not None else None,
         "loss": loss,
         "kernels": kernels,
-        "kernels_from": "an untimed pass of the same steps, events around every launch",
+        "kernels_from": KERNELS_FROM,
         "roofline": roof,
-        "roofline_from": "the timed steps, events around the dominant kernel's launches only",
+        "roofline_from": ROOFLINE_FROM,
     }
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle on {args.cpu_sample_tokens} tokens ...")
