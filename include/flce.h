@@ -381,9 +381,10 @@ int flce_kto_reference_point(const void *X, const void *W, const int64_t *labels
 int flce_scale_inplace(void *buf, int64_t n, int dtype, const float *scale, void *stream);
 
 /*
- * Per-kernel timing.  While enabled (process-wide), every kernel that
- * flce_fwd_bwd / flce_fwd launch is bracketed by a pair of HIP events on the
- * call's stream.  flce_profile_read waits for the recorded events, writes the
+ * Per-kernel timing.  While enabled (process-wide), every kernel launch of
+ * the entry points above whose class is selected (flce_profile_select; all
+ * classes by default) is bracketed by a pair of HIP events on the call's
+ * stream.  flce_profile_read waits for the recorded events, writes the
  * summed milliseconds and the launch count of each kernel class k < n
  * (FLCE_K_*) into ms[k] and launches[k] (either may be NULL), and clears the
  * records.  Both return FLCE_OK or FLCE_EHIP.
