@@ -489,6 +489,9 @@ def main():
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the multi-GPU "
               "sharding of this path is a design only)", file=sys.stderr)
         sys.exit(2)
+    if args.steps < 1 or args.warmup < 0:
+        print("bench.py needs --steps >= 1 and --warmup >= 0", file=sys.stderr)
+        sys.exit(2)
 
     if args.op == "ce":
         bench_ce(args)
