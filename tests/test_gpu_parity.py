@@ -98,6 +98,42 @@ def test_empty_input():
     assert np.all(g["dW"] == 0.0)
 
 
+@pytest.mark.parametrize("ignored", [False, True])
+def test_non_finite_input_propagates(ignored):
+    """A NaN in one row of X is not checked and propagates as the oracle's
+    plain definition does: a scored row makes the loss, its dX row and all of
+    dW NaN; an ignored row leaves the loss and every dX row finite (its G row
+    is exactly 0) and turns only dW's column of the NaN NaN (0 times NaN)."""
+    import copy
+    inp = copy.copy(datagen.make_custom(300, 64, 1000, "bf16", seed=5, ignore_frac=0.1))
+    X = inp.X.copy()
+    X[17, 5] = 0x7FC0                                  # bf16 quiet NaN
+    inp.X = X
+    labels = inp.labels.copy()
+    labels[17] = II if ignored else 458
+    say(f"case non-finite N=300 H=64 V=1000 bf16 seed=5 chunk=128 row 17 ignored={ignored}")
+    g = run_gpu(inp, 128, labels=labels)
+    r = oracle.flce(inp.X_f64(), inp.W_f64(), labels)
+    finite_rows = np.ones(300, dtype=bool)
+    if ignored:
+        check_loss(g["loss"], r.loss, "bf16")
+        assert np.all(g["dX"][17] == 0.0)
+    else:
+        assert math.isnan(g["loss"]) and math.isnan(r.loss)
+        assert np.all(np.isnan(g["dX"][17]))
+        finite_rows[17] = False
+    assert np.all(np.isfinite(g["dX"][finite_rows]))
+    check_grad(g["dX"][finite_rows], r.dX[finite_rows], "bf16", "dX (finite rows)")
+    nan_cols = np.zeros(64, dtype=bool)
+    nan_cols[5] = True
+    if not ignored:
+        nan_cols[:] = True
+    assert np.array_equal(np.isnan(g["dW"]).all(axis=0), nan_cols)
+    assert np.array_equal(np.isnan(r.dW).all(axis=0), nan_cols)
+    if ignored:
+        check_grad(g["dW"][:, ~nan_cols], r.dW[:, ~nan_cols], "bf16", "dW (finite columns)")
+
+
 def test_invalid_label_reports_elabel():
     inp = datagen.make_custom(50, 64, 100, "bf16", seed=4)
     labels = inp.labels.copy()
