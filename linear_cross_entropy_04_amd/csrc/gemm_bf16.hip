@@ -990,7 +990,9 @@ __global__ __launch_bounds__(256) void dlogits_kernel(
     const float *__restrict__ wrow_c, const Scalars *__restrict__ sc) {
   // slot u = (blk * 16 + f) * 64 + sl of block blk = (rt, ks); thread t of the
   // block takes f = t / 64 + 4 k, sl = t % 64: slot sl = 32 h + (r % 32 ^ 4 h ^ 8 (f % 2))
-  const int64_t blk = blockIdx.x;
+  // blocks in reverse order: dW, which reads G next, measured 2% faster per
+  // chunk after this order than after the forward one
+  const int64_t blk = (int64_t)gridDim.x - 1 - blockIdx.x;
   const int64_t rt = blk / nks_z, ks = blk - rt * nks_z;
   const int w = threadIdx.x >> 6, sl = threadIdx.x & 63, h = sl >> 5;
   const int v0 = (int)(ks * 32) + (w & 1) * 16 + h * 8;
