@@ -61,6 +61,27 @@ def test_bf16_ragged(N, H, V, chunk):
     _full_check(inp, chunk)
 
 
+def _random_shapes(count, seed):
+    """Seeded shapes off every tile grid: N, V and the chunk anywhere in
+    their ranges (chunk 0 lets the planner choose), H a multiple of 8 (the
+    bf16 path's requirement)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(count):
+        N = int(rng.integers(1, 1600))
+        H = 8 * int(rng.integers(1, 97))
+        V = int(rng.integers(1, 6000))
+        chunk = int(rng.choice([0, int(rng.integers(1, N + 1)), int(rng.integers(1, 1100))]))
+        out.append((N, H, V, chunk))
+    return out
+
+
+@pytest.mark.parametrize("N,H,V,chunk", _random_shapes(12, 20261203))
+def test_bf16_random_shapes(N, H, V, chunk):
+    inp = datagen.make_custom(N, H, V, "bf16", seed=N * 7 + V, ignore_frac=0.1)
+    _full_check(inp, chunk)
+
+
 @pytest.mark.parametrize("N,H,V,chunk", [(77, 33, 130, 32), (200, 64, 1000, 0)])
 def test_fp32_ragged(N, H, V, chunk):
     inp = datagen.make_custom(N, H, V, "f32", seed=N, ignore_frac=0.1)
