@@ -50,6 +50,27 @@ def _run(Zraw, y, kind, reduction, grad_rows=None, grad=True):
     return loss, L, rl.double().cpu().numpy(), rs.double().cpu().numpy(), lp.double().cpu().numpy()
 
 
+def _random_ce_shapes(count, seed):
+    """Seeded (kind, N, V): any row count and vocabulary size, including
+    vocabularies shorter than one thread's vector and longer than a row's
+    first pass holds in cache."""
+    rng = np.random.default_rng(seed)
+    return [(str(rng.choice(["bf16", "f32"])), int(rng.integers(1, 700)),
+             int(rng.choice([rng.integers(1, 64), rng.integers(64, 9000), rng.integers(9000, 140000)])))
+            for _ in range(count)]
+
+
+@pytest.mark.parametrize("kind,N,V", _random_ce_shapes(8, 20261204))
+def test_ce_random_shapes(kind, N, V):
+    Zraw, Z, y = _logits(N, V, kind, seed=N * 11 + V)
+    loss, L, rl, rs, lp = _run(Zraw, y, kind, "mean")
+    r = oracle.cross_entropy(Z, y, II, "mean")
+    check_loss(loss, r.loss, kind)
+    check_grad(L.double().cpu().numpy(), r.dZ, kind, "dlogits")
+    tol = 1e-3 if kind == "bf16" else 1e-5
+    assert np.max(np.abs(rs - r.lse) / np.abs(r.lse)) <= tol
+
+
 @pytest.mark.parametrize("kind,N,V", [("bf16", 300, 4096), ("bf16", 257, 1003),
                                       ("f32", 200, 1000), ("f32", 65, 999)])
 @pytest.mark.parametrize("reduction", ["mean", "sum", "none"])
