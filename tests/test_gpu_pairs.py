@@ -92,6 +92,27 @@ def test_pair_parity(kind, dtype, B, T, H, V, chunk_pairs):
     _check(out, _oracle(kind, inp, B, ref), kind, dtype)
 
 
+def _random_pair_shapes(count, seed):
+    """Seeded (kind, dtype, pairs, T, H, V, chunk_pairs): sequence lengths
+    off the 256-row tile grid, so pairs straddle row tiles inside a chunk."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(count):
+        B = int(rng.integers(1, 6))
+        out.append((str(rng.choice(["simpo", "cpo", "dpo", "orpo"])), str(rng.choice(["bf16", "f32"])),
+                    B, int(rng.integers(2, 300)), 8 * int(rng.integers(1, 49)),
+                    int(rng.integers(2, 4000)), int(rng.integers(1, B + 1))))
+    return out
+
+
+@pytest.mark.parametrize("kind,dtype,B,T,H,V,chunk_pairs", _random_pair_shapes(8, 20261205))
+def test_pair_random_shapes(kind, dtype, B, T, H, V, chunk_pairs):
+    inp = datagen.make_pairs(B, T, H, V, dtype, seed=B * 1000 + T + V)
+    ref = _ref_logps(B, T) if kind == "dpo" else None
+    out = _run(kind, inp, B, chunk_pairs, ref)
+    _check(out, _oracle(kind, inp, B, ref), kind, dtype)
+
+
 def test_pair_forward_only():
     inp = datagen.make_pairs(3, 64, 128, 700, "bf16", seed=9)
     for kind in ("simpo", "cpo"):
