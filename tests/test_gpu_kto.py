@@ -70,6 +70,31 @@ def test_kto_parity(dtype, S, T, H, V, chunk_seqs):
     check_loss(fwd["loss"], r.loss, dtype)
 
 
+def _random_kto_shapes(count, seed):
+    """Seeded (dtype, sequences, T, H, V, chunk_seqs); chunk 0 lets the
+    planner choose."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(count):
+        S = int(rng.integers(1, 9))
+        out.append((str(rng.choice(["bf16", "f32"])), S, int(rng.integers(2, 260)),
+                    8 * int(rng.integers(1, 41)), int(rng.integers(2, 3500)),
+                    int(rng.integers(0, S + 1))))
+    return out
+
+
+@pytest.mark.parametrize("dtype,S,T,H,V,chunk_seqs", _random_kto_shapes(6, 20261206))
+def test_kto_random_shapes(dtype, S, T, H, V, chunk_seqs):
+    inp, des, R = datagen.make_unpaired(S, T, H, V, dtype, seed=S * 1000 + T + V)
+    out = _run(inp, des, R, S, chunk_seqs)
+    r = oracle.kto(inp.X_f64(), inp.W_f64(), inp.labels, S, des.astype(bool), R.astype(np.float64),
+                   II, **P)
+    check_loss(out["loss"], r.loss, dtype)
+    _check_seq(out, r, dtype)
+    check_grad(out["dX_t"].double().cpu().numpy(), r.dX, dtype, "dX")
+    check_grad(out["dW_t"].double().cpu().numpy(), r.dW, dtype, "dW")
+
+
 def test_kto_module_with_reference_head():
     S, T, H, V = 5, 40, 64, 300
     inp, des, _ = datagen.make_unpaired(S, T, H, V, "f32", seed=61)
