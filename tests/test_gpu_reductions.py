@@ -66,6 +66,33 @@ def test_reduction(kind, N, H, V, chunk, reduction):
     assert np.all(dX[~valid] == 0.0)
 
 
+def _random_ex_cases(count, seed):
+    """Seeded (kind, N, H, V, chunk, reduction, accumulate) off the tile grids."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(count):
+        kind = str(rng.choice(["bf16", "f32"]))
+        N = int(rng.integers(1, 1200))
+        H = 8 * int(rng.integers(1, 65)) if kind == "bf16" else int(rng.integers(1, 300))
+        out.append((kind, N, H, int(rng.integers(1, 4000)), int(rng.integers(0, N + 1)),
+                    str(rng.choice(["mean", "sum", "none"])), bool(rng.integers(0, 2))))
+    return out
+
+
+@pytest.mark.parametrize("kind,N,H,V,chunk,reduction,acc", _random_ex_cases(6, 20261207))
+def test_ex_random_shapes(kind, N, H, V, chunk, reduction, acc):
+    inp = datagen.make_custom(N, H, V, kind, seed=5 * N + V, ignore_frac=0.1)
+    gr = _grad_rows(N, N + 1) if reduction == "none" else None
+    dW0 = np.random.default_rng(V).standard_normal((V, H)).astype(np.float32) * 1e-3 if acc else None
+    loss, dX, dW, rl, lp = _run_ex(inp, chunk, reduction, gr, dW0)
+    r = oracle.flce_ex(inp.X_f64(), inp.W_f64(), inp.labels, II, reduction,
+                       grad_rows=None if gr is None else gr.astype(np.float64))
+    check_loss(loss, r.loss, kind)
+    check_grad(dX, r.dX, kind, "dX")
+    # an accumulated result is measured on dL/dW's own scale
+    check_grad(dW - (dW0.astype(np.float64) if acc else 0.0), r.dW, kind, "dW")
+
+
 def test_accumulate_into_dw():
     inp = datagen.make_custom(600, 512, 3000, "bf16", seed=17, ignore_frac=0.1)
     dW0 = np.random.default_rng(5).standard_normal((3000, 512)).astype(np.float32) * 1e-3
