@@ -170,8 +170,11 @@ def timed_steps(step, steps, chunks, H, V, workload):
     around every launch, then `steps` timed steps with events around the
     dominant kernel class's launches only (its live duration for the
     roofline; about 50 event pairs per step would cost the stream a
-    fraction of a millisecond).  Returns (ms per timed step, the kernels
-    table, the roofline, the last step's result)."""
+    fraction of a millisecond).  Each step ends in the call's own
+    synchronisation (the loss comes back to the host), so the host clock
+    also times every step on its own.  Returns (ms per timed step, the
+    median step in ms, the kernels table, the roofline, the last step's
+    result)."""
     import torch
     import linear_cross_entropy_04_amd as fl
     fl.flce_profile_select(None)
@@ -185,15 +188,19 @@ def timed_steps(step, steps, chunks, H, V, workload):
     fl.flce_profile_select([dom])
     fl.flce_profile_read()
     torch.cuda.synchronize()
+    each = []
     t0 = time.perf_counter()
     for _ in range(steps):
+        t1 = time.perf_counter()
         res = step()
+        each.append(time.perf_counter() - t1)
     torch.cuda.synchronize()
     ms = 1e3 * (time.perf_counter() - t0) / steps
     prof = fl.flce_profile_read()
     fl.flce_profile_enable(False)
     fl.flce_profile_select(None)
-    return ms, kernels, roofline(dom, prof[dom], steps, chunks, H, V, workload), res
+    median = 1e3 * sorted(each)[len(each) // 2]
+    return ms, median, kernels, roofline(dom, prof[dom], steps, chunks, H, V, workload), res
 
 
 def copy_reference(mib, dev):
@@ -334,13 +341,14 @@ def bench_orpo(args):
         loss, nll = step()
     torch.cuda.synchronize()
     chunks = [2 * chunk_pairs * T] * (B // chunk_pairs)
-    ms, kernels, roof, (loss, nll) = timed_steps(step, args.steps, chunks, H, V,
-                                                 f"llama3-8b-head-{kind}")
+    ms, med, kernels, roof, (loss, nll) = timed_steps(step, args.steps, chunks, H, V,
+                                                      f"llama3-8b-head-{kind}")
     tflops = 6.0 * N * H * V / (ms * 1e-3) / 1e12
     out = {
         "metric": f"{kind.upper()} fused-linear preference loss fwd+bwd tokens/s, Llama-3-8B head",
         "value": round(N / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "ms_per_step_median": round(med, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded; X ~ N(0,1), W ~ N(0,0.02^2); per pair a shared prompt of "
                 "T/8..T/2 unscored tokens, per sequence 0..T/4 unscored padding tokens, "
@@ -420,12 +428,13 @@ def bench_kto(args):
         loss = step()
     torch.cuda.synchronize()
     chunks = [chunk_seqs * T] * (S // chunk_seqs)
-    ms, kernels, roof, loss = timed_steps(step, args.steps, chunks, H, V, "llama3-8b-head-kto")
+    ms, med, kernels, roof, loss = timed_steps(step, args.steps, chunks, H, V, "llama3-8b-head-kto")
     tflops = 6.0 * N * H * V / (ms * 1e-3) / 1e12
     out = {
         "metric": "KTO fused-linear preference loss fwd+bwd tokens/s, Llama-3-8B head",
         "value": round(N / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "ms_per_step_median": round(med, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded; X ~ N(0,1), W ~ N(0,0.02^2); per sequence T/8..T/2 prompt "
                 "and 0..T/4 padding tokens unscored, uniform response labels, half desirable, "
@@ -544,7 +553,7 @@ def main():
         loss = step()
     torch.cuda.synchronize()
     chunks = [min(C, N - c0) for c0 in range(0, N, C)]
-    ms, kernels, roof, loss = timed_steps(step, args.steps, chunks, H, V, wl.name)
+    ms, med, kernels, roof, loss = timed_steps(step, args.steps, chunks, H, V, wl.name)
 
     # the same steps without events, to show what the event records cost
     torch.cuda.synchronize()
@@ -577,6 +586,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "ms_per_step_median": round(med, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
